@@ -1,0 +1,188 @@
+"""CPU fp64 oracle for block-sparse masked attention (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package. The product path never does.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over independent
+rows); this module builds it with gcc and wraps it with ctypes. Definitions and
+the passages they follow are cited in ``oracle.c``:
+
+* ``attention``   -- softmax(Q K^T * scale + mask bias) V per row, optional
+  tanh soft-cap on the scaled score, O = 0 and lse = -inf for a row with no
+  live key.
+* ``block_mask``  -- 128x128 block classification by brute force over every
+  in-range pair: skip / partial / full, with ascending index lists padded by 0.
+* ``count_live``  -- number of live (query, key) pairs of a mask.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against values the
+pages print, closed forms, invariances and library routines.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+
+NONE, CAUSAL, SLIDING, DOCUMENT = 0, 1, 2, 3
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle C source file into a shared library at ``out``."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+           "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    """Compile oracle.c into oracle/_build/liboracle.so (always rebuilds)."""
+    return compile_source(SOURCE, _LIB_PATH)
+
+
+def _ptr(a: Optional[np.ndarray], ctype):
+    if a is None:
+        return ctypes.POINTER(ctype)()
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _doc(doc) -> Optional[np.ndarray]:
+    return None if doc is None else np.ascontiguousarray(doc, dtype=np.int32)
+
+
+class Oracle:
+    """ctypes front end over one compiled copy of the oracle."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        i64, i32p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_live.restype = ctypes.c_int
+        lib.oracle_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64]
+        lib.oracle_count_live.restype = i64
+        lib.oracle_count_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64]
+        lib.oracle_block_mask.restype = ctypes.c_int
+        lib.oracle_block_mask.argtypes = [ctypes.c_int, i64, i32p, i64, i64, i64,
+                                          i32p, i32p, i32p, i32p]
+        lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [f64p, f64p, f64p, i64, i64, i64, i64, i64, i64,
+                                         ctypes.c_int, i64, i32p, ctypes.c_double,
+                                         ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64,
+                                         f64p, f64p]
+        self._lib = lib
+
+    @staticmethod
+    def _check_doc(kind, d, L, S):
+        if kind == DOCUMENT and (d is None or len(d) < max(L, S)):
+            raise ValueError("document kind needs ids for max(L, S) positions")
+
+    def num_threads(self) -> int:
+        return int(self._lib.oracle_num_threads())
+
+    def live(self, kind: int, i: int, j: int, window: int = 0, doc=None) -> bool:
+        d = _doc(doc)
+        return bool(self._lib.oracle_live(kind, window, _ptr(d, ctypes.c_int32), i, j))
+
+    def count_live(self, kind: int, L: int, S: int, window: int = 0, doc=None) -> int:
+        d = _doc(doc)
+        self._check_doc(kind, d, L, S)
+        return int(self._lib.oracle_count_live(kind, window, _ptr(d, ctypes.c_int32), L, S))
+
+    def block_mask(self, kind: int, L: int, S: int, window: int = 0, doc=None, block: int = 128):
+        """(kv_num_blocks [nq], kv_indices [nq,nk], full_kv_num_blocks [nq],
+        full_kv_indices [nq,nk]) as int32 arrays."""
+        d = _doc(doc)
+        self._check_doc(kind, d, L, S)
+        nq, nk = -(-L // block), -(-S // block)
+        kv_num = np.zeros(nq, np.int32)
+        kv_idx = np.zeros((nq, nk), np.int32)
+        full_num = np.zeros(nq, np.int32)
+        full_idx = np.zeros((nq, nk), np.int32)
+        rc = self._lib.oracle_block_mask(kind, window, _ptr(d, ctypes.c_int32), L, S, block,
+                                         _ptr(kv_num, ctypes.c_int32), _ptr(kv_idx, ctypes.c_int32),
+                                         _ptr(full_num, ctypes.c_int32),
+                                         _ptr(full_idx, ctypes.c_int32))
+        if rc != 0:
+            raise ValueError("oracle_block_mask rejected its arguments")
+        return kv_num, kv_idx, full_num, full_idx
+
+    def attention(self, q, k, v, kind: int, scale: float, window: int = 0, doc=None,
+                  softcap: float = 0.0, rows=None):
+        """fp64 masked softmax attention.
+
+        q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev] (any float dtype; converted to
+        fp64 exactly). Returns (out, lse): for rows=None, out [B,H,L,Ev] and
+        lse [B,H,L]; otherwise out [len(rows), Ev] and lse [len(rows)] for the
+        flat row ids (b*H + h)*L + i.
+        """
+        q = np.ascontiguousarray(q, dtype=np.float64)
+        k = np.ascontiguousarray(k, dtype=np.float64)
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        B, H, L, E = q.shape
+        S, Ev = k.shape[2], v.shape[3]
+        if k.shape != (B, H, S, E) or v.shape[:3] != (B, H, S):
+            raise ValueError("q/k/v shapes disagree")
+        d = _doc(doc)
+        self._check_doc(kind, d, L, S)
+        if rows is None:
+            n, rows_arr = B * H * L, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            if rows_arr.size and (rows_arr.min() < 0 or rows_arr.max() >= B * H * L):
+                raise ValueError("row id out of range")
+            n = rows_arr.size
+        out = np.zeros((n, Ev), np.float64)
+        lse = np.zeros(n, np.float64)
+        rc = self._lib.oracle_attention(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                        _ptr(v, ctypes.c_double), B, H, L, S, E, Ev, kind, window,
+                                        _ptr(d, ctypes.c_int32), softcap, scale,
+                                        _ptr(rows_arr, ctypes.c_int64), n,
+                                        _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+        if rc != 0:
+            raise RuntimeError("oracle_attention failed")
+        if rows is None:
+            return out.reshape(B, H, L, Ev), lse.reshape(B, H, L)
+        return out, lse
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (built on first use if missing or stale)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def live(kind, i, j, window=0, doc=None):
+    return default().live(kind, i, j, window, doc)
+
+
+def count_live(kind, L, S, window=0, doc=None):
+    return default().count_live(kind, L, S, window, doc)
+
+
+def block_mask(kind, L, S, window=0, doc=None, block=128):
+    return default().block_mask(kind, L, S, window, doc, block)
+
+
+def attention(q, k, v, kind, scale, window=0, doc=None, softcap=0.0, rows=None):
+    return default().attention(q, k, v, kind, scale, window, doc, softcap, rows)

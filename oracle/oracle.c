@@ -1,0 +1,197 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for block-sparse masked attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or constant with the HIP library, and includes nothing from it.
+ *
+ * What it computes, and where the definition comes from:
+ *
+ *  - The attention definition: O = softmax(Q K^T * scale + B) V, with B = 0 on
+ *    live pairs and -inf on masked ones, applied in four steps (score table,
+ *    scale, add the mask bias, softmax then mix V). Page "SDPA replaces
+ *    hand-written attention" (qiita GeneLab_999), section 1, the Attention
+ *    equation and the four steps listed under it. Default scale 1/sqrt(E) is
+ *    the caller's business; this function takes scale explicitly.
+ *
+ *  - The mask rules (all return "live"):
+ *      causal:   q_idx >= kv_idx
+ *      sliding:  q_idx >= kv_idx and q_idx - kv_idx < W
+ *      document: q_idx >= kv_idx and doc[q_idx] == doc[kv_idx]
+ *    Page "FlexAttention on Apple Silicon: block masks" (dreaming.press),
+ *    sections "Mask 1: causal", "Mask 2: sliding-window causal",
+ *    "Mask 3: document-packed".
+ *
+ *  - The score_mod soft-cap s <- c * tanh(s / c), applied to the scaled score
+ *    of every pair; the mask then removes dead pairs. Same page, section
+ *    "Bonus: a score_mod for soft-capping" (score_mod changes the value, the
+ *    mask decides liveness; sparsity from the mask, score_mod on survivors).
+ *
+ *  - A row with no live key yields O = 0 and logsumexp = -inf, the
+ *    fully-masked-row behaviour that the SDPA page measures (section 4,
+ *    pitfall 1, the "all rows masked" aside: zeros, not NaN).
+ *
+ *  - The 128x128 BlockMask: per query block, kv blocks with no live pair are
+ *    skipped, blocks whose every pair is live are "full", the rest "partial".
+ *    Page "FlexAttention on MPS vs SDPA" (qiita kiarina), data-flow section
+ *    (BlockMask groups tokens into 128x128 blocks and skips unneeded blocks);
+ *    "FlexAttention on Apple Silicon", closing section (only fully masked
+ *    blocks can be skipped; causal leaves blocks partially live).
+ *    Here each block is classified by brute force: every in-range pair is
+ *    evaluated with the predicate and counted.
+ *
+ * Arithmetic is fp64 throughout (libm exp, tanh, log). Rows are independent;
+ * OpenMP spreads whole rows over threads and changes no arithmetic order
+ * inside a row.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_NONE 0
+#define ORACLE_CAUSAL 1
+#define ORACLE_SLIDING 2
+#define ORACLE_DOCUMENT 3
+
+/* The mask predicate: 1 when query i may attend to key j. */
+static int live(int kind, int64_t window, const int32_t* doc, int64_t i, int64_t j) {
+  switch (kind) {
+    case ORACLE_NONE:
+      return 1;
+    case ORACLE_CAUSAL:
+      return i >= j;
+    case ORACLE_SLIDING:
+      return i >= j && (i - j) < window;
+    case ORACLE_DOCUMENT:
+      return i >= j && doc[i] == doc[j];
+    default:
+      return 0;
+  }
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Evaluate the predicate itself (used by the tests to count live pairs). */
+int oracle_live(int kind, int64_t window, const int32_t* doc, int64_t i, int64_t j) {
+  return live(kind, window, doc, i, j);
+}
+
+/* Number of live pairs over [0,L) x [0,S). */
+int64_t oracle_count_live(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S) {
+  int64_t total = 0;
+#pragma omp parallel for reduction(+ : total) schedule(dynamic, 16)
+  for (int64_t i = 0; i < L; ++i) {
+    int64_t c = 0;
+    for (int64_t j = 0; j < S; ++j) c += live(kind, window, doc, i, j);
+    total += c;
+  }
+  return total;
+}
+
+/*
+ * Brute-force BlockMask. Outputs (caller-allocated, int32):
+ *   kv_num[nq], kv_idx[nq*nk]         partial blocks, ascending, pad 0
+ *   full_num[nq], full_idx[nq*nk]     full blocks, ascending, pad 0
+ * with nq = ceil(L/bs), nk = ceil(S/bs). A block is full only when all
+ * bs*bs of its pairs are in range and live. Returns 0, or -1 on bad sizes.
+ */
+int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S,
+                      int64_t bs, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
+                      int32_t* full_idx) {
+  if (L < 0 || S < 0 || bs <= 0) return -1;
+  int64_t nq = (L + bs - 1) / bs, nk = (S + bs - 1) / bs;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t qb = 0; qb < nq; ++qb) {
+    int32_t np = 0, nf = 0;
+    for (int64_t t = 0; t < nk; ++t) {
+      kv_idx[qb * nk + t] = 0;
+      full_idx[qb * nk + t] = 0;
+    }
+    for (int64_t kb = 0; kb < nk; ++kb) {
+      int64_t count = 0;
+      for (int64_t i = qb * bs; i < (qb + 1) * bs && i < L; ++i)
+        for (int64_t j = kb * bs; j < (kb + 1) * bs && j < S; ++j)
+          count += live(kind, window, doc, i, j);
+      if (count == 0) continue;
+      if (count == bs * bs)
+        full_idx[qb * nk + nf++] = (int32_t)kb;
+      else
+        kv_idx[qb * nk + np++] = (int32_t)kb;
+    }
+    kv_num[qb] = np;
+    full_num[qb] = nf;
+  }
+  return 0;
+}
+
+/*
+ * Masked softmax attention, fp64, for a list of rows.
+ *   q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev]: contiguous fp64.
+ *   rows: flat row ids r = (b*H + h)*L + i, or NULL for all B*H*L rows.
+ *   out [nrows, Ev], lse [nrows] (natural log; -inf for a row with no live key).
+ *   softcap > 0 applies s <- softcap * tanh(s / softcap) to the scaled score.
+ * Returns 0, or -1 on bad sizes / allocation failure.
+ */
+int oracle_attention(const double* q, const double* k, const double* v, int64_t B, int64_t H,
+                     int64_t L, int64_t S, int64_t E, int64_t Ev, int kind, int64_t window,
+                     const int32_t* doc, double softcap, double scale, const int64_t* rows,
+                     int64_t nrows, double* out, double* lse) {
+  if (B < 0 || H < 0 || L < 0 || S < 0 || E <= 0 || Ev <= 0) return -1;
+  if (rows == NULL) nrows = B * H * L;
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (s == NULL) failed = 1;
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t n = 0; n < nrows; ++n) {
+      if (s == NULL) continue;
+      int64_t r = rows ? rows[n] : n;
+      int64_t bh = r / L, i = r % L;
+      const double* qi = q + r * E;
+      const double* kh = k + bh * S * E;
+      const double* vh = v + bh * S * Ev;
+      double* o = out + n * Ev;
+
+      /* Step 1-3: scores, scale, score_mod, mask. */
+      double m = -INFINITY;
+      for (int64_t j = 0; j < S; ++j) {
+        double dot = 0.0;
+        for (int64_t e = 0; e < E; ++e) dot += qi[e] * kh[j * E + e];
+        double sc = dot * scale;
+        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
+        if (!live(kind, window, doc, i, j)) sc = -INFINITY;
+        s[j] = sc;
+        if (sc > m) m = sc;
+      }
+      /* Step 4: softmax, then mix V. */
+      for (int64_t e = 0; e < Ev; ++e) o[e] = 0.0;
+      if (m == -INFINITY) {
+        lse[n] = -INFINITY;
+        continue;
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < S; ++j) {
+        double w = exp(s[j] - m); /* exp(-inf) = 0 for masked pairs */
+        l += w;
+        if (w != 0.0)
+          for (int64_t e = 0; e < Ev; ++e) o[e] += w * vh[j * Ev + e];
+      }
+      for (int64_t e = 0; e < Ev; ++e) o[e] /= l;
+      lse[n] = m + log(l);
+    }
+    free(s);
+  }
+  return failed ? -1 : 0;
+}

@@ -1,0 +1,354 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``check_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with the pages, a closed form, an invariance the pages state,
+or an independent library routine. ``test_oracle_pins.py`` runs them on the
+real oracle; ``test_oracle_mutants.py`` runs them on deliberately broken copies
+to show that each plausible mistake fails at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+NONE, CAUSAL, SLIDING, DOCUMENT = 0, 1, 2, 3
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------------------
+# Block mask and predicate pins
+# ---------------------------------------------------------------------------
+
+def check_flex_table_densities(orc, max_S=32768):
+    """Token and block densities of the FlexAttention-on-MPS results table
+    (causal and sliding-window rows, 128x128 blocks), to the printed 2 decimals."""
+    g = _golden("flex_mps_densities.json")
+    for row in g["rows"]:
+        S, W = row["S"], row["W"]
+        if S > max_S:
+            continue
+        kind, win = (CAUSAL, 0) if row["pattern"] == "causal" else (SLIDING, W)
+        live = orc.count_live(kind, S, S, win)
+        assert round(100.0 * live / (S * S), 2) == row["token_pct"], (row, live)
+        kv_num, _, full_num, _ = orc.block_mask(kind, S, S, win, block=g["block"])
+        nb = -(-S // g["block"])
+        blocks = int(kv_num.sum() + full_num.sum())
+        assert round(100.0 * blocks / (nb * nb), 2) == row["block_pct"], (row, blocks)
+
+
+def check_live_pair_closed_forms(orc):
+    """Live pairs: causal S(S+1)/2; window W*S - W(W-1)/2 (W <= S);
+    document-causal sum over documents of n(n+1)/2; none L*S."""
+    for S in (1, 7, 128, 1000):
+        assert orc.count_live(CAUSAL, S, S) == S * (S + 1) // 2
+        assert orc.count_live(NONE, S, S + 3) == S * (S + 3)
+        for W in sorted({w for w in (1, 2, 37, S) if w <= S}):
+            assert orc.count_live(SLIDING, S, S, W) == W * S - W * (W - 1) // 2, (S, W)
+    bounds = (100, 190, 191)
+    doc = wl.document_ids(300, bounds)
+    sizes = np.diff([0, *bounds, 300])
+    assert orc.count_live(DOCUMENT, 300, 300, doc=doc) == int(sum(n * (n + 1) // 2 for n in sizes))
+
+
+def check_block_mask_worked_examples(orc):
+    """The 2x2 causal example and the 3-document totals (hand derivation)."""
+    g = _golden("block_mask_small.json")
+    kv_num, kv_idx, full_num, full_idx = orc.block_mask(CAUSAL, 256, 256)
+    ex = g["causal_256"]
+    assert kv_num.tolist() == ex["kv_num_blocks"]
+    assert kv_idx.tolist() == ex["kv_indices"]
+    assert full_num.tolist() == ex["full_kv_num_blocks"]
+    assert full_idx.tolist() == ex["full_kv_indices"]
+    d = g["document_8192"]
+    doc = wl.document_ids(8192, tuple(d["bounds"]))
+    kv_num, _, full_num, _ = orc.block_mask(DOCUMENT, 8192, 8192, doc=doc)
+    assert int(full_num.sum()) == d["full_total"]
+    assert int(kv_num.sum()) == d["partial_total"]
+
+
+def check_block_mask_window_closed_form(orc):
+    """For W = 128*w the pair offsets i-j of block offset d = qb-kb span
+    [128d-127, 128d+127]; the block is full iff that range sits inside [0, W-1]
+    (1 <= d <= w-1) and partial iff it only overlaps (d == 0 or d == w)."""
+    S = 2048
+    nb = S // 128
+    for w in (1, 2, 3):
+        kv_num, kv_idx, full_num, full_idx = orc.block_mask(SLIDING, S, S, 128 * w)
+        for qb in range(nb):
+            full = [kb for kb in range(nb) if 1 <= qb - kb <= w - 1]
+            part = [kb for kb in range(nb) if qb - kb in (0, w)]
+            assert full_idx[qb, : full_num[qb]].tolist() == full
+            assert kv_idx[qb, : kv_num[qb]].tolist() == part
+            assert not full_idx[qb, full_num[qb]:].any() and not kv_idx[qb, kv_num[qb]:].any()
+
+
+def check_block_mask_ragged_tail(orc):
+    """Lengths not multiple of 128: out-of-range pairs are absent, so a tail
+    block can never be full; kind none gives full interior blocks only."""
+    L, S = 300, 200
+    kv_num, kv_idx, full_num, full_idx = orc.block_mask(NONE, L, S)
+    # blocks are (qb in 0..2) x (kb in 0..1); only (0,0) and (1,0) are whole.
+    assert full_num.tolist() == [1, 1, 0]
+    assert kv_num.tolist() == [1, 1, 2]
+    assert kv_idx[2].tolist() == [0, 1]
+
+
+# ---------------------------------------------------------------------------
+# Attention pins
+# ---------------------------------------------------------------------------
+
+def _weights(orc, scores, kind=NONE, window=0, doc=None, softcap=0.0):
+    """Attention weights of one row per query by the V = identity trick:
+    with E=1, q=1, k_j = s_j and scale=1 the scores are s_j, and with V = I
+    the output row is exactly the weight vector."""
+    L, S = scores.shape
+    k = np.zeros((1, 1, S, 1))
+    out = np.zeros((L, S))
+    lses = np.zeros(L)
+    # scores differ per row, so run one row (one query) at a time
+    for i in range(L):
+        k[0, 0, :, 0] = scores[i]
+        qi = np.ones((1, 1, L, 1))
+        o, lse = orc.attention(qi, k, np.eye(S)[None, None], kind, 1.0, window, doc, softcap,
+                               rows=[i])
+        out[i] = o[0]
+        lses[i] = lse[0]
+    return out, lses
+
+
+def check_tiled_softmax_equivalence(orc):
+    """FlashAttention page: softmax over 4096 values computed tile by tile with
+    a running max and running sum equals the plain softmax to double rounding
+    (max error <= ~2e-18 on that page). The tiled form here is written
+    independently of the oracle and compared with the oracle's weights."""
+    g = _golden("tiled_softmax_error.json")
+    n = g["n_values"]
+    s = _rand(n, 3)
+    w_or, _ = _weights(orc, s[None, :])
+    w_or = w_or[0]
+    for tile in g["tiles"]:
+        m, l = -math.inf, 0.0
+        chunks = []
+        for t0 in range(0, n, tile):
+            x = s[t0:t0 + tile]
+            m_new = max(m, float(x.max()))
+            l = l * math.exp(m - m_new) + float(np.exp(x - m_new).sum())
+            chunks = [(c, mm) for c, mm in chunks] + [(x, m_new)]
+            m = m_new
+        w_tiled = np.concatenate([np.exp(x - mm) * math.exp(mm - m) for x, mm in chunks]) / l
+        err = np.abs(w_tiled - w_or)
+        assert err.max() <= 10 * max(g["max_abs_err"]), (tile, err.max())
+        assert err.mean() <= 10 * max(g["mean_abs_err"]), (tile, err.mean())
+
+
+def check_weights_are_a_distribution(orc):
+    """Each non-empty row's weights sum to 1 and dead pairs weigh exactly 0."""
+    L = S = 40
+    scores = _rand((L, S), 5, 3.0)
+    doc = wl.document_ids(S, (13, 29))
+    for kind, W in ((NONE, 0), (CAUSAL, 0), (SLIDING, 5), (DOCUMENT, 0)):
+        w, _ = _weights(orc, scores, kind, W, doc if kind == DOCUMENT else None)
+        for i in range(L):
+            dead = [j for j in range(S) if not _live_py(kind, W, doc, i, j)]
+            assert np.all(w[i, dead] == 0.0), (kind, i)
+            assert abs(w[i].sum() - 1.0) <= 1e-15, (kind, i, w[i].sum())
+
+
+def _live_py(kind, W, doc, i, j):
+    # restated from the page's mask_mod functions for the dead-pair check
+    if kind == NONE:
+        return True
+    if kind == CAUSAL:
+        return i >= j
+    if kind == SLIDING:
+        return i >= j and i - j < W
+    return i >= j and doc[i] == doc[j]
+
+
+def check_uniform_v(orc):
+    """V rows all equal to v gives O_i = v for every row with a live key."""
+    B, H, L, S, E = 1, 2, 70, 70, 8
+    q, k = _rand((B, H, L, E), 7), _rand((B, H, S, E), 8)
+    vrow = _rand(E, 9)
+    v = np.broadcast_to(vrow, (B, H, S, E)).copy()
+    doc = wl.document_ids(S, (20, 50))
+    for kind, W, cap in ((NONE, 0, 0.0), (CAUSAL, 0, 0.0), (SLIDING, 9, 0.0),
+                         (DOCUMENT, 0, 30.0)):
+        o, _ = orc.attention(q, k, v, kind, 0.35, W, doc if kind == DOCUMENT else None, cap)
+        assert np.abs(o - vrow).max() <= 1e-14, kind
+
+
+def check_window_one_is_identity(orc):
+    """Window W=1 leaves each query only its own key: O_i = V_i exactly and
+    lse_i equals that single score."""
+    B, H, L, E = 1, 2, 50, 16
+    q, k, v = _rand((B, H, L, E), 10), _rand((B, H, L, E), 11), _rand((B, H, L, E), 12)
+    o, lse = orc.attention(q, k, v, SLIDING, 0.25, 1)
+    assert np.array_equal(o, v)
+    single = 0.25 * np.einsum("bhle,bhle->bhl", q, k)
+    assert np.abs(lse - single).max() <= 1e-13
+
+
+def check_causal_first_row(orc):
+    """Row 0 of a causal mask sees key 0 only: O_0 = V_0 exactly."""
+    q, k, v = _rand((1, 3, 20, 8), 13), _rand((1, 3, 20, 8), 14), _rand((1, 3, 20, 8), 15)
+    o, lse = orc.attention(q, k, v, CAUSAL, 0.5)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+    assert np.abs(lse[:, :, 0] - 0.5 * (q[:, :, 0] * k[:, :, 0]).sum(-1)).max() <= 1e-13
+
+
+def check_two_key_closed_form(orc):
+    """E=2, q=(a,0), k1=(1,0), k2=(0,1): scores s1 = f(scale*a), s2 = f(0) = 0
+    with f the identity or the soft-cap c*tanh(x/c) on the scaled score.
+    Then O = sigmoid(s1) v1 + sigmoid(-s1) v2 and lse = log(1 + e^{s1})."""
+    v1, v2 = np.array([1.5, -2.0, 0.25]), np.array([-0.5, 3.0, 1.0])
+    k = np.array([[1.0, 0.0], [0.0, 1.0]])[None, None]
+    v = np.stack([v1, v2])[None, None]
+    for a, scale, cap in ((0.7, 1.0, 0.0), (-3.0, 0.125, 0.0), (200.0, 0.5, 30.0),
+                          (-90.0, 0.5, 30.0), (4.0, 0.5, 30.0)):
+        q = np.array([[a, 0.0]])[None, None]
+        s1 = scale * a
+        if cap:
+            s1 = cap * math.tanh(s1 / cap)
+        w1 = 1.0 / (1.0 + math.exp(-s1))
+        o, lse = orc.attention(q, k, v, NONE, scale, softcap=cap)
+        want = w1 * v1 + (1.0 - w1) * v2
+        assert np.abs(o[0, 0, 0] - want).max() <= 1e-13, (a, scale, cap)
+        assert abs(lse[0, 0, 0] - np.logaddexp(0.0, s1)) <= 1e-13, (a, scale, cap)
+
+
+def check_scipy_softmax(orc):
+    """Small random cases against scipy.special.softmax of the masked, scaled
+    (and soft-capped) score table times V, for every mask kind; L != S."""
+    B, H, L, S, E, Ev = 2, 2, 9, 13, 5, 3
+    q, k, v = _rand((B, H, L, E), 16), _rand((B, H, S, E), 17), _rand((B, H, S, Ev), 18)
+    doc = wl.document_ids(S, (4, 10))
+    for kind, W, cap in ((NONE, 0, 0.0), (CAUSAL, 0, 0.0), (SLIDING, 3, 0.0),
+                         (DOCUMENT, 0, 0.0), (CAUSAL, 0, 1.5)):
+        scale = 0.6
+        sc = scale * np.einsum("bhle,bhse->bhls", q, k)
+        if cap:
+            sc = cap * np.tanh(sc / cap)
+        bias = np.array([[0.0 if _live_py(kind, W, doc, i, j) else -np.inf for j in range(S)]
+                         for i in range(L)])
+        want = scipy.special.softmax(sc + bias, axis=-1) @ v
+        want_lse = scipy.special.logsumexp(sc + bias, axis=-1)
+        o, lse = orc.attention(q, k, v, kind, scale, W, doc if kind == DOCUMENT else None, cap)
+        assert np.abs(o - want).max() <= 1e-14, kind
+        assert np.abs(lse - want_lse).max() <= 1e-13, kind
+
+
+def check_empty_rows(orc):
+    """A query with no live key returns zeros and lse = -inf (SDPA page,
+    fully-masked-row aside). L=8 > S=3 with W=2: rows 4..7 see nothing."""
+    q, k, v = _rand((1, 1, 8, 4), 19), _rand((1, 1, 3, 4), 20), _rand((1, 1, 3, 4), 21)
+    o, lse = orc.attention(q, k, v, SLIDING, 0.5, 2)
+    assert np.all(o[0, 0, 4:] == 0.0) and np.all(np.isneginf(lse[0, 0, 4:]))
+    assert np.all(np.isfinite(lse[0, 0, :4])) and np.abs(o[0, 0, :4]).sum() > 0
+
+
+def check_causal_prefix_invariance(orc):
+    """SDPA page, pitfall 3: causal row i equals unmasked attention of q_i over
+    keys 0..i (the one-token decode against a cache)."""
+    q, k, v = _rand((1, 2, 24, 8), 22), _rand((1, 2, 24, 8), 23), _rand((1, 2, 24, 8), 24)
+    o, lse = orc.attention(q, k, v, CAUSAL, 0.3)
+    for i in (0, 5, 23):
+        oi, li = orc.attention(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], NONE, 0.3)
+        assert np.abs(o[:, :, i] - oi[:, :, 0]).max() <= 1e-14
+        assert np.abs(lse[:, :, i] - li[:, :, 0]).max() <= 1e-14
+
+
+def check_sliding_equals_window_slice(orc):
+    """Window W: row i equals unmasked attention over keys i-W+1..i."""
+    W = 6
+    q, k, v = _rand((1, 2, 30, 8), 25), _rand((1, 2, 30, 8), 26), _rand((1, 2, 30, 8), 27)
+    o, _ = orc.attention(q, k, v, SLIDING, 0.3, W)
+    for i in (0, 3, 5, 6, 29):
+        lo = max(0, i - W + 1)
+        oi, _ = orc.attention(q[:, :, i:i + 1], k[:, :, lo:i + 1], v[:, :, lo:i + 1], NONE, 0.3)
+        assert np.abs(o[:, :, i] - oi[:, :, 0]).max() <= 1e-14
+
+
+def check_document_isolation(orc):
+    """Block-mask page, document packing: no attention across documents, so the
+    packed result equals each document run alone with a causal mask."""
+    bounds = (11, 40)
+    S = 57
+    doc = wl.document_ids(S, bounds)
+    q, k, v = _rand((1, 2, S, 8), 28), _rand((1, 2, S, 8), 29), _rand((1, 2, S, 8), 30)
+    o, lse = orc.attention(q, k, v, DOCUMENT, 0.3, doc=doc)
+    edges = [0, *bounds, S]
+    for a, b in zip(edges[:-1], edges[1:]):
+        od, ld = orc.attention(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], CAUSAL, 0.3)
+        assert np.abs(o[:, :, a:b] - od).max() <= 1e-14
+        assert np.abs(lse[:, :, a:b] - ld).max() <= 1e-14
+
+
+def check_library_equivalence(orc):
+    """SDPA page, section 1: the hand-written matmul-softmax-matmul attention
+    and SDPA agree to ~1e-15 in fp64 and ~5e-7 in fp32 at (2,8,512,64).
+    The oracle is compared with that composition in torch fp64 (same bound,
+    with a small margin) and with torch fp32 (the fp32 bound)."""
+    g = _golden("sdpa_naive_equivalence.json")
+    B, H, L, E = g["shape"]
+    q, k, v = _rand((B, H, L, E), 31), _rand((B, H, L, E), 32), _rand((B, H, L, E), 33)
+    scale = 1.0 / math.sqrt(E)
+    for name, kind in (("none", NONE), ("causal", CAUSAL)):
+        o, _ = orc.attention(q, k, v, kind, scale)
+        for dt, bound in ((torch.float64, 4 * g["fp64_max_abs"][name]),
+                          (torch.float32, 4 * g["fp32_max_abs"][name])):
+            tq, tk, tv = (torch.from_numpy(x).to(dt) for x in (q, k, v))
+            sc = (tq @ tk.transpose(-2, -1).contiguous()) * scale
+            if kind == CAUSAL:
+                tri = torch.ones(L, L, dtype=torch.bool).tril()
+                sc = sc.masked_fill(~tri, float("-inf"))
+            ref = (torch.softmax(sc, dim=-1) @ tv).double().numpy()
+            assert np.abs(o - ref).max() <= bound, (name, dt, np.abs(o - ref).max())
+
+
+def check_softcap_limits(orc):
+    """The soft-cap bounds every score by c, and a huge c leaves scores as they are."""
+    q, k, v = _rand((1, 1, 12, 4), 34, 40.0), _rand((1, 1, 12, 4), 35, 40.0), _rand((1, 1, 12, 4), 36)
+    o1, l1 = orc.attention(q, k, v, NONE, 0.5, softcap=1e12)
+    o0, l0 = orc.attention(q, k, v, NONE, 0.5)
+    assert np.abs(o1 - o0).max() <= 1e-9 and np.abs(l1 - l0).max() <= 1e-9
+    _, lw = orc.attention(q, k, v, SLIDING, 0.5, 1, softcap=2.0)   # single key: lse = s'
+    assert np.all(np.abs(lw) <= 2.0) and np.abs(lw).max() > 1.9
+
+
+ALL_CHECKS = [
+    check_flex_table_densities,
+    check_live_pair_closed_forms,
+    check_block_mask_worked_examples,
+    check_block_mask_window_closed_form,
+    check_block_mask_ragged_tail,
+    check_tiled_softmax_equivalence,
+    check_weights_are_a_distribution,
+    check_uniform_v,
+    check_window_one_is_identity,
+    check_causal_first_row,
+    check_two_key_closed_form,
+    check_scipy_softmax,
+    check_empty_rows,
+    check_causal_prefix_invariance,
+    check_sliding_equals_window_slice,
+    check_document_isolation,
+    check_library_equivalence,
+    check_softcap_limits,
+]

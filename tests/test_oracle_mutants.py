@@ -1,0 +1,56 @@
+"""Each plausible mistake planted in a copy of the oracle (on the CPU) must
+fail at least one pin. This shows the pins constrain every part of the oracle:
+mask rules, block classification, scale, soft-cap order, normalisation, the
+logsumexp base, operand indexing and the empty-row convention."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("causal_direction", "      return i >= j;\n", "      return i <= j;\n"),
+    ("window_inclusive", "(i - j) < window", "(i - j) <= window"),
+    ("document_without_causal", "return i >= j && doc[i] == doc[j];", "return doc[i] == doc[j];"),
+    ("dropped_scale", "double sc = dot * scale;", "double sc = dot;"),
+    ("softcap_before_scale",
+     "double sc = dot * scale;\n        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);",
+     "double sc = dot;\n        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);\n"
+     "        sc *= scale;"),
+    ("lse_log2", "lse[n] = m + log(l);", "lse[n] = m + log2(l);"),
+    ("missing_normalisation", "for (int64_t e = 0; e < Ev; ++e) o[e] /= l;", ""),
+    ("transposed_k", "kh[j * E + e]", "kh[e * S + j]"),
+    ("reversed_v", "vh[j * Ev + e]", "vh[(S - 1 - j) * Ev + e]"),
+    ("full_threshold", "if (count == bs * bs)", "if (count * 2 >= bs * bs)"),
+    ("pad_minus_one", "      kv_idx[qb * nk + t] = 0;", "      kv_idx[qb * nk + t] = -1;"),
+    ("block_row_off_by_one", "i < (qb + 1) * bs && i < L", "i <= (qb + 1) * bs && i < L"),
+    ("empty_row_lse_zero", "        lse[n] = -INFINITY;\n        continue;",
+     "        lse[n] = 0.0;\n        continue;"),
+    ("max_not_subtracted_in_lse", "lse[n] = m + log(l);", "lse[n] = log(l);"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, name, old, new):
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique in oracle.c"
+    src = tmp_path / f"{name}.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.compile_source(str(src), str(tmp_path / f"lib{name}.so"))
+    orc = oracle.Oracle(lib)
+    failures = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, ValueError, RuntimeError, FloatingPointError) as e:
+            failures.append(check.__name__)
+            break
+    assert failures, f"mutant {name} passed every pin"
+    os.remove(lib)

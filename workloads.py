@@ -1,0 +1,127 @@
+"""Seeded synthetic workloads shared by the tests, the benchmark and smoke().
+
+This module holds only input generation: shapes, dtypes, mask recipes and
+seeded random tensors. It contains none of the attention arithmetic, so both
+the HIP path and the CPU oracle may take their inputs from here.
+
+Workloads (all B=1, E=64, layout [B, H, seq, E] contiguous, i.i.d. N(0,1)):
+
+* ``causal_256_f32`` -- H=2, L=S=256, fp32, causal (the small case).
+* ``causal_8192_bf16`` -- H=8, L=S=8192, bf16, causal. The FlexAttention
+  benchmark on Apple M1 Max ("FlexAttention on MPS vs SDPA", results table,
+  causal row) uses this shape: batch 1, 8 heads, head dim 64, bf16.
+* ``sliding_8192_w{64,256,1024,4096}_bf16`` -- the same shape with a
+  sliding-window causal mask, one workload per window of that table.
+* ``sliding_32768_w256_bf16`` -- H=8, L=S=32768, window 256 (the table's
+  last row).
+* ``document_8192_f16_softcap`` -- H=16, L=S=8192, fp16, document-packed
+  causal mask with ids 0 on [0,2048), 1 on [2048,5000), 2 on [5000,8192), and
+  a tanh soft-cap of 30 ("FlexAttention on Apple Silicon: block masks",
+  sections "Mask 3: document-packed" and "Bonus: a score_mod for soft-capping").
+
+Generation: ``numpy.random.default_rng(seed).standard_normal(shape, float32)``
+drawn for q, then k, then v, then rounded to the workload dtype with
+round-to-nearest-even (torch's CPU cast). Both sides read the rounded values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+# Mask kinds, numbered as in include/bsattn.h.
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_SLIDING_WINDOW = 2
+MASK_DOCUMENT = 3
+
+BLOCK = 128
+
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    L: int
+    S: int
+    E: int
+    dtype: str            # "f32" | "bf16" | "f16"
+    kind: int             # MASK_*
+    window: int = 0       # sliding-window size W (kind == MASK_SLIDING_WINDOW)
+    doc_bounds: tuple = ()  # document start offsets after the first (MASK_DOCUMENT)
+    softcap: float = 0.0  # 0 = no score_mod, else c in c*tanh(s/c)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _DTYPES[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.E)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("causal_256_f32", 1, 2, 256, 256, 64, "f32", MASK_CAUSAL),
+        Workload("causal_8192_bf16", 1, 8, 8192, 8192, 64, "bf16", MASK_CAUSAL),
+        Workload("sliding_8192_w64_bf16", 1, 8, 8192, 8192, 64, "bf16", MASK_SLIDING_WINDOW, 64),
+        Workload("sliding_8192_w256_bf16", 1, 8, 8192, 8192, 64, "bf16", MASK_SLIDING_WINDOW, 256),
+        Workload("sliding_8192_w1024_bf16", 1, 8, 8192, 8192, 64, "bf16", MASK_SLIDING_WINDOW, 1024),
+        Workload("sliding_8192_w4096_bf16", 1, 8, 8192, 8192, 64, "bf16", MASK_SLIDING_WINDOW, 4096),
+        Workload("sliding_32768_w256_bf16", 1, 8, 32768, 32768, 64, "bf16", MASK_SLIDING_WINDOW, 256),
+        Workload("document_8192_f16_softcap", 1, 16, 8192, 8192, 64, "f16", MASK_DOCUMENT, 0,
+                 (2048, 5000), 30.0),
+    ]
+}
+
+
+def document_ids(length: int, bounds: tuple) -> np.ndarray:
+    """int32 ids: 0 before bounds[0], 1 from bounds[0], 2 from bounds[1], ..."""
+    ids = np.zeros(length, dtype=np.int32)
+    for d, start in enumerate(bounds, start=1):
+        ids[start:] = d
+    return ids
+
+
+def make_qkv(w: Workload, seed: int = 0):
+    """Seeded q, k, v as CPU torch tensors of the workload dtype, [B,H,seq,E]."""
+    rng = np.random.default_rng(seed)
+    shapes = [(w.B, w.H, w.L, w.E), (w.B, w.H, w.S, w.E), (w.B, w.H, w.S, w.E)]
+    out = []
+    for shp in shapes:
+        x = rng.standard_normal(shp, dtype=np.float32)
+        out.append(torch.from_numpy(x).to(w.torch_dtype))
+    return tuple(out)
+
+
+def make_doc(w: Workload) -> Optional[np.ndarray]:
+    if w.kind != MASK_DOCUMENT:
+        return None
+    return document_ids(max(w.L, w.S), w.doc_bounds)
+
+
+def sample_rows(w: Workload, count: int, seed: int = 1234) -> np.ndarray:
+    """Flat row ids (b*H*L + h*L + i) for spot checks at full size.
+
+    Always includes the first and last row of every head plus the rows at
+    each 128-block boundary of head 0; the rest are drawn uniformly.
+    """
+    rng = np.random.default_rng(seed)
+    n = w.B * w.H * w.L
+    fixed = []
+    for bh in range(w.B * w.H):
+        fixed += [bh * w.L, bh * w.L + w.L - 1]
+    fixed += [min(i, w.L - 1) for i in range(0, w.L, BLOCK)]
+    fixed += [min(i + BLOCK - 1, w.L - 1) for i in range(0, w.L, BLOCK)]
+    extra = rng.integers(0, n, size=max(0, count - len(fixed)))
+    return np.unique(np.concatenate([np.asarray(fixed, dtype=np.int64), extra.astype(np.int64)]))
