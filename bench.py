@@ -1,0 +1,232 @@
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch: build the BlockMask
+(classification + schedule kernels) and run the fused forward, on the causal
+S=8192 workload (B=1, H=8, E=64, bf16, i.i.d. N(0,1) inputs). W untimed
+steps, then K steps timed between two device synchronisations. The forward
+kernel is also timed launch by launch with events on the stream it runs on,
+for the roofline figure. The second headline workload (sliding window 256
+over S=32768) is measured the same way and reported in the same line.
+
+Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
+(4 * E flops per unmasked (query, key) pair); ``forward_only`` has the
+forward kernel alone, which is what the FlexAttention-on-MPS table times.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_attention_35_amd as bsa  # noqa: E402
+import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "ms/forward and live-pair TFLOPS (% bf16 MFMA peak), S=8192 causal & S=32768 W=256"
+HEADLINE = "causal_8192_bf16"
+SECOND = "sliding_32768_w256_bf16"
+
+
+def live_pairs(w: wl.Workload) -> int:
+    """Live (query, key) pairs of one head from the closed forms of the rules."""
+    L, S = w.L, w.S
+    if w.kind == wl.MASK_CAUSAL and L == S:
+        return S * (S + 1) // 2
+    if w.kind == wl.MASK_SLIDING_WINDOW and L == S and w.window <= S:
+        W = w.window
+        return W * S - W * (W - 1) // 2
+    if w.kind == wl.MASK_DOCUMENT and L == S:
+        edges = [0, *w.doc_bounds, S]
+        return sum((b - a) * (b - a + 1) // 2 for a, b in zip(edges[:-1], edges[1:]))
+    if w.kind == wl.MASK_NONE:
+        return L * S
+    raise ValueError("no closed form for this workload")
+
+
+def algorithmic_bytes(w: wl.Workload) -> int:
+    """Read Q, K, V once, write O once and the fp32 logsumexp."""
+    esize = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
+    n = w.B * w.H
+    return n * (w.L * w.E * 2 + w.S * w.E * 2) * esize + n * w.L * 4
+
+
+def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
+    q, k, v = (x.to(dev) for x in wl.make_qkv(w, 0))
+    doc = wl.make_doc(w)
+    doc_t = torch.from_numpy(doc).to(dev) if doc is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.L, dtype=torch.float32, device=dev)
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None, document_id=doc_t,
+                               device=dev)
+    score_mod = "softcap" if w.softcap else None
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bm.rebuild()
+        if ev is not None:
+            ev[1].record()
+        bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
+                      scale=w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` whole steps between two synchronisations.
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Per-launch durations with events on the stream the kernels run on.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    mask_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    return dict(wall_ms=wall_ms, mask_ms=mask_ms, fwd_ms=fwd_ms)
+
+
+def summarize(w: wl.Workload, r):
+    flops = 4.0 * w.E * live_pairs(w) * w.B * w.H
+    fwd_avg = float(r["fwd_ms"].mean())
+    nbytes = algorithmic_bytes(w)
+    return {
+        "workload": w.name,
+        "ms_per_step": r["wall_ms"],
+        "step_tflops": flops / (r["wall_ms"] * 1e-3) / 1e12,
+        "forward_ms": {"mean": fwd_avg, "median": float(np.median(r["fwd_ms"])),
+                       "min": float(r["fwd_ms"].min()), "max": float(r["fwd_ms"].max())},
+        "forward_tflops": flops / (fwd_avg * 1e-3) / 1e12,
+        "forward_frac_bf16_peak": flops / (fwd_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "forward_gbs": nbytes / (fwd_avg * 1e-3) / 1e9,
+        "mask_build_ms": {"mean": float(r["mask_ms"].mean()), "median": float(np.median(r["mask_ms"]))},
+        "live_gflop": flops / 1e9,
+        "algorithmic_bytes": nbytes,
+    }
+
+
+def cpu_baseline(w: wl.Workload, budget_s: float):
+    """The fp64 oracle on a bounded, seeded sample of the workload's rows,
+    reported in live-pair TFLOPS of the rows it computed."""
+    import oracle
+
+    q, k, v = wl.make_qkv(w, 0)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    doc = wl.make_doc(w)
+    rng = np.random.default_rng(7)
+    n_rows = w.B * w.H * w.L
+
+    def live_in(rows):
+        i = rows % w.L
+        if w.kind == wl.MASK_CAUSAL:
+            return int((i + 1).sum())
+        if w.kind == wl.MASK_SLIDING_WINDOW:
+            return int(np.minimum(i + 1, w.window).sum())
+        raise ValueError("cpu baseline sample supports causal and sliding workloads")
+
+    probe = rng.choice(n_rows, size=64, replace=False)
+    t0 = time.perf_counter()
+    oracle.attention(qd, kd, vd, w.kind, w.scale, w.window, doc, w.softcap, rows=probe)
+    per_row = (time.perf_counter() - t0) / 64
+    count = int(min(n_rows, max(64, budget_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(n_rows, size=count, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(qd, kd, vd, w.kind, w.scale, w.window, doc, w.softcap, rows=rows)
+    secs = time.perf_counter() - t0
+    flops = 4.0 * w.E * live_in(rows)
+    return {"value": flops / secs / 1e12, "unit": "TFLOPS (live pairs)",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{count} of {n_rows} query rows of {w.name} drawn uniformly (seed 7), "
+                      f"fp64, {secs:.1f} s wall",
+            "seconds": secs}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--workloads", default=f"{HEADLINE},{SECOND}")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X; see the sharding note in the design)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    names = args.workloads.split(",")
+    results = {}
+    for n in names:
+        w = wl.WORKLOADS[n]
+        print(f"bench: {n} ...", file=sys.stderr, flush=True)
+        results[n] = summarize(w, run_workload(w, args.steps, args.warmup, dev))
+        print(f"bench: {n} forward {results[n]['forward_ms']['mean']:.4f} ms "
+              f"{results[n]['forward_tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
+
+    head = results[names[0]]
+    w = wl.WORKLOADS[names[0]]
+    line = {
+        "metric": METRIC,
+        "value": head["step_tflops"],
+        "unit": "TFLOPS (live pairs, whole step: mask build + forward)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) q/k/v rounded to the workload dtype",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "S": w.S, "E": w.E,
+                   "mask": "causal", "block": 128, "scale": w.scale},
+        "frac_bf16_peak": head["step_tflops"] / PEAK_BF16_TFLOPS,
+        "forward_only": {"ms": head["forward_ms"], "tflops": head["forward_tflops"],
+                         "frac_bf16_peak": head["forward_frac_bf16_peak"]},
+        "mask_build_ms": head["mask_build_ms"],
+        "roofline": {"bound": "mfma", "achieved": head["forward_tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": head["forward_tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": None,
+                     "kernel": "fwd16_kernel<bf16, causal>",
+                     "per_launch_flop": head["live_gflop"] * 1e9,
+                     "launch_ms": head["forward_ms"]["mean"]},
+        "workloads": results,
+    }
+    if SECOND in results:
+        s = results[SECOND]
+        line["sliding_32768_w256"] = {
+            "forward_ms": s["forward_ms"], "tflops": s["forward_tflops"],
+            "frac_bf16_peak": s["forward_frac_bf16_peak"], "gbs": s["forward_gbs"],
+            "frac_hbm_peak": s["forward_gbs"] / PEAK_HBM_GBS, "step_ms": s["ms_per_step"]}
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

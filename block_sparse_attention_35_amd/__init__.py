@@ -1,0 +1,242 @@
+"""Block-sparse fused attention forward for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libbsattn.so`` (C ABI in ``include/bsattn.h``).
+It only marshals arguments: torch tensors provide device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+    bm = create_block_mask("sliding_window", S, S, window=256)
+    out, lse = attention(q, k, v, bm, return_lse=True)
+
+Mask rules ("FlexAttention on Apple Silicon: block masks", sections Mask 1-3):
+``"none"``, ``"causal"`` (q >= kv), ``"sliding_window"`` (q >= kv and
+q - kv < window), ``"document"`` (q >= kv and same document id). score_mod:
+``None`` or ``"softcap"`` (c * tanh(s / c), same page, section "Bonus").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Union
+
+import torch
+
+__all__ = [
+    "BlockMask", "BsattnError", "create_block_mask", "attention", "num_blocks", "library_path",
+    "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libbsattn.so")
+
+# Values from include/bsattn.h.
+ATTN_OK = 0
+F32, BF16, F16 = 0, 1, 2
+MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
+SCORE_NONE, SCORE_SOFTCAP = 0, 1
+BLOCK_SIZE = 128
+
+_KINDS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "sliding_window": MASK_SLIDING_WINDOW,
+          "sliding": MASK_SLIDING_WINDOW, "document": MASK_DOCUMENT}
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"bsattn status {status}: {message}")
+        self.status = status
+
+
+class _BlockMaskStruct(ctypes.Structure):
+    _fields_ = [
+        ("kv_num_blocks", ctypes.c_void_p),
+        ("kv_indices", ctypes.c_void_p),
+        ("full_kv_num_blocks", ctypes.c_void_p),
+        ("full_kv_indices", ctypes.c_void_p),
+        ("schedule", ctypes.c_void_p),
+        ("q_len", ctypes.c_int32),
+        ("kv_len", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_q_blocks", ctypes.c_int32),
+        ("num_kv_blocks", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("document_id", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m block_sparse_attention_35_amd.build` "
+            "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, vp = ctypes.c_int32, ctypes.c_void_p
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.attn_num_blocks.restype = i32
+    lib.attn_num_blocks.argtypes = [i32, i32]
+    lib.attn_build_block_mask.restype = i32
+    lib.attn_build_block_mask.argtypes = [i32, i32, vp, i32, i32, i32,
+                                          ctypes.POINTER(_BlockMaskStruct), vp]
+    lib.attn_forward.restype = i32
+    lib.attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                 i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
+                                 i32, ctypes.c_float, ctypes.c_float, vp]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = _load()
+        msg = lib.attn_last_error().decode() or lib.attn_status_string(status).decode()
+        raise BsattnError(status, msg)
+
+
+def num_blocks(length: int, block_size: int = BLOCK_SIZE) -> int:
+    n = _load().attn_num_blocks(length, block_size)
+    if n < 0:
+        raise BsattnError(-1, f"bad length {length} or block size {block_size}")
+    return n
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class BlockMask:
+    """Device-resident 128x128 BlockMask (shared by every batch and head).
+
+    Tensors (int32, on the mask's device): ``kv_num_blocks [nq]``,
+    ``kv_indices [nq, nk]`` (partial blocks), ``full_kv_num_blocks [nq]``,
+    ``full_kv_indices [nq, nk]`` (full blocks), ``schedule [nq]`` (the order
+    in which the forward visits query blocks).
+    """
+
+    def __init__(self, kind: int, q_len: int, kv_len: int, window: int,
+                 document_id: Optional[torch.Tensor], device: torch.device):
+        nq, nk = num_blocks(q_len), num_blocks(kv_len)
+        opt = dict(dtype=torch.int32, device=device)
+        self.kind, self.q_len, self.kv_len, self.window = kind, q_len, kv_len, window
+        self.document_id = document_id
+        self.device = device
+        self.kv_num_blocks = torch.empty(nq, **opt)
+        self.kv_indices = torch.empty(nq, nk, **opt)
+        self.full_kv_num_blocks = torch.empty(nq, **opt)
+        self.full_kv_indices = torch.empty(nq, nk, **opt)
+        self.schedule = torch.empty(nq, **opt)
+        self._struct = _BlockMaskStruct()
+        s = self._struct
+        s.kv_num_blocks = self.kv_num_blocks.data_ptr()
+        s.kv_indices = self.kv_indices.data_ptr()
+        s.full_kv_num_blocks = self.full_kv_num_blocks.data_ptr()
+        s.full_kv_indices = self.full_kv_indices.data_ptr()
+        s.schedule = self.schedule.data_ptr()
+
+    @property
+    def num_q_blocks(self) -> int:
+        return self.kv_num_blocks.shape[0]
+
+    @property
+    def num_kv_blocks(self) -> int:
+        return self.kv_indices.shape[1]
+
+    def rebuild(self):
+        """Enqueue the library's mask build on the current stream."""
+        doc = self.document_id.data_ptr() if self.document_id is not None else None
+        with torch.cuda.device(self.device):
+            _check(_load().attn_build_block_mask(self.kind, self.window, doc, self.q_len,
+                                                 self.kv_len, BLOCK_SIZE,
+                                                 ctypes.byref(self._struct),
+                                                 _stream_handle(self.device)))
+        return self
+
+
+def create_block_mask(kind: Union[str, int], q_len: int, kv_len: int, window: Optional[int] = None,
+                      document_id: Optional[torch.Tensor] = None,
+                      device: Union[str, torch.device] = "cuda") -> BlockMask:
+    """Build a BlockMask with attn_build_block_mask (asynchronous on the
+    current stream of ``device``)."""
+    k = _KINDS[kind] if isinstance(kind, str) else int(kind)
+    device = torch.device(device)
+    if device.type != "cuda":
+        raise ValueError("the BlockMask lives in GPU memory; pass a cuda device")
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    if k == MASK_SLIDING_WINDOW:
+        if window is None:
+            raise ValueError("sliding_window needs window=")
+        w = int(window)
+    else:
+        w = 0
+    doc = None
+    if k == MASK_DOCUMENT:
+        if document_id is None:
+            raise ValueError("document mask needs document_id=")
+        if document_id.numel() < max(q_len, kv_len):
+            raise ValueError("document_id must cover max(q_len, kv_len) positions")
+        doc = document_id.to(device=device, dtype=torch.int32).contiguous()
+    return BlockMask(k, q_len, kv_len, w, doc, device).rebuild()
+
+
+def _strides(t: torch.Tensor):
+    arr = (ctypes.c_int64 * 4)(*t.stride())
+    return arr
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
+              score_mod: Optional[str] = None, softcap: float = 30.0,
+              scale: Optional[float] = None, return_lse: bool = False,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Fused block-sparse attention forward (attn_forward).
+
+    q [B,H,L,E], k/v [B,H,S,E] on the GPU, one dtype among fp32/bf16/fp16,
+    head dim contiguous. ``scale`` defaults to 1/sqrt(E) ("SDPA replaces
+    hand-written attention", section 1). Returns O [B,H,L,E] (and the fp32
+    natural-log logsumexp [B,H,L] when ``return_lse``).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, seq, E]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    B, H, L, E = q.shape
+    S = k.shape[2]
+    if k.shape != (B, H, S, E) or v.shape != (B, H, S, E):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(E)
+    sm = {None: SCORE_NONE, "none": SCORE_NONE, "softcap": SCORE_SOFTCAP}[score_mod]
+    if out is None:
+        out = torch.empty(B, H, L, E, dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.shape != (B, H, L)):
+        raise ValueError("lse must be a contiguous float32 [B, H, L] tensor")
+    with torch.cuda.device(q.device):
+        _check(_load().attn_forward(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            _DTYPES[q.dtype], B, H, L, S, E,
+            _strides(q), _strides(k), _strides(v), _strides(out),
+            ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
+            _stream_handle(q.device)))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,197 @@
+// C ABI entry points: host-side validation, then an asynchronous launch on
+// the caller's stream. Nothing here allocates device memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "bsattn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+attn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ATTN_OK;
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Arrays with no elements may be null (an empty tensor has no storage).
+bool arrays_present(const attn_block_mask* bm, int32_t nq, int32_t nk) {
+  const bool per_q = nq == 0 || (bm->kv_num_blocks && bm->full_kv_num_blocks && bm->schedule);
+  const bool per_pair = (int64_t)nq * nk == 0 || (bm->kv_indices && bm->full_kv_indices);
+  return per_q && per_pair;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Fill batch/head/sequence strides (elements) and check the head-dim stride
+// and 16-byte row alignment.
+// The stride of a dimension of size 1 is never used and may be anything.
+attn_status strides_of(const char* name, const int64_t* st, int32_t B, int32_t H, int32_t len,
+                       int32_t E, int esize, int64_t out[3]) {
+  if (st == nullptr) {
+    out[2] = E;
+    out[1] = (int64_t)len * E;
+    out[0] = (int64_t)H * len * E;
+    return ATTN_OK;
+  }
+  if (st[3] != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: head-dim stride must be 1", name);
+  const int32_t size[3] = {B, H, len};
+  for (int d = 0; d < 3; ++d) {
+    if (size[d] <= 1) {
+      out[d] = 0;
+      continue;
+    }
+    if (st[d] < 0) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: negative stride", name);
+    if ((st[d] * esize) % 16 != 0)
+      return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: stride %d (%lld elements) breaks 16-byte alignment",
+                  name, d, (long long)st[d]);
+    out[d] = st[d];
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_num_blocks(int32_t len, int32_t block_size) {
+  if (len < 0 || block_size != ATTN_BLOCK_SIZE) return -1;
+  return (int32_t)(((int64_t)len + block_size - 1) / block_size);
+}
+
+attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* document_id,
+                                  int32_t q_len, int32_t kv_len, int32_t block_size,
+                                  attn_block_mask* bm, void* stream) {
+  g_last_error[0] = '\0';
+  if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask struct is null");
+  if (kind < ATTN_MASK_NONE || kind > ATTN_MASK_DOCUMENT)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask kind %d", kind);
+  if (q_len < 0 || kv_len < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "negative length (q_len=%d, kv_len=%d)", q_len, kv_len);
+  if (block_size != ATTN_BLOCK_SIZE)
+    return fail(ATTN_ERR_UNSUPPORTED, "block_size %d: only %d is supported", block_size,
+                ATTN_BLOCK_SIZE);
+  if (kind == ATTN_MASK_SLIDING_WINDOW && window < 1)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "sliding window must be >= 1 (got %d)", window);
+  if (kind == ATTN_MASK_DOCUMENT && document_id == nullptr)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "document mask needs document_id");
+  const int32_t nq = attn_num_blocks(q_len, block_size);
+  const int32_t nk = attn_num_blocks(kv_len, block_size);
+  if (!arrays_present(bm, nq, nk))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask array pointer is null");
+  if (nk > ATTN_MAX_KV_BLOCKS)
+    return fail(ATTN_ERR_UNSUPPORTED, "%d kv blocks exceed the supported %d", nk,
+                ATTN_MAX_KV_BLOCKS);
+  bm->q_len = q_len;
+  bm->kv_len = kv_len;
+  bm->block_size = block_size;
+  bm->num_q_blocks = nq;
+  bm->num_kv_blocks = nk;
+  bm->kind = kind;
+  bm->window = (kind == ATTN_MASK_SLIDING_WINDOW) ? window : 0;
+  bm->document_id = (kind == ATTN_MASK_DOCUMENT) ? document_id : nullptr;
+  return hip_status(bsattn::launch_block_mask(kind, bm->window, bm->document_id, q_len, kv_len, nq,
+                                              nk, bm->kv_num_blocks, bm->kv_indices,
+                                              bm->full_kv_num_blocks, bm->full_kv_indices,
+                                              bm->schedule, static_cast<hipStream_t>(stream)),
+                    "block mask launch");
+}
+
+attn_status attn_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t S, int32_t E,
+                         const int64_t* q_strides, const int64_t* k_strides,
+                         const int64_t* v_strides, const int64_t* o_strides,
+                         const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
+                         void* stream) {
+  g_last_error[0] = '\0';
+  if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
+  // A tensor with no elements may have a null pointer.
+  if ((!q && L > 0) || (!o && L > 0) || (!k && S > 0) || (!v && S > 0))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-null");
+  int esize;
+  switch (dtype) {
+    case ATTN_F32: esize = 4; break;
+    case ATTN_BF16: esize = 2; break;
+    case ATTN_F16: esize = 2; break;
+    default: return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  }
+  if (B < 1 || H < 1 || L < 0 || S < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d L=%d S=%d", B, H, L, S);
+  if (E != bsattn::kHeadDim)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only %d is supported", E, bsattn::kHeadDim);
+  if (bm->q_len != L || bm->kv_len != S || bm->block_size != ATTN_BLOCK_SIZE)
+    return fail(ATTN_ERR_INVALID_ARGUMENT,
+                "block mask was built for q_len=%d kv_len=%d block=%d, tensors have L=%d S=%d",
+                bm->q_len, bm->kv_len, bm->block_size, L, S);
+  if (bm->num_q_blocks != attn_num_blocks(L, ATTN_BLOCK_SIZE) ||
+      bm->num_kv_blocks != attn_num_blocks(S, ATTN_BLOCK_SIZE) ||
+      !arrays_present(bm, bm->num_q_blocks, bm->num_kv_blocks))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is not built");
+  if (bm->kind < ATTN_MASK_NONE || bm->kind > ATTN_MASK_DOCUMENT ||
+      (bm->kind == ATTN_MASK_SLIDING_WINDOW && bm->window < 1) ||
+      (bm->kind == ATTN_MASK_DOCUMENT && bm->document_id == nullptr))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask fields are inconsistent");
+  if (score_mod != ATTN_SCORE_NONE && score_mod != ATTN_SCORE_SOFTCAP)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown score_mod %d", score_mod);
+  if (score_mod == ATTN_SCORE_SOFTCAP && !(std::isfinite(softcap) && softcap > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "soft-cap must be finite and > 0");
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+
+  bsattn::FwdArgs a{};
+  int64_t st[3];
+  attn_status s;
+  if ((s = strides_of("q", q_strides, B, H, L, E, esize, st)) != ATTN_OK) return s;
+  a.q_sb = st[0], a.q_sh = st[1], a.q_sl = st[2];
+  if ((s = strides_of("k", k_strides, B, H, S, E, esize, st)) != ATTN_OK) return s;
+  a.k_sb = st[0], a.k_sh = st[1], a.k_sl = st[2];
+  if ((s = strides_of("v", v_strides, B, H, S, E, esize, st)) != ATTN_OK) return s;
+  a.v_sb = st[0], a.v_sh = st[1], a.v_sl = st[2];
+  if ((s = strides_of("o", o_strides, B, H, L, E, esize, st)) != ATTN_OK) return s;
+  a.o_sb = st[0], a.o_sh = st[1], a.o_sl = st[2];
+  if ((int64_t)B * H * bm->num_q_blocks > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "too many work items");
+
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
+  a.B = B, a.H = H, a.L = L, a.S = S;
+  a.m.kv_num = bm->kv_num_blocks;
+  a.m.kv_idx = bm->kv_indices;
+  a.m.full_num = bm->full_kv_num_blocks;
+  a.m.full_idx = bm->full_kv_indices;
+  a.m.schedule = bm->schedule;
+  a.m.doc = bm->document_id;
+  a.m.nq = bm->num_q_blocks;
+  a.m.nk = bm->num_kv_blocks;
+  a.m.kind = bm->kind;
+  a.m.window = bm->window;
+  a.scale = scale;
+  a.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
+  return hip_status(bsattn::launch_forward(dtype, a, static_cast<hipStream_t>(stream)),
+                    "forward launch");
+}
+
+const char* attn_status_string(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,498 @@
+// Fused block-sparse attention forward for gfx950.
+//
+// O = softmax(Q K^T * scale + mask bias [+ soft-cap score_mod]) V and the
+// per-row logsumexp, without writing the L x S score table anywhere: a
+// workgroup owns one (batch, head, 128-query block) item, walks that block's
+// full kv blocks and then its partial kv blocks from the BlockMask, and keeps
+// a running row max and row sum (online softmax) while accumulating P V.
+// Definition: "SDPA replaces hand-written attention", section 1 (Attention
+// equation and its four steps); running max / running sum instead of the
+// score table: same page, section 2, and "FlashAttention" (service-dock),
+// tiled softmax is exact; tiles kept in on-chip memory with only the result
+// written back: "Flash Attention 2 and the IO bottleneck" (tcdigital),
+// section on tiling. Skipped / partial / full blocks: "FlexAttention on Apple
+// Silicon: block masks", closing section; soft-cap: same page, "Bonus".
+//
+// Work layout (4 waves of 64 lanes, each wave owns 32 query rows):
+//  * S^T = K_j Q^T is computed with 32x32 MFMA tiles, kv along M and queries
+//    along N, so each lane holds one query (lane % 32) and 16 kv values per
+//    32x32 tile. Row max / row sum are then in-lane reductions plus one swap
+//    between the two 32-lane halves.
+//  * The S^T accumulator layout (lane = query, registers = kv) is exactly the
+//    B operand layout of O^T = V^T P^T once probabilities are packed to
+//    16 bits, because the contraction index may be permuted freely as long as
+//    both operands use the same permutation; V^T is staged in LDS in that
+//    permuted order so each A operand is one 16-byte LDS read.
+//  * K is staged row-major in LDS with an XOR swizzle of its 16-byte chunks.
+//
+// bf16/fp16 use v_mfma_f32_32x32x16_{bf16,f16}; fp32 uses v_mfma_f32_32x32x2_f32
+// and keeps probabilities in fp32.
+#include <cmath>
+
+#include "bsattn.h"
+#include "internal.h"
+
+namespace bsattn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<__bf16> {
+  using x8 = bf16x8_t;
+  using x4 = bf16x4_t;
+  static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Vec<_Float16> {
+  using x8 = f16x8_t;
+  using x4 = f16x4_t;
+  static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Other half's value combined with ours: v_permlane32_swap exchanges lanes
+// l and l^32 between its two operands; with both operands equal, the two
+// results of each lane are {x_l, x_(l^32)} in some order.
+__device__ inline float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// c * tanh(y) in base-2 units of the result, from tanh|y| = (1 - e)/(1 + e)
+// with e = exp(-2|y|) and the sign of y.
+__device__ inline float softcap_log2(float s, float scale_over_cap, float cap_log2e) {
+  const float y = s * scale_over_cap;
+  const float e = fast_exp2(-2.0f * kLog2e * fabsf(y));
+  const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+  return copysignf(t, y) * cap_log2e;
+}
+
+// Query row i may see key j (both absolute positions), with j < S checked.
+template <int KIND>
+__device__ inline bool pair_live(int i, int j, int S, int W, int32_t di, int32_t dj) {
+  bool ok = j < S;
+  if (KIND == ATTN_MASK_CAUSAL) ok &= j <= i;
+  if (KIND == ATTN_MASK_SLIDING_WINDOW) ok &= (j <= i) & (i - j < W);
+  if (KIND == ATTN_MASK_DOCUMENT) ok &= (j <= i) & (di == dj);
+  return ok;
+}
+
+// Row of the 32x32 MFMA accumulator held in register r by lane half hf.
+__device__ inline int acc_row(int r, int hf) { return ((r >> 2) << 3) + (hf << 2) + (r & 3); }
+
+// Per-lane online-softmax state for one query row (half of its kv values).
+struct RowState {
+  float m;  // running max in log2 units (-inf before the first live key)
+  float l;  // running sum of this lane half's probabilities
+};
+
+// Turn four S^T tiles (raw q.k) into probabilities in place and update the
+// running statistics. Returns alpha, the factor that rescales the previous
+// accumulator. kv0: absolute index of the block's first key.
+template <int KIND, bool PARTIAL, bool SOFTCAP>
+__device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, int kv0, int hf,
+                                      const FwdArgs& a, int32_t dq, const int32_t* doc_k) {
+  const float c1 = a.scale * kLog2e;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[t][r];
+      if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
+      if (PARTIAL) {
+        const int jl = t * 32 + acc_row(r, hf);
+        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? doc_k[jl] : 0;
+        if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
+      }
+      s[t][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = half_max(mx);
+  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
+  const float m_blk = SOFTCAP ? mx : mx * c1;
+  const float m_new = fmaxf(st.m, m_blk);
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = s[t][r];
+      s[t][r] = SOFTCAP ? fast_exp2(x - m_use) : fast_exp2(fmaf(x, c1, -m_use));
+    }
+  }
+  st.m = m_new;
+  return alpha;
+}
+
+__device__ inline int swz_v(int e) { return (e ^ (e >> 3)) & 7; }
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel
+// ---------------------------------------------------------------------------
+template <typename T, int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  using x4 = typename V::x4;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBlock * kHeadDim * 2];  // [kv][e]
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kHeadDim * kBlock * 2];  // [e][kv perm]
+  __shared__ int32_t doc_k[kBlock];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = a.B * a.H;
+  const int item = blockIdx.x;
+  const int qb = a.m.schedule[item / BH];
+  const int bh = item % BH;
+  const int b = bh / a.H, h = bh % a.H;
+
+  const T* qg = static_cast<const T*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + h * a.k_sh;
+  const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + h * a.v_sh;
+  T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
+
+  const int qi = qb * kBlock + wave * 32 + lq;  // this lane's query row
+  x8 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (qi < a.L)
+      qop[c] = *reinterpret_cast<const x8*>(qg + (int64_t)qi * a.q_sl + c * 16 + hf * 8);
+    else
+      qop[c] = x8{};
+  }
+  const int32_t dq = (KIND == ATTN_MASK_DOCUMENT && qi < a.L) ? a.m.doc[qi] : -1;
+
+  f32x16_t oacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
+  RowState st{-INFINITY, 0.0f};
+
+  const int nfull = a.m.full_num[qb];
+  const int npart = a.m.kv_num[qb];
+  const int32_t* full_list = a.m.full_idx + (int64_t)qb * a.m.nk;
+  const int32_t* part_list = a.m.kv_idx + (int64_t)qb * a.m.nk;
+
+  for (int n = 0; n < nfull + npart; ++n) {
+    const bool partial = n >= nfull;
+    const int kb = partial ? part_list[n - nfull] : full_list[n];
+    const int kv0 = kb * kBlock;
+
+    __syncthreads();  // the previous block's LDS reads are done
+    // K: 1024 chunks of 16 bytes, row-major, chunk index XOR (row & 7).
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cidx = tid + u * kThreads;
+      const int row = cidx >> 3, ch = cidx & 7;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (kv0 + row < a.S)
+        val = *reinterpret_cast<const uint4*>(kg + (int64_t)(kv0 + row) * a.k_sl + ch * 8);
+      *reinterpret_cast<uint4*>(k_lds + row * 128 + ((ch ^ (row & 7)) << 4)) = val;
+    }
+    // V: thread owns kv rows 4*kvg..4*kvg+3 and head-dim columns 8*ec..8*ec+7
+    // and writes them transposed: for each column e, the 4 kv values as one
+    // 8-byte group. Within a 16-kv group g the stored order is
+    // [0..3, 8..11 | 4..7, 12..15] so lane half hf reads kv 4hf+{0..3} and
+    // 8+4hf+{0..3} as one 16-byte chunk (2g + hf).
+    {
+      const int kvg = tid >> 3, ec = tid & 7;
+      uint4 rows[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kv = kv0 + kvg * 4 + r;
+        rows[r] = make_uint4(0, 0, 0, 0);
+        if (kv < a.S)
+          rows[r] = *reinterpret_cast<const uint4*>(vg + (int64_t)kv * a.v_sl + ec * 8);
+      }
+      const int g = kvg >> 2, rr = kvg & 3;
+      const int chunk = 2 * g + (rr & 1);
+      const int byte_in = (rr >> 1) * 8;
+      const uint16_t* r16[4] = {reinterpret_cast<const uint16_t*>(&rows[0]),
+                                reinterpret_cast<const uint16_t*>(&rows[1]),
+                                reinterpret_cast<const uint16_t*>(&rows[2]),
+                                reinterpret_cast<const uint16_t*>(&rows[3])};
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int e = ec * 8 + x;
+        uint2 pk;
+        pk.x = (uint32_t)r16[0][x] | ((uint32_t)r16[1][x] << 16);
+        pk.y = (uint32_t)r16[2][x] | ((uint32_t)r16[3][x] << 16);
+        *reinterpret_cast<uint2*>(v_lds + e * 256 + ((chunk ^ swz_v(e)) << 4) + byte_in) = pk;
+      }
+    }
+    if (KIND == ATTN_MASK_DOCUMENT && partial && tid < kBlock)
+      doc_k[tid] = (kv0 + tid < a.S) ? a.m.doc[kv0 + tid] : -1;
+    __syncthreads();
+
+    // S^T = K Q^T: 4 tiles of 32 kv x 32 queries, contraction over E=64.
+    f32x16_t s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+      const int row = t * 32 + lq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int ch = 2 * c + hf;
+        const x8 ka = *reinterpret_cast<const x8*>(k_lds + row * 128 + ((ch ^ (row & 7)) << 4));
+        s[t] = V::mma(ka, qop[c], s[t]);
+      }
+    }
+
+    float alpha;
+    if (partial)
+      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
+    else
+      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
+
+    // Pack probabilities to 16 bits (round to nearest even) and sum the
+    // rounded values, so the normaliser matches the weights used in P V.
+    x8 pk[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const T pv = (T)s[g >> 1][(g & 1) * 8 + u];
+        pk[g][u] = pv;
+        psum += (float)pv;
+      }
+    }
+    st.l = st.l * alpha + psum;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
+
+    // O^T += V^T P^T: 2 tiles of 32 head-dims x 32 queries, contraction over
+    // the block's 128 keys in 8 chunks of 16.
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+      const int e = te * 32 + lq;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const x8 va = *reinterpret_cast<const x8*>(v_lds + e * 256 + (((2 * g + hf) ^ swz_v(e)) << 4));
+        oacc[te] = V::mma(va, pk[g], oacc[te]);
+      }
+    }
+  }
+
+  // Epilogue: O = O^T / l (0 for a row without live keys), lse = ln(sum exp).
+  const float l = half_sum(st.l);
+  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+  if (qi < a.L) {
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int e0 = te * 32 + r4 * 8 + hf * 4;
+        x4 outv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) outv[u] = (T)(oacc[te][r4 * 4 + u] * inv);
+        *reinterpret_cast<x4*>(og + (int64_t)qi * a.o_sl + e0) = outv;
+      }
+    }
+    if (a.lse != nullptr && hf == 0)
+      a.lse[(int64_t)bh * a.L + qi] = (l > 0.0f) ? (st.m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same structure with v_mfma_f32_32x32x2_f32 (one element of the
+// contraction per lane and step), probabilities kept in fp32.
+// ---------------------------------------------------------------------------
+constexpr int kF32RowStride = 68;  // floats per LDS row (64 + 4 padding)
+
+template <int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float k_lds[kBlock * kF32RowStride];
+  __shared__ __attribute__((aligned(16))) float v_lds[kBlock * kF32RowStride];
+  __shared__ int32_t doc_k[kBlock];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = a.B * a.H;
+  const int item = blockIdx.x;
+  const int qb = a.m.schedule[item / BH];
+  const int bh = item % BH;
+  const int b = bh / a.H, h = bh % a.H;
+
+  const float* qg = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh;
+  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh;
+  float* og = static_cast<float*>(a.o) + b * a.o_sb + h * a.o_sh;
+
+  const int qi = qb * kBlock + wave * 32 + lq;
+  // Contraction step j of lane half hf covers head dim e = 32*hf + j.
+  float qv[32];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qi < a.L) x = *reinterpret_cast<const float4*>(qg + (int64_t)qi * a.q_sl + hf * 32 + c * 4);
+    qv[4 * c + 0] = x.x;
+    qv[4 * c + 1] = x.y;
+    qv[4 * c + 2] = x.z;
+    qv[4 * c + 3] = x.w;
+  }
+  const int32_t dq = (KIND == ATTN_MASK_DOCUMENT && qi < a.L) ? a.m.doc[qi] : -1;
+
+  f32x16_t oacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
+  RowState st{-INFINITY, 0.0f};
+
+  const int nfull = a.m.full_num[qb];
+  const int npart = a.m.kv_num[qb];
+  const int32_t* full_list = a.m.full_idx + (int64_t)qb * a.m.nk;
+  const int32_t* part_list = a.m.kv_idx + (int64_t)qb * a.m.nk;
+
+  for (int n = 0; n < nfull + npart; ++n) {
+    const bool partial = n >= nfull;
+    const int kb = partial ? part_list[n - nfull] : full_list[n];
+    const int kv0 = kb * kBlock;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int cidx = tid + u * kThreads;  // 2048 float4 chunks per tile
+      const int row = cidx >> 4, ch = cidx & 15;
+      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+      if (kv0 + row < a.S) {
+        kx = *reinterpret_cast<const float4*>(kg + (int64_t)(kv0 + row) * a.k_sl + ch * 4);
+        vx = *reinterpret_cast<const float4*>(vg + (int64_t)(kv0 + row) * a.v_sl + ch * 4);
+      }
+      *reinterpret_cast<float4*>(k_lds + row * kF32RowStride + ch * 4) = kx;
+      *reinterpret_cast<float4*>(v_lds + row * kF32RowStride + ch * 4) = vx;
+    }
+    if (KIND == ATTN_MASK_DOCUMENT && partial && tid < kBlock)
+      doc_k[tid] = (kv0 + tid < a.S) ? a.m.doc[kv0 + tid] : -1;
+    __syncthreads();
+
+    f32x16_t s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+      const float* krow = k_lds + (t * 32 + lq) * kF32RowStride + hf * 32;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) s[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[j], qv[j], s[t], 0, 0, 0);
+    }
+
+    float alpha;
+    if (partial)
+      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
+    else
+      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
+
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) psum += s[t][r];
+    st.l = st.l * alpha + psum;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
+
+    // O^T += V^T P^T: step (t, r) pairs lane half 0's key acc_row(r,0) with
+    // lane half 1's key acc_row(r,1) of tile t; A = V[key][e], B = p.
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float va = v_lds[(t * 32 + acc_row(r, hf)) * kF32RowStride + te * 32 + lq];
+          oacc[te] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, s[t][r], oacc[te], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float l = half_sum(st.l);
+  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+  if (qi < a.L) {
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int e0 = te * 32 + r4 * 8 + hf * 4;
+        float4 outv = make_float4(oacc[te][r4 * 4 + 0] * inv, oacc[te][r4 * 4 + 1] * inv,
+                                  oacc[te][r4 * 4 + 2] * inv, oacc[te][r4 * 4 + 3] * inv);
+        *reinterpret_cast<float4*>(og + (int64_t)qi * a.o_sl + e0) = outv;
+      }
+    }
+    if (a.lse != nullptr && hf == 0)
+      a.lse[(int64_t)bh * a.L + qi] = (l > 0.0f) ? (st.m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int KIND, bool SOFTCAP>
+hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq));
+  const dim3 block(kThreads);
+  switch (dtype) {
+    case ATTN_BF16:
+      hipLaunchKernelGGL((fwd16_kernel<__bf16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      break;
+    case ATTN_F16:
+      hipLaunchKernelGGL((fwd16_kernel<_Float16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      break;
+    case ATTN_F32:
+      hipLaunchKernelGGL((fwd32_kernel<KIND, SOFTCAP>), grid, block, 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_softcap(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  return a.softcap > 0.0f ? launch_kind<KIND, true>(dtype, a, stream)
+                          : launch_kind<KIND, false>(dtype, a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_forward(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  if ((int64_t)a.B * a.H * a.m.nq == 0) return hipSuccess;
+  switch (a.m.kind) {
+    case ATTN_MASK_NONE: return launch_softcap<ATTN_MASK_NONE>(dtype, a, stream);
+    case ATTN_MASK_CAUSAL: return launch_softcap<ATTN_MASK_CAUSAL>(dtype, a, stream);
+    case ATTN_MASK_SLIDING_WINDOW: return launch_softcap<ATTN_MASK_SLIDING_WINDOW>(dtype, a, stream);
+    case ATTN_MASK_DOCUMENT: return launch_softcap<ATTN_MASK_DOCUMENT>(dtype, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bsattn

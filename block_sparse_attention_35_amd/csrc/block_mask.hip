@@ -1,0 +1,183 @@
+// BlockMask construction on the GPU.
+//
+// A 128x128 block (qb, kb) is classified from the mask rule: no live pair ->
+// skipped, every pair live (and the whole block in range) -> full, otherwise
+// partial. Rules: "FlexAttention on Apple Silicon: block masks", sections
+// "Mask 1: causal", "Mask 2: sliding-window causal", "Mask 3: document-packed";
+// only fully masked blocks may be skipped (same page, closing section); 128x128
+// blocks: "FlexAttention on MPS vs SDPA", data-flow section.
+//
+// Causal and sliding-window blocks are classified in closed form: all pair
+// offsets d = i - j of a block form the integer interval [q0 - k1, q1 - k0],
+// and a pair is live iff 0 <= d < W (W = infinity for causal), so the block
+// is skipped iff the two intervals are disjoint and full iff the first lies
+// inside the second. Document blocks are classified exactly by evaluating
+// every in-range pair cooperatively (ids may be in any order).
+//
+// Kernel 1 (one workgroup per query block) writes the classes to LDS, then
+// compacts them in ascending kb order with wave ballots and writes the counts,
+// the index lists and the zero padding. Kernel 2 ranks query blocks by their
+// number of live kv blocks, descending, ties by index, and writes the order.
+#include "internal.h"
+
+#include "bsattn.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+enum : uint8_t { kSkip = 0, kPartial = 1, kFull = 2 };
+
+__device__ inline uint8_t classify_interval(int64_t q0, int64_t q1, int64_t k0, int64_t k1,
+                                            int64_t window, bool whole) {
+  const int64_t dmin = q0 - k1, dmax = q1 - k0;
+  if (dmax < 0 || dmin > window - 1) return kSkip;
+  if (dmin >= 0 && dmax <= window - 1 && whole) return kFull;
+  return kPartial;
+}
+
+__global__ __launch_bounds__(kThreads) void classify_compact_kernel(
+    int32_t kind, int32_t window, const int32_t* __restrict__ doc, int32_t q_len, int32_t kv_len,
+    int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
+    int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
+  extern __shared__ uint8_t cls[];  // [nk]
+  __shared__ int32_t doc_q[kBlock];
+  __shared__ int32_t doc_k[kBlock];
+  __shared__ int32_t wave_counts[2][kWaves];
+
+  const int tid = threadIdx.x;
+  const int qb = blockIdx.x;
+  const int64_t q0 = (int64_t)qb * kBlock;
+  const int64_t q1 = min<int64_t>(q_len, q0 + kBlock) - 1;
+  const bool q_whole = (q1 - q0 + 1) == kBlock;
+
+  if (kind == ATTN_MASK_DOCUMENT) {
+    if (tid < kBlock) doc_q[tid] = (q0 + tid <= q1) ? doc[q0 + tid] : 0;
+    // Each thread owns query row tid/2 and 64 keys; the workgroup votes.
+    const int il = tid >> 1;
+    const int jbase = (tid & 1) * 64;
+    for (int kb = 0; kb < nk; ++kb) {
+      const int64_t k0 = (int64_t)kb * kBlock;
+      const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
+      if (q1 < k0) {  // every key after every query: no causal pair
+        if (tid == 0) cls[kb] = kSkip;
+        continue;
+      }
+      __syncthreads();  // previous doc_k readers are done (and doc_q is written)
+      if (tid < kBlock) doc_k[tid] = (k0 + tid <= k1) ? doc[k0 + tid] : 0;
+      __syncthreads();
+      const int64_t i = q0 + il;
+      const int32_t di = doc_q[il];
+      int any = 0, all = 1;
+      for (int jj = 0; jj < 64; ++jj) {
+        const int64_t j = k0 + jbase + jj;
+        const int in_range = (i <= q1) & (j <= k1);
+        const int lv = in_range & (j <= i) & (doc_k[jbase + jj] == di);
+        any |= lv;
+        all &= lv;
+      }
+      const int any_live = __syncthreads_or(any);
+      const int all_live = __syncthreads_and(all);
+      if (tid == 0) cls[kb] = all_live ? kFull : (any_live ? kPartial : kSkip);
+    }
+  } else {
+    const int64_t w = (kind == ATTN_MASK_SLIDING_WINDOW) ? (int64_t)window : INT64_MAX / 4;
+    for (int kb = tid; kb < nk; kb += kThreads) {
+      const int64_t k0 = (int64_t)kb * kBlock;
+      const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
+      const bool whole = q_whole && (k1 - k0 + 1) == kBlock;
+      uint8_t c;
+      if (kind == ATTN_MASK_NONE)
+        c = whole ? kFull : kPartial;
+      else
+        c = classify_interval(q0, q1, k0, k1, w, whole);
+      cls[kb] = c;
+    }
+  }
+  __syncthreads();
+
+  // Stable compaction in ascending kb order.
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t base_p = 0, base_f = 0;
+  int32_t* prow = kv_idx + (int64_t)qb * nk;
+  int32_t* frow = full_idx + (int64_t)qb * nk;
+  for (int c0 = 0; c0 < nk; c0 += kThreads) {
+    const int kb = c0 + tid;
+    const uint8_t c = (kb < nk) ? cls[kb] : kSkip;
+    const uint64_t bp = __ballot(c == kPartial);
+    const uint64_t bf = __ballot(c == kFull);
+    if (lane == 0) {
+      wave_counts[0][wave] = __popcll(bp);
+      wave_counts[1][wave] = __popcll(bf);
+    }
+    __syncthreads();
+    int32_t off_p = base_p, off_f = base_f, tot_p = 0, tot_f = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) {
+        off_p += wave_counts[0][w];
+        off_f += wave_counts[1][w];
+      }
+      tot_p += wave_counts[0][w];
+      tot_f += wave_counts[1][w];
+    }
+    if (c == kPartial) prow[off_p + __popcll(bp & lower)] = kb;
+    if (c == kFull) frow[off_f + __popcll(bf & lower)] = kb;
+    base_p += tot_p;
+    base_f += tot_f;
+    __syncthreads();  // wave_counts reused next chunk
+  }
+  for (int t = tid; t < nk; t += kThreads) {
+    if (t >= base_p) prow[t] = 0;
+    if (t >= base_f) frow[t] = 0;
+  }
+  if (tid == 0) {
+    kv_num[qb] = base_p;
+    full_num[qb] = base_f;
+  }
+}
+
+// rank(qb) = #{q : cost(q) > cost(qb)} + #{q < qb : cost(q) == cost(qb)};
+// schedule[rank(qb)] = qb.
+__global__ __launch_bounds__(kThreads) void schedule_kernel(int32_t nq,
+                                                            const int32_t* __restrict__ kv_num,
+                                                            const int32_t* __restrict__ full_num,
+                                                            int32_t* __restrict__ schedule) {
+  __shared__ int32_t cost_tile[kThreads];
+  const int qb = blockIdx.x * kThreads + threadIdx.x;
+  const int32_t mine = (qb < nq) ? kv_num[qb] + full_num[qb] : 0;
+  int32_t rank = 0;
+  for (int t0 = 0; t0 < nq; t0 += kThreads) {
+    const int t = t0 + threadIdx.x;
+    cost_tile[threadIdx.x] = (t < nq) ? kv_num[t] + full_num[t] : -1;
+    __syncthreads();
+    const int lim = min(kThreads, nq - t0);
+    for (int u = 0; u < lim; ++u) {
+      const int32_t c = cost_tile[u];
+      rank += (c > mine) | ((c == mine) & (t0 + u < qb));
+    }
+    __syncthreads();
+  }
+  if (qb < nq) schedule[rank] = qb;
+}
+
+}  // namespace
+
+hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, int32_t q_len,
+                             int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
+                             int32_t* kv_idx, int32_t* full_num, int32_t* full_idx,
+                             int32_t* schedule, hipStream_t stream) {
+  if (nq == 0) return hipSuccess;
+  const size_t lds = (size_t)((nk + 15) & ~15);
+  hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, window,
+                     doc, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(schedule_kernel, dim3((nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, nq, kv_num, full_num, schedule);
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

@@ -1,0 +1,186 @@
+/*
+ * bsattn.h -- C ABI of the block-sparse fused attention forward for AMD
+ * MI355X (gfx950).
+ *
+ * Two operations make up the path:
+ *
+ *   attn_build_block_mask  turns a mask rule into a 128x128 BlockMask: for
+ *                          every query block, the ascending list of "partial"
+ *                          kv blocks (some but not all pairs live; the rule is
+ *                          evaluated per element there) and of "full" kv blocks
+ *                          (every pair live; no per-element rule), plus the
+ *                          order in which the forward visits query blocks.
+ *                          Fully masked blocks appear in neither list and are
+ *                          never touched. Mask rules: "FlexAttention on Apple
+ *                          Silicon: block masks" (dreaming.press), sections
+ *                          "Mask 1" to "Mask 3"; 128x128 blocks and block
+ *                          skipping: "FlexAttention on MPS vs SDPA" (qiita,
+ *                          kiarina), data-flow section.
+ *
+ *   attn_forward           O = softmax(Q K^T * scale + mask bias [+ score_mod]) V
+ *                          and the per-row logsumexp, fused: the L x S score
+ *                          table never leaves registers/LDS. Definition: "SDPA
+ *                          replaces hand-written attention" (qiita, GeneLab_999),
+ *                          section 1, the Attention equation; online softmax
+ *                          over tiles: same page, section 2 (only a running max
+ *                          and running sum are kept), and "FlashAttention"
+ *                          (service-dock), exactness of tiled softmax;
+ *                          score_mod soft-cap: block-mask page, section "Bonus".
+ *
+ * Conventions for every entry point:
+ *  - Memory: the caller owns every buffer. Pointers documented as "device"
+ *    must be device memory of the current HIP device; the library never
+ *    allocates, frees or synchronises, and only enqueues work on `stream`
+ *    (a hipStream_t; NULL means the default stream). Results are visible
+ *    after the caller synchronises with that stream.
+ *  - Errors: every call returns an attn_status. Arguments are validated on
+ *    the host before anything is enqueued; on a validation failure nothing is
+ *    enqueued and no output is touched. A combination the library has no
+ *    kernel for returns ATTN_ERR_UNSUPPORTED; there is no fallback path.
+ *    attn_last_error() returns a message for the calling thread's last
+ *    failure. No exception or abort crosses this interface.
+ *  - Thread safety: calls may be made from several host threads; calls that
+ *    write the same BlockMask arrays or outputs concurrently race.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARGUMENT (-1) /* a null pointer, bad size, stride or alignment */
+#define ATTN_ERR_UNSUPPORTED (-2)      /* valid, but no kernel for it (e.g. head dim != 64) */
+#define ATTN_ERR_HIP (-3)              /* the HIP runtime reported an error at launch */
+typedef int32_t attn_status;
+
+/* Element types of q, k, v and o. */
+#define ATTN_F32 0
+#define ATTN_BF16 1
+#define ATTN_F16 2
+
+/* Mask rules; each returns "live" for query position i and key position j.
+ *   NONE             every pair is live
+ *   CAUSAL           i >= j
+ *   SLIDING_WINDOW   i >= j && i - j < window   (the window holds `window`
+ *                    keys including the query's own position)
+ *   DOCUMENT         i >= j && document_id[i] == document_id[j]
+ * Positions are absolute and start at 0 for both queries and keys, also
+ * when q_len != kv_len (upper-left alignment). */
+#define ATTN_MASK_NONE 0
+#define ATTN_MASK_CAUSAL 1
+#define ATTN_MASK_SLIDING_WINDOW 2
+#define ATTN_MASK_DOCUMENT 3
+
+/* score_mod applied to each scaled score s before the mask:
+ *   NONE      s
+ *   SOFTCAP   softcap * tanh(s / softcap)   */
+#define ATTN_SCORE_NONE 0
+#define ATTN_SCORE_SOFTCAP 1
+
+/* The only block size: 128 x 128. */
+#define ATTN_BLOCK_SIZE 128
+/* Largest number of kv blocks per query block the mask builder supports. */
+#define ATTN_MAX_KV_BLOCKS 16384
+
+/*
+ * A BlockMask. The caller allocates the five int32 device arrays (sizes from
+ * attn_num_blocks) and sets the pointers; attn_build_block_mask fills the
+ * arrays and every other field. One BlockMask serves every batch and head
+ * (the rule does not depend on them) and any number of attn_forward calls.
+ *
+ *   kv_num_blocks[nq]          number of partial kv blocks of query block qb
+ *   kv_indices[nq * nk]        row qb: its partial kv block indices, ascending,
+ *                              then 0 up to nk entries
+ *   full_kv_num_blocks[nq]     number of full kv blocks of query block qb
+ *   full_kv_indices[nq * nk]   row qb: its full kv block indices, ascending,
+ *                              then 0 up to nk entries
+ *   schedule[nq]               query blocks ordered by decreasing number of
+ *                              live kv blocks (ties: lower index first); the
+ *                              forward visits them in this order
+ * with nq = ceil(q_len / 128) and nk = ceil(kv_len / 128). A block is full only
+ * if all 128 x 128 of its positions are in range and live, so the blocks at a
+ * ragged end are at most partial.
+ */
+typedef struct attn_block_mask {
+  /* set by the caller: device arrays */
+  int32_t* kv_num_blocks;
+  int32_t* kv_indices;
+  int32_t* full_kv_num_blocks;
+  int32_t* full_kv_indices;
+  int32_t* schedule;
+  /* filled by attn_build_block_mask */
+  int32_t q_len;
+  int32_t kv_len;
+  int32_t block_size;
+  int32_t num_q_blocks;
+  int32_t num_kv_blocks;
+  int32_t kind;
+  int32_t window;
+  const int32_t* document_id; /* device, borrowed: must stay valid while the mask is used */
+} attn_block_mask;
+
+/* ceil(len / block_size) for len >= 0 and block_size == 128; -1 otherwise. */
+int32_t attn_num_blocks(int32_t len, int32_t block_size);
+
+/*
+ * Build a BlockMask for `kind` over q_len queries and kv_len keys.
+ *   window        SLIDING_WINDOW: >= 1; ignored (and stored as 0) otherwise
+ *   document_id   DOCUMENT: device int32[max(q_len, kv_len)]; ignored otherwise
+ *   block_size    must be 128
+ *   bm            host struct with the five array pointers set (non-null
+ *                 unless the array has no elements)
+ * Errors: INVALID_ARGUMENT for a null bm/array, q_len or kv_len < 0, a bad
+ * window, a missing document_id or an unknown kind; UNSUPPORTED for
+ * block_size != 128 or more than ATTN_MAX_KV_BLOCKS kv blocks.
+ */
+attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* document_id,
+                                  int32_t q_len, int32_t kv_len, int32_t block_size,
+                                  attn_block_mask* bm, void* stream);
+
+/*
+ * Fused block-sparse attention forward.
+ *   q  device [B, H, L, E], k device [B, H, S, E], v device [B, H, S, E],
+ *   o  device [B, H, L, E] output, all of element type `dtype`;
+ *   q_strides, k_strides, v_strides, o_strides: host int64[4], the element
+ *   strides of the four dimensions (batch, head, sequence, head dim), or NULL
+ *   for the contiguous layout. The head-dim stride must be 1; base pointers
+ *   and the other strides must keep every row 16-byte aligned.
+ *   lse  device fp32 [B, H, L] contiguous, natural-log logsumexp of each row's
+ *        scores after scale, score_mod and mask; may be NULL.
+ *   bm   a BlockMask built for q_len == L and kv_len == S.
+ *   score_mod ATTN_SCORE_NONE or ATTN_SCORE_SOFTCAP (then softcap > 0).
+ *   scale  multiplier of q.k (pass 1/sqrt(E) for the usual attention).
+ * A row whose every key is masked gets O = 0 and lse = -inf.
+ * Arithmetic: products in fp32 (MFMA) from the input type, fp32 softmax
+ * statistics and accumulation; probabilities are rounded to the input type
+ * (round to nearest even) before the P.V product for bf16/fp16; O is rounded
+ * to the output type with round to nearest even.
+ * Errors: INVALID_ARGUMENT for null pointers, sizes < 0 (B, H >= 1), a mask
+ * built for other lengths, bad strides/alignment, a bad score_mod/softcap or
+ * a scale that is not finite and > 0; UNSUPPORTED for E != 64 or an unknown dtype; HIP for a
+ * failed launch.
+ */
+attn_status attn_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t S, int32_t E,
+                         const int64_t* q_strides, const int64_t* k_strides,
+                         const int64_t* v_strides, const int64_t* o_strides,
+                         const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
+                         void* stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(attn_status status);
+
+/* Detail of the calling thread's last failed call ("" if none). The pointer
+ * stays valid until the thread's next call into this library. */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,163 @@
+"""The C ABI library: it loads, exports every function include/bsattn.h
+declares, and its host-side validation returns the documented status codes.
+
+Validation cases pass placeholder device addresses that are never
+dereferenced: each case is invalid, so the library returns before it enqueues
+anything. They run only where no GPU is visible, so a validation bug can never
+turn into a launch on fake addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_sparse_attention_35_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="placeholder-address validation runs only without a GPU")
+
+OK, INVALID, UNSUPPORTED = 0, -1, -2
+FAKE = 0x10000  # 16-byte aligned placeholder address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("attn_build_block_mask", "attn_forward", "attn_num_blocks",
+                     "attn_status_string", "attn_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bsa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in bsattn.h but not exported"
+
+
+def test_num_blocks():
+    assert [bsa.num_blocks(n) for n in (0, 1, 127, 128, 129, 256, 8192, 32768)] == \
+        [0, 1, 1, 1, 2, 2, 64, 256]
+    lib = bsa._load()
+    assert lib.attn_num_blocks(-1, 128) == -1
+    assert lib.attn_num_blocks(100, 64) == -1
+
+
+def test_status_strings():
+    lib = bsa._load()
+    assert lib.attn_status_string(OK) == b"ok"
+    assert lib.attn_status_string(INVALID) == b"invalid argument"
+    assert lib.attn_status_string(UNSUPPORTED) == b"unsupported"
+    assert lib.attn_status_string(-3) == b"HIP runtime error"
+
+
+def _bm(**kw):
+    s = bsa._BlockMaskStruct()
+    for f in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices", "schedule"):
+        setattr(s, f, FAKE)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _build(kind=1, window=0, doc=None, q_len=256, kv_len=256, block=128, bm=None):
+    lib = bsa._load()
+    bm = _bm() if bm is None else bm
+    return lib.attn_build_block_mask(kind, window, doc, q_len, kv_len, block, ctypes.byref(bm), None)
+
+
+BUILD_CASES = [
+    ("unknown_kind", dict(kind=7), INVALID, "kind"),
+    ("negative_len", dict(q_len=-1), INVALID, "negative"),
+    ("block_64", dict(block=64), UNSUPPORTED, "block_size"),
+    ("window_zero", dict(kind=2, window=0), INVALID, "window"),
+    ("document_without_ids", dict(kind=3, doc=None), INVALID, "document"),
+    ("null_array", dict(bm=_bm(kv_indices=None)), INVALID, "null"),
+    ("too_many_kv_blocks", dict(kv_len=16385 * 128), UNSUPPORTED, "kv blocks"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code,words", BUILD_CASES, ids=[c[0] for c in BUILD_CASES])
+def test_build_block_mask_validation(name, kw, code, words):
+    assert _build(**kw) == code
+    assert words in bsa._load().attn_last_error().decode()
+
+
+@no_gpu
+def test_build_null_struct():
+    lib = bsa._load()
+    assert lib.attn_build_block_mask(1, 0, None, 256, 256, 128, None, None) == INVALID
+
+
+def _built_mask(L=256, S=256, kind=1, window=0, doc=None):
+    return _bm(q_len=L, kv_len=S, block_size=128, num_q_blocks=-(-L // 128),
+               num_kv_blocks=-(-S // 128), kind=kind, window=window, document_id=doc)
+
+
+def _fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=1, B=1, H=2, L=256, S=256, E=64,
+         qs=None, ks=None, vs=None, os_=None, bm=None, score_mod=0, softcap=0.0, scale=0.125):
+    lib = bsa._load()
+    bm = _built_mask(L, S) if bm is None else bm
+
+    def st(x):
+        return None if x is None else (ctypes.c_int64 * 4)(*x)
+
+    return lib.attn_forward(q, k, v, o, lse, dtype, B, H, L, S, E, st(qs), st(ks), st(vs),
+                            st(os_), ctypes.byref(bm), score_mod, softcap, scale, None)
+
+
+FWD_CASES = [
+    ("null_q", dict(q=None), INVALID, "non-null"),
+    ("unknown_dtype", dict(dtype=9), UNSUPPORTED, "dtype"),
+    ("zero_heads", dict(H=0), INVALID, "sizes"),
+    ("head_dim_128", dict(E=128), UNSUPPORTED, "head dim"),
+    ("mask_for_other_lengths", dict(bm=_built_mask(512, 512)), INVALID, "built for"),
+    ("mask_not_built", dict(bm=_built_mask(256, 256, kind=2, window=0)), INVALID, "inconsistent"),
+    ("document_mask_without_ids", dict(bm=_built_mask(256, 256, kind=3)), INVALID, "inconsistent"),
+    ("unknown_score_mod", dict(score_mod=4), INVALID, "score_mod"),
+    ("softcap_zero", dict(score_mod=1, softcap=0.0), INVALID, "soft-cap"),
+    ("softcap_nan", dict(score_mod=1, softcap=float("nan")), INVALID, "soft-cap"),
+    ("scale_zero", dict(scale=0.0), INVALID, "scale"),
+    ("scale_negative", dict(scale=-0.125), INVALID, "scale"),
+    ("scale_inf", dict(scale=float("inf")), INVALID, "scale"),
+    ("misaligned_k", dict(k=FAKE + 2), INVALID, "aligned"),
+    ("head_dim_stride", dict(qs=(2 * 256 * 128, 256 * 128, 128, 2)), INVALID, "head-dim stride"),
+    ("row_stride_breaks_alignment", dict(ks=(2 * 256 * 65, 256 * 65, 65, 1)), INVALID, "alignment"),
+    ("negative_stride", dict(vs=(2 * 256 * 64, -256 * 64, 64, 1)), INVALID, "negative"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code,words", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward_validation(name, kw, code, words):
+    assert _fwd(**kw) == code
+    msg = bsa._load().attn_last_error().decode()
+    assert words in msg, msg
+
+
+@no_gpu
+def test_forward_null_mask():
+    lib = bsa._load()
+    assert lib.attn_forward(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 1, 128, 128, 64, None, None,
+                            None, None, None, 0, 0.0, 0.125, None) == INVALID
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bsa.attention(q, q, q, block_mask=None)
+
+
+def test_binding_rejects_float64():
+    q = torch.zeros(1, 1, 128, 64, dtype=torch.float64)
+    with pytest.raises(ValueError):
+        bsa.attention(q, q, q, block_mask=None)

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path against the fp64 oracle, through the C ABI.
+
+* BlockMask arrays bit-exact (counts, index lists, zero padding) and the
+  schedule equal to the unique descending-cost order.
+* Forward O and logsumexp within the stated tolerance: max-abs 1e-2 and
+  mean-abs 1e-3 for bf16/fp16, 1e-5 for fp32 (max and mean); lse 1e-3 for
+  bf16/fp16 and 1e-5 for fp32. Small cases compare every element; the full
+  workloads (the shapes and launch configuration the benchmark times)
+  compare sampled rows, and check properties of all rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_35_amd as bsa
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5, 1e-5), "bf16": (1e-2, 1e-3, 1e-3), "f16": (1e-2, 1e-3, 1e-3)}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda", 0)
+
+
+def _mask_on_gpu(w: wl.Workload, dev, doc=None):
+    doc = wl.make_doc(w) if doc is None else doc
+    dt = torch.from_numpy(doc).to(dev) if doc is not None else None
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None, document_id=dt, device=dev)
+    return bm, doc
+
+
+def _check_mask(bm, w: wl.Workload, doc):
+    torch.cuda.synchronize()
+    want = oracle.block_mask(w.kind, w.L, w.S, w.window, doc)
+    got = (bm.kv_num_blocks, bm.kv_indices, bm.full_kv_num_blocks, bm.full_kv_indices)
+    for name, g, e in zip(("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                           "full_kv_indices"), got, want):
+        g = g.cpu().numpy()
+        assert g.shape == e.shape and np.array_equal(g, e), f"{w.name}: {name} differs"
+    cost = want[0] + want[2]
+    order = sorted(range(len(cost)), key=lambda i: (-int(cost[i]), i))
+    assert bm.schedule.cpu().numpy().tolist() == order, f"{w.name}: schedule"
+
+
+def _odd(name, dtype, H, L, S, kind, window=0, bounds=(), softcap=0.0, B=1):
+    return wl.Workload(name, B, H, L, S, 64, dtype, kind, window, bounds, softcap)
+
+
+MASK_CASES = list(wl.WORKLOADS.values()) + [
+    _odd("none_300x200", "bf16", 1, 300, 200, wl.MASK_NONE),
+    _odd("causal_1000", "bf16", 1, 1000, 1000, wl.MASK_CAUSAL),
+    _odd("causal_L200_S700", "bf16", 1, 200, 700, wl.MASK_CAUSAL),
+    _odd("causal_L700_S200", "bf16", 1, 700, 200, wl.MASK_CAUSAL),
+    _odd("sliding_w1", "bf16", 1, 1000, 1000, wl.MASK_SLIDING_WINDOW, 1),
+    _odd("sliding_w_gt_S", "bf16", 1, 1000, 1000, wl.MASK_SLIDING_WINDOW, 5000),
+    _odd("sliding_empty_rows", "bf16", 1, 400, 130, wl.MASK_SLIDING_WINDOW, 20),
+    _odd("document_ragged", "f16", 1, 1000, 1000, wl.MASK_DOCUMENT, 0, (300, 777)),
+    _odd("document_L_ne_S", "f16", 1, 600, 900, wl.MASK_DOCUMENT, 0, (130, 500)),
+    _odd("none_zero_kv", "bf16", 1, 256, 0, wl.MASK_NONE),
+]
+
+
+@pytest.mark.parametrize("w", MASK_CASES, ids=[w.name for w in MASK_CASES])
+def test_block_mask_bit_exact(dev, w):
+    bm, doc = _mask_on_gpu(w, dev)
+    _check_mask(bm, w, doc)
+
+
+def test_block_mask_unsorted_document_ids(dev):
+    w = _odd("document_random_ids", "bf16", 1, 777, 777, wl.MASK_DOCUMENT)
+    doc = np.random.default_rng(4).integers(0, 3, size=777).astype(np.int32)
+    bm, _ = _mask_on_gpu(w, dev, doc)
+    _check_mask(bm, w, doc)
+
+
+def _run(w: wl.Workload, dev, seed=0, doc=None, qkv=None):
+    q, k, v = wl.make_qkv(w, seed) if qkv is None else qkv
+    bm, doc = _mask_on_gpu(w, dev, doc)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o, lse = bsa.attention(qd, kd, vd, bm, score_mod="softcap" if w.softcap else None,
+                           softcap=w.softcap or 30.0, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    return (q, k, v), doc, o, lse
+
+
+def _compare(w, got_o, got_lse, want_o, want_lse, what):
+    tmax, tmean, tlse = TOL[w.dtype]
+    got_o = got_o.astype(np.float64)
+    err = np.abs(got_o - want_o)
+    assert np.isfinite(got_o).all(), f"{what}: non-finite output"
+    assert err.max() <= tmax, f"{what}: max-abs {err.max():.3g} > {tmax}"
+    assert err.mean() <= tmean, f"{what}: mean-abs {err.mean():.3g} > {tmean}"
+    empty = np.isneginf(want_lse)
+    assert np.array_equal(np.isneginf(got_lse), empty), f"{what}: empty-row pattern"
+    if (~empty).any():
+        lerr = np.abs(got_lse[~empty] - want_lse[~empty])
+        assert lerr.max() <= tlse, f"{what}: lse max-abs {lerr.max():.3g} > {tlse}"
+    assert np.all(got_o[empty] == 0.0), f"{what}: empty rows must be zero"
+
+
+SMALL = [
+    wl.WORKLOADS["causal_256_f32"],
+    _odd("causal_1024_bf16", "bf16", 2, 1024, 1024, wl.MASK_CAUSAL),
+    _odd("causal_1024_f16", "f16", 2, 1024, 1024, wl.MASK_CAUSAL),
+    _odd("sliding_w64_1024_bf16", "bf16", 2, 1024, 1024, wl.MASK_SLIDING_WINDOW, 64),
+    _odd("sliding_w256_2048_bf16", "bf16", 1, 2048, 2048, wl.MASK_SLIDING_WINDOW, 256),
+    _odd("sliding_w200_1000_f16", "f16", 2, 1000, 1000, wl.MASK_SLIDING_WINDOW, 200),
+    _odd("document_softcap_1000_f16", "f16", 2, 1000, 1000, wl.MASK_DOCUMENT, 0, (300, 777), 30.0),
+    _odd("document_softcap_1024_bf16", "bf16", 1, 1024, 1024, wl.MASK_DOCUMENT, 0, (256, 700), 30.0),
+    _odd("none_300x200_bf16", "bf16", 2, 300, 200, wl.MASK_NONE),
+    _odd("none_300x200_f32_softcap", "f32", 1, 300, 200, wl.MASK_NONE, 0, (), 5.0),
+    _odd("causal_L700_S200_f16", "f16", 1, 700, 200, wl.MASK_CAUSAL),
+    _odd("causal_L200_S700_bf16", "bf16", 1, 200, 700, wl.MASK_CAUSAL),
+    _odd("sliding_empty_rows_bf16", "bf16", 1, 400, 130, wl.MASK_SLIDING_WINDOW, 20),
+    _odd("sliding_w7_f32", "f32", 2, 333, 333, wl.MASK_SLIDING_WINDOW, 7),
+    _odd("document_f32", "f32", 1, 512, 512, wl.MASK_DOCUMENT, 0, (100, 300)),
+    _odd("causal_B2H3_bf16", "bf16", 3, 256, 256, wl.MASK_CAUSAL, B=2),
+    _odd("none_zero_kv_bf16", "bf16", 1, 256, 0, wl.MASK_NONE),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_forward_small_full_compare(dev, w):
+    (q, k, v), doc, o, lse = _run(w, dev)
+    want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(),
+                                        v.double().numpy(), w.kind, w.scale, w.window, doc,
+                                        w.softcap)
+    _compare(w, o.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), want_o, want_lse,
+             w.name)
+
+
+FULL = [wl.WORKLOADS[n] for n in ("causal_8192_bf16", "sliding_8192_w64_bf16",
+                                  "sliding_8192_w256_bf16", "sliding_8192_w1024_bf16",
+                                  "sliding_8192_w4096_bf16", "sliding_32768_w256_bf16",
+                                  "document_8192_f16_softcap")]
+
+
+@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def test_forward_full_size_sampled_rows(dev, w):
+    (q, k, v), doc, o, lse = _run(w, dev)
+    rows = wl.sample_rows(w, 192)
+    want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(),
+                                        v.double().numpy(), w.kind, w.scale, w.window, doc,
+                                        w.softcap, rows=rows)
+    o_all = o.float().reshape(-1, w.E)
+    got = o_all[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    got_lse = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    _compare(w, got, got_lse, want_o, want_lse, w.name)
+    # properties of every row: finite, a convex combination of V rows
+    assert torch.isfinite(o_all).all()
+    vmax = v.float().abs().amax().item()
+    assert o_all.abs().amax().item() <= vmax * (1 + 1e-2)
+    assert torch.isfinite(lse).all()  # no empty rows in these workloads
+
+
+def test_window_one_is_identity_bit_exact(dev):
+    w = _odd("sliding_w1_bf16", "bf16", 2, 1000, 1000, wl.MASK_SLIDING_WINDOW, 1)
+    (q, k, v), _, o, lse = _run(w, dev)
+    assert torch.equal(o.cpu(), v)
+    want = (q.double() * k.double()).sum(-1) * w.scale
+    assert (lse.cpu().double() - want).abs().max().item() <= 1e-5
+
+
+def test_uniform_v_gives_that_row(dev):
+    w = _odd("doc_uniform_v_f16", "f16", 2, 1000, 1000, wl.MASK_DOCUMENT, 0, (300, 777), 30.0)
+    q, k, v = wl.make_qkv(w, 1)
+    v = v[:, :, :1, :].expand_as(v).contiguous()
+    _, _, o, _ = _run(w, dev, qkv=(q, k, v))
+    err = (o.cpu().float() - v.float()).abs().max().item()
+    assert err <= 1e-2
+
+
+def test_deterministic_repeat(dev):
+    w = wl.WORKLOADS["causal_8192_bf16"]
+    q, k, v = (x.to(dev) for x in wl.make_qkv(w, 2))
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, device=dev)
+    o1, l1 = bsa.attention(q, k, v, bm, return_lse=True)
+    for _ in range(3):
+        o2, l2 = bsa.attention(q, k, v, bm, return_lse=True)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_strided_inputs_match_contiguous(dev):
+    """q/k/v as [B, H, S, E] views of [B, S, H, E] storage."""
+    w = _odd("causal_strided", "bf16", 4, 640, 640, wl.MASK_CAUSAL, B=2)
+    q, k, v = (x.to(dev) for x in wl.make_qkv(w, 3))
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, device=dev)
+    ref = bsa.attention(q, k, v, bm)
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    assert qs.stride(2) != 64
+    out = torch.empty(2, 640, 4, 64, dtype=torch.bfloat16, device=dev).transpose(1, 2)
+    got = bsa.attention(qs, ks, vs, bm, out=out)
+    assert torch.equal(got, ref)
+
+
+def test_lse_optional_and_mask_reuse(dev):
+    w = _odd("reuse", "bf16", 2, 512, 512, wl.MASK_SLIDING_WINDOW, 100)
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window, device=dev)
+    for seed in (0, 1):
+        q, k, v = (x.to(dev) for x in wl.make_qkv(w, seed))
+        o1 = bsa.attention(q, k, v, bm)
+        o2, _ = bsa.attention(q, k, v, bm, return_lse=True)
+        assert torch.equal(o1, o2)
+
+
+def test_errors_raise(dev):
+    q = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16, device=dev)
+    bm = bsa.create_block_mask("causal", 128, 128, device=dev)
+    with pytest.raises(bsa.BsattnError):
+        bsa.attention(q, q, q, bm)  # mask built for other lengths
+    q128 = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(bsa.BsattnError):
+        bsa.attention(q128, q128, q128, bm)  # head dim 128 has no kernel
