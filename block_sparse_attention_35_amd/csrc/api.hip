@@ -44,6 +44,10 @@ attn_status strides_of(const char* name, const int64_t* st, int32_t B, int32_t H
     out[0] = (int64_t)H * len * E;
     return ATTN_OK;
   }
+  if (len == 0) {  // no elements: strides are never used
+    out[0] = out[1] = out[2] = 0;
+    return ATTN_OK;
+  }
   if (st[3] != 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "%s: head-dim stride must be 1", name);
   const int32_t size[3] = {B, H, len};
   for (int d = 0; d < 3; ++d) {

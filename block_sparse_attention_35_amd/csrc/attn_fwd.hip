@@ -39,6 +39,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -52,16 +54,28 @@ template <>
 struct Vec<__bf16> {
   using x8 = bf16x8_t;
   using x4 = bf16x4_t;
+  using x2 = bf16x2_t;
   static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // acc + a.x + a.y in fp32 (v_dot2c_f32_bf16 against (1, 1))
+  static __device__ inline float add_pair(x2 a, float acc) {
+    const x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(a, one, acc, false);
   }
 };
 template <>
 struct Vec<_Float16> {
   using x8 = f16x8_t;
   using x4 = f16x4_t;
+  using x2 = f16x2_t;
   static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // acc + a.x + a.y in fp32 (v_dot2c_f32_f16 against (1, 1))
+  static __device__ inline float add_pair(x2 a, float acc) {
+    const x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(a, one, acc, false);
   }
 };
 
@@ -278,10 +292,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const T pv = (T)s[g >> 1][(g & 1) * 8 + u];
-        pk[g][u] = pv;
-        psum += (float)pv;
+      for (int u = 0; u < 8; u += 2) {
+        const typename V::x2 pr = {(T)s[g >> 1][(g & 1) * 8 + u], (T)s[g >> 1][(g & 1) * 8 + u + 1]};
+        psum = V::add_pair(pr, psum);
+        pk[g][u] = pr[0];
+        pk[g][u + 1] = pr[1];
       }
     }
     st.l = st.l * alpha + psum;

@@ -151,7 +151,11 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
  *   for the contiguous layout. The head-dim stride must be 1; base pointers
  *   and the other strides must keep every row 16-byte aligned.
  *   lse  device fp32 [B, H, L] contiguous, natural-log logsumexp of each row's
- *        scores after scale, score_mod and mask; may be NULL.
+ *        scores after scale, score_mod and mask; may be NULL. It is the log
+ *        of the normaliser O is divided by, whose terms are the probabilities
+ *        as rounded for the P.V product (relative rounding <= 2^-8 for bf16,
+ *        2^-11 for fp16), so it carries that rounding.
+ *   q, k, v, o may be NULL only when they have no elements.
  *   bm   a BlockMask built for q_len == L and kv_len == S.
  *   score_mod ATTN_SCORE_NONE or ATTN_SCORE_SOFTCAP (then softcap > 0).
  *   scale  multiplier of q.k (pass 1/sqrt(E) for the usual attention).
