@@ -162,19 +162,188 @@ __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, in
   return alpha;
 }
 
-__device__ inline int swz_v(int e) { return (e ^ (e >> 3)) & 7; }
-
 // ---------------------------------------------------------------------------
 // bf16 / fp16 kernel
 // ---------------------------------------------------------------------------
+// One pipeline stage in LDS: a 128-key tile of K and of V, both row-major
+// (128 rows x 128 bytes), and the tile's document ids. Rows are split in eight
+// 16-byte chunks stored XOR-swizzled: K chunk c of row r sits in slot
+// c ^ (r & 7) (conflict-free 16-byte reads of 8 consecutive rows); V chunk c
+// sits in slot c ^ 2(r & 3) (conflict-free transposed reads of 4 rows x 32
+// bytes by each 16-lane group).
+struct alignas(16) Stage16 {
+  uint8_t k[kBlock * 128];
+  uint8_t v[kBlock * 128];
+  int32_t doc[kBlock];
+};
+
+// The running max only moves when a block's max exceeds it by more than this
+// many powers of two, so probabilities stay <= 2^8 and the accumulator rescale
+// is skipped for most blocks. The result is algebraically the same: numerator
+// and normaliser share the reference.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Workgroup barrier without memory fences: the caller waits for exactly the
+// memory operations it needs first (the fences of __syncthreads would also
+// wait for the next tile's in-flight copies). The signal fences only keep the
+// compiler from moving memory accesses across the barrier.
+__device__ inline void barrier_only() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ inline void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Block index lists are read through the constant address space so the loads
+// are scalar (they never change during a launch).
+typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+
+__device__ inline void wait_vmcnt_le(int n) {
+  // s_waitcnt immediate (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+  else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+  else __builtin_amdgcn_s_waitcnt(0x0F79);  // 9
+}
+
+// Direct global -> LDS copies of one key tile (each wave: 4 KiB of K, 4 KiB of
+// V, and for document masks the tile's ids). Lane l of a wave-load writes
+// bytes [16l, 16l+16) of a 1 KiB LDS block, i.e. slot l & 7 of row
+// 8*block + l/8, so it fetches the global chunk that the swizzle puts there.
+// Rows past the end are clamped to the last key (their scores are masked).
+template <typename T, int KIND>
+__device__ inline void issue_tile(const T* kg, const T* vg, int64_t k_sl, int64_t v_sl,
+                                  const int32_t* doc, int kv0, int S, Stage16& st, int wave,
+                                  int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-copy builtin exists only for the device pass
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave * 4 + i;
+    const int row = blk * 8 + (lane >> 3);
+    const int slot = lane & 7;
+    const int64_t grow = min(kv0 + row, S - 1);
+    const T* ksrc = kg + grow * k_sl + ((slot ^ (row & 7)) << 3);
+    const T* vsrc = vg + grow * v_sl + ((slot ^ ((row & 3) << 1)) << 3);
+    __builtin_amdgcn_global_load_lds(ksrc, st.k + blk * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vsrc, st.v + blk * 1024, 16, 0, 0);
+  }
+  if (KIND == ATTN_MASK_DOCUMENT) {
+    // ids of keys 32*wave .. 32*wave+31 of the tile, 4 bytes per lane
+    if (lane < 32) {
+      const int64_t j = min(kv0 + wave * 32 + lane, S - 1);
+      __builtin_amdgcn_global_load_lds(doc + j, st.doc + wave * 32, 4, 0, 0);
+    }
+  }
+#endif
+}
+
+template <typename T, int KIND, bool SOFTCAP, bool PARTIAL>
+__device__ inline void compute_block(const Stage16& stg, const typename Vec<T>::x8 (&qop)[4],
+                                     f32x16_t (&oacc)[2], RowState& rs, int qi, int kv0, int lane,
+                                     const FwdArgs& a, int32_t dq) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  const int lq = lane & 31, hf = lane >> 5;
+
+  // S^T = K Q^T: 4 tiles of 32 keys x 32 queries, contraction over E=64.
+  f32x16_t s[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+    const int row = t * 32 + lq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const x8 ka = *reinterpret_cast<const x8*>(stg.k + row * 128 + (((2 * c + hf) ^ (row & 7)) << 4));
+      s[t] = V::mma(ka, qop[c], s[t]);
+    }
+  }
+
+  // Scale, score_mod, mask; block max.
+  const float c1 = a.scale * kLog2e;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[t][r];
+      if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
+      if (PARTIAL) {
+        const int jl = t * 32 + acc_row(r, hf);
+        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? stg.doc[jl] : 0;
+        if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
+      }
+      s[t][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = half_max(mx);
+  const float m_blk = SOFTCAP ? mx : mx * c1;
+  const bool grow = m_blk > rs.m + kRescaleLog2;
+  const float alpha = grow ? fast_exp2(rs.m - m_blk) : 1.0f;
+  if (grow) rs.m = m_blk;
+  const float m_use = (rs.m == -INFINITY) ? 0.0f : rs.m;
+
+  // Probabilities, rounded to T (nearest even) for P V; the normaliser sums
+  // the rounded values.
+  x8 pk[8];
+  float psum = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const float x0 = s[g >> 1][(g & 1) * 8 + u], x1 = s[g >> 1][(g & 1) * 8 + u + 1];
+      const float p0 = SOFTCAP ? fast_exp2(x0 - m_use) : fast_exp2(fmaf(x0, c1, -m_use));
+      const float p1 = SOFTCAP ? fast_exp2(x1 - m_use) : fast_exp2(fmaf(x1, c1, -m_use));
+      const typename V::x2 pr = {(T)p0, (T)p1};
+      psum = V::add_pair(pr, psum);
+      pk[g][u] = pr[0];
+      pk[g][u + 1] = pr[1];
+    }
+  }
+  if (__ballot(grow) != 0) {
+    rs.l *= alpha;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
+  }
+  rs.l += psum;
+
+  // O^T += V^T P^T. For 16-key group g, lane half hf holds keys
+  // 16g + 4hf + {0..3} and 16g + 8 + 4hf + {0..3} of P^T; the matching V^T
+  // operand comes from two transposed LDS reads: in each 16-lane group, lane i
+  // supplies the address of row (key) r0 + i/4, head dims eb + 4(i%4) .. +3,
+  // and receives head dim eb + i of rows r0 .. r0+3.
+  const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+  for (int te = 0; te < 2; ++te) {
+    const int e = te * 32 + (g16 & 1) * 16 + (i16 & 3) * 4;
+    const int c16 = e >> 3, half = (e >> 2) & 1;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int r1 = g * 16 + hf * 4 + (i16 >> 2);
+      const int off = ((c16 ^ ((r1 & 3) << 1)) << 4) + half * 8;
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(stg.v + r1 * 128 + off));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(stg.v + (r1 + 8) * 128 + off));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[te] = V::mma(__builtin_bit_cast(x8, both), pk[g], oacc[te]);
+    }
+  }
+}
+
 template <typename T, int KIND, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   using V = Vec<T>;
   using x8 = typename V::x8;
   using x4 = typename V::x4;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBlock * kHeadDim * 2];  // [kv][e]
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kHeadDim * kBlock * 2];  // [e][kv perm]
-  __shared__ int32_t doc_k[kBlock];
+  __shared__ Stage16 stage0;
+  __shared__ Stage16 stage1;
+  constexpr int kLoads = (KIND == ATTN_MASK_DOCUMENT) ? 9 : 8;  // per wave per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -189,6 +358,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + h * a.k_sh;
   const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + h * a.v_sh;
   T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
+
+  const int nfull = a.m.full_num[qb];
+  const int npart = a.m.kv_num[qb];
+  const int nblk = nfull + npart;
+  const const_i32_ptr full_list = (const_i32_ptr)(a.m.full_idx + (int64_t)qb * a.m.nk);
+  const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
+  auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
+
+  int kv_cur = 0;
+  if (nblk > 0) {
+    kv_cur = kv_start(0);
+    issue_tile<T, KIND>(kg, vg, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, stage0, wave, lane);
+  }
 
   const int qi = qb * kBlock + wave * 32 + lq;  // this lane's query row
   x8 qop[4];
@@ -206,120 +388,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   for (int te = 0; te < 2; ++te)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
-  RowState st{-INFINITY, 0.0f};
+  RowState rs{-INFINITY, 0.0f};
 
-  const int nfull = a.m.full_num[qb];
-  const int npart = a.m.kv_num[qb];
-  const int32_t* full_list = a.m.full_idx + (int64_t)qb * a.m.nk;
-  const int32_t* part_list = a.m.kv_idx + (int64_t)qb * a.m.nk;
-
-  for (int n = 0; n < nfull + npart; ++n) {
-    const bool partial = n >= nfull;
-    const int kb = partial ? part_list[n - nfull] : full_list[n];
-    const int kv0 = kb * kBlock;
-
-    __syncthreads();  // the previous block's LDS reads are done
-    // K: 1024 chunks of 16 bytes, row-major, chunk index XOR (row & 7).
+  // Two LDS stages: while block n is computed from one, block n+1 streams
+  // into the other.
+  for (int n = 0; n < nblk; n += 2) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int cidx = tid + u * kThreads;
-      const int row = cidx >> 3, ch = cidx & 7;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (kv0 + row < a.S)
-        val = *reinterpret_cast<const uint4*>(kg + (int64_t)(kv0 + row) * a.k_sl + ch * 8);
-      *reinterpret_cast<uint4*>(k_lds + row * 128 + ((ch ^ (row & 7)) << 4)) = val;
-    }
-    // V: thread owns kv rows 4*kvg..4*kvg+3 and head-dim columns 8*ec..8*ec+7
-    // and writes them transposed: for each column e, the 4 kv values as one
-    // 8-byte group. Within a 16-kv group g the stored order is
-    // [0..3, 8..11 | 4..7, 12..15] so lane half hf reads kv 4hf+{0..3} and
-    // 8+4hf+{0..3} as one 16-byte chunk (2g + hf).
-    {
-      const int kvg = tid >> 3, ec = tid & 7;
-      uint4 rows[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kv = kv0 + kvg * 4 + r;
-        rows[r] = make_uint4(0, 0, 0, 0);
-        if (kv < a.S)
-          rows[r] = *reinterpret_cast<const uint4*>(vg + (int64_t)kv * a.v_sl + ec * 8);
-      }
-      const int g = kvg >> 2, rr = kvg & 3;
-      const int chunk = 2 * g + (rr & 1);
-      const int byte_in = (rr >> 1) * 8;
-      const uint16_t* r16[4] = {reinterpret_cast<const uint16_t*>(&rows[0]),
-                                reinterpret_cast<const uint16_t*>(&rows[1]),
-                                reinterpret_cast<const uint16_t*>(&rows[2]),
-                                reinterpret_cast<const uint16_t*>(&rows[3])};
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int e = ec * 8 + x;
-        uint2 pk;
-        pk.x = (uint32_t)r16[0][x] | ((uint32_t)r16[1][x] << 16);
-        pk.y = (uint32_t)r16[2][x] | ((uint32_t)r16[3][x] << 16);
-        *reinterpret_cast<uint2*>(v_lds + e * 256 + ((chunk ^ swz_v(e)) << 4) + byte_in) = pk;
-      }
-    }
-    if (KIND == ATTN_MASK_DOCUMENT && partial && tid < kBlock)
-      doc_k[tid] = (kv0 + tid < a.S) ? a.m.doc[kv0 + tid] : -1;
-    __syncthreads();
-
-    // S^T = K Q^T: 4 tiles of 32 kv x 32 queries, contraction over E=64.
-    f32x16_t s[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-      const int row = t * 32 + lq;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int ch = 2 * c + hf;
-        const x8 ka = *reinterpret_cast<const x8*>(k_lds + row * 128 + ((ch ^ (row & 7)) << 4));
-        s[t] = V::mma(ka, qop[c], s[t]);
-      }
-    }
-
-    float alpha;
-    if (partial)
-      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
-    else
-      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
-
-    // Pack probabilities to 16 bits (round to nearest even) and sum the
-    // rounded values, so the normaliser matches the weights used in P V.
-    x8 pk[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-#pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        const typename V::x2 pr = {(T)s[g >> 1][(g & 1) * 8 + u], (T)s[g >> 1][(g & 1) * 8 + u + 1]};
-        psum = V::add_pair(pr, psum);
-        pk[g][u] = pr[0];
-        pk[g][u + 1] = pr[1];
-      }
-    }
-    st.l = st.l * alpha + psum;
-#pragma unroll
-    for (int te = 0; te < 2; ++te)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
-
-    // O^T += V^T P^T: 2 tiles of 32 head-dims x 32 queries, contraction over
-    // the block's 128 keys in 8 chunks of 16.
-#pragma unroll
-    for (int te = 0; te < 2; ++te) {
-      const int e = te * 32 + lq;
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const x8 va = *reinterpret_cast<const x8*>(v_lds + e * 256 + (((2 * g + hf) ^ swz_v(e)) << 4));
-        oacc[te] = V::mma(va, pk[g], oacc[te]);
+    for (int par = 0; par < 2; ++par) {
+      const int m = n + par;
+      if (m < nblk) {
+        Stage16& cur = par ? stage1 : stage0;
+        Stage16& nxt = par ? stage0 : stage1;
+        const int kv0 = kv_cur;
+        if (m + 1 < nblk) {
+          kv_cur = kv_start(m + 1);
+          issue_tile<T, KIND>(kg, vg, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, nxt, wave, lane);
+          wait_vmcnt_le(kLoads);
+        } else {
+          wait_vmcnt_le(0);
+        }
+        barrier_only();  // this tile is in LDS for every wave
+        if (m >= nfull)
+          compute_block<T, KIND, SOFTCAP, true>(cur, qop, oacc, rs, qi, kv0, lane, a, dq);
+        else
+          compute_block<T, KIND, SOFTCAP, false>(cur, qop, oacc, rs, qi, kv0, lane, a, dq);
+        wait_lgkm_zero();
+        barrier_only();  // every wave is done reading this stage before it is refilled
       }
     }
   }
 
   // Epilogue: O = O^T / l (0 for a row without live keys), lse = ln(sum exp).
-  const float l = half_sum(st.l);
+  const float l = half_sum(rs.l);
   const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
   if (qi < a.L) {
 #pragma unroll
@@ -334,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       }
     }
     if (a.lse != nullptr && hf == 0)
-      a.lse[(int64_t)bh * a.L + qi] = (l > 0.0f) ? (st.m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)bh * a.L + qi] = (l > 0.0f) ? (rs.m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   }
 }
 
