@@ -193,48 +193,90 @@ __device__ inline void barrier_only() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
+// | vmcnt[5:4] << 14), leaving the other counters unconstrained.
+__device__ inline void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Block index lists are read through the constant address space so the loads
 // are scalar (they never change during a launch).
 typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 
-__device__ inline void wait_vmcnt_le(int n) {
-  // s_waitcnt immediate (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-  if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
-  else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
-  else __builtin_amdgcn_s_waitcnt(0x0F79);  // 9
+// Global -> LDS copies (global_load_lds_dword{x4}): lane l writes bytes
+// [size*l, size*(l+1)) after the wave-uniform base in M0. They are issued as
+// inline asm so that the compiler's own wait insertion, which cannot tell
+// these LDS writes from the stage being read, adds no wait for the copies in
+// flight before every LDS read; every wait on them is explicit (wait_vm_zero,
+// then a barrier). The instructions have no result registers and their
+// address registers are read at issue.
+__device__ inline uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ inline void lds_copy16(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_wave_base)
+               : "memory");
+}
+__device__ inline void lds_copy4(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds_wave_base)
+               : "memory");
 }
 
-// Direct global -> LDS copies of one key tile (each wave: 4 KiB of K, 4 KiB of
-// V, and for document masks the tile's ids). Lane l of a wave-load writes
-// bytes [16l, 16l+16) of a 1 KiB LDS block, i.e. slot l & 7 of row
-// 8*block + l/8, so it fetches the global chunk that the swizzle puts there.
-// Rows past the end are clamped to the last key (their scores are masked).
+// One wave's share of a tile copy: tile rows 32w .. 32w+31 of K and of V
+// (4 KiB each) and, for document masks, their ids. Lane l of copy i fills
+// slot l & 7 of tile row 32w + 8i + l/8 and fetches the global chunk that the
+// swizzle puts there; the chunk index depends only on the lane, so the
+// per-lane element offsets are computed once and each copy adds a
+// wave-uniform base. Rows past the end are clamped to the last key (their
+// scores are masked); that only happens on a ragged last tile.
+struct CopyPlan {
+  int64_t koff, voff;  // element offset of copy 0 for this lane, relative to the tile's row 0
+  int row;             // tile row of copy 0 for this lane
+};
+
+template <typename T>
+__device__ inline CopyPlan make_copy_plan(int64_t k_sl, int64_t v_sl, int wave, int lane) {
+  const int row = wave * 32 + (lane >> 3);
+  const int ck = (lane & 7) ^ (lane >> 3);               // K: slot ^ (row & 7)
+  const int cv = (lane & 7) ^ (((lane >> 3) & 3) << 1);  // V: slot ^ 2(row & 3)
+  return CopyPlan{row * k_sl + ck * 8, row * v_sl + cv * 8, row};
+}
+
 template <typename T, int KIND>
-__device__ inline void issue_tile(const T* kg, const T* vg, int64_t k_sl, int64_t v_sl,
-                                  const int32_t* doc, int kv0, int S, Stage16& st, int wave,
-                                  int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-copy builtin exists only for the device pass
+__device__ inline void issue_tile(const T* kg, const T* vg, const CopyPlan& cp, int64_t k_sl,
+                                  int64_t v_sl, const int32_t* doc, int kv0, int S, Stage16& st,
+                                  int wave, int lane) {
+  const T* kb = kg + (int64_t)kv0 * k_sl;
+  const T* vb = vg + (int64_t)kv0 * v_sl;
+  if (kv0 + kBlock <= S) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave * 4 + i;
-    const int row = blk * 8 + (lane >> 3);
-    const int slot = lane & 7;
-    const int64_t grow = min(kv0 + row, S - 1);
-    const T* ksrc = kg + grow * k_sl + ((slot ^ (row & 7)) << 3);
-    const T* vsrc = vg + grow * v_sl + ((slot ^ ((row & 3) << 1)) << 3);
-    __builtin_amdgcn_global_load_lds(ksrc, st.k + blk * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vsrc, st.v + blk * 1024, 16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      lds_copy16(kb + i * 8 * k_sl + cp.koff, __builtin_amdgcn_readfirstlane(lds_offset(st.k + blk * 1024)));
+      lds_copy16(vb + i * 8 * v_sl + cp.voff, __builtin_amdgcn_readfirstlane(lds_offset(st.v + blk * 1024)));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      const int row = cp.row + i * 8;
+      const int64_t back = (int64_t)max(kv0 + row - (S - 1), 0);  // rows to step back
+      lds_copy16(kb + i * 8 * k_sl + cp.koff - back * k_sl,
+                 __builtin_amdgcn_readfirstlane(lds_offset(st.k + blk * 1024)));
+      lds_copy16(vb + i * 8 * v_sl + cp.voff - back * v_sl,
+                 __builtin_amdgcn_readfirstlane(lds_offset(st.v + blk * 1024)));
+    }
   }
   if (KIND == ATTN_MASK_DOCUMENT) {
     // ids of keys 32*wave .. 32*wave+31 of the tile, 4 bytes per lane
     if (lane < 32) {
       const int64_t j = min(kv0 + wave * 32 + lane, S - 1);
-      __builtin_amdgcn_global_load_lds(doc + j, st.doc + wave * 32, 4, 0, 0);
+      lds_copy4(doc + j, __builtin_amdgcn_readfirstlane(lds_offset(st.doc + wave * 32)));
     }
   }
-#endif
 }
 
 template <typename T, int KIND, bool SOFTCAP, bool PARTIAL>
@@ -343,7 +385,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   using x4 = typename V::x4;
   __shared__ Stage16 stage0;
   __shared__ Stage16 stage1;
-  constexpr int kLoads = (KIND == ATTN_MASK_DOCUMENT) ? 9 : 8;  // per wave per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -364,12 +405,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const int nblk = nfull + npart;
   const const_i32_ptr full_list = (const_i32_ptr)(a.m.full_idx + (int64_t)qb * a.m.nk);
   const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
+  // First key of the n-th visited block: full blocks first, then partial.
   auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
+  const CopyPlan cp = make_copy_plan<T>(a.k_sl, a.v_sl, wave, lane);
 
   int kv_cur = 0;
   if (nblk > 0) {
     kv_cur = kv_start(0);
-    issue_tile<T, KIND>(kg, vg, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, stage0, wave, lane);
+    issue_tile<T, KIND>(kg, vg, cp, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, stage0, wave, lane);
   }
 
   const int qi = qb * kBlock + wave * 32 + lq;  // this lane's query row
@@ -382,6 +425,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       qop[c] = x8{};
   }
   const int32_t dq = (KIND == ATTN_MASK_DOCUMENT && qi < a.L) ? a.m.doc[qi] : -1;
+  // Q, dq and tile 0 have landed: no load the compiler tracks is still in
+  // flight inside the loop, so it adds no wait there (such a wait would also
+  // drain the next tile's copies, which share the in-order counter).
+  wait_vm_zero();
 
   f32x16_t oacc[2];
 #pragma unroll
@@ -390,8 +437,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
   RowState rs{-INFINITY, 0.0f};
 
-  // Two LDS stages: while block n is computed from one, block n+1 streams
-  // into the other.
+  // Two LDS stages and one barrier per block: once every wave's copies of
+  // block m have landed and every wave has finished block m-1, the copies of
+  // block m+1 go into the stage block m-1 used, and block m is computed.
   for (int n = 0; n < nblk; n += 2) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
@@ -400,20 +448,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
         Stage16& cur = par ? stage1 : stage0;
         Stage16& nxt = par ? stage0 : stage1;
         const int kv0 = kv_cur;
+        wait_vm_zero();    // this wave's copies of block m
+        wait_lgkm_zero();  // this wave's reads of block m-1
+        barrier_only();
         if (m + 1 < nblk) {
           kv_cur = kv_start(m + 1);
-          issue_tile<T, KIND>(kg, vg, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, nxt, wave, lane);
-          wait_vmcnt_le(kLoads);
-        } else {
-          wait_vmcnt_le(0);
+          issue_tile<T, KIND>(kg, vg, cp, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, nxt, wave, lane);
         }
-        barrier_only();  // this tile is in LDS for every wave
         if (m >= nfull)
           compute_block<T, KIND, SOFTCAP, true>(cur, qop, oacc, rs, qi, kv0, lane, a, dq);
         else
           compute_block<T, KIND, SOFTCAP, false>(cur, qop, oacc, rs, qi, kv0, lane, a, dq);
-        wait_lgkm_zero();
-        barrier_only();  // every wave is done reading this stage before it is refilled
       }
     }
   }
