@@ -31,6 +31,8 @@ bool arrays_present(const attn_block_mask* bm, int32_t nq, int32_t nk) {
   return per_q && per_pair;
 }
 
+constexpr int64_t kMaxSeqStride = int64_t(1) << 24;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Fill batch/head/sequence strides (elements) and check the head-dim stride
@@ -165,6 +167,10 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
   a.v_sb = st[0], a.v_sh = st[1], a.v_sl = st[2];
   if ((s = strides_of("o", o_strides, B, H, L, E, esize, st)) != ATTN_OK) return s;
   a.o_sb = st[0], a.o_sh = st[1], a.o_sl = st[2];
+  // Tile copies address 8 consecutive K/V rows with a 32-bit byte offset.
+  if (a.k_sl > kMaxSeqStride || a.v_sl > kMaxSeqStride)
+    return fail(ATTN_ERR_UNSUPPORTED, "k/v sequence stride above %lld elements",
+                (long long)kMaxSeqStride);
   if ((int64_t)B * H * bm->num_q_blocks > 0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "too many work items");
 

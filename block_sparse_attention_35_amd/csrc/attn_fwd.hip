@@ -28,6 +28,7 @@
 // bf16/fp16 use v_mfma_f32_32x32x16_{bf16,f16}; fp32 uses v_mfma_f32_32x32x2_f32
 // and keeps probabilities in fp32.
 #include <cmath>
+#include <type_traits>
 
 #include "bsattn.h"
 #include "internal.h"
@@ -165,16 +166,18 @@ __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, in
 // ---------------------------------------------------------------------------
 // bf16 / fp16 kernel
 // ---------------------------------------------------------------------------
-// One pipeline stage in LDS: a 128-key tile of K and of V, both row-major
-// (128 rows x 128 bytes), and the tile's document ids. Rows are split in eight
-// 16-byte chunks stored XOR-swizzled: K chunk c of row r sits in slot
-// c ^ (r & 7) (conflict-free 16-byte reads of 8 consecutive rows); V chunk c
-// sits in slot c ^ 2(r & 3) (conflict-free transposed reads of 4 rows x 32
-// bytes by each 16-lane group).
-struct alignas(16) Stage16 {
+// LDS holds two K tiles and two V tiles (128 rows x 128 bytes each, row-major)
+// plus the document ids of each K tile. Rows are split in eight 16-byte
+// chunks stored XOR-swizzled: K chunk c of row r sits in slot c ^ (r & 7)
+// (conflict-free 16-byte reads of 8 consecutive rows); V chunk c sits in slot
+// c ^ 2(r & 3) (conflict-free transposed reads of 4 rows x 32 bytes by each
+// 16-lane group).
+struct alignas(16) KStage {
   uint8_t k[kBlock * 128];
-  uint8_t v[kBlock * 128];
   int32_t doc[kBlock];
+};
+struct alignas(16) VStage {
+  uint8_t v[kBlock * 128];
 };
 
 // The running max only moves when a block's max exceeds it by more than this
@@ -205,104 +208,102 @@ typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 // Global -> LDS copies (global_load_lds_dword{x4}): lane l writes bytes
 // [size*l, size*(l+1)) after the wave-uniform base in M0. They are issued as
 // inline asm so that the compiler's own wait insertion, which cannot tell
-// these LDS writes from the stage being read, adds no wait for the copies in
+// these LDS writes from the tiles being read, adds no wait for the copies in
 // flight before every LDS read; every wait on them is explicit (wait_vm_zero,
 // then a barrier). The instructions have no result registers and their
-// address registers are read at issue.
+// address registers are read at issue. The first form takes a 64-bit
+// address per lane; the second a wave-uniform base in SGPRs plus a 32-bit
+// byte offset per lane, which keeps the per-tile address arithmetic scalar.
 __device__ inline uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 __device__ inline void lds_copy16(const void* src, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(lds_wave_base)
-               : "memory");
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
+}
+__device__ inline void lds_copy16_base(const void* sbase, uint32_t lane_off, uint32_t lds_wave_base) {
+  // readfirstlane returns int: widen through uint32_t so the low word is
+  // zero-extended (a sign extension would set the high word's bits).
+  const uint64_t p = (uint64_t)(uintptr_t)sbase;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"((const void*)(uintptr_t)(lo | (hi << 32))),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
 }
 __device__ inline void lds_copy4(const void* src, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                :
-               : "v"(src), "s"(lds_wave_base)
-               : "memory");
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
 }
 
-// One wave's share of a tile copy: tile rows 32w .. 32w+31 of K and of V
-// (4 KiB each) and, for document masks, their ids. Lane l of copy i fills
-// slot l & 7 of tile row 32w + 8i + l/8 and fetches the global chunk that the
-// swizzle puts there; the chunk index depends only on the lane, so the
-// per-lane element offsets are computed once and each copy adds a
-// wave-uniform base. Rows past the end are clamped to the last key (their
-// scores are masked); that only happens on a ragged last tile.
-struct CopyPlan {
-  int64_t koff, voff;  // element offset of copy 0 for this lane, relative to the tile's row 0
-  int row;             // tile row of copy 0 for this lane
-};
-
-template <typename T>
-__device__ inline CopyPlan make_copy_plan(int64_t k_sl, int64_t v_sl, int wave, int lane) {
-  const int row = wave * 32 + (lane >> 3);
-  const int ck = (lane & 7) ^ (lane >> 3);               // K: slot ^ (row & 7)
-  const int cv = (lane & 7) ^ (((lane >> 3) & 3) << 1);  // V: slot ^ 2(row & 3)
-  return CopyPlan{row * k_sl + ck * 8, row * v_sl + cv * 8, row};
+// One wave's share of a tile copy: tile rows 32w .. 32w+31 (4 KiB), four
+// copies of 8 rows. Lane l of copy i fills slot l & 7 of tile row
+// 32w + 8i + l/8 and fetches the global chunk that the swizzle puts there;
+// that chunk depends only on the lane, so the per-lane byte offset (relative
+// to the copy's first row) is fixed for the whole launch. Rows past the end
+// are clamped to the last key (their scores are masked); that only happens on
+// a ragged last tile.
+template <typename T, bool IS_V>
+__device__ inline void issue_rows(const T* g, int64_t sl, uint32_t lane_off, int kv0, int S,
+                                  uint8_t* tile, int wave, int lane) {
+  const int row0 = kv0 + wave * 32;  // first key of this wave's rows
+  const uint32_t lds0 = lds_offset(tile) + (uint32_t)wave * 4096u;
+  if (kv0 + kBlock <= S) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_copy16_base(g + (int64_t)(row0 + 8 * i) * sl, lane_off, lds0 + 1024u * i);
+  } else {
+    const int chunk = IS_V ? ((lane & 7) ^ (((lane >> 3) & 3) << 1)) : ((lane & 7) ^ (lane >> 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(row0 + 8 * i + (lane >> 3), S - 1);
+      lds_copy16(g + (int64_t)key * sl + chunk * 8, lds0 + 1024u * i);
+    }
+  }
 }
 
 template <typename T, int KIND>
-__device__ inline void issue_tile(const T* kg, const T* vg, const CopyPlan& cp, int64_t k_sl,
-                                  int64_t v_sl, const int32_t* doc, int kv0, int S, Stage16& st,
-                                  int wave, int lane) {
-  const T* kb = kg + (int64_t)kv0 * k_sl;
-  const T* vb = vg + (int64_t)kv0 * v_sl;
-  if (kv0 + kBlock <= S) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = wave * 4 + i;
-      lds_copy16(kb + i * 8 * k_sl + cp.koff, __builtin_amdgcn_readfirstlane(lds_offset(st.k + blk * 1024)));
-      lds_copy16(vb + i * 8 * v_sl + cp.voff, __builtin_amdgcn_readfirstlane(lds_offset(st.v + blk * 1024)));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = wave * 4 + i;
-      const int row = cp.row + i * 8;
-      const int64_t back = (int64_t)max(kv0 + row - (S - 1), 0);  // rows to step back
-      lds_copy16(kb + i * 8 * k_sl + cp.koff - back * k_sl,
-                 __builtin_amdgcn_readfirstlane(lds_offset(st.k + blk * 1024)));
-      lds_copy16(vb + i * 8 * v_sl + cp.voff - back * v_sl,
-                 __builtin_amdgcn_readfirstlane(lds_offset(st.v + blk * 1024)));
-    }
-  }
+__device__ inline void issue_k(const T* kg, int64_t k_sl, uint32_t k_off, const int32_t* doc, int kv0,
+                               int S, KStage& st, int wave, int lane) {
+  issue_rows<T, false>(kg, k_sl, k_off, kv0, S, st.k, wave, lane);
   if (KIND == ATTN_MASK_DOCUMENT) {
     // ids of keys 32*wave .. 32*wave+31 of the tile, 4 bytes per lane
     if (lane < 32) {
       const int64_t j = min(kv0 + wave * 32 + lane, S - 1);
-      lds_copy4(doc + j, __builtin_amdgcn_readfirstlane(lds_offset(st.doc + wave * 32)));
+      lds_copy4(doc + j, lds_offset(st.doc) + (uint32_t)wave * 128u);
     }
   }
 }
 
-template <typename T, int KIND, bool SOFTCAP, bool PARTIAL>
-__device__ inline void compute_block(const Stage16& stg, const typename Vec<T>::x8 (&qop)[4],
-                                     f32x16_t (&oacc)[2], RowState& rs, int qi, int kv0, int lane,
-                                     const FwdArgs& a, int32_t dq) {
-  using V = Vec<T>;
-  using x8 = typename V::x8;
-  const int lq = lane & 31, hf = lane >> 5;
-
-  // S^T = K Q^T: 4 tiles of 32 keys x 32 queries, contraction over E=64.
-  f32x16_t s[4];
+// S^T = K Q^T for one 128-key tile: 4 tiles of 32 keys x 32 queries,
+// contraction over E = 64 (kp: per-lane K addresses of the stage, see
+// LanePtrs).
+template <typename T>
+__device__ inline void qk_tile(__attribute__((address_space(3))) const uint8_t* const (&kp)[4],
+                               const typename Vec<T>::x8 (&qop)[4], f32x16_t (&s)[4]) {
+  using x8 = typename Vec<T>::x8;
+  typedef __attribute__((address_space(3))) const x8 lds_x8;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-    const int row = t * 32 + lq;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const x8 ka = *reinterpret_cast<const x8*>(stg.k + row * 128 + (((2 * c + hf) ^ (row & 7)) << 4));
-      s[t] = V::mma(ka, qop[c], s[t]);
-    }
+    for (int c = 0; c < 4; ++c) s[t] = Vec<T>::mma(*reinterpret_cast<const lds_x8*>(kp[c] + t * 4096), qop[c], s[t]);
   }
+}
 
-  // Scale, score_mod, mask; block max.
-  const float c1 = a.scale * kLog2e;
+// Score_mod and mask applied in place; returns the block's row max in log2
+// units (-inf when no key of the block is live for this row).
+template <int KIND, bool SOFTCAP, bool PARTIAL>
+__device__ inline float mask_max(f32x16_t (&s)[4], const KStage& st, int qi, int kv0, int lane,
+                                 const FwdArgs& a, int32_t dq) {
+  const int hf = lane >> 5;
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -312,7 +313,7 @@ __device__ inline void compute_block(const Stage16& stg, const typename Vec<T>::
       if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
       if (PARTIAL) {
         const int jl = t * 32 + acc_row(r, hf);
-        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? stg.doc[jl] : 0;
+        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? st.doc[jl] : 0;
         if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
       }
       s[t][r] = x;
@@ -320,62 +321,190 @@ __device__ inline void compute_block(const Stage16& stg, const typename Vec<T>::
     }
   }
   mx = half_max(mx);
-  const float m_blk = SOFTCAP ? mx : mx * c1;
-  const bool grow = m_blk > rs.m + kRescaleLog2;
-  const float alpha = grow ? fast_exp2(rs.m - m_blk) : 1.0f;
-  if (grow) rs.m = m_blk;
-  const float m_use = (rs.m == -INFINITY) ? 0.0f : rs.m;
+  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
+  return SOFTCAP ? mx : mx * (a.scale * kLog2e);
+}
 
-  // Probabilities, rounded to T (nearest even) for P V; the normaliser sums
-  // the rounded values.
-  x8 pk[8];
-  float psum = 0.0f;
+typedef __attribute__((address_space(3))) const uint8_t* lds_u8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// All LDS of a workgroup: two K stages and two V stages.
+struct alignas(16) Lds {
+  KStage k[2];
+  VStage v[2];
+};
+
+// Per-lane LDS read addresses into stage 0; stage 1 is a constant away, and
+// every read of a step is one of these plus a constant that fits the
+// instruction's offset field.
+//  * k[c]: K operand of contraction step c (head dims 16c + 8hf .. +7) of
+//    key lq of the tile's first 32-key tile: row lq, chunk 2c + hf, stored
+//    in slot (2c + hf) ^ (lq & 7). Tile t adds 4096 bytes.
+//  * v[te]: V^T operand of head-dim tile te. For 16-key group g, lane half
+//    hf holds keys 16g + 4hf + {0..3} and 16g + 8 + 4hf + {0..3} of P^T; the
+//    matching V^T operand comes from two transposed LDS reads: in each
+//    16-lane group, lane i16 supplies the address of row (key)
+//    r0 + i16/4, head dims eb + 4(i16%4) .. +3 (16-byte chunk eb/8 + ...,
+//    swizzled by 2(row & 3)), and receives head dim eb + i16 of rows
+//    r0 .. r0+3. Group g adds 2048 bytes; the second read adds 1024.
+struct LanePtrs {
+  lds_u8 k[4];
+  lds_u8 v[2];
+};
+
+__device__ inline LanePtrs make_lane_ptrs(const Lds& lds, int lane) {
+  LanePtrs p;
+  const int lq = lane & 31, hf = lane >> 5;
+  const lds_u8 kb = (lds_u8)lds.k[0].k;
+  const lds_u8 vb = (lds_u8)lds.v[0].v;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int c = 0; c < 4; ++c) p.k[c] = kb + lq * 128 + (((2 * c + hf) ^ (lq & 7)) << 4);
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int r1 = hf * 4 + (i16 >> 2);  // row of group 0
 #pragma unroll
-    for (int u = 0; u < 8; u += 2) {
-      const float x0 = s[g >> 1][(g & 1) * 8 + u], x1 = s[g >> 1][(g & 1) * 8 + u + 1];
-      const float p0 = SOFTCAP ? fast_exp2(x0 - m_use) : fast_exp2(fmaf(x0, c1, -m_use));
-      const float p1 = SOFTCAP ? fast_exp2(x1 - m_use) : fast_exp2(fmaf(x1, c1, -m_use));
-      const typename V::x2 pr = {(T)p0, (T)p1};
-      psum = V::add_pair(pr, psum);
-      pk[g][u] = pr[0];
-      pk[g][u + 1] = pr[1];
-    }
+  for (int te = 0; te < 2; ++te) {
+    const int e = te * 32 + (g16 & 1) * 16 + (i16 & 3) * 4;
+    const int c16 = e >> 3, half = (e >> 2) & 1;
+    p.v[te] = vb + r1 * 128 + ((c16 ^ ((r1 & 3) << 1)) << 4) + half * 8;
   }
+  return p;
+}
+
+// Score_mod and mask of one score of block kv0: 32-key tile t, accumulator
+// register r of this lane.
+template <int KIND, bool SOFTCAP, bool PARTIAL>
+__device__ inline float mod_mask(float x, const KStage& st, int t, int r, int hf, int qi, int kv0,
+                                 const FwdArgs& a, int32_t dq) {
+  if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
+  if (PARTIAL) {
+    const int jl = t * 32 + acc_row(r, hf);
+    const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? st.doc[jl] : 0;
+    if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
+  }
+  return x;
+}
+
+// Keeps the compiler's schedulers from moving any instruction across this
+// point, so the source order of the chunks below is the issue order.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One KV block for this wave's 32 query rows, in two phases of 16 chunks,
+// each chunk one MFMA plus a slice of vector work that does not depend on
+// it, so LDS latency is covered and the matrix and vector units overlap:
+//  Q. S^T = K Q^T (MFMA j: 32-key tile j / 4, contraction step j % 4; K
+//     fragments read four MFMAs ahead), with the score_mod, mask and max of
+//     the tile finished before.
+//  P. O^T += V^T P^T (MFMA i: 16-key group i / 2, head-dim tile i % 2; V
+//     fragments read four MFMAs ahead), with the probabilities of the next
+//     group.
+template <typename T, int KIND, bool SOFTCAP, bool PARTIAL>
+__device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
+                                          const typename Vec<T>::x8 (&qop)[4], f32x16_t (&oacc)[2],
+                                          float& m_ref, float& l, int qi, int kv0, int lane, const FwdArgs& a,
+                                          int32_t dq) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  typedef __attribute__((address_space(3))) const x8 lds_x8;
+  const int hf = lane >> 5;
+  const float c1 = a.scale * kLog2e;
+
+  // K operand of QK MFMA j: head dims 16c + 8hf .. +7 of key 32t + lq.
+  auto k_frag = [&](int j) -> x8 {
+    const int t = j >> 2, c = j & 3;
+    return *reinterpret_cast<const lds_x8*>(kp[c] + t * 4096);
+  };
+  // V^T operand of PV MFMA i: two transposed reads, 8 rows apart (see
+  // LanePtrs).
+  auto v_frag = [&](int i) -> x8 {
+    const int g = i >> 1, te = i & 1;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[te] + g * 2048));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[te] + g * 2048 + 1024));
+    const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(x8, both);
+  };
+  // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4).
+  float mx = -INFINITY;
+  f32x16_t s[4];
+  auto mask_chunk = [&](int k) {
+#pragma unroll
+    for (int e = 4 * k; e < 4 * k + 4; ++e) {
+      const int t = e >> 4, r = e & 15;
+      const float x = mod_mask<KIND, SOFTCAP, PARTIAL>(s[t][r], kst, t, r, hf, qi, kv0, a, dq);
+      s[t][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  };
+
+  // Phase Q. Tile t is complete after chunk 4t + 3; its scores are
+  // processed in chunks 4t + 4 .. 4t + 7 (tile 3 after the phase).
+  x8 kf[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kf[j] = k_frag(j);
+  sched_fence();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j + 4 < 16) kf[j + 4] = k_frag(j + 4);
+    const int t = j >> 2, c = j & 3;
+    s[t] = V::mma(kf[j], qop[c], c == 0 ? f32x16_t{} : s[t]);
+    if (j >= 4) mask_chunk(j - 4);
+    sched_fence();
+  }
+  x8 vf[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vf[i] = v_frag(i);
+#pragma unroll
+  for (int k = 12; k < 16; ++k) mask_chunk(k);
+  mx = half_max(mx);
+  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
+  const float m_blk = SOFTCAP ? mx : mx * c1;
+
+  // Lazy rescale (wave-uniform branch).
+  const bool grow = m_blk > m_ref + kRescaleLog2;
   if (__ballot(grow) != 0) {
-    rs.l *= alpha;
+    const float alpha = grow ? fast_exp2(m_ref - m_blk) : 1.0f;
+    l *= alpha;
 #pragma unroll
     for (int te = 0; te < 2; ++te)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
   }
-  rs.l += psum;
+  if (grow) m_ref = m_blk;
+  const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
 
-  // O^T += V^T P^T. For 16-key group g, lane half hf holds keys
-  // 16g + 4hf + {0..3} and 16g + 8 + 4hf + {0..3} of P^T; the matching V^T
-  // operand comes from two transposed LDS reads: in each 16-lane group, lane i
-  // supplies the address of row (key) r0 + i/4, head dims eb + 4(i%4) .. +3,
-  // and receives head dim eb + i of rows r0 .. r0+3.
-  const int g16 = lane >> 4, i16 = lane & 15;
+  // Probabilities of scores 4k .. 4k+3 (group k / 2, entries 4(k % 2) ..),
+  // rounded to T (nearest even) for P V; the normaliser sums the rounded
+  // values.
+  x8 pk[8];
+  float psum[2] = {0.0f, 0.0f};
+  auto prob_chunk = [&](int k) {
+    const int g = k >> 1;
 #pragma unroll
-  for (int te = 0; te < 2; ++te) {
-    const int e = te * 32 + (g16 & 1) * 16 + (i16 & 3) * 4;
-    const int c16 = e >> 3, half = (e >> 2) & 1;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int r1 = g * 16 + hf * 4 + (i16 >> 2);
-      const int off = ((c16 ^ ((r1 & 3) << 1)) << 4) + half * 8;
-      typedef short s16x4 __attribute__((ext_vector_type(4)));
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(stg.v + r1 * 128 + off));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(stg.v + (r1 + 8) * 128 + off));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[te] = V::mma(__builtin_bit_cast(x8, both), pk[g], oacc[te]);
+    for (int u = (k & 1) * 4; u < (k & 1) * 4 + 4; u += 2) {
+      const float x0 = s[g >> 1][(g & 1) * 8 + u], x1 = s[g >> 1][(g & 1) * 8 + u + 1];
+      const float p0 = SOFTCAP ? fast_exp2(x0 - m_use) : fast_exp2(fmaf(x0, c1, -m_use));
+      const float p1 = SOFTCAP ? fast_exp2(x1 - m_use) : fast_exp2(fmaf(x1, c1, -m_use));
+      const typename V::x2 pr = {(T)p0, (T)p1};
+      psum[(u >> 1) & 1] = V::add_pair(pr, psum[(u >> 1) & 1]);
+      pk[g][u] = pr[0];
+      pk[g][u + 1] = pr[1];
     }
+  };
+
+  // Phase P. Group g's probabilities are made in chunks 2g - 2 and 2g - 1
+  // (group 0 before the phase) and used by MFMAs 2g and 2g + 1.
+  prob_chunk(0);
+  prob_chunk(1);
+  sched_fence();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + 4 < 16) vf[i + 4] = v_frag(i + 4);
+    oacc[i & 1] = V::mma(vf[i], pk[i >> 1], oacc[i & 1]);
+    if (i + 2 < 16) prob_chunk(i + 2);
+    sched_fence();
   }
+  l += psum[0] + psum[1];
 }
 
 template <typename T, int KIND, bool SOFTCAP>
@@ -383,11 +512,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   using V = Vec<T>;
   using x8 = typename V::x8;
   using x4 = typename V::x4;
-  __shared__ Stage16 stage0;
-  __shared__ Stage16 stage1;
+  __shared__ Lds lds;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const int BH = a.B * a.H;
   const int item = blockIdx.x;
@@ -407,12 +536,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
   // First key of the n-th visited block: full blocks first, then partial.
   auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
-  const CopyPlan cp = make_copy_plan<T>(a.k_sl, a.v_sl, wave, lane);
+  // Per-lane byte offsets of the tile copies (see issue_rows).
+  const uint32_t k_off =
+      (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  const uint32_t v_off = (uint32_t)((lane >> 3) * a.v_sl * (int64_t)sizeof(T)) +
+                         (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
 
-  int kv_cur = 0;
+  // Block n's K and V tiles live in stage n % 2.
+  int kv_next = 0;  // first key of the next block to copy
   if (nblk > 0) {
-    kv_cur = kv_start(0);
-    issue_tile<T, KIND>(kg, vg, cp, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, stage0, wave, lane);
+    kv_next = kv_start(0);
+    issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[0], wave, lane);
+    issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[0].v, wave, lane);
   }
 
   const int qi = qb * kBlock + wave * 32 + lq;  // this lane's query row
@@ -430,42 +565,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   // drain the next tile's copies, which share the in-order counter).
   wait_vm_zero();
 
+  // Per-lane LDS read addresses of each stage.
+  const LanePtrs lp = make_lane_ptrs(lds, lane);
+
   f32x16_t oacc[2];
 #pragma unroll
   for (int te = 0; te < 2; ++te)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
-  RowState rs{-INFINITY, 0.0f};
+  float m_ref = -INFINITY, l = 0.0f;
 
-  // Two LDS stages and one barrier per block: once every wave's copies of
-  // block m have landed and every wave has finished block m-1, the copies of
-  // block m+1 go into the stage block m-1 used, and block m is computed.
-  for (int n = 0; n < nblk; n += 2) {
+  // Two stages and one barrier per block: once every wave's copies of block
+  // m have landed and every wave has finished block m-1, the copies of block
+  // m+1 go into the stage block m-1 used, and block m is computed. Full and
+  // partial blocks run in separate loops, so each loop body has a single
+  // definition of the accumulators and they stay in place.
+  auto block = [&](auto partial_c, int m) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_c)::value;
+    const int par = m & 1;
+    lds_u8 kp[4], vp[2];
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int m = n + par;
-      if (m < nblk) {
-        Stage16& cur = par ? stage1 : stage0;
-        Stage16& nxt = par ? stage0 : stage1;
-        const int kv0 = kv_cur;
-        wait_vm_zero();    // this wave's copies of block m
-        wait_lgkm_zero();  // this wave's reads of block m-1
-        barrier_only();
-        if (m + 1 < nblk) {
-          kv_cur = kv_start(m + 1);
-          issue_tile<T, KIND>(kg, vg, cp, a.k_sl, a.v_sl, a.m.doc, kv_cur, a.S, nxt, wave, lane);
-        }
-        if (m >= nfull)
-          compute_block<T, KIND, SOFTCAP, true>(cur, qop, oacc, rs, qi, kv0, lane, a, dq);
-        else
-          compute_block<T, KIND, SOFTCAP, false>(cur, qop, oacc, rs, qi, kv0, lane, a, dq);
-      }
+    for (int c = 0; c < 4; ++c) kp[c] = lp.k[c] + par * (int)sizeof(KStage);
+#pragma unroll
+    for (int te = 0; te < 2; ++te) vp[te] = lp.v[te] + par * (int)sizeof(VStage);
+    const int kv0 = kv_next;
+    wait_vm_zero();    // this wave's copies of block m
+    wait_lgkm_zero();  // this wave's reads of block m-1
+    barrier_only();
+    if (m + 1 < nblk) {
+      kv_next = kv_start(m + 1);
+      issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[1 - par], wave, lane);
+      issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
     }
-  }
+    fwd_block<T, KIND, SOFTCAP, PARTIAL>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, kv0, lane, a, dq);
+  };
+  int m = 0;
+  for (; m < nfull; ++m) block(std::false_type{}, m);
+  for (; m < nblk; ++m) block(std::true_type{}, m);
 
   // Epilogue: O = O^T / l (0 for a row without live keys), lse = ln(sum exp).
-  const float l = half_sum(rs.l);
-  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+  const float lt = half_sum(l);
+  const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
   if (qi < a.L) {
 #pragma unroll
     for (int te = 0; te < 2; ++te) {
@@ -479,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       }
     }
     if (a.lse != nullptr && hf == 0)
-      a.lse[(int64_t)bh * a.L + qi] = (l > 0.0f) ? (rs.m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)bh * a.L + qi] = (lt > 0.0f) ? (m_ref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   }
 }
 

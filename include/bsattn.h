@@ -149,7 +149,9 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
  *   q_strides, k_strides, v_strides, o_strides: host int64[4], the element
  *   strides of the four dimensions (batch, head, sequence, head dim), or NULL
  *   for the contiguous layout. The head-dim stride must be 1; base pointers
- *   and the other strides must keep every row 16-byte aligned.
+ *   and the other strides must keep every row 16-byte aligned. The sequence
+ *   strides of k and v may be at most 2^24 elements (ATTN_ERR_UNSUPPORTED
+ *   otherwise).
  *   lse  device fp32 [B, H, L] contiguous, natural-log logsumexp of each row's
  *        scores after scale, score_mod and mask; may be NULL. It is the log
  *        of the normaliser O is divided by, whose terms are the probabilities

@@ -133,6 +133,8 @@ FWD_CASES = [
     ("head_dim_stride", dict(qs=(2 * 256 * 128, 256 * 128, 128, 2)), INVALID, "head-dim stride"),
     ("row_stride_breaks_alignment", dict(ks=(2 * 256 * 65, 256 * 65, 65, 1)), INVALID, "alignment"),
     ("negative_stride", dict(vs=(2 * 256 * 64, -256 * 64, 64, 1)), INVALID, "negative"),
+    ("k_seq_stride_too_large", dict(ks=(0, 0, (1 << 24) + 8, 1)), UNSUPPORTED, "sequence stride"),
+    ("v_seq_stride_too_large", dict(vs=(0, 0, (1 << 24) + 8, 1)), UNSUPPORTED, "sequence stride"),
 ]
 
 
