@@ -6,8 +6,8 @@ A step is one pass of the whole path over one batch: build the BlockMask
 (classification + schedule kernels) and run the fused forward, on the causal
 S=8192 workload (B=1, H=8, E=64, bf16, i.i.d. N(0,1) inputs). W untimed
 steps, then K steps timed between two device synchronisations. The forward
-kernel is also timed launch by launch with events on the stream it runs on,
-for the roofline figure. The second headline workload (sliding window 256
+kernel is also timed alone with events on the stream it runs on (batches of
+back-to-back launches), for the roofline figure. The second headline workload (sliding window 256
 over S=32768) is measured the same way and reported in the same line.
 
 Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
@@ -72,16 +72,10 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
                                device=dev)
     score_mod = "softcap" if w.softcap else None
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step():
         bm.rebuild()
-        if ev is not None:
-            ev[1].record()
         bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
                       scale=w.scale, out=o, lse=lse)
-        if ev is not None:
-            ev[2].record()
 
     for _ in range(warmup):
         step()
@@ -94,13 +88,29 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
 
-    # Per-launch durations with events on the stream the kernels run on.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # Per-launch durations with events on the stream the kernels run on: the
+    # mask build alone, and the forward alone as back-to-back batches of
+    # launches (so host launch gaps between steps are not counted).
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
-        step(evs[i])
+        evs[i][0].record(stream)
+        bm.rebuild()
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     mask_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    fwd_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    batch = 10
+    fwd = []
+    for _ in range(max(1, steps // batch)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
+                          scale=w.scale, out=o, lse=lse)
+        e1.record(stream)
+        fwd.append((e0, e1))
+    torch.cuda.synchronize()
+    fwd_ms = np.array([a.elapsed_time(b) / batch for a, b in fwd])
     return dict(wall_ms=wall_ms, mask_ms=mask_ms, fwd_ms=fwd_ms)
 
 

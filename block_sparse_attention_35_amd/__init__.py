@@ -25,6 +25,7 @@ import torch
 
 __all__ = [
     "BlockMask", "BsattnError", "create_block_mask", "attention", "num_blocks", "library_path",
+    "workspace_size",
     "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
 ]
 
@@ -93,7 +94,10 @@ def _load():
     lib.attn_forward.restype = i32
     lib.attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
-                                 i32, ctypes.c_float, ctypes.c_float, vp]
+                                 i32, ctypes.c_float, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.attn_forward_workspace_size.restype = i32
+    lib.attn_forward_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(_BlockMaskStruct),
+                                                ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i32]
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -125,8 +129,9 @@ class BlockMask:
 
     Tensors (int32, on the mask's device): ``kv_num_blocks [nq]``,
     ``kv_indices [nq, nk]`` (partial blocks), ``full_kv_num_blocks [nq]``,
-    ``full_kv_indices [nq, nk]`` (full blocks), ``schedule [nq]`` (the order
-    in which the forward visits query blocks).
+    ``full_kv_indices [nq, nk]`` (full blocks), ``schedule [2 nq + 1]`` (the
+    forward's work plan: item count, then items ``qb | chunk << 20 | split
+    << 21`` by decreasing cost).
     """
 
     def __init__(self, kind: int, q_len: int, kv_len: int, window: int,
@@ -140,7 +145,7 @@ class BlockMask:
         self.kv_indices = torch.empty(nq, nk, **opt)
         self.full_kv_num_blocks = torch.empty(nq, **opt)
         self.full_kv_indices = torch.empty(nq, nk, **opt)
-        self.schedule = torch.empty(nq, **opt)
+        self.schedule = torch.zeros(2 * nq + 1, **opt)
         self._struct = _BlockMaskStruct()
         s = self._struct
         s.kv_num_blocks = self.kv_num_blocks.data_ptr()
@@ -195,6 +200,28 @@ def create_block_mask(kind: Union[str, int], q_len: int, kv_len: int, window: Op
     return BlockMask(k, q_len, kv_len, w, doc, device).rebuild()
 
 
+_workspaces = {}
+
+
+def _workspace(nbytes: int, device: torch.device, stream: int) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes, one per (device, stream),
+    kept for later calls (the library leaves its counters at zero again)."""
+    key = (device.index, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def workspace_size(q: torch.Tensor, block_mask: BlockMask) -> int:
+    """Bytes of workspace attention() needs for q's batch, heads and dtype."""
+    n = ctypes.c_size_t(0)
+    _check(_load().attn_forward_workspace_size(_DTYPES[q.dtype], q.shape[0], q.shape[1],
+                                               ctypes.byref(block_mask._struct), ctypes.byref(n)))
+    return n.value
+
+
 def _strides(t: torch.Tensor):
     arr = (ctypes.c_int64 * 4)(*t.stride())
     return arr
@@ -203,13 +230,16 @@ def _strides(t: torch.Tensor):
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
               score_mod: Optional[str] = None, softcap: float = 30.0,
               scale: Optional[float] = None, return_lse: bool = False,
-              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
     """Fused block-sparse attention forward (attn_forward).
 
     q [B,H,L,E], k/v [B,H,S,E] on the GPU, one dtype among fp32/bf16/fp16,
     head dim contiguous. ``scale`` defaults to 1/sqrt(E) ("SDPA replaces
     hand-written attention", section 1). Returns O [B,H,L,E] (and the fp32
-    natural-log logsumexp [B,H,L] when ``return_lse``).
+    natural-log logsumexp [B,H,L] when ``return_lse``). ``workspace``: a
+    zero-filled uint8 GPU tensor of at least ``workspace_size(q, block_mask)``
+    bytes; by default one cached per device and stream is used.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, seq, E]")
@@ -232,11 +262,17 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
                             or lse.shape != (B, H, L)):
         raise ValueError("lse must be a contiguous float32 [B, H, L] tensor")
     with torch.cuda.device(q.device):
+        stream = _stream_handle(q.device)
+        need = workspace_size(q, block_mask)
+        if workspace is None and need > 0:
+            workspace = _workspace(need, q.device, stream)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         _check(_load().attn_forward(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
             lse.data_ptr() if lse is not None else None,
             _DTYPES[q.dtype], B, H, L, S, E,
             _strides(q), _strides(k), _strides(v), _strides(out),
             ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
-            _stream_handle(q.device)))
+            ws_ptr, ws_bytes, stream))
     return (out, lse) if return_lse else out

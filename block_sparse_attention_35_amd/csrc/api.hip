@@ -118,7 +118,7 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
                          const int64_t* q_strides, const int64_t* k_strides,
                          const int64_t* v_strides, const int64_t* o_strides,
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
-                         void* stream) {
+                         void* workspace, size_t workspace_size, void* stream) {
   g_last_error[0] = '\0';
   if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
   // A tensor with no elements may have a null pointer.
@@ -171,8 +171,20 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
   if (a.k_sl > kMaxSeqStride || a.v_sl > kMaxSeqStride)
     return fail(ATTN_ERR_UNSUPPORTED, "k/v sequence stride above %lld elements",
                 (long long)kMaxSeqStride);
-  if ((int64_t)B * H * bm->num_q_blocks > 0x7fffffffLL)
+  if ((int64_t)B * H * bm->num_q_blocks * 2 > 0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "too many work items");
+  const size_t need = bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks);
+  if (need > 0) {
+    if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+        workspace_size < need)
+      return fail(ATTN_ERR_INVALID_ARGUMENT,
+                  "workspace must be 256-byte aligned and hold %zu bytes (got %zu)", need,
+                  workspace == nullptr ? (size_t)0 : workspace_size);
+    a.split = 1;
+    a.counters = static_cast<int32_t*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          bsattn::counters_bytes((int64_t)B * H, bm->num_q_blocks));
+  }
 
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
   a.B = B, a.H = H, a.L = L, a.S = S;
@@ -190,6 +202,16 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
   a.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
   return hip_status(bsattn::launch_forward(dtype, a, static_cast<hipStream_t>(stream)),
                     "forward launch");
+}
+
+attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,
+                                        const attn_block_mask* bm, size_t* bytes) {
+  g_last_error[0] = '\0';
+  if (bm == nullptr || bytes == nullptr)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask and bytes must be non-null");
+  if (B < 1 || H < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d", B, H);
+  *bytes = bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks);
+  return ATTN_OK;
 }
 
 const char* attn_status_string(attn_status status) {

@@ -507,6 +507,27 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   l += psum[0] + psum[1];
 }
 
+// One work item of the plan written by the mask builder: query block qb and,
+// for a split item, which half of its kv blocks it visits.
+struct WorkItem {
+  int qb, chunk;
+  bool split;  // the item is one of two halves whose results are merged
+  bool skip;   // no work (past the end of the plan, or a second half when
+               // splitting is off: then the first item visits every block)
+};
+
+__device__ inline WorkItem work_item(const FwdArgs& a, int e) {
+  const const_i32_ptr plan = (const_i32_ptr)a.m.schedule;
+  WorkItem w{0, 0, false, true};
+  if (e >= plan[0]) return w;
+  const int32_t code = plan[1 + e];
+  w.qb = code & 0xFFFFF;
+  w.chunk = (code >> 20) & 1;
+  w.split = a.split && ((code >> 21) & 1);
+  w.skip = w.chunk == 1 && !w.split;
+  return w;
+}
+
 template <typename T, int KIND, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   using V = Vec<T>;
@@ -520,7 +541,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const int lq = lane & 31, hf = lane >> 5;
   const int BH = a.B * a.H;
   const int item = blockIdx.x;
-  const int qb = a.m.schedule[item / BH];
+  const WorkItem wi = work_item(a, item / BH);
+  if (wi.skip) return;
+  const int qb = wi.qb;
   const int bh = item % BH;
   const int b = bh / a.H, h = bh % a.H;
 
@@ -536,16 +559,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
   // First key of the n-th visited block: full blocks first, then partial.
   auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
+  // This item visits blocks [m_begin, m_end) of that order.
+  const int half = (nblk + 1) >> 1;
+  const int m_begin = (wi.split && wi.chunk == 1) ? half : 0;
+  const int m_end = (wi.split && wi.chunk == 0) ? half : nblk;
   // Per-lane byte offsets of the tile copies (see issue_rows).
   const uint32_t k_off =
       (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
   const uint32_t v_off = (uint32_t)((lane >> 3) * a.v_sl * (int64_t)sizeof(T)) +
                          (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
 
-  // Block n's K and V tiles live in stage n % 2.
+  // Block m's K and V tiles live in stage (m - m_begin) % 2.
   int kv_next = 0;  // first key of the next block to copy
-  if (nblk > 0) {
-    kv_next = kv_start(0);
+  if (m_end > m_begin) {
+    kv_next = kv_start(m_begin);
     issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[0], wave, lane);
     issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[0].v, wave, lane);
   }
@@ -582,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   // definition of the accumulators and they stay in place.
   auto block = [&](auto partial_c, int m) __attribute__((always_inline)) {
     constexpr bool PARTIAL = decltype(partial_c)::value;
-    const int par = m & 1;
+    const int par = (m - m_begin) & 1;
     lds_u8 kp[4], vp[2];
 #pragma unroll
     for (int c = 0; c < 4; ++c) kp[c] = lp.k[c] + par * (int)sizeof(KStage);
@@ -592,19 +619,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     wait_vm_zero();    // this wave's copies of block m
     wait_lgkm_zero();  // this wave's reads of block m-1
     barrier_only();
-    if (m + 1 < nblk) {
+    if (m + 1 < m_end) {
       kv_next = kv_start(m + 1);
       issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[1 - par], wave, lane);
       issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
     }
     fwd_block<T, KIND, SOFTCAP, PARTIAL>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, kv0, lane, a, dq);
   };
-  int m = 0;
-  for (; m < nfull; ++m) block(std::false_type{}, m);
-  for (; m < nblk; ++m) block(std::true_type{}, m);
+  int m = m_begin;
+  for (; m < min(m_end, nfull); ++m) block(std::false_type{}, m);
+  for (; m < m_end; ++m) block(std::true_type{}, m);
+
+  float lt = half_sum(l);  // the row's sum of (rounded) probabilities
+
+  if (wi.split) {
+    // Leave this half's partial result, then take a ticket; the second
+    // half to finish merges the two. The partials are written and read with
+    // device-scope (sc1) accesses, and every write has completed before the
+    // ticket is taken, so the halves may run on different XCDs; this avoids
+    // device-scope fences, which would write back and invalidate the whole
+    // L2 of the XCD (and with it the K/V tiles other workgroups reuse).
+    const int64_t bhn = (int64_t)a.B * a.H;
+    float* mine = a.partials + (((int64_t)qb * 2 + wi.chunk) * bhn + bh) * kSlotFloats;
+    float* other = a.partials + (((int64_t)qb * 2 + (1 - wi.chunk)) * bhn + bh) * kSlotFloats;
+    auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto get = [](float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) put(mine + (wave * 32 + te * 16 + r) * 64 + lane, oacc[te][r]);
+    if (hf == 0) {
+      put(mine + 4 * 32 * 64 + wave * 32 + lq, m_ref);
+      put(mine + 4 * 32 * 64 + kBlock + wave * 32 + lq, lt);
+    }
+    wait_vm_zero();  // this wave's partial writes have completed
+    __syncthreads();
+    __shared__ int ticket;
+    int32_t* counter = a.counters + (int64_t)qb * bhn + bh;
+    if (tid == 0) ticket = atomicAdd(counter, 1);
+    __syncthreads();
+    if (ticket == 0) return;  // the other half merges
+    if (tid == 0) atomicExch(counter, 0);  // ready for the next call
+    const float m_o = get(other + 4 * 32 * 64 + wave * 32 + lq);
+    const float l_o = get(other + 4 * 32 * 64 + kBlock + wave * 32 + lq);
+    const float m_new = fmaxf(m_ref, m_o);
+    const float w_s = (m_ref == -INFINITY) ? 0.0f : fast_exp2(m_ref - m_new);
+    const float w_o = (m_o == -INFINITY) ? 0.0f : fast_exp2(m_o - m_new);
+    // Combine in chunk order (chunk 0's term times its weight, plus chunk
+    // 1's), whichever half merges, so the result does not depend on which
+    // half finished last.
+    const bool first = wi.chunk == 0;
+    const float w0 = first ? w_s : w_o, w1 = first ? w_o : w_s;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ov = get(other + (wave * 32 + te * 16 + r) * 64 + lane);
+        const float o0 = first ? oacc[te][r] : ov, o1 = first ? ov : oacc[te][r];
+        oacc[te][r] = fmaf(w0, o0, w1 * o1);
+      }
+    const float l0 = first ? lt : l_o, l1 = first ? l_o : lt;
+    lt = fmaf(w0, l0, w1 * l1);
+    m_ref = m_new;
+  }
 
   // Epilogue: O = O^T / l (0 for a row without live keys), lse = ln(sum exp).
-  const float lt = half_sum(l);
   const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
   if (qi < a.L) {
 #pragma unroll
@@ -640,7 +719,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   const int lq = lane & 31, hf = lane >> 5;
   const int BH = a.B * a.H;
   const int item = blockIdx.x;
-  const int qb = a.m.schedule[item / BH];
+  // fp32 never splits (no workspace): a first item visits every block.
+  const WorkItem wi = work_item(a, item / BH);
+  if (wi.skip) return;
+  const int qb = wi.qb;
   const int bh = item % BH;
   const int b = bh / a.H, h = bh % a.H;
 
@@ -758,7 +840,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
 
 template <int KIND, bool SOFTCAP>
 hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq));
+  // Up to two work items per query block; items past the plan's end return.
+  const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * 2));
   const dim3 block(kThreads);
   switch (dtype) {
     case ATTN_BF16:

@@ -139,28 +139,65 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
   }
 }
 
-// rank(qb) = #{q : cost(q) > cost(qb)} + #{q < qb : cost(q) == cost(qb)};
-// schedule[rank(qb)] = qb.
-__global__ __launch_bounds__(kThreads) void schedule_kernel(int32_t nq,
-                                                            const int32_t* __restrict__ kv_num,
-                                                            const int32_t* __restrict__ full_num,
-                                                            int32_t* __restrict__ schedule) {
+// Work plan. A query block with n live kv blocks is one work item, or two
+// (its first ceil(n/2) blocks and the rest) when n exceeds the split length
+// C = max(kMinSplit, ceil(max_n / 2)), max_n being the largest n of the mask;
+// then no item is longer than C and the long rows no longer set the length
+// of a launch. Item t in [0, 2 nq) is (qb = t / 2, chunk = t % 2); chunk 1
+// exists only for split blocks. Items are ranked by decreasing cost (blocks
+// visited), ties by t:
+//   plan[0] = number of items; plan[1 + rank(t)] = qb | chunk << 20 | split << 21.
+// Every workgroup recomputes max_n, so the kernel needs no second pass.
+constexpr int kMinSplit = 16;
+
+__device__ inline int32_t item_cost(int32_t t, const int32_t* kv_num, const int32_t* full_num,
+                                    int32_t split_len) {
+  const int32_t qb = t >> 1, chunk = t & 1;
+  const int32_t n = kv_num[qb] + full_num[qb];
+  const bool split = n > split_len;
+  if (!split) return chunk ? -1 : n;  // -1: no such item
+  const int32_t h = (n + 1) >> 1;
+  return chunk ? n - h : h;
+}
+
+__global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, const int32_t* __restrict__ kv_num,
+                                                        const int32_t* __restrict__ full_num,
+                                                        int32_t* __restrict__ plan) {
   __shared__ int32_t cost_tile[kThreads];
-  const int qb = blockIdx.x * kThreads + threadIdx.x;
-  const int32_t mine = (qb < nq) ? kv_num[qb] + full_num[qb] : 0;
-  int32_t rank = 0;
-  for (int t0 = 0; t0 < nq; t0 += kThreads) {
-    const int t = t0 + threadIdx.x;
-    cost_tile[threadIdx.x] = (t < nq) ? kv_num[t] + full_num[t] : -1;
+  __shared__ int32_t red[kThreads / 64];
+  const int tid = threadIdx.x;
+  // max_n over all query blocks
+  int32_t mx = 0;
+  for (int q = tid; q < nq; q += kThreads) mx = max(mx, kv_num[q] + full_num[q]);
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) mx = max(mx, red[w]);
+  const int32_t split_len = max(kMinSplit, (mx + 1) >> 1);
+
+  const int32_t n_items_total = 2 * nq;
+  const int t = blockIdx.x * kThreads + tid;
+  const int32_t mine = (t < n_items_total) ? item_cost(t, kv_num, full_num, split_len) : -1;
+  int32_t rank = 0, count = 0;
+  for (int t0 = 0; t0 < n_items_total; t0 += kThreads) {
     __syncthreads();
-    const int lim = min(kThreads, nq - t0);
-    for (int u = 0; u < lim; ++u) {
-      const int32_t c = cost_tile[u];
-      rank += (c > mine) | ((c == mine) & (t0 + u < qb));
+    const int u = t0 + tid;
+    cost_tile[tid] = (u < n_items_total) ? item_cost(u, kv_num, full_num, split_len) : -1;
+    __syncthreads();
+    const int lim = min(kThreads, n_items_total - t0);
+    for (int v = 0; v < lim; ++v) {
+      const int32_t c = cost_tile[v];
+      rank += (c > mine) | ((c == mine) & (t0 + v < t));
+      count += c >= 0;
     }
-    __syncthreads();
   }
-  if (qb < nq) schedule[rank] = qb;
+  if (t < n_items_total && mine >= 0) {
+    const int32_t qb = t >> 1, chunk = t & 1;
+    const int32_t n = kv_num[qb] + full_num[qb];
+    plan[1 + rank] = qb | (chunk << 20) | ((n > split_len ? 1 : 0) << 21);
+  }
+  if (t == 0) plan[0] = count;
 }
 
 }  // namespace
@@ -175,7 +212,7 @@ hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, i
                      doc, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(schedule_kernel, dim3((nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
+  hipLaunchKernelGGL(plan_kernel, dim3((2 * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      stream, nq, kv_num, full_num, schedule);
   return hipGetLastError();
 }

@@ -37,7 +37,30 @@ struct FwdArgs {
   MaskView m;
   float scale;
   float softcap;  // > 0 only when the soft-cap score_mod is on
+  // Split work items (see the work plan): ticket counters [nq][B*H] and
+  // partial results, one slot per (query block, chunk, batch*head).
+  int32_t split;
+  int32_t* counters;
+  float* partials;
 };
+
+// Partial result of one split item: the 4 waves' O^T accumulators in
+// register order ([wave][32 registers][64 lanes]), then the running max and
+// the sum of each of the 128 rows.
+constexpr int64_t kSlotFloats = 4 * 32 * 64 + 2 * kBlock;
+// Long query blocks are split only when there are few work items.
+constexpr int64_t kSplitMaxItems = 2048;
+
+inline bool use_split(int32_t dtype, int64_t bh, int32_t nq) {
+  return dtype != 0 /* ATTN_F32 */ && nq > 0 && bh * nq <= kSplitMaxItems;
+}
+inline size_t counters_bytes(int64_t bh, int32_t nq) {
+  return ((size_t)(bh * nq) * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq) {
+  if (!use_split(dtype, bh, nq)) return 0;
+  return counters_bytes(bh, nq) + (size_t)nq * 2 * (size_t)bh * kSlotFloats * sizeof(float);
+}
 
 // Enqueue the block classification and the query-block schedule.
 hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, int32_t q_len,

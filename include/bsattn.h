@@ -45,6 +45,7 @@
 #ifndef BSATTN_H
 #define BSATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -99,9 +100,16 @@ typedef int32_t attn_status;
  *   full_kv_num_blocks[nq]     number of full kv blocks of query block qb
  *   full_kv_indices[nq * nk]   row qb: its full kv block indices, ascending,
  *                              then 0 up to nk entries
- *   schedule[nq]               query blocks ordered by decreasing number of
- *                              live kv blocks (ties: lower index first); the
- *                              forward visits them in this order
+ *   schedule[2 * nq + 1]       work plan of the forward: schedule[0] is the
+ *                              number of work items, schedule[1 + r] the r-th
+ *                              item, qb | chunk << 20 | split << 21. A query
+ *                              block with n live kv blocks is one item
+ *                              (split = 0, chunk = 0), or two when n exceeds
+ *                              max(16, ceil(max_n / 2)), max_n the largest n
+ *                              of the mask (split = 1; chunk 0 visits its
+ *                              first ceil(n / 2) blocks, chunk 1 the rest).
+ *                              Items are ordered by decreasing number of
+ *                              blocks visited, ties by 2 qb + chunk.
  * with nq = ceil(q_len / 128) and nk = ceil(kv_len / 128). A block is full only
  * if all 128 x 128 of its positions are in range and live, so the blocks at a
  * ragged end are at most partial.
@@ -143,6 +151,18 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
                                   attn_block_mask* bm, void* stream);
 
 /*
+ * Bytes of device workspace attn_forward needs for this problem (0 when it
+ * needs none). The forward splits long query blocks in two work items (see
+ * the work plan) when there are few query blocks for the GPU, that is when
+ * B * H * num_q_blocks <= 2048 and dtype is ATTN_BF16 or ATTN_F16; each
+ * split item then leaves fp32 partial results and a ticket counter in the
+ * workspace, and the second item to finish merges the two.
+ * Errors: INVALID_ARGUMENT for a null bm or bytes, or B, H < 1.
+ */
+attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,
+                                        const attn_block_mask* bm, size_t* bytes);
+
+/*
  * Fused block-sparse attention forward.
  *   q  device [B, H, L, E], k device [B, H, S, E], v device [B, H, S, E],
  *   o  device [B, H, L, E] output, all of element type `dtype`;
@@ -161,6 +181,11 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
  *   bm   a BlockMask built for q_len == L and kv_len == S.
  *   score_mod ATTN_SCORE_NONE or ATTN_SCORE_SOFTCAP (then softcap > 0).
  *   scale  multiplier of q.k (pass 1/sqrt(E) for the usual attention).
+ *   workspace  device memory of at least attn_forward_workspace_size bytes,
+ *        256-byte aligned, owned by the caller; may be NULL when that size is
+ *        0. Its first use must see it zero-filled; every call leaves its
+ *        counters at zero again, so it can be reused by later calls. Calls
+ *        that share a workspace must not run concurrently.
  * A row whose every key is masked gets O = 0 and lse = -inf.
  * Arithmetic: products in fp32 (MFMA) from the input type, fp32 softmax
  * statistics and accumulation; probabilities are rounded to the input type
@@ -168,15 +193,16 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
  * to the output type with round to nearest even.
  * Errors: INVALID_ARGUMENT for null pointers, sizes < 0 (B, H >= 1), a mask
  * built for other lengths, bad strides/alignment, a bad score_mod/softcap or
- * a scale that is not finite and > 0; UNSUPPORTED for E != 64 or an unknown dtype; HIP for a
- * failed launch.
+ * a scale that is not finite and > 0, a missing, misaligned or too small
+ * workspace; UNSUPPORTED for E != 64 or an unknown dtype; HIP for a failed
+ * launch.
  */
 attn_status attn_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                          int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t S, int32_t E,
                          const int64_t* q_strides, const int64_t* k_strides,
                          const int64_t* v_strides, const int64_t* o_strides,
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
-                         void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(attn_status status);

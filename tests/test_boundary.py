@@ -103,8 +103,12 @@ def _built_mask(L=256, S=256, kind=1, window=0, doc=None):
                num_kv_blocks=-(-S // 128), kind=kind, window=window, document_id=doc)
 
 
+WS_FAKE = 0x100000  # 256-byte aligned placeholder workspace, never dereferenced
+
+
 def _fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=1, B=1, H=2, L=256, S=256, E=64,
-         qs=None, ks=None, vs=None, os_=None, bm=None, score_mod=0, softcap=0.0, scale=0.125):
+         qs=None, ks=None, vs=None, os_=None, bm=None, score_mod=0, softcap=0.0, scale=0.125,
+         ws=WS_FAKE, ws_bytes=1 << 30):
     lib = bsa._load()
     bm = _built_mask(L, S) if bm is None else bm
 
@@ -112,7 +116,8 @@ def _fwd(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=1, B=1, H=2, L=256, S=2
         return None if x is None else (ctypes.c_int64 * 4)(*x)
 
     return lib.attn_forward(q, k, v, o, lse, dtype, B, H, L, S, E, st(qs), st(ks), st(vs),
-                            st(os_), ctypes.byref(bm), score_mod, softcap, scale, None)
+                            st(os_), ctypes.byref(bm), score_mod, softcap, scale, ws, ws_bytes,
+                            None)
 
 
 FWD_CASES = [
@@ -135,6 +140,9 @@ FWD_CASES = [
     ("negative_stride", dict(vs=(2 * 256 * 64, -256 * 64, 64, 1)), INVALID, "negative"),
     ("k_seq_stride_too_large", dict(ks=(0, 0, (1 << 24) + 8, 1)), UNSUPPORTED, "sequence stride"),
     ("v_seq_stride_too_large", dict(vs=(0, 0, (1 << 24) + 8, 1)), UNSUPPORTED, "sequence stride"),
+    ("workspace_missing", dict(ws=None, ws_bytes=0), INVALID, "workspace"),
+    ("workspace_misaligned", dict(ws=WS_FAKE + 16), INVALID, "workspace"),
+    ("workspace_too_small", dict(ws_bytes=1024), INVALID, "workspace"),
 ]
 
 
@@ -150,7 +158,41 @@ def test_forward_validation(name, kw, code, words):
 def test_forward_null_mask():
     lib = bsa._load()
     assert lib.attn_forward(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 1, 128, 128, 64, None, None,
-                            None, None, None, 0, 0.0, 0.125, None) == INVALID
+                            None, None, None, 0, 0.0, 0.125, None, 0, None) == INVALID
+
+
+def _ws_size(dtype, B, H, L, S=None):
+    S = L if S is None else S
+    n = ctypes.c_size_t(123)
+    bm = _built_mask(L, S)
+    assert bsa._load().attn_forward_workspace_size(dtype, B, H, ctypes.byref(bm),
+                                                   ctypes.byref(n)) == OK
+    return n.value
+
+
+def test_workspace_size():
+    # split items need ticket counters (int32 per query block and head, padded
+    # to 256 bytes) and two fp32 partial slots per query block and head of
+    # 4 waves x 32 registers x 64 lanes plus a max and a sum per row
+    slot = (4 * 32 * 64 + 2 * 128) * 4
+    nq, bh = 64, 8
+    counters = -(-(nq * bh * 4) // 256) * 256
+    assert _ws_size(1, 1, 8, 8192) == counters + nq * 2 * bh * slot
+    assert _ws_size(2, 2, 4, 8192) == counters + nq * 2 * bh * slot
+    assert _ws_size(0, 1, 8, 8192) == 0            # fp32 never splits
+    assert _ws_size(1, 1, 32, 8192) == 64 * 32 * 4 + 64 * 2 * 32 * slot  # 2048 items
+    assert _ws_size(1, 1, 33, 8192) == 0           # many items: no split
+    assert _ws_size(1, 1, 8, 0) == 0               # no query blocks
+
+
+@no_gpu
+def test_workspace_size_validation():
+    lib = bsa._load()
+    n = ctypes.c_size_t(0)
+    assert lib.attn_forward_workspace_size(1, 1, 1, None, ctypes.byref(n)) == INVALID
+    bm = _built_mask()
+    assert lib.attn_forward_workspace_size(1, 0, 1, ctypes.byref(bm), ctypes.byref(n)) == INVALID
+    assert lib.attn_forward_workspace_size(1, 1, 1, ctypes.byref(bm), None) == INVALID
 
 
 def test_binding_rejects_cpu_tensors():

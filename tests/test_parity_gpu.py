@@ -34,6 +34,25 @@ def dev():
     return torch.device("cuda", 0)
 
 
+def expected_plan(n):
+    """The forward's work plan from the live block counts n[qb]: a query
+    block with more than max(16, ceil(max n / 2)) blocks becomes two items
+    (first ceil(n/2) blocks, rest), items by decreasing cost, ties by
+    2 qb + chunk; [count, qb | chunk << 20 | split << 21, ...]."""
+    n = [int(x) for x in n]
+    split_len = max(16, (max(n, default=0) + 1) // 2)
+    items = []
+    for qb, c in enumerate(n):
+        if c > split_len:
+            h = (c + 1) // 2
+            items.append((h, 2 * qb, qb | (1 << 21)))
+            items.append((c - h, 2 * qb + 1, qb | (1 << 20) | (1 << 21)))
+        else:
+            items.append((c, 2 * qb, qb))
+    items.sort(key=lambda it: (-it[0], it[1]))
+    return [len(items)] + [code for _, _, code in items]
+
+
 def _mask_on_gpu(w: wl.Workload, dev, doc=None):
     doc = wl.make_doc(w) if doc is None else doc
     dt = torch.from_numpy(doc).to(dev) if doc is not None else None
@@ -49,9 +68,9 @@ def _check_mask(bm, w: wl.Workload, doc):
                            "full_kv_indices"), got, want):
         g = g.cpu().numpy()
         assert g.shape == e.shape and np.array_equal(g, e), f"{w.name}: {name} differs"
-    cost = want[0] + want[2]
-    order = sorted(range(len(cost)), key=lambda i: (-int(cost[i]), i))
-    assert bm.schedule.cpu().numpy().tolist() == order, f"{w.name}: schedule"
+    plan = expected_plan(want[0] + want[2])
+    got_plan = bm.schedule.cpu().numpy().tolist()
+    assert got_plan[:len(plan)] == plan, f"{w.name}: work plan"
 
 
 def _odd(name, dtype, H, L, S, kind, window=0, bounds=(), softcap=0.0, B=1):
@@ -128,6 +147,11 @@ SMALL = [
     _odd("document_f32", "f32", 1, 512, 512, wl.MASK_DOCUMENT, 0, (100, 300)),
     _odd("causal_B2H3_bf16", "bf16", 3, 256, 256, wl.MASK_CAUSAL, B=2),
     _odd("none_zero_kv_bf16", "bf16", 1, 256, 0, wl.MASK_NONE),
+    # 34 query blocks: blocks with more than 17 live kv blocks run as two
+    # halves merged through the workspace
+    _odd("causal_4352_bf16_split", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL),
+    _odd("document_4400_f16_split", "f16", 1, 4400, 4400, wl.MASK_DOCUMENT, 0, (600, 2500), 30.0),
+    _odd("none_3000x4300_bf16_split", "bf16", 1, 3000, 4300, wl.MASK_NONE),
 ]
 
 
@@ -190,6 +214,38 @@ def test_deterministic_repeat(dev):
     for _ in range(3):
         o2, l2 = bsa.attention(q, k, v, bm, return_lse=True)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_workspace_is_left_clean(dev):
+    """Split items leave the workspace's ticket counters at zero, so an
+    explicit zero-filled workspace, reused, gives the cached one's results."""
+    w = wl.WORKLOADS["causal_8192_bf16"]
+    q, k, v = (x.to(dev) for x in wl.make_qkv(w, 5))
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, device=dev)
+    need = bsa.workspace_size(q, bm)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ref = bsa.attention(q, k, v, bm)
+    n_counters = w.B * w.H * bm.num_q_blocks * 4
+    for _ in range(3):
+        got = bsa.attention(q, k, v, bm, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+        assert int(ws[:n_counters].count_nonzero()) == 0
+
+
+def test_many_heads_without_split_sampled_rows(dev):
+    """B*H*nq above 2048: long query blocks are not split."""
+    w = _odd("causal_8192_h33_bf16", "bf16", 33, 8192, 8192, wl.MASK_CAUSAL)
+    (q, k, v), doc, o, lse = _run(w, dev)
+    rows = wl.sample_rows(w, 96)
+    want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(),
+                                        v.double().numpy(), w.kind, w.scale, w.window, doc,
+                                        w.softcap, rows=rows)
+    idx = torch.from_numpy(rows).to(dev)
+    got = o.float().reshape(-1, w.E)[idx].cpu().numpy()
+    got_lse = lse.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+    _compare(w, got, got_lse, want_o, want_lse, w.name)
 
 
 def test_strided_inputs_match_contiguous(dev):
