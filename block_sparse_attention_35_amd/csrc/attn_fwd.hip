@@ -493,7 +493,11 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   };
 
   // Phase P. Group g's probabilities are made in chunks 2g - 2 and 2g - 1
-  // (group 0 before the phase) and used by MFMAs 2g and 2g + 1.
+  // (group 0 before the phase) and used by MFMAs 2g and 2g + 1. The phase
+  // runs at raised wave priority: it is bound by the vector unit, and when
+  // the other wave on the SIMD is in its MFMA-bound phase Q, issuing this
+  // wave's vector work first keeps both units busy.
+  __builtin_amdgcn_s_setprio(1);
   prob_chunk(0);
   prob_chunk(1);
   sched_fence();
@@ -505,6 +509,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
     sched_fence();
   }
   l += psum[0] + psum[1];
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // One work item of the plan written by the mask builder: query block qb and,

@@ -11,8 +11,10 @@
 // offsets d = i - j of a block form the integer interval [q0 - k1, q1 - k0],
 // and a pair is live iff 0 <= d < W (W = infinity for causal), so the block
 // is skipped iff the two intervals are disjoint and full iff the first lies
-// inside the second. Document blocks are classified exactly by evaluating
-// every in-range pair cooperatively (ids may be in any order).
+// inside the second. Document blocks whose queries share one id and whose
+// keys share one id follow the causal rule (or are skipped when the ids
+// differ); the rest are classified exactly by evaluating every in-range pair
+// cooperatively (ids may be in any order).
 //
 // Kernel 1 (one workgroup per query block) writes the classes to LDS, then
 // compacts them in ascending kb order with wave ballots and writes the counts,
@@ -44,7 +46,6 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
   extern __shared__ uint8_t cls[];  // [nk]
   __shared__ int32_t doc_q[kBlock];
-  __shared__ int32_t doc_k[kBlock];
   __shared__ int32_t wave_counts[2][kWaves];
 
   const int tid = threadIdx.x;
@@ -54,33 +55,49 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
   const bool q_whole = (q1 - q0 + 1) == kBlock;
 
   if (kind == ATTN_MASK_DOCUMENT) {
+    // Shortcut, exact: when every in-range query of the block has one id and
+    // every in-range key of a kv block has one id, a pair is live iff its
+    // causal condition holds and the two ids are equal, so the class follows
+    // from the causal interval rule (or is skip for different ids). A block
+    // that mixes ids can never be full; for those, every in-range pair is
+    // evaluated (ids may be in any order). One wave classifies one kv block
+    // at a time, each lane holding two of its keys, with no workgroup
+    // barrier per block.
     if (tid < kBlock) doc_q[tid] = (q0 + tid <= q1) ? doc[q0 + tid] : 0;
-    // Each thread owns query row tid/2 and 64 keys; the workgroup votes.
-    const int il = tid >> 1;
-    const int jbase = (tid & 1) * 64;
-    for (int kb = 0; kb < nk; ++kb) {
+    __syncthreads();
+    const int32_t q_id = doc_q[0];
+    const bool q_uniform = __syncthreads_and(tid >= kBlock || q0 + tid > q1 || doc_q[tid] == q_id);
+    const int n_rows = (int)(q1 - q0 + 1);
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int kb = wave; kb < nk; kb += kWaves) {
       const int64_t k0 = (int64_t)kb * kBlock;
       const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
-      if (q1 < k0) {  // every key after every query: no causal pair
-        if (tid == 0) cls[kb] = kSkip;
-        continue;
+      uint8_t c = kSkip;
+      if (q1 >= k0) {  // else every key comes after every query
+        const int64_t j0 = k0 + lane, j1 = k0 + lane + 64;
+        const bool v0 = j0 <= k1, v1 = j1 <= k1;
+        const int32_t d0 = v0 ? doc[j0] : 0, d1 = v1 ? doc[j1] : 0;
+        const int32_t first = __shfl(d0, 0);  // key k0 is always in range
+        const bool uni = __all((!v0 || d0 == first) && (!v1 || d1 == first));
+        if (q_uniform && uni) {
+          c = (first == q_id) ? classify_interval(q0, q1, k0, k1, INT64_MAX / 4,
+                                                  q_whole && (k1 - k0 + 1) == kBlock)
+                              : kSkip;
+        } else {
+          // any in-range pair (i, j) with j <= i and equal ids
+          bool any = false;
+          for (int il0 = 0; il0 < n_rows && !__any(any); il0 += 32) {
+            const int lim = min(n_rows, il0 + 32);
+            for (int il = il0; il < lim; ++il) {
+              const int64_t i = q0 + il;
+              const int32_t di = doc_q[il];
+              any |= (v0 & (j0 <= i) & (d0 == di)) | (v1 & (j1 <= i) & (d1 == di));
+            }
+          }
+          c = __any(any) ? kPartial : kSkip;
+        }
       }
-      __syncthreads();  // previous doc_k readers are done (and doc_q is written)
-      if (tid < kBlock) doc_k[tid] = (k0 + tid <= k1) ? doc[k0 + tid] : 0;
-      __syncthreads();
-      const int64_t i = q0 + il;
-      const int32_t di = doc_q[il];
-      int any = 0, all = 1;
-      for (int jj = 0; jj < 64; ++jj) {
-        const int64_t j = k0 + jbase + jj;
-        const int in_range = (i <= q1) & (j <= k1);
-        const int lv = in_range & (j <= i) & (doc_k[jbase + jj] == di);
-        any |= lv;
-        all &= lv;
-      }
-      const int any_live = __syncthreads_or(any);
-      const int all_live = __syncthreads_and(all);
-      if (tid == 0) cls[kb] = all_live ? kFull : (any_live ? kPartial : kSkip);
+      if (lane == 0) cls[kb] = c;
     }
   } else {
     const int64_t w = (kind == ATTN_MASK_SLIDING_WINDOW) ? (int64_t)window : INT64_MAX / 4;
