@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import gc
+import hashlib
 import json
 import math
 import os
@@ -146,6 +147,28 @@ def summarize(w: wl.Workload, r):
     }
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "fwd16_causal_8192_sliding_32768_w256_hbm_traffic.md")
+FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_35_amd", "csrc", "attn_fwd.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, or None when the forward source has changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src_hash = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic-bytes "):
+            fields = dict(f.split("=", 1) for f in line.split()[1:])
+            if fields.get("source") != src_hash or workload not in fields:
+                return None
+            return int(fields[workload])
+    return None
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float):
     """The fp64 oracle on a bounded, seeded sample of the workload's rows,
     reported in live-pair TFLOPS of the rows it computed."""
@@ -244,7 +267,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": head["forward_tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": head["forward_tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": None,
+                     "traffic": measured_traffic(names[0]),
                      "kernel": "fwd16_kernel<bf16, causal>",
                      "per_launch_flop": head["live_gflop"] * 1e9,
                      "launch_ms": head["forward_ms"]["mean"]},
@@ -255,7 +278,8 @@ def main():
         line["sliding_32768_w256"] = {
             "forward_ms": s["forward_ms"], "tflops": s["forward_tflops"],
             "frac_bf16_peak": s["forward_frac_bf16_peak"], "gbs": s["forward_gbs"],
-            "frac_hbm_peak": s["forward_gbs"] / PEAK_HBM_GBS, "step_ms": s["ms_per_step"]}
+            "frac_hbm_peak": s["forward_gbs"] / PEAK_HBM_GBS, "step_ms": s["ms_per_step"],
+            "traffic": measured_traffic(SECOND)}
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
