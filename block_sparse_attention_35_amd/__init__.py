@@ -130,8 +130,8 @@ class BlockMask:
     Tensors (int32, on the mask's device): ``kv_num_blocks [nq]``,
     ``kv_indices [nq, nk]`` (partial blocks), ``full_kv_num_blocks [nq]``,
     ``full_kv_indices [nq, nk]`` (full blocks), ``schedule [2 nq + 1]`` (the
-    forward's work plan: item count, then items ``qb | chunk << 20 | split
-    << 21`` by decreasing cost).
+    forward's work plan: item count, then items ``qb | chunk << 20 | (k - 1)
+    << 22`` by decreasing cost).
     """
 
     def __init__(self, kind: int, q_len: int, kv_len: int, window: int,

@@ -59,10 +59,13 @@ struct Vec<__bf16> {
   static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // acc + a.x + a.y in fp32 (v_dot2c_f32_bf16 against (1, 1))
+  // acc + a.x + a.y in fp32 (v_dot2c_f32_bf16 against (1, 1)). Written as
+  // volatile asm so it stays in the chunk that produces `a` (a plain builtin
+  // is only ordered by its data and gets sunk to the end of the phase, where
+  // the sum is used).
   static __device__ inline float add_pair(x2 a, float acc) {
-    const x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(a, one, acc, false);
+    asm volatile("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(a));
+    return acc;
   }
 };
 template <>
@@ -73,10 +76,11 @@ struct Vec<_Float16> {
   static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  // acc + a.x + a.y in fp32 (v_dot2c_f32_f16 against (1, 1))
+  // acc + a.x + a.y in fp32 (v_dot2c_f32_f16 against (1, 1)), volatile asm
+  // for the same reason as the bf16 form.
   static __device__ inline float add_pair(x2 a, float acc) {
-    const x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(a, one, acc, false);
+    asm volatile("v_dot2c_f32_f16 %0, 0x3c003c00, %1" : "+v"(acc) : "v"(a));
+    return acc;
   }
 };
 
@@ -513,23 +517,24 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
 }
 
 // One work item of the plan written by the mask builder: query block qb and,
-// for a split item, which half of its kv blocks it visits.
+// for a split item, which of its k chunks of kv blocks it visits.
 struct WorkItem {
-  int qb, chunk;
-  bool split;  // the item is one of two halves whose results are merged
-  bool skip;   // no work (past the end of the plan, or a second half when
+  int qb, chunk, k;
+  bool split;  // the item is one of k > 1 chunks whose results are merged
+  bool skip;   // no work (past the end of the plan, or a later chunk when
                // splitting is off: then the first item visits every block)
 };
 
 __device__ inline WorkItem work_item(const FwdArgs& a, int e) {
   const const_i32_ptr plan = (const_i32_ptr)a.m.schedule;
-  WorkItem w{0, 0, false, true};
+  WorkItem w{0, 0, 1, false, true};
   if (e >= plan[0]) return w;
   const int32_t code = plan[1 + e];
   w.qb = code & 0xFFFFF;
-  w.chunk = (code >> 20) & 1;
-  w.split = a.split && ((code >> 21) & 1);
-  w.skip = w.chunk == 1 && !w.split;
+  w.chunk = (code >> 20) & 3;
+  w.k = ((code >> 22) & 3) + 1;
+  w.split = a.split && w.k > 1;
+  w.skip = w.chunk > 0 && !w.split;
   return w;
 }
 
@@ -565,9 +570,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   // First key of the n-th visited block: full blocks first, then partial.
   auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
   // This item visits blocks [m_begin, m_end) of that order.
-  const int half = (nblk + 1) >> 1;
-  const int m_begin = (wi.split && wi.chunk == 1) ? half : 0;
-  const int m_end = (wi.split && wi.chunk == 0) ? half : nblk;
+  const int m_begin = wi.split ? (wi.chunk * nblk) / wi.k : 0;
+  const int m_end = wi.split ? ((wi.chunk + 1) * nblk) / wi.k : nblk;
   // Per-lane byte offsets of the tile copies (see issue_rows).
   const uint32_t k_off =
       (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
@@ -616,10 +620,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     constexpr bool PARTIAL = decltype(partial_c)::value;
     const int par = (m - m_begin) & 1;
     lds_u8 kp[4], vp[2];
+    // Computed once per block; the empty asm keeps the compiler from
+    // recomputing each address before every read instead of holding it.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kp[c] = lp.k[c] + par * (int)sizeof(KStage);
+    for (int c = 0; c < 4; ++c) {
+      kp[c] = lp.k[c] + par * (int)sizeof(KStage);
+      asm volatile("" : "+v"(kp[c]));
+    }
 #pragma unroll
-    for (int te = 0; te < 2; ++te) vp[te] = lp.v[te] + par * (int)sizeof(VStage);
+    for (int te = 0; te < 2; ++te) {
+      vp[te] = lp.v[te] + par * (int)sizeof(VStage);
+      asm volatile("" : "+v"(vp[te]));
+    }
     const int kv0 = kv_next;
     wait_vm_zero();    // this wave's copies of block m
     wait_lgkm_zero();  // this wave's reads of block m-1
@@ -638,17 +650,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   float lt = half_sum(l);  // the row's sum of (rounded) probabilities
 
   if (wi.split) {
-    // Leave this half's partial result, then take a ticket; the second
-    // half to finish merges the two. The partials are written and read with
-    // device-scope (sc1) accesses, and every write has completed before the
-    // ticket is taken, so the halves may run on different XCDs; this avoids
-    // device-scope fences, which would write back and invalidate the whole
-    // L2 of the XCD (and with it the K/V tiles other workgroups reuse).
+    // Leave this chunk's partial result, then take a ticket; the last of the
+    // k chunks to finish merges them all. The partials are written and read
+    // with device-scope (sc1) accesses, and every write has completed before
+    // the ticket is taken, so the chunks may run on different XCDs; this
+    // avoids device-scope fences, which would write back and invalidate the
+    // whole L2 of the XCD (and with it the K/V tiles other workgroups reuse).
     const int64_t bhn = (int64_t)a.B * a.H;
-    float* mine = a.partials + (((int64_t)qb * 2 + wi.chunk) * bhn + bh) * kSlotFloats;
-    float* other = a.partials + (((int64_t)qb * 2 + (1 - wi.chunk)) * bhn + bh) * kSlotFloats;
+    auto slot = [&](int c) { return a.partials + (((int64_t)qb * kMaxChunks + c) * bhn + bh) * kSlotFloats; };
     auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     auto get = [](float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    float* mine = slot(wi.chunk);
 #pragma unroll
     for (int te = 0; te < 2; ++te)
 #pragma unroll
@@ -663,28 +675,42 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     int32_t* counter = a.counters + (int64_t)qb * bhn + bh;
     if (tid == 0) ticket = atomicAdd(counter, 1);
     __syncthreads();
-    if (ticket == 0) return;  // the other half merges
+    if (ticket != wi.k - 1) return;  // a later chunk merges
     if (tid == 0) atomicExch(counter, 0);  // ready for the next call
-    const float m_o = get(other + 4 * 32 * 64 + wave * 32 + lq);
-    const float l_o = get(other + 4 * 32 * 64 + kBlock + wave * 32 + lq);
-    const float m_new = fmaxf(m_ref, m_o);
-    const float w_s = (m_ref == -INFINITY) ? 0.0f : fast_exp2(m_ref - m_new);
-    const float w_o = (m_o == -INFINITY) ? 0.0f : fast_exp2(m_o - m_new);
-    // Combine in chunk order (chunk 0's term times its weight, plus chunk
-    // 1's), whichever half merges, so the result does not depend on which
-    // half finished last.
-    const bool first = wi.chunk == 0;
-    const float w0 = first ? w_s : w_o, w1 = first ? w_o : w_s;
+    // Merge in chunk order (the same operations whichever chunk merges):
+    // weights w_c = 2^(m_c - max m), O = sum_c w_c O_c, l = sum_c w_c l_c.
+    float mc[kMaxChunks], lc[kMaxChunks], wc[kMaxChunks];
+    float m_new = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c < wi.k) {
+        mc[c] = (c == wi.chunk) ? m_ref : get(slot(c) + 4 * 32 * 64 + wave * 32 + lq);
+        lc[c] = (c == wi.chunk) ? lt : get(slot(c) + 4 * 32 * 64 + kBlock + wave * 32 + lq);
+        m_new = fmaxf(m_new, mc[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < wi.k) wc[c] = (mc[c] == -INFINITY) ? 0.0f : fast_exp2(mc[c] - m_new);
 #pragma unroll
     for (int te = 0; te < 2; ++te)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float ov = get(other + (wave * 32 + te * 16 + r) * 64 + lane);
-        const float o0 = first ? oacc[te][r] : ov, o1 = first ? ov : oacc[te][r];
-        oacc[te][r] = fmaf(w0, o0, w1 * o1);
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+          if (c < wi.k) {
+            const float ov = (c == wi.chunk) ? oacc[te][r] : get(slot(c) + (wave * 32 + te * 16 + r) * 64 + lane);
+            acc = (c == 0) ? wc[0] * ov : fmaf(wc[c], ov, acc);
+          }
+        }
+        oacc[te][r] = acc;
       }
-    const float l0 = first ? lt : l_o, l1 = first ? l_o : lt;
-    lt = fmaf(w0, l0, w1 * l1);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < wi.k) lsum = (c == 0) ? wc[0] * lc[0] : fmaf(wc[c], lc[c], lsum);
+    lt = lsum;
     m_ref = m_new;
   }
 
@@ -845,8 +871,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
 
 template <int KIND, bool SOFTCAP>
 hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
-  // Up to two work items per query block; items past the plan's end return.
-  const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * 2));
+  // Up to kMaxChunks work items per query block; items past the plan's end
+  // return at once.
+  const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * kMaxChunks));
   const dim3 block(kThreads);
   switch (dtype) {
     case ATTN_BF16:

@@ -156,25 +156,32 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
   }
 }
 
-// Work plan. A query block with n live kv blocks is one work item, or two
-// (its first ceil(n/2) blocks and the rest) when n exceeds the split length
-// C = max(kMinSplit, ceil(max_n / 2)), max_n being the largest n of the mask;
-// then no item is longer than C and the long rows no longer set the length
-// of a launch. Item t in [0, 2 nq) is (qb = t / 2, chunk = t % 2); chunk 1
-// exists only for split blocks. Items are ranked by decreasing cost (blocks
-// visited), ties by t:
-//   plan[0] = number of items; plan[1 + rank(t)] = qb | chunk << 20 | split << 21.
+// Work plan (kMaxChunks = 2: three-way splits measured slower, each extra
+// item costing its own prologue latency and a larger merge). With max_n the
+// largest number of live kv blocks of any query block and the split length
+// C = max(kMinSplit, ceil(max_n / kMaxChunks)), a
+// query block with n > C blocks becomes k = min(kMaxChunks, ceil(n / C)) work
+// items, chunk c visiting its blocks [c n / k, (c+1) n / k); otherwise it is
+// one item. No item is then much longer than C, so the longest rows no longer
+// set the length of a launch. Item t in [0, kMaxChunks nq) is
+// (qb = t / kMaxChunks, chunk = t % kMaxChunks) and exists when chunk < k. Items are ranked by decreasing
+// cost (blocks visited), ties by t:
+//   plan[0] = number of items;
+//   plan[1 + rank(t)] = qb | chunk << 20 | (k - 1) << 22.
 // Every workgroup recomputes max_n, so the kernel needs no second pass.
 constexpr int kMinSplit = 16;
 
+__device__ inline int32_t split_count(int32_t n, int32_t split_len) {
+  return n <= split_len ? 1 : min(kMaxChunks, (n + split_len - 1) / split_len);
+}
+
 __device__ inline int32_t item_cost(int32_t t, const int32_t* kv_num, const int32_t* full_num,
                                     int32_t split_len) {
-  const int32_t qb = t >> 1, chunk = t & 1;
+  const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
   const int32_t n = kv_num[qb] + full_num[qb];
-  const bool split = n > split_len;
-  if (!split) return chunk ? -1 : n;  // -1: no such item
-  const int32_t h = (n + 1) >> 1;
-  return chunk ? n - h : h;
+  const int32_t k = split_count(n, split_len);
+  if (chunk >= k) return -1;  // no such item
+  return ((chunk + 1) * n) / k - (chunk * n) / k;
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, const int32_t* __restrict__ kv_num,
@@ -191,9 +198,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, const int32_
   __syncthreads();
   mx = red[0];
   for (int w = 1; w < kThreads / 64; ++w) mx = max(mx, red[w]);
-  const int32_t split_len = max(kMinSplit, (mx + 1) >> 1);
+  const int32_t split_len = max(kMinSplit, (mx + kMaxChunks - 1) / kMaxChunks);
 
-  const int32_t n_items_total = 2 * nq;
+  const int32_t n_items_total = kMaxChunks * nq;
   const int t = blockIdx.x * kThreads + tid;
   const int32_t mine = (t < n_items_total) ? item_cost(t, kv_num, full_num, split_len) : -1;
   int32_t rank = 0, count = 0;
@@ -210,9 +217,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, const int32_
     }
   }
   if (t < n_items_total && mine >= 0) {
-    const int32_t qb = t >> 1, chunk = t & 1;
-    const int32_t n = kv_num[qb] + full_num[qb];
-    plan[1 + rank] = qb | (chunk << 20) | ((n > split_len ? 1 : 0) << 21);
+    const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
+    const int32_t k = split_count(kv_num[qb] + full_num[qb], split_len);
+    plan[1 + rank] = qb | (chunk << 20) | ((k - 1) << 22);
   }
   if (t == 0) plan[0] = count;
 }
@@ -229,7 +236,7 @@ hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, i
                      doc, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_kernel, dim3((2 * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
+  hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      stream, nq, kv_num, full_num, schedule);
   return hipGetLastError();
 }

@@ -8,6 +8,7 @@
 namespace bsattn {
 
 constexpr int kBlock = 128;   // BlockMask granularity and query/key tile size
+constexpr int kMaxChunks = 2; // work items a query block may be split into
 constexpr int kHeadDim = 64;  // the one head dimension with kernels
 
 // Everything the forward kernels need from a BlockMask.
@@ -46,7 +47,7 @@ struct FwdArgs {
 
 // Partial result of one split item: the 4 waves' O^T accumulators in
 // register order ([wave][32 registers][64 lanes]), then the running max and
-// the sum of each of the 128 rows.
+// the sum of each of the 128 rows. Slots are [query block][chunk][B*H].
 constexpr int64_t kSlotFloats = 4 * 32 * 64 + 2 * kBlock;
 // Long query blocks are split only when there are few work items.
 constexpr int64_t kSplitMaxItems = 2048;
@@ -59,7 +60,7 @@ inline size_t counters_bytes(int64_t bh, int32_t nq) {
 }
 inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq) {
   if (!use_split(dtype, bh, nq)) return 0;
-  return counters_bytes(bh, nq) + (size_t)nq * 2 * (size_t)bh * kSlotFloats * sizeof(float);
+  return counters_bytes(bh, nq) + (size_t)nq * kMaxChunks * (size_t)bh * kSlotFloats * sizeof(float);
 }
 
 // Enqueue the block classification and the query-block schedule.

@@ -102,14 +102,15 @@ typedef int32_t attn_status;
  *                              then 0 up to nk entries
  *   schedule[2 * nq + 1]       work plan of the forward: schedule[0] is the
  *                              number of work items, schedule[1 + r] the r-th
- *                              item, qb | chunk << 20 | split << 21. A query
- *                              block with n live kv blocks is one item
- *                              (split = 0, chunk = 0), or two when n exceeds
- *                              max(16, ceil(max_n / 2)), max_n the largest n
- *                              of the mask (split = 1; chunk 0 visits its
- *                              first ceil(n / 2) blocks, chunk 1 the rest).
- *                              Items are ordered by decreasing number of
- *                              blocks visited, ties by 2 qb + chunk.
+ *                              item, qb | chunk << 20 | (k - 1) << 22. With
+ *                              max_n the largest number n of live kv blocks of
+ *                              any query block and C = max(16, ceil(max_n/2)),
+ *                              a query block with n > C becomes k = 2 items,
+ *                              chunk c visiting its blocks [c n / 2,
+ *                              (c + 1) n / 2) of the order full blocks then
+ *                              partial blocks; other query blocks are one item
+ *                              (k = 1). Items are ordered by decreasing number
+ *                              of blocks visited, ties by 2 qb + chunk.
  * with nq = ceil(q_len / 128) and nk = ceil(kv_len / 128). A block is full only
  * if all 128 x 128 of its positions are in range and live, so the blocks at a
  * ragged end are at most partial.
@@ -152,11 +153,12 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
 
 /*
  * Bytes of device workspace attn_forward needs for this problem (0 when it
- * needs none). The forward splits long query blocks in two work items (see
- * the work plan) when there are few query blocks for the GPU, that is when
- * B * H * num_q_blocks <= 2048 and dtype is ATTN_BF16 or ATTN_F16; each
- * split item then leaves fp32 partial results and a ticket counter in the
- * workspace, and the second item to finish merges the two.
+ * needs none). The forward splits long query blocks into two work items
+ * (see the work plan) when there are few query blocks for the GPU,
+ * that is when B * H * num_q_blocks <= 2048 and dtype is ATTN_BF16 or
+ * ATTN_F16; each split item then leaves fp32 partial results and takes a
+ * ticket in the workspace, and the last item of a query block to finish
+ * merges them.
  * Errors: INVALID_ARGUMENT for a null bm or bytes, or B, H < 1.
  */
 attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,

@@ -34,21 +34,20 @@ def dev():
     return torch.device("cuda", 0)
 
 
-def expected_plan(n):
-    """The forward's work plan from the live block counts n[qb]: a query
-    block with more than max(16, ceil(max n / 2)) blocks becomes two items
-    (first ceil(n/2) blocks, rest), items by decreasing cost, ties by
-    2 qb + chunk; [count, qb | chunk << 20 | split << 21, ...]."""
+def expected_plan(n, max_chunks=2):
+    """The forward's work plan from the live block counts n[qb]: with
+    C = max(16, ceil(max n / 2)), a query block with n > C blocks becomes
+    k = 2 items, chunk c visiting blocks [c n / k, (c + 1) n / k); items by
+    decreasing cost, ties by 2 qb + chunk;
+    [count, qb | chunk << 20 | (k - 1) << 22, ...]."""
     n = [int(x) for x in n]
-    split_len = max(16, (max(n, default=0) + 1) // 2)
+    split_len = max(16, -(-max(n, default=0) // max_chunks))
     items = []
     for qb, c in enumerate(n):
-        if c > split_len:
-            h = (c + 1) // 2
-            items.append((h, 2 * qb, qb | (1 << 21)))
-            items.append((c - h, 2 * qb + 1, qb | (1 << 20) | (1 << 21)))
-        else:
-            items.append((c, 2 * qb, qb))
+        k = 1 if c <= split_len else min(max_chunks, -(-c // split_len))
+        for ch in range(k):
+            cost = ((ch + 1) * c) // k - (ch * c) // k
+            items.append((cost, max_chunks * qb + ch, qb | (ch << 20) | ((k - 1) << 22)))
     items.sort(key=lambda it: (-it[0], it[1]))
     return [len(items)] + [code for _, _, code in items]
 
@@ -148,7 +147,7 @@ SMALL = [
     _odd("causal_B2H3_bf16", "bf16", 3, 256, 256, wl.MASK_CAUSAL, B=2),
     _odd("none_zero_kv_bf16", "bf16", 1, 256, 0, wl.MASK_NONE),
     # 34 query blocks: blocks with more than 17 live kv blocks run as two
-    # halves merged through the workspace
+    # chunks merged through the workspace
     _odd("causal_4352_bf16_split", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL),
     _odd("document_4400_f16_split", "f16", 1, 4400, 4400, wl.MASK_DOCUMENT, 0, (600, 2500), 30.0),
     _odd("none_3000x4300_bf16_split", "bf16", 1, 3000, 4300, wl.MASK_NONE),
