@@ -129,9 +129,10 @@ class BlockMask:
 
     Tensors (int32, on the mask's device): ``kv_num_blocks [nq]``,
     ``kv_indices [nq, nk]`` (partial blocks), ``full_kv_num_blocks [nq]``,
-    ``full_kv_indices [nq, nk]`` (full blocks), ``schedule [2 nq + 1]`` (the
-    forward's work plan: item count, then items ``qb | chunk << 20 | (k - 1)
-    << 22`` by decreasing cost).
+    ``full_kv_indices [nq, nk]`` (full blocks), ``schedule [4 + 8 nq]`` (the
+    forward's work plan: item count, then 4-int descriptors ``(qb | chunk <<
+    20 | (k - 1) << 22, full blocks, partial blocks, first block)`` by
+    decreasing cost).
     """
 
     def __init__(self, kind: int, q_len: int, kv_len: int, window: int,
@@ -145,7 +146,7 @@ class BlockMask:
         self.kv_indices = torch.empty(nq, nk, **opt)
         self.full_kv_num_blocks = torch.empty(nq, **opt)
         self.full_kv_indices = torch.empty(nq, nk, **opt)
-        self.schedule = torch.zeros(2 * nq + 1, **opt)
+        self.schedule = torch.zeros(4 + 8 * nq, **opt)
         self._struct = _BlockMaskStruct()
         s = self._struct
         s.kv_num_blocks = self.kv_num_blocks.data_ptr()

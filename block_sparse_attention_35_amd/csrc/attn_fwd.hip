@@ -428,16 +428,61 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
     const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(x8, both);
   };
+  // In a partial block, each 32 x 32 tile of this wave (its 32 rows x keys
+  // kv0 + 32t .. +31) is classified in closed form, wave-uniformly, from the
+  // rule's offset interval and the key range, as for whole blocks: all pairs
+  // live, none live, or mixed; only mixed tiles evaluate the predicate per
+  // element (for document masks the interval decides only "none live").
+  enum { kTileLive = 0, kTileMixed = 1, kTileDead = 2 };
+  int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
+  if (PARTIAL) {
+    const int i0 = qi - (lane & 31), i1 = i0 + 31;  // this wave's rows
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j0 = kv0 + 32 * t, j1 = min(j0 + 31, a.S - 1);
+      int c;
+      if (j0 > a.S - 1) {
+        c = kTileDead;
+      } else if (KIND == ATTN_MASK_NONE) {
+        c = (j0 + 31 > a.S - 1) ? kTileMixed : kTileLive;
+      } else {
+        const int dmin = i0 - j1, dmax = i1 - j0;  // offsets i - j of the tile
+        const int w = (KIND == ATTN_MASK_SLIDING_WINDOW) ? a.m.window : 0x7fffffff;
+        if (dmax < 0 || dmin > w - 1)
+          c = kTileDead;
+        else if (KIND != ATTN_MASK_DOCUMENT && dmin >= 0 && dmax <= w - 1 && j0 + 31 <= a.S - 1)
+          c = kTileLive;
+        else
+          c = kTileMixed;
+      }
+      tile_cls[t] = __builtin_amdgcn_readfirstlane(c);
+    }
+  }
+
   // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4).
   float mx = -INFINITY;
   f32x16_t s[4];
   auto mask_chunk = [&](int k) {
+    const int t = k >> 2;
+    if (PARTIAL && tile_cls[t] == kTileMixed) {
 #pragma unroll
-    for (int e = 4 * k; e < 4 * k + 4; ++e) {
-      const int t = e >> 4, r = e & 15;
-      const float x = mod_mask<KIND, SOFTCAP, PARTIAL>(s[t][r], kst, t, r, hf, qi, kv0, a, dq);
-      s[t][r] = x;
-      mx = fmaxf(mx, x);
+      for (int e = 4 * k; e < 4 * k + 4; ++e) {
+        const int r = e & 15;
+        const float x = mod_mask<KIND, SOFTCAP, true>(s[t][r], kst, t, r, hf, qi, kv0, a, dq);
+        s[t][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    } else if (PARTIAL && tile_cls[t] == kTileDead) {
+#pragma unroll
+      for (int e = 4 * k; e < 4 * k + 4; ++e) s[t][e & 15] = -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 4 * k; e < 4 * k + 4; ++e) {
+        const int r = e & 15;
+        const float x = mod_mask<KIND, SOFTCAP, false>(s[t][r], kst, t, r, hf, qi, kv0, a, dq);
+        s[t][r] = x;
+        mx = fmaxf(mx, x);
+      }
     }
   };
 
@@ -516,25 +561,34 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   __builtin_amdgcn_s_setprio(0);
 }
 
-// One work item of the plan written by the mask builder: query block qb and,
-// for a split item, which of its k chunks of kv blocks it visits.
+// One work item of the plan written by the mask builder (a 16-byte
+// descriptor, one scalar load): query block qb, which of its k chunks of kv
+// blocks the item visits, the block counts of qb and the item's first block.
 struct WorkItem {
   int qb, chunk, k;
-  bool split;  // the item is one of k > 1 chunks whose results are merged
-  bool skip;   // no work (past the end of the plan, or a later chunk when
-               // splitting is off: then the first item visits every block)
+  int nfull, npart;  // full and partial kv blocks of qb
+  int first_kb;      // kv block index of the item's first visited block
+  bool split;        // the item is one of k > 1 chunks whose results are merged
+  bool skip;         // no work (past the end of the plan, or a later chunk when
+                     // splitting is off: then the first item visits every block)
 };
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const i32x4_t* const_i32x4_ptr;
+
 __device__ inline WorkItem work_item(const FwdArgs& a, int e) {
-  const const_i32_ptr plan = (const_i32_ptr)a.m.schedule;
-  WorkItem w{0, 0, 1, false, true};
-  if (e >= plan[0]) return w;
-  const int32_t code = plan[1 + e];
-  w.qb = code & 0xFFFFF;
-  w.chunk = (code >> 20) & 3;
-  w.k = ((code >> 22) & 3) + 1;
+  const i32x4_t d = ((const_i32x4_ptr)(a.m.schedule + 4))[e];
+  WorkItem w;
+  w.skip = d[0] < 0;
+  w.qb = d[0] & 0xFFFFF;
+  w.chunk = (d[0] >> 20) & 3;
+  w.k = ((d[0] >> 22) & 3) + 1;
+  w.nfull = d[1];
+  w.npart = d[2];
+  w.first_kb = d[3];
   w.split = a.split && w.k > 1;
-  w.skip = w.chunk > 0 && !w.split;
+  w.skip = w.skip || (w.chunk > 0 && !w.split);
+  if (w.skip) w.qb = w.chunk = w.nfull = w.npart = w.first_kb = 0;
   return w;
 }
 
@@ -562,8 +616,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + h * a.v_sh;
   T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
 
-  const int nfull = a.m.full_num[qb];
-  const int npart = a.m.kv_num[qb];
+  const int nfull = wi.nfull;
+  const int npart = wi.npart;
   const int nblk = nfull + npart;
   const const_i32_ptr full_list = (const_i32_ptr)(a.m.full_idx + (int64_t)qb * a.m.nk);
   const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
@@ -578,10 +632,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const uint32_t v_off = (uint32_t)((lane >> 3) * a.v_sl * (int64_t)sizeof(T)) +
                          (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
 
-  // Block m's K and V tiles live in stage (m - m_begin) % 2.
-  int kv_next = 0;  // first key of the next block to copy
+  // Block m's K and V tiles live in stage (m - m_begin) % 2. The index of
+  // the block after the next one is loaded a block ahead, so no block waits
+  // on a scalar load before issuing its copies.
+  int kv_next = 0;   // first key of the next block to copy
+  int kv_after = 0;  // first key of the block after it
   if (m_end > m_begin) {
-    kv_next = kv_start(m_begin);
+    kv_next = wi.first_kb * kBlock;
+    if (m_begin + 1 < m_end) kv_after = kv_start(m_begin + 1);
     issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[0], wave, lane);
     issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[0].v, wave, lane);
   }
@@ -637,9 +695,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     wait_lgkm_zero();  // this wave's reads of block m-1
     barrier_only();
     if (m + 1 < m_end) {
-      kv_next = kv_start(m + 1);
+      kv_next = kv_after;
       issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[1 - par], wave, lane);
       issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
+      if (m + 2 < m_end) kv_after = kv_start(m + 2);
     }
     fwd_block<T, KIND, SOFTCAP, PARTIAL>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, kv0, lane, a, dq);
   };

@@ -166,8 +166,11 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
 // set the length of a launch. Item t in [0, kMaxChunks nq) is
 // (qb = t / kMaxChunks, chunk = t % kMaxChunks) and exists when chunk < k. Items are ranked by decreasing
 // cost (blocks visited), ties by t:
-//   plan[0] = number of items;
-//   plan[1 + rank(t)] = qb | chunk << 20 | (k - 1) << 22.
+// Each item is stored as a 16-byte descriptor, so the forward fetches all it
+// needs to start an item with one scalar load:
+//   plan[0] = number of items; plan[4 + 4 rank(t) + {0, 1, 2, 3}] =
+//   {qb | chunk << 20 | (k - 1) << 22, full blocks of qb, partial blocks of
+//   qb, index of the item's first visited kv block}; unused entries hold -1.
 // Every workgroup recomputes max_n, so the kernel needs no second pass.
 constexpr int kMinSplit = 16;
 
@@ -184,8 +187,11 @@ __device__ inline int32_t item_cost(int32_t t, const int32_t* kv_num, const int3
   return ((chunk + 1) * n) / k - (chunk * n) / k;
 }
 
-__global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, const int32_t* __restrict__ kv_num,
+__global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
+                                                        const int32_t* __restrict__ kv_num,
+                                                        const int32_t* __restrict__ kv_idx,
                                                         const int32_t* __restrict__ full_num,
+                                                        const int32_t* __restrict__ full_idx,
                                                         int32_t* __restrict__ plan) {
   __shared__ int32_t cost_tile[kThreads];
   __shared__ int32_t red[kThreads / 64];
@@ -218,10 +224,22 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, const int32_
   }
   if (t < n_items_total && mine >= 0) {
     const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
-    const int32_t k = split_count(kv_num[qb] + full_num[qb], split_len);
-    plan[1 + rank] = qb | (chunk << 20) | ((k - 1) << 22);
+    const int32_t nf = full_num[qb], np = kv_num[qb];
+    const int32_t k = split_count(nf + np, split_len);
+    const int32_t first = (chunk * (nf + np)) / k;  // first visited block of the item
+    int4 d;
+    d.x = qb | (chunk << 20) | ((k - 1) << 22);
+    d.y = nf;
+    d.z = np;
+    d.w = (first < nf) ? full_idx[(int64_t)qb * nk + first]
+                       : (first - nf < np ? kv_idx[(int64_t)qb * nk + first - nf] : 0);
+    reinterpret_cast<int4*>(plan + 4)[rank] = d;
   }
-  if (t == 0) plan[0] = count;
+  if (t < n_items_total && t >= count) reinterpret_cast<int4*>(plan + 4)[t] = make_int4(-1, -1, -1, -1);
+  if (t == 0) {
+    plan[0] = count;
+    plan[1] = plan[2] = plan[3] = 0;
+  }
 }
 
 }  // namespace
@@ -237,7 +255,7 @@ hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, nq, kv_num, full_num, schedule);
+                     stream, nq, nk, kv_num, kv_idx, full_num, full_idx, schedule);
   return hipGetLastError();
 }
 

@@ -100,9 +100,13 @@ typedef int32_t attn_status;
  *   full_kv_num_blocks[nq]     number of full kv blocks of query block qb
  *   full_kv_indices[nq * nk]   row qb: its full kv block indices, ascending,
  *                              then 0 up to nk entries
- *   schedule[2 * nq + 1]       work plan of the forward: schedule[0] is the
- *                              number of work items, schedule[1 + r] the r-th
- *                              item, qb | chunk << 20 | (k - 1) << 22. With
+ *   schedule[4 + 8 * nq]       work plan of the forward: schedule[0] is the
+ *                              number of work items, schedule[1..3] are 0, and
+ *                              schedule[4 + 4r .. 4r + 7] describes the r-th
+ *                              item: {qb | chunk << 20 | (k - 1) << 22, full
+ *                              blocks of qb, partial blocks of qb, kv block
+ *                              index of the item's first visited block}
+ *                              (entries past the last item hold -1). With
  *                              max_n the largest number n of live kv blocks of
  *                              any query block and C = max(16, ceil(max_n/2)),
  *                              a query block with n > C becomes k = 2 items,

@@ -68,8 +68,19 @@ def _check_mask(bm, w: wl.Workload, doc):
         g = g.cpu().numpy()
         assert g.shape == e.shape and np.array_equal(g, e), f"{w.name}: {name} differs"
     plan = expected_plan(want[0] + want[2])
-    got_plan = bm.schedule.cpu().numpy().tolist()
-    assert got_plan[:len(plan)] == plan, f"{w.name}: work plan"
+    got = bm.schedule.cpu().numpy()
+    count = int(got[0])
+    assert count == plan[0] and got[1:4].tolist() == [0, 0, 0], f"{w.name}: work plan header"
+    desc = got[4:].reshape(-1, 4)
+    assert desc[:count, 0].tolist() == plan[1:], f"{w.name}: work plan order"
+    assert (desc[count:] == -1).all(), f"{w.name}: unused plan entries"
+    for code, nf, npart, first in desc[:count].tolist():
+        qb, chunk, k = code & 0xFFFFF, (code >> 20) & 3, ((code >> 22) & 3) + 1
+        assert (nf, npart) == (int(want[2][qb]), int(want[0][qb])), f"{w.name}: counts of {qb}"
+        m0 = (chunk * (nf + npart)) // k
+        lists = list(want[3][qb][:nf]) + list(want[1][qb][:npart])
+        if m0 < nf + npart:
+            assert first == lists[m0], f"{w.name}: first block of item {code}"
 
 
 def _odd(name, dtype, H, L, S, kind, window=0, bounds=(), softcap=0.0, B=1):
