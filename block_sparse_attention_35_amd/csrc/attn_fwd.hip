@@ -623,9 +623,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
   // First key of the n-th visited block: full blocks first, then partial.
   auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
-  // This item visits blocks [m_begin, m_end) of that order.
-  const int m_begin = wi.split ? (wi.chunk * nblk) / wi.k : 0;
-  const int m_end = wi.split ? ((wi.chunk + 1) * nblk) / wi.k : nblk;
+  // This item visits blocks [m_begin, m_end) of that order: a split query
+  // block's first chunk is its first C blocks (C from the plan), the second
+  // the rest.
+  const int split_len = a.m.schedule[1];
+  const int m_begin = (wi.split && wi.chunk == 1) ? split_len : 0;
+  const int m_end = (wi.split && wi.chunk == 0) ? split_len : nblk;
   // Per-lane byte offsets of the tile copies (see issue_rows).
   const uint32_t k_off =
       (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);

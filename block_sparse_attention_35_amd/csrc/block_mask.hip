@@ -156,26 +156,30 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
   }
 }
 
-// Work plan (kMaxChunks = 2: three-way splits measured slower, each extra
-// item costing its own prologue latency and a larger merge). With max_n the
-// largest number of live kv blocks of any query block and the split length
-// C = max(kMinSplit, ceil(max_n / kMaxChunks)), a
-// query block with n > C blocks becomes k = min(kMaxChunks, ceil(n / C)) work
-// items, chunk c visiting its blocks [c n / k, (c+1) n / k); otherwise it is
-// one item. No item is then much longer than C, so the longest rows no longer
-// set the length of a launch. Item t in [0, kMaxChunks nq) is
-// (qb = t / kMaxChunks, chunk = t % kMaxChunks) and exists when chunk < k. Items are ranked by decreasing
-// cost (blocks visited), ties by t:
+// Work plan. With max_n the largest number of live kv blocks of any query
+// block, the split length is C = max(kMinSplit, ceil(max_n / 2)); a query
+// block with n > C blocks becomes two work items, its first C visited blocks
+// and the remaining n - C, and other query blocks are one item. Items are
+// ranked by decreasing cost (blocks visited), ties by t = 2 qb + chunk. Cutting
+// a fixed first chunk (rather than halves) leaves short remainders that fill
+// in beside short unsplit rows when the items are run longest first, so a
+// causal launch is no longer set by its longest rows (three-way splits were
+// measured slower: each extra item pays its own prologue latency and a
+// larger merge).
 // Each item is stored as a 16-byte descriptor, so the forward fetches all it
 // needs to start an item with one scalar load:
-//   plan[0] = number of items; plan[4 + 4 rank(t) + {0, 1, 2, 3}] =
+//   plan[0] = number of items, plan[1] = C; plan[4 + 4 rank(t) + {0..3}] =
 //   {qb | chunk << 20 | (k - 1) << 22, full blocks of qb, partial blocks of
 //   qb, index of the item's first visited kv block}; unused entries hold -1.
 // Every workgroup recomputes max_n, so the kernel needs no second pass.
 constexpr int kMinSplit = 16;
 
-__device__ inline int32_t split_count(int32_t n, int32_t split_len) {
-  return n <= split_len ? 1 : min(kMaxChunks, (n + split_len - 1) / split_len);
+__device__ inline int32_t split_count(int32_t n, int32_t split_len) { return n <= split_len ? 1 : 2; }
+
+// Blocks visited by chunk `chunk` of a query block with n blocks: [first, end).
+__device__ inline int32_t chunk_first(int32_t chunk, int32_t split_len) { return chunk ? split_len : 0; }
+__device__ inline int32_t chunk_end(int32_t chunk, int32_t k, int32_t n, int32_t split_len) {
+  return (k > 1 && chunk == 0) ? split_len : n;
 }
 
 __device__ inline int32_t item_cost(int32_t t, const int32_t* kv_num, const int32_t* full_num,
@@ -184,7 +188,7 @@ __device__ inline int32_t item_cost(int32_t t, const int32_t* kv_num, const int3
   const int32_t n = kv_num[qb] + full_num[qb];
   const int32_t k = split_count(n, split_len);
   if (chunk >= k) return -1;  // no such item
-  return ((chunk + 1) * n) / k - (chunk * n) / k;
+  return chunk_end(chunk, k, n, split_len) - chunk_first(chunk, split_len);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
   __syncthreads();
   mx = red[0];
   for (int w = 1; w < kThreads / 64; ++w) mx = max(mx, red[w]);
-  const int32_t split_len = max(kMinSplit, (mx + kMaxChunks - 1) / kMaxChunks);
+  const int32_t split_len = max(kMinSplit, (mx + 1) / 2);
 
   const int32_t n_items_total = kMaxChunks * nq;
   const int t = blockIdx.x * kThreads + tid;
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
     const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
     const int32_t nf = full_num[qb], np = kv_num[qb];
     const int32_t k = split_count(nf + np, split_len);
-    const int32_t first = (chunk * (nf + np)) / k;  // first visited block of the item
+    const int32_t first = chunk_first(chunk, split_len);  // first visited block of the item
     int4 d;
     d.x = qb | (chunk << 20) | ((k - 1) << 22);
     d.y = nf;
@@ -238,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
   if (t < n_items_total && t >= count) reinterpret_cast<int4*>(plan + 4)[t] = make_int4(-1, -1, -1, -1);
   if (t == 0) {
     plan[0] = count;
-    plan[1] = plan[2] = plan[3] = 0;
+    plan[1] = split_len;
+    plan[2] = plan[3] = 0;
   }
 }
 

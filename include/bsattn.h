@@ -101,20 +101,21 @@ typedef int32_t attn_status;
  *   full_kv_indices[nq * nk]   row qb: its full kv block indices, ascending,
  *                              then 0 up to nk entries
  *   schedule[4 + 8 * nq]       work plan of the forward: schedule[0] is the
- *                              number of work items, schedule[1..3] are 0, and
+ *                              number of work items, schedule[1] the split
+ *                              length C = max(16, ceil(max_n / 2)) (max_n the
+ *                              largest number n of live kv blocks of any query
+ *                              block), schedule[2..3] are 0, and
  *                              schedule[4 + 4r .. 4r + 7] describes the r-th
  *                              item: {qb | chunk << 20 | (k - 1) << 22, full
  *                              blocks of qb, partial blocks of qb, kv block
  *                              index of the item's first visited block}
- *                              (entries past the last item hold -1). With
- *                              max_n the largest number n of live kv blocks of
- *                              any query block and C = max(16, ceil(max_n/2)),
- *                              a query block with n > C becomes k = 2 items,
- *                              chunk c visiting its blocks [c n / 2,
- *                              (c + 1) n / 2) of the order full blocks then
- *                              partial blocks; other query blocks are one item
- *                              (k = 1). Items are ordered by decreasing number
- *                              of blocks visited, ties by 2 qb + chunk.
+ *                              (entries past the last item hold -1). A query
+ *                              block with n > C is k = 2 items, chunk 0 its
+ *                              first C visited blocks and chunk 1 the rest (in
+ *                              the order full blocks then partial blocks);
+ *                              others are one item (k = 1). Items are ordered
+ *                              by decreasing number of blocks visited, ties by
+ *                              2 qb + chunk.
  * with nq = ceil(q_len / 128) and nk = ceil(kv_len / 128). A block is full only
  * if all 128 x 128 of its positions are in range and live, so the blocks at a
  * ragged end are at most partial.

@@ -34,22 +34,22 @@ def dev():
     return torch.device("cuda", 0)
 
 
-def expected_plan(n, max_chunks=2):
+def expected_plan(n):
     """The forward's work plan from the live block counts n[qb]: with
-    C = max(16, ceil(max n / 2)), a query block with n > C blocks becomes
-    k = 2 items, chunk c visiting blocks [c n / k, (c + 1) n / k); items by
-    decreasing cost, ties by 2 qb + chunk;
-    [count, qb | chunk << 20 | (k - 1) << 22, ...]."""
+    C = max(16, ceil(max n / 2)), a query block with n > C blocks becomes two
+    items (its first C blocks, then the rest); items by decreasing cost, ties
+    by 2 qb + chunk. Returns (C, [qb | chunk << 20 | (k - 1) << 22, ...])."""
     n = [int(x) for x in n]
-    split_len = max(16, -(-max(n, default=0) // max_chunks))
+    split_len = max(16, -(-max(n, default=0) // 2))
     items = []
     for qb, c in enumerate(n):
-        k = 1 if c <= split_len else min(max_chunks, -(-c // split_len))
-        for ch in range(k):
-            cost = ((ch + 1) * c) // k - (ch * c) // k
-            items.append((cost, max_chunks * qb + ch, qb | (ch << 20) | ((k - 1) << 22)))
+        if c > split_len:
+            items.append((split_len, 2 * qb, qb | (1 << 22)))
+            items.append((c - split_len, 2 * qb + 1, qb | (1 << 20) | (1 << 22)))
+        else:
+            items.append((c, 2 * qb, qb))
     items.sort(key=lambda it: (-it[0], it[1]))
-    return [len(items)] + [code for _, _, code in items]
+    return split_len, [code for _, _, code in items]
 
 
 def _mask_on_gpu(w: wl.Workload, dev, doc=None):
@@ -67,17 +67,17 @@ def _check_mask(bm, w: wl.Workload, doc):
                            "full_kv_indices"), got, want):
         g = g.cpu().numpy()
         assert g.shape == e.shape and np.array_equal(g, e), f"{w.name}: {name} differs"
-    plan = expected_plan(want[0] + want[2])
+    split_len, codes = expected_plan(want[0] + want[2])
     got = bm.schedule.cpu().numpy()
     count = int(got[0])
-    assert count == plan[0] and got[1:4].tolist() == [0, 0, 0], f"{w.name}: work plan header"
+    assert count == len(codes) and got[1:4].tolist() == [split_len, 0, 0], f"{w.name}: plan header"
     desc = got[4:].reshape(-1, 4)
-    assert desc[:count, 0].tolist() == plan[1:], f"{w.name}: work plan order"
+    assert desc[:count, 0].tolist() == codes, f"{w.name}: work plan order"
     assert (desc[count:] == -1).all(), f"{w.name}: unused plan entries"
     for code, nf, npart, first in desc[:count].tolist():
         qb, chunk, k = code & 0xFFFFF, (code >> 20) & 3, ((code >> 22) & 3) + 1
         assert (nf, npart) == (int(want[2][qb]), int(want[0][qb])), f"{w.name}: counts of {qb}"
-        m0 = (chunk * (nf + npart)) // k
+        m0 = split_len if chunk == 1 else 0
         lists = list(want[3][qb][:nf]) + list(want[1][qb][:npart])
         if m0 < nf + npart:
             assert first == lists[m0], f"{w.name}: first block of item {code}"
