@@ -2,9 +2,10 @@
 //
 // O = softmax(Q K^T * scale + mask bias [+ soft-cap score_mod]) V and the
 // per-row logsumexp, without writing the L x S score table anywhere: a
-// workgroup owns one (batch, head, 128-query block) item, walks that block's
-// full kv blocks and then its partial kv blocks from the BlockMask, and keeps
-// a running row max and row sum (online softmax) while accumulating P V.
+// workgroup owns one work item (128 query rows of one batch*head, all of
+// their live kv blocks or one chunk of them), walks the item's full kv
+// blocks and then its partial kv blocks from the BlockMask, and keeps a
+// running row max and row sum (online softmax) while accumulating P V.
 // Definition: "SDPA replaces hand-written attention", section 1 (Attention
 // equation and its four steps); running max / running sum instead of the
 // score table: same page, section 2, and "FlashAttention" (service-dock),
@@ -21,9 +22,13 @@
 //  * The S^T accumulator layout (lane = query, registers = kv) is exactly the
 //    B operand layout of O^T = V^T P^T once probabilities are packed to
 //    16 bits, because the contraction index may be permuted freely as long as
-//    both operands use the same permutation; V^T is staged in LDS in that
-//    permuted order so each A operand is one 16-byte LDS read.
-//  * K is staged row-major in LDS with an XOR swizzle of its 16-byte chunks.
+//    both operands use the same permutation; the matching V^T operand comes
+//    from transposed LDS reads (ds_read_b64_tr_b16) of the row-major V tile.
+//  * K and V tiles go from global memory straight to LDS (double buffered,
+//    16-byte chunks XOR-swizzled); each block is two phases of MFMA chunks
+//    with the vector work of the softmax placed between the MFMAs.
+//  * Long query blocks are split into two work items whose partial results
+//    the later one merges (see the work plan of the block-mask builder).
 //
 // bf16/fp16 use v_mfma_f32_32x32x16_{bf16,f16}; fp32 uses v_mfma_f32_32x32x2_f32
 // and keeps probabilities in fp32.
@@ -98,13 +103,14 @@ __device__ inline float half_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// c * tanh(y) in base-2 units of the result, from tanh|y| = (1 - e)/(1 + e)
-// with e = exp(-2|y|) and the sign of y.
-__device__ inline float softcap_log2(float s, float scale_over_cap, float cap_log2e) {
-  const float y = s * scale_over_cap;
-  const float e = fast_exp2(-2.0f * kLog2e * fabsf(y));
-  const float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
-  return copysignf(t, y) * cap_log2e;
+// c * tanh(y), y = s * scale / c, in base-2 units of the result, from
+// c tanh(y) = c - 2c / (e^(2y) + 1): one multiply, exp, add, reciprocal and
+// FMA. It saturates to +-c for large |y| (e = inf or 0); near y = 0 the
+// cancellation costs at most an absolute 2^-23 c, far below the rounding of
+// the probabilities.
+__device__ inline float softcap_log2(float s, float two_log2e_scale_over_cap, float cap_log2e) {
+  const float e = fast_exp2(s * two_log2e_scale_over_cap);
+  return fmaf(-2.0f * cap_log2e, __builtin_amdgcn_rcpf(1.0f + e), cap_log2e);
 }
 
 // Query row i may see key j (both absolute positions), with j < S checked.
@@ -139,7 +145,7 @@ __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, in
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float x = s[t][r];
-      if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
+      if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
       if (PARTIAL) {
         const int jl = t * 32 + acc_row(r, hf);
         const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? doc_k[jl] : 0;
@@ -285,50 +291,6 @@ __device__ inline void issue_k(const T* kg, int64_t k_sl, uint32_t k_off, const 
   }
 }
 
-// S^T = K Q^T for one 128-key tile: 4 tiles of 32 keys x 32 queries,
-// contraction over E = 64 (kp: per-lane K addresses of the stage, see
-// LanePtrs).
-template <typename T>
-__device__ inline void qk_tile(__attribute__((address_space(3))) const uint8_t* const (&kp)[4],
-                               const typename Vec<T>::x8 (&qop)[4], f32x16_t (&s)[4]) {
-  using x8 = typename Vec<T>::x8;
-  typedef __attribute__((address_space(3))) const x8 lds_x8;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s[t] = Vec<T>::mma(*reinterpret_cast<const lds_x8*>(kp[c] + t * 4096), qop[c], s[t]);
-  }
-}
-
-// Score_mod and mask applied in place; returns the block's row max in log2
-// units (-inf when no key of the block is live for this row).
-template <int KIND, bool SOFTCAP, bool PARTIAL>
-__device__ inline float mask_max(f32x16_t (&s)[4], const KStage& st, int qi, int kv0, int lane,
-                                 const FwdArgs& a, int32_t dq) {
-  const int hf = lane >> 5;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[t][r];
-      if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
-      if (PARTIAL) {
-        const int jl = t * 32 + acc_row(r, hf);
-        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? st.doc[jl] : 0;
-        if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
-      }
-      s[t][r] = x;
-      mx = fmaxf(mx, x);
-    }
-  }
-  mx = half_max(mx);
-  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
-  return SOFTCAP ? mx : mx * (a.scale * kLog2e);
-}
-
 typedef __attribute__((address_space(3))) const uint8_t* lds_u8;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -381,7 +343,7 @@ __device__ inline LanePtrs make_lane_ptrs(const Lds& lds, int lane) {
 template <int KIND, bool SOFTCAP, bool PARTIAL>
 __device__ inline float mod_mask(float x, const KStage& st, int t, int r, int hf, int qi, int kv0,
                                  const FwdArgs& a, int32_t dq) {
-  if (SOFTCAP) x = softcap_log2(x, a.scale / a.softcap, a.softcap * kLog2e);
+  if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
   if (PARTIAL) {
     const int jl = t * 32 + acc_row(r, hf);
     const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? st.doc[jl] : 0;
