@@ -265,9 +265,11 @@ __device__ inline void issue_rows(const T* g, int64_t sl, uint32_t lane_off, int
   const int row0 = kv0 + wave * 32;  // first key of this wave's rows
   const uint32_t lds0 = lds_offset(tile) + (uint32_t)wave * 4096u;
   if (kv0 + kBlock <= S) {
+    // One 64-bit multiply per tile; copy i starts 8 i rows further on.
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(g + (int64_t)row0 * sl);
+    const int64_t step = sl * (int64_t)(8 * sizeof(T));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_copy16_base(g + (int64_t)(row0 + 8 * i) * sl, lane_off, lds0 + 1024u * i);
+    for (int i = 0; i < 4; ++i) lds_copy16_base(base + i * step, lane_off, lds0 + 1024u * i);
   } else {
     const int chunk = IS_V ? ((lane & 7) ^ (((lane >> 3) & 3) << 1)) : ((lane & 7) ^ (lane >> 3));
 #pragma unroll
