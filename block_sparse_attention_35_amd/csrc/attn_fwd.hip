@@ -354,6 +354,9 @@ __device__ inline float mod_mask(float x, const KStage& st, int t, int r, int hf
   return x;
 }
 
+// Classes of a 32 x 32 score tile in a partial block.
+enum { kTileLive = 0, kTileMixed = 1, kTileDead = 2 };
+
 // Keeps the compiler's schedulers from moving any instruction across this
 // point, so the source order of the chunks below is the issue order.
 __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -370,7 +373,7 @@ __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 template <typename T, int KIND, bool SOFTCAP, bool PARTIAL>
 __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
                                           const typename Vec<T>::x8 (&qop)[4], f32x16_t (&oacc)[2],
-                                          float& m_ref, float& l, int qi, int kv0, int lane, const FwdArgs& a,
+                                          float& m_ref, float& l, int qi, int row0, int kv0, int lane, const FwdArgs& a,
                                           int32_t dq) {
   using V = Vec<T>;
   using x8 = typename V::x8;
@@ -392,15 +395,15 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
     const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(x8, both);
   };
-  // In a partial block, each 32 x 32 tile of this wave (its 32 rows x keys
-  // kv0 + 32t .. +31) is classified in closed form, wave-uniformly, from the
-  // rule's offset interval and the key range, as for whole blocks: all pairs
-  // live, none live, or mixed; only mixed tiles evaluate the predicate per
-  // element (for document masks the interval decides only "none live").
-  enum { kTileLive = 0, kTileMixed = 1, kTileDead = 2 };
+  // In a partial block, each 32 x 32 tile of this wave (its rows row0 ..
+  // row0 + 31 x keys kv0 + 32t .. +31) is classified in closed form, with
+  // scalar arithmetic only, from the rule's offset interval and the key range,
+  // as whole blocks are: all pairs live, none live, or mixed. Only mixed tiles
+  // test pairs, and only live tiles skip the test; for document masks the
+  // interval decides only "none live".
   int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
   if (PARTIAL) {
-    const int i0 = qi - (lane & 31), i1 = i0 + 31;  // this wave's rows
+    const int i0 = row0, i1 = row0 + 31;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j0 = kv0 + 32 * t, j1 = min(j0 + 31, a.S - 1);
@@ -419,35 +422,58 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
         else
           c = kTileMixed;
       }
-      tile_cls[t] = __builtin_amdgcn_readfirstlane(c);
+      tile_cls[t] = c;
     }
   }
+  // Pair test of a mixed tile as an interval of the key's offset inside the
+  // tile: this lane's key of register r is kv0 + 32t + 4hf + c(r), with
+  // c(r) = 8(r / 4) + r % 4; it is live when lo - 32t <= c(r) <= hi - 32t.
+  // hi bounds by j <= i and j < S, lo by i - j < W (sliding windows only).
+  const int rel = qi - kv0 - 4 * hf;
+  const int hi = (KIND == ATTN_MASK_NONE) ? a.S - 1 - kv0 - 4 * hf : min(rel, a.S - 1 - kv0 - 4 * hf);
+  // (A window wider than 2^30 never bites: S is far smaller.)
+  const int lo = (KIND == ATTN_MASK_SLIDING_WINDOW) ? rel - min(a.m.window - 1, 1 << 30) : 0;
 
-  // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4).
+  // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4), in
+  // the tile's mode.
   float mx = -INFINITY;
   f32x16_t s[4];
-  auto mask_chunk = [&](int k) {
+  auto mask_chunk = [&](auto mode_c, int k) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
     const int t = k >> 2;
-    if (PARTIAL && tile_cls[t] == kTileMixed) {
 #pragma unroll
-      for (int e = 4 * k; e < 4 * k + 4; ++e) {
-        const int r = e & 15;
-        const float x = mod_mask<KIND, SOFTCAP, true>(s[t][r], kst, t, r, hf, qi, kv0, a, dq);
-        s[t][r] = x;
-        mx = fmaxf(mx, x);
+    for (int e = 4 * k; e < 4 * k + 4; ++e) {
+      const int r = e & 15;
+      if (MODE == kTileDead) {
+        // Written here, in the dead tile's own path (a constant would be
+        // materialised before the branch, on every path).
+        float ninf;
+        asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
+        s[t][r] = ninf;
+        continue;
       }
-    } else if (PARTIAL && tile_cls[t] == kTileDead) {
-#pragma unroll
-      for (int e = 4 * k; e < 4 * k + 4; ++e) s[t][e & 15] = -INFINITY;
-    } else {
-#pragma unroll
-      for (int e = 4 * k; e < 4 * k + 4; ++e) {
-        const int r = e & 15;
-        const float x = mod_mask<KIND, SOFTCAP, false>(s[t][r], kst, t, r, hf, qi, kv0, a, dq);
-        s[t][r] = x;
-        mx = fmaxf(mx, x);
+      float x = s[t][r];
+      if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
+      if (MODE == kTileMixed) {
+        const int c = ((r >> 2) << 3) + (r & 3);
+        bool live = c <= hi - 32 * t;
+        if (KIND == ATTN_MASK_SLIDING_WINDOW) live = live && c >= lo - 32 * t;
+        if (KIND == ATTN_MASK_DOCUMENT) live = live && kst.doc[t * 32 + acc_row(r, hf)] == dq;
+        x = live ? x : -INFINITY;
       }
+      s[t][r] = x;
+      mx = fmaxf(mx, x);
     }
+  };
+  // Runs f with the mode of tile t as a compile-time constant (one scalar
+  // branch per tile).
+  auto with_mode = [&](int t, auto&& f) __attribute__((always_inline)) {
+    if (!PARTIAL || tile_cls[t] == kTileLive)
+      f(std::integral_constant<int, kTileLive>{});
+    else if (tile_cls[t] == kTileDead)
+      f(std::integral_constant<int, kTileDead>{});
+    else
+      f(std::integral_constant<int, kTileMixed>{});
   };
 
   // Phase Q. Tile t is complete after chunk 4t + 3; its scores are
@@ -456,19 +482,34 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
 #pragma unroll
   for (int j = 0; j < 4; ++j) kf[j] = k_frag(j);
   sched_fence();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  auto q_chunk = [&](int j) __attribute__((always_inline)) {
     if (j + 4 < 16) kf[j + 4] = k_frag(j + 4);
     const int t = j >> 2, c = j & 3;
     s[t] = V::mma(kf[j], qop[c], c == 0 ? f32x16_t{} : s[t]);
-    if (j >= 4) mask_chunk(j - 4);
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    q_chunk(j);
     sched_fence();
+  }
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    with_mode(t, [&](auto mode_c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 4 * t + 4; j < 4 * t + 8; ++j) {
+        q_chunk(j);
+        mask_chunk(mode_c, j - 4);
+        sched_fence();
+      }
+    });
   }
   x8 vf[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) vf[i] = v_frag(i);
+  with_mode(3, [&](auto mode_c) __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 12; k < 16; ++k) mask_chunk(k);
+    for (int k = 12; k < 16; ++k) mask_chunk(mode_c, k);
+  });
   mx = half_max(mx);
   // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
   const float m_blk = SOFTCAP ? mx : mx * c1;
@@ -611,7 +652,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[0].v, wave, lane);
   }
 
-  const int qi = qb * kBlock + wave * 32 + lq;  // this lane's query row
+  const int row0 = qb * kBlock + wave * 32;  // this wave's first query row
+  const int qi = row0 + lq;                   // this lane's query row
   x8 qop[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -667,7 +709,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
       if (m + 2 < m_end) kv_after = kv_start(m + 2);
     }
-    fwd_block<T, KIND, SOFTCAP, PARTIAL>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, kv0, lane, a, dq);
+    fwd_block<T, KIND, SOFTCAP, PARTIAL>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0, lane, a, dq);
   };
   int m = m_begin;
   for (; m < min(m_end, nfull); ++m) block(std::false_type{}, m);
