@@ -457,8 +457,10 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
       if (MODE == kTileMixed) {
         const int c = ((r >> 2) << 3) + (r & 3);
         bool live = c <= hi - 32 * t;
-        if (KIND == ATTN_MASK_SLIDING_WINDOW) live = live && c >= lo - 32 * t;
-        if (KIND == ATTN_MASK_DOCUMENT) live = live && kst.doc[t * 32 + acc_row(r, hf)] == dq;
+        if (KIND == ATTN_MASK_SLIDING_WINDOW) live &= c >= lo - 32 * t;
+        // (Read unconditionally: the four ids of a register group are one
+        // 16-byte LDS read.)
+        if (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
         x = live ? x : -INFINITY;
       }
       s[t][r] = x;
