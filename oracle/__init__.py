@@ -7,6 +7,10 @@ The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over independent
 rows); this module builds it with gcc and wraps it with ctypes. Definitions and
 the passages they follow are cited in ``oracle.c``:
 
+Mask kinds: NONE, CAUSAL, SLIDING, DOCUMENT, and the variants
+CAUSAL_LOWER_RIGHT, SLIDING_LOWER_RIGHT (query position shifted by S - L) and
+DOCUMENT_BIDIRECTIONAL (same document, no causal part).
+
 * ``attention``   -- softmax(Q K^T * scale + mask bias) V per row, optional
   tanh soft-cap on the scaled score, O = 0 and lse = -inf for a row with no
   live key.
@@ -31,6 +35,8 @@ SOURCE = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
 
 NONE, CAUSAL, SLIDING, DOCUMENT = 0, 1, 2, 3
+CAUSAL_LOWER_RIGHT, SLIDING_LOWER_RIGHT, DOCUMENT_BIDIRECTIONAL = 4, 5, 6
+_DOC_KINDS = (DOCUMENT, DOCUMENT_BIDIRECTIONAL)
 
 
 def compile_source(src: str, out: str) -> str:
@@ -68,7 +74,7 @@ class Oracle:
         f64p = ctypes.POINTER(ctypes.c_double)
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_live.restype = ctypes.c_int
-        lib.oracle_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64]
+        lib.oracle_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64, i64, i64]
         lib.oracle_count_live.restype = i64
         lib.oracle_count_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64]
         lib.oracle_block_mask.restype = ctypes.c_int
@@ -83,15 +89,18 @@ class Oracle:
 
     @staticmethod
     def _check_doc(kind, d, L, S):
-        if kind == DOCUMENT and (d is None or len(d) < max(L, S)):
+        if kind in _DOC_KINDS and (d is None or len(d) < max(L, S)):
             raise ValueError("document kind needs ids for max(L, S) positions")
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
 
-    def live(self, kind: int, i: int, j: int, window: int = 0, doc=None) -> bool:
+    def live(self, kind: int, i: int, j: int, window: int = 0, doc=None, L: int = 0,
+             S: int = 0) -> bool:
+        """The predicate for query i and key j (L and S matter only to the
+        lower-right kinds)."""
         d = _doc(doc)
-        return bool(self._lib.oracle_live(kind, window, _ptr(d, ctypes.c_int32), i, j))
+        return bool(self._lib.oracle_live(kind, window, _ptr(d, ctypes.c_int32), L, S, i, j))
 
     def count_live(self, kind: int, L: int, S: int, window: int = 0, doc=None) -> int:
         d = _doc(doc)
@@ -172,8 +181,8 @@ def num_threads() -> int:
     return default().num_threads()
 
 
-def live(kind, i, j, window=0, doc=None):
-    return default().live(kind, i, j, window, doc)
+def live(kind, i, j, window=0, doc=None, L=0, S=0):
+    return default().live(kind, i, j, window, doc, L, S)
 
 
 def count_live(kind, L, S, window=0, doc=None):

@@ -21,6 +21,14 @@
  *    Page "FlexAttention on Apple Silicon: block masks" (dreaming.press),
  *    sections "Mask 1: causal", "Mask 2: sliding-window causal",
  *    "Mask 3: document-packed".
+ *    Variants on the same rules:
+ *      causal, lower right:   q_idx + (S - L) >= kv_idx
+ *      sliding, lower right:  with p = q_idx + (S - L): p >= kv_idx and p - kv_idx < W
+ *    the causal triangle aligned to the bottom-right corner when L != S, so
+ *    the last query sees every key (page "SDPA replaces hand-written
+ *    attention" (qiita GeneLab_999), section 4, pitfall 3, causal_lower_right);
+ *      document, bidirectional: doc[q_idx] == doc[kv_idx]
+ *    the block-diagonal document mask without the causal part.
  *
  *  - The score_mod soft-cap s <- c * tanh(s / c), applied to the scaled score
  *    of every pair; the mask then removes dead pairs. Same page, section
@@ -57,9 +65,14 @@
 #define ORACLE_CAUSAL 1
 #define ORACLE_SLIDING 2
 #define ORACLE_DOCUMENT 3
+#define ORACLE_CAUSAL_LOWER_RIGHT 4
+#define ORACLE_SLIDING_LOWER_RIGHT 5
+#define ORACLE_DOCUMENT_BIDIRECTIONAL 6
 
-/* The mask predicate: 1 when query i may attend to key j. */
-static int live(int kind, int64_t window, const int32_t* doc, int64_t i, int64_t j) {
+/* The mask predicate: 1 when query i may attend to key j, for L queries and
+ * S keys (the lower-right kinds shift the query position by S - L). */
+static int live(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S, int64_t i,
+                int64_t j) {
   switch (kind) {
     case ORACLE_NONE:
       return 1;
@@ -69,6 +82,14 @@ static int live(int kind, int64_t window, const int32_t* doc, int64_t i, int64_t
       return i >= j && (i - j) < window;
     case ORACLE_DOCUMENT:
       return i >= j && doc[i] == doc[j];
+    case ORACLE_CAUSAL_LOWER_RIGHT:
+      return i + (S - L) >= j;
+    case ORACLE_SLIDING_LOWER_RIGHT: {
+      const int64_t p = i + (S - L);
+      return p >= j && (p - j) < window;
+    }
+    case ORACLE_DOCUMENT_BIDIRECTIONAL:
+      return doc[i] == doc[j];
     default:
       return 0;
   }
@@ -83,8 +104,9 @@ int oracle_num_threads(void) {
 }
 
 /* Evaluate the predicate itself (used by the tests to count live pairs). */
-int oracle_live(int kind, int64_t window, const int32_t* doc, int64_t i, int64_t j) {
-  return live(kind, window, doc, i, j);
+int oracle_live(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S, int64_t i,
+                int64_t j) {
+  return live(kind, window, doc, L, S, i, j);
 }
 
 /* Number of live pairs over [0,L) x [0,S). */
@@ -93,7 +115,7 @@ int64_t oracle_count_live(int kind, int64_t window, const int32_t* doc, int64_t 
 #pragma omp parallel for reduction(+ : total) schedule(dynamic, 16)
   for (int64_t i = 0; i < L; ++i) {
     int64_t c = 0;
-    for (int64_t j = 0; j < S; ++j) c += live(kind, window, doc, i, j);
+    for (int64_t j = 0; j < S; ++j) c += live(kind, window, doc, L, S, i, j);
     total += c;
   }
   return total;
@@ -122,7 +144,7 @@ int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, i
       int64_t count = 0;
       for (int64_t i = qb * bs; i < (qb + 1) * bs && i < L; ++i)
         for (int64_t j = kb * bs; j < (kb + 1) * bs && j < S; ++j)
-          count += live(kind, window, doc, i, j);
+          count += live(kind, window, doc, L, S, i, j);
       if (count == 0) continue;
       if (count == bs * bs)
         full_idx[qb * nk + nf++] = (int32_t)kb;
@@ -171,7 +193,7 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
         for (int64_t e = 0; e < E; ++e) dot += qi[e] * kh[j * E + e];
         double sc = dot * scale;
         if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
-        if (!live(kind, window, doc, i, j)) sc = -INFINITY;
+        if (!live(kind, window, doc, L, S, i, j)) sc = -INFINITY;
         s[j] = sc;
         if (sc > m) m = sc;
       }

@@ -20,6 +20,7 @@ import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 NONE, CAUSAL, SLIDING, DOCUMENT = 0, 1, 2, 3
+CAUSAL_LR, SLIDING_LR, DOCUMENT_BIDIR = 4, 5, 6
 
 
 def _golden(name):
@@ -332,6 +333,96 @@ def check_softcap_limits(orc):
     assert np.all(np.abs(lw) <= 2.0) and np.abs(lw).max() > 1.9
 
 
+# ---------------------------------------------------------------------------
+# Variant masks: bottom-right alignment and bidirectional documents
+# ---------------------------------------------------------------------------
+
+def check_kv_cache_alignment_example(orc):
+    """SDPA page, pitfall 3: for L=1, S=6 the upper-left causal row is the
+    printed [T, F, F, F, F, F]; the bottom-right row sees every key, and the
+    one-query result equals the last row of full causal attention (and the
+    unmasked one-query result), while the upper-left one does not."""
+    g = _golden("sdpa_kv_cache_alignment.json")
+    L, S = g["L"], g["S"]
+    assert [orc.live(CAUSAL, 0, j, L=L, S=S) for j in range(S)] == g["upper_left_row"]
+    assert [orc.live(CAUSAL_LR, 0, j, L=L, S=S) for j in range(S)] == g["lower_right_row"]
+    q, k, v = _rand((1, 1, S, 8), 40), _rand((1, 1, S, 8), 41), _rand((1, 1, S, 8), 42)
+    ref, ref_lse = orc.attention(q, k, v, CAUSAL, 0.35)
+    ok, ok_lse = orc.attention(q[:, :, -1:], k, v, CAUSAL_LR, 0.35)
+    un, _ = orc.attention(q[:, :, -1:], k, v, NONE, 0.35)
+    bad, _ = orc.attention(q[:, :, -1:], k, v, CAUSAL, 0.35)
+    assert np.abs(ok[:, :, 0] - ref[:, :, -1]).max() <= 1e-14
+    assert np.abs(ok_lse[:, :, 0] - ref_lse[:, :, -1]).max() <= 1e-14
+    assert np.abs(un - ok).max() <= 1e-14
+    assert np.abs(bad[:, :, 0] - ref[:, :, -1]).max() > 1e-3
+
+
+def check_lower_right_is_last_rows(orc):
+    """Chunked inference (same page and pitfall): L queries at the end of an
+    S-token sequence, bottom-right aligned, equal the last L rows of the full
+    causal (or sliding-window) attention over all S tokens. L > S leaves the
+    first L - S rows with no key (zeros, lse = -inf)."""
+    S, W = 40, 7
+    q, k, v = _rand((1, 2, S, 8), 43), _rand((1, 2, S, 8), 44), _rand((1, 2, S, 8), 45)
+    for kind, lr, win in ((CAUSAL, CAUSAL_LR, 0), (SLIDING, SLIDING_LR, W)):
+        full, full_lse = orc.attention(q, k, v, kind, 0.3, win)
+        for L in (1, 3, 17, S):
+            o, lse = orc.attention(q[:, :, S - L:], k, v, lr, 0.3, win)
+            assert np.abs(o - full[:, :, S - L:]).max() <= 1e-14, (kind, L)
+            assert np.abs(lse - full_lse[:, :, S - L:]).max() <= 1e-14, (kind, L)
+    qq = _rand((1, 1, 9, 8), 46)
+    o, lse = orc.attention(qq, k[:, :1, :5], v[:, :1, :5], CAUSAL_LR, 0.3)
+    assert np.all(o[0, 0, :4] == 0.0) and np.all(np.isneginf(lse[0, 0, :4]))
+    assert np.all(np.isfinite(lse[0, 0, 4:]))
+
+
+def check_variant_live_pair_closed_forms(orc):
+    """Live pairs: bottom-right causal with L <= S is sum_i (S - L + 1 + i) =
+    L(S - L + 1) + L(L - 1)/2; with L > S it is S(S + 1)/2; bidirectional
+    documents give sum over documents of n^2."""
+    for L, S in ((1, 6), (5, 12), (12, 12), (7, 100), (20, 9)):
+        want = L * (S - L + 1) + L * (L - 1) // 2 if L <= S else S * (S + 1) // 2
+        assert orc.count_live(CAUSAL_LR, L, S) == want, (L, S)
+    for L, S, W in ((4, 30, 5), (30, 30, 5), (10, 25, 1)):
+        # each query sees min(W, position + 1) keys, position = i + S - L
+        want = sum(min(W, i + S - L + 1) for i in range(L) if i + S - L >= 0)
+        assert orc.count_live(SLIDING_LR, L, S, W) == want, (L, S, W)
+    bounds = (100, 190, 191)
+    doc = wl.document_ids(300, bounds)
+    sizes = np.diff([0, *bounds, 300])
+    assert orc.count_live(DOCUMENT_BIDIR, 300, 300, doc=doc) == int(sum(n * n for n in sizes))
+
+
+def check_bidirectional_document_isolation(orc):
+    """Packed documents without the causal part: the result equals each
+    document run alone with no mask (block-diagonal attention)."""
+    bounds = (11, 40)
+    S = 57
+    doc = wl.document_ids(S, bounds)
+    q, k, v = _rand((1, 2, S, 8), 47), _rand((1, 2, S, 8), 48), _rand((1, 2, S, 8), 49)
+    o, lse = orc.attention(q, k, v, DOCUMENT_BIDIR, 0.3, doc=doc)
+    edges = [0, *bounds, S]
+    for a, b in zip(edges[:-1], edges[1:]):
+        od, ld = orc.attention(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], NONE, 0.3)
+        assert np.abs(o[:, :, a:b] - od).max() <= 1e-14
+        assert np.abs(lse[:, :, a:b] - ld).max() <= 1e-14
+
+
+def check_variant_block_masks(orc):
+    """Block classification of the variants, by hand: bottom-right causal with
+    L=256, S=640 shifts the diagonal by 384 = 3 blocks (query block 0: kv
+    blocks 0-2 full, 3 partial; block 1: 0-3 full, 4 partial); bidirectional
+    documents on aligned boundaries give only full diagonal blocks."""
+    kv_num, kv_idx, full_num, full_idx = orc.block_mask(CAUSAL_LR, 256, 640)
+    assert full_num.tolist() == [3, 4] and kv_num.tolist() == [1, 1]
+    assert full_idx[0, :3].tolist() == [0, 1, 2] and full_idx[1, :4].tolist() == [0, 1, 2, 3]
+    assert kv_idx[0, 0] == 3 and kv_idx[1, 0] == 4
+    doc = wl.document_ids(512, (256,))
+    kv_num, _, full_num, full_idx = orc.block_mask(DOCUMENT_BIDIR, 512, 512, doc=doc)
+    assert kv_num.tolist() == [0, 0, 0, 0] and full_num.tolist() == [2, 2, 2, 2]
+    assert full_idx[:, :2].tolist() == [[0, 1], [0, 1], [2, 3], [2, 3]]
+
+
 ALL_CHECKS = [
     check_flex_table_densities,
     check_live_pair_closed_forms,
@@ -351,4 +442,9 @@ ALL_CHECKS = [
     check_document_isolation,
     check_library_equivalence,
     check_softcap_limits,
+    check_kv_cache_alignment_example,
+    check_lower_right_is_last_rows,
+    check_variant_live_pair_closed_forms,
+    check_bidirectional_document_isolation,
+    check_variant_block_masks,
 ]

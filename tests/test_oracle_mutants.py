@@ -29,6 +29,10 @@ MUTANTS = [
     ("empty_row_lse_zero", "        lse[n] = -INFINITY;\n        continue;",
      "        lse[n] = 0.0;\n        continue;"),
     ("max_not_subtracted_in_lse", "lse[n] = m + log(l);", "lse[n] = log(l);"),
+    ("lower_right_offset_sign", "return i + (S - L) >= j;", "return i + (L - S) >= j;"),
+    ("sliding_lower_right_unshifted", "const int64_t p = i + (S - L);", "const int64_t p = i;"),
+    ("bidirectional_keeps_causal", "      return doc[i] == doc[j];\n",
+     "      return i >= j && doc[i] == doc[j];\n"),
 ]
 
 
