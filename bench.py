@@ -8,7 +8,9 @@ S=8192 workload (B=1, H=8, E=64, bf16, i.i.d. N(0,1) inputs). W untimed
 steps, then K steps timed between two device synchronisations. The forward
 kernel is also timed alone with events on the stream it runs on (batches of
 back-to-back launches), for the roofline figure. The second headline workload (sliding window 256
-over S=32768) is measured the same way and reported in the same line.
+over S=32768) is measured the same way and reported in the same line, and so
+are the mask and head-sharing variants (bottom-right causal, grouped-query
+heads, bidirectional documents) under "workloads".
 
 Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
 (4 * E flops per unmasked (query, key) pair); ``forward_only`` has the
@@ -39,6 +41,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "ms/forward and live-pair TFLOPS (% bf16 MFMA peak), S=8192 causal & S=32768 W=256"
 HEADLINE = "causal_8192_bf16"
 SECOND = "sliding_32768_w256_bf16"
+# Mask and head-sharing variants of the same kernel, reported in "workloads".
+VARIANTS = ("causal_lower_right_2048x8192_bf16", "gqa_causal_8192_h32_kv8_bf16",
+            "document_bidirectional_8192_f16_softcap")
 
 
 def live_pairs(w: wl.Workload) -> int:
@@ -54,14 +59,23 @@ def live_pairs(w: wl.Workload) -> int:
         return sum((b - a) * (b - a + 1) // 2 for a, b in zip(edges[:-1], edges[1:]))
     if w.kind == wl.MASK_NONE:
         return L * S
+    if w.kind == wl.MASK_CAUSAL_LOWER_RIGHT:
+        # query i sees keys 0 .. i + S - L
+        return L * (S - L + 1) + L * (L - 1) // 2 if L <= S else S * (S + 1) // 2
+    if w.kind == wl.MASK_SLIDING_WINDOW_LOWER_RIGHT:
+        return sum(min(w.window, i + S - L + 1) for i in range(L) if i + S - L >= 0)
+    if w.kind == wl.MASK_DOCUMENT_BIDIRECTIONAL and L == S:
+        edges = [0, *w.doc_bounds, S]
+        return sum((b - a) ** 2 for a, b in zip(edges[:-1], edges[1:]))
     raise ValueError("no closed form for this workload")
 
 
 def algorithmic_bytes(w: wl.Workload) -> int:
-    """Read Q, K, V once, write O once and the fp32 logsumexp."""
+    """Read Q, K, V once, write O once and the fp32 logsumexp (K and V have
+    kv_heads heads)."""
     esize = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
-    n = w.B * w.H
-    return n * (w.L * w.E * 2 + w.S * w.E * 2) * esize + n * w.L * 4
+    n, nkv = w.B * w.H, w.B * w.kv_heads
+    return (n * w.L * w.E * 2 + nkv * w.S * w.E * 2) * esize + n * w.L * 4
 
 
 def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
@@ -212,7 +226,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workloads", default=f"{HEADLINE},{SECOND}")
+    ap.add_argument("--workloads", default=",".join((HEADLINE, SECOND) + VARIANTS))
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel that scales HBM traffic counters in profiler runs)")

@@ -11,8 +11,14 @@ exception is raised.
 
 Mask rules ("FlexAttention on Apple Silicon: block masks", sections Mask 1-3):
 ``"none"``, ``"causal"`` (q >= kv), ``"sliding_window"`` (q >= kv and
-q - kv < window), ``"document"`` (q >= kv and same document id). score_mod:
-``None`` or ``"softcap"`` (c * tanh(s / c), same page, section "Bonus").
+q - kv < window), ``"document"`` (q >= kv and same document id); the
+bottom-right aligned ``"causal_lower_right"`` and
+``"sliding_window_lower_right"`` (query position shifted by kv_len - q_len,
+"SDPA replaces hand-written attention", section 4, pitfall 3) and
+``"document_bidirectional"`` (same document id only). score_mod: ``None`` or
+``"softcap"`` (c * tanh(s / c), "FlexAttention on Apple Silicon", section
+"Bonus"). K/V with fewer heads than Q (a divisor) is grouped-query attention
+(query head h reads K/V head h // (H // H_kv); SDPA page, section 5).
 """
 from __future__ import annotations
 
@@ -27,6 +33,7 @@ __all__ = [
     "BlockMask", "BsattnError", "create_block_mask", "attention", "num_blocks", "library_path",
     "workspace_size",
     "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
+    "MASK_CAUSAL_LOWER_RIGHT", "MASK_SLIDING_WINDOW_LOWER_RIGHT", "MASK_DOCUMENT_BIDIRECTIONAL",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,11 +43,17 @@ _LIB_PATH = os.path.join(_PKG, "libbsattn.so")
 ATTN_OK = 0
 F32, BF16, F16 = 0, 1, 2
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
+MASK_CAUSAL_LOWER_RIGHT, MASK_SLIDING_WINDOW_LOWER_RIGHT, MASK_DOCUMENT_BIDIRECTIONAL = 4, 5, 6
+_WINDOWED = (MASK_SLIDING_WINDOW, MASK_SLIDING_WINDOW_LOWER_RIGHT)
+_DOCUMENTS = (MASK_DOCUMENT, MASK_DOCUMENT_BIDIRECTIONAL)
 SCORE_NONE, SCORE_SOFTCAP = 0, 1
 BLOCK_SIZE = 128
 
 _KINDS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "sliding_window": MASK_SLIDING_WINDOW,
-          "sliding": MASK_SLIDING_WINDOW, "document": MASK_DOCUMENT}
+          "sliding": MASK_SLIDING_WINDOW, "document": MASK_DOCUMENT,
+          "causal_lower_right": MASK_CAUSAL_LOWER_RIGHT,
+          "sliding_window_lower_right": MASK_SLIDING_WINDOW_LOWER_RIGHT,
+          "document_bidirectional": MASK_DOCUMENT_BIDIRECTIONAL}
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
@@ -95,6 +108,10 @@ def _load():
     lib.attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
                                  i32, ctypes.c_float, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.attn_forward_gqa.restype = i32
+    lib.attn_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
+                                     i32, ctypes.c_float, ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.attn_forward_workspace_size.restype = i32
     lib.attn_forward_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(_BlockMaskStruct),
                                                 ctypes.POINTER(ctypes.c_size_t)]
@@ -185,14 +202,14 @@ def create_block_mask(kind: Union[str, int], q_len: int, kv_len: int, window: Op
         raise ValueError("the BlockMask lives in GPU memory; pass a cuda device")
     if device.index is None:
         device = torch.device("cuda", torch.cuda.current_device())
-    if k == MASK_SLIDING_WINDOW:
+    if k in _WINDOWED:
         if window is None:
             raise ValueError("sliding_window needs window=")
         w = int(window)
     else:
         w = 0
     doc = None
-    if k == MASK_DOCUMENT:
+    if k in _DOCUMENTS:
         if document_id is None:
             raise ValueError("document mask needs document_id=")
         if document_id.numel() < max(q_len, kv_len):
@@ -233,9 +250,11 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
               scale: Optional[float] = None, return_lse: bool = False,
               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None):
-    """Fused block-sparse attention forward (attn_forward).
+    """Fused block-sparse attention forward (attn_forward, or attn_forward_gqa
+    when k and v have fewer heads than q).
 
-    q [B,H,L,E], k/v [B,H,S,E] on the GPU, one dtype among fp32/bf16/fp16,
+    q [B,H,L,E], k/v [B,H_kv,S,E] (H a multiple of H_kv) on the GPU, one dtype
+    among fp32/bf16/fp16,
     head dim contiguous. ``scale`` defaults to 1/sqrt(E) ("SDPA replaces
     hand-written attention", section 1). Returns O [B,H,L,E] (and the fp32
     natural-log logsumexp [B,H,L] when ``return_lse``). ``workspace``: a
@@ -249,8 +268,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
     B, H, L, E = q.shape
-    S = k.shape[2]
-    if k.shape != (B, H, S, E) or v.shape != (B, H, S, E):
+    H_kv, S = k.shape[1], k.shape[2]
+    if k.shape != (B, H_kv, S, E) or v.shape != (B, H_kv, S, E) or H_kv < 1 or H % H_kv:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if scale is None:
         scale = 1.0 / math.sqrt(E)
@@ -269,11 +288,19 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
             workspace = _workspace(need, q.device, stream)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        _check(_load().attn_forward(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            lse.data_ptr() if lse is not None else None,
-            _DTYPES[q.dtype], B, H, L, S, E,
-            _strides(q), _strides(k), _strides(v), _strides(out),
-            ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
-            ws_ptr, ws_bytes, stream))
+        lse_ptr = lse.data_ptr() if lse is not None else None
+        if H_kv == H:
+            _check(_load().attn_forward(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                _DTYPES[q.dtype], B, H, L, S, E,
+                _strides(q), _strides(k), _strides(v), _strides(out),
+                ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
+                ws_ptr, ws_bytes, stream))
+        else:
+            _check(_load().attn_forward_gqa(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                _DTYPES[q.dtype], B, H, H_kv, L, S, E,
+                _strides(q), _strides(k), _strides(v), _strides(out),
+                ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
+                ws_ptr, ws_bytes, stream))
     return (out, lse) if return_lse else out

@@ -80,16 +80,18 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
                                   attn_block_mask* bm, void* stream) {
   g_last_error[0] = '\0';
   if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask struct is null");
-  if (kind < ATTN_MASK_NONE || kind > ATTN_MASK_DOCUMENT)
+  if (kind < ATTN_MASK_NONE || kind > ATTN_MASK_DOCUMENT_BIDIRECTIONAL)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask kind %d", kind);
   if (q_len < 0 || kv_len < 0)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "negative length (q_len=%d, kv_len=%d)", q_len, kv_len);
   if (block_size != ATTN_BLOCK_SIZE)
     return fail(ATTN_ERR_UNSUPPORTED, "block_size %d: only %d is supported", block_size,
                 ATTN_BLOCK_SIZE);
-  if (kind == ATTN_MASK_SLIDING_WINDOW && window < 1)
+  const bool windowed = kind == ATTN_MASK_SLIDING_WINDOW || kind == ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT;
+  const bool documents = kind == ATTN_MASK_DOCUMENT || kind == ATTN_MASK_DOCUMENT_BIDIRECTIONAL;
+  if (windowed && window < 1)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "sliding window must be >= 1 (got %d)", window);
-  if (kind == ATTN_MASK_DOCUMENT && document_id == nullptr)
+  if (documents && document_id == nullptr)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "document mask needs document_id");
   const int32_t nq = attn_num_blocks(q_len, block_size);
   const int32_t nk = attn_num_blocks(kv_len, block_size);
@@ -104,18 +106,25 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
   bm->num_q_blocks = nq;
   bm->num_kv_blocks = nk;
   bm->kind = kind;
-  bm->window = (kind == ATTN_MASK_SLIDING_WINDOW) ? window : 0;
-  bm->document_id = (kind == ATTN_MASK_DOCUMENT) ? document_id : nullptr;
-  return hip_status(bsattn::launch_block_mask(kind, bm->window, bm->document_id, q_len, kv_len, nq,
-                                              nk, bm->kv_num_blocks, bm->kv_indices,
-                                              bm->full_kv_num_blocks, bm->full_kv_indices,
-                                              bm->schedule, static_cast<hipStream_t>(stream)),
+  bm->window = windowed ? window : 0;
+  bm->document_id = documents ? document_id : nullptr;
+  const bsattn::MaskForm form = bsattn::mask_form(kind, q_len, kv_len);
+  return hip_status(bsattn::launch_block_mask(form.kind, form.q_off, bm->window, bm->document_id,
+                                              q_len, kv_len, nq, nk, bm->kv_num_blocks,
+                                              bm->kv_indices, bm->full_kv_num_blocks,
+                                              bm->full_kv_indices, bm->schedule,
+                                              static_cast<hipStream_t>(stream)),
                     "block mask launch");
 }
 
-attn_status attn_forward(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t S, int32_t E,
-                         const int64_t* q_strides, const int64_t* k_strides,
+}  // extern "C"
+
+namespace {
+
+// attn_forward with H_kv K/V heads (H_kv == H: no sharing).
+attn_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L, int32_t S,
+                         int32_t E, const int64_t* q_strides, const int64_t* k_strides,
                          const int64_t* v_strides, const int64_t* o_strides,
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
                          void* workspace, size_t workspace_size, void* stream) {
@@ -133,6 +142,8 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
   }
   if (B < 1 || H < 1 || L < 0 || S < 0)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d L=%d S=%d", B, H, L, S);
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "H=%d query heads cannot share H_kv=%d K/V heads", H, H_kv);
   if (E != bsattn::kHeadDim)
     return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only %d is supported", E, bsattn::kHeadDim);
   if (bm->q_len != L || bm->kv_len != S || bm->block_size != ATTN_BLOCK_SIZE)
@@ -143,9 +154,11 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
       bm->num_kv_blocks != attn_num_blocks(S, ATTN_BLOCK_SIZE) ||
       !arrays_present(bm, bm->num_q_blocks, bm->num_kv_blocks))
     return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is not built");
-  if (bm->kind < ATTN_MASK_NONE || bm->kind > ATTN_MASK_DOCUMENT ||
-      (bm->kind == ATTN_MASK_SLIDING_WINDOW && bm->window < 1) ||
-      (bm->kind == ATTN_MASK_DOCUMENT && bm->document_id == nullptr))
+  if (bm->kind < ATTN_MASK_NONE || bm->kind > ATTN_MASK_DOCUMENT_BIDIRECTIONAL ||
+      ((bm->kind == ATTN_MASK_SLIDING_WINDOW || bm->kind == ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT) &&
+       bm->window < 1) ||
+      ((bm->kind == ATTN_MASK_DOCUMENT || bm->kind == ATTN_MASK_DOCUMENT_BIDIRECTIONAL) &&
+       bm->document_id == nullptr))
     return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask fields are inconsistent");
   if (score_mod != ATTN_SCORE_NONE && score_mod != ATTN_SCORE_SOFTCAP)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown score_mod %d", score_mod);
@@ -161,9 +174,9 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
   attn_status s;
   if ((s = strides_of("q", q_strides, B, H, L, E, esize, st)) != ATTN_OK) return s;
   a.q_sb = st[0], a.q_sh = st[1], a.q_sl = st[2];
-  if ((s = strides_of("k", k_strides, B, H, S, E, esize, st)) != ATTN_OK) return s;
+  if ((s = strides_of("k", k_strides, B, H_kv, S, E, esize, st)) != ATTN_OK) return s;
   a.k_sb = st[0], a.k_sh = st[1], a.k_sl = st[2];
-  if ((s = strides_of("v", v_strides, B, H, S, E, esize, st)) != ATTN_OK) return s;
+  if ((s = strides_of("v", v_strides, B, H_kv, S, E, esize, st)) != ATTN_OK) return s;
   a.v_sb = st[0], a.v_sh = st[1], a.v_sl = st[2];
   if ((s = strides_of("o", o_strides, B, H, L, E, esize, st)) != ATTN_OK) return s;
   a.o_sb = st[0], a.o_sh = st[1], a.o_sl = st[2];
@@ -182,12 +195,12 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
                   workspace == nullptr ? (size_t)0 : workspace_size);
     a.split = 1;
     a.counters = static_cast<int32_t*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          bsattn::counters_bytes((int64_t)B * H, bm->num_q_blocks));
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + bsattn::kCountersBytes);
   }
 
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
   a.B = B, a.H = H, a.L = L, a.S = S;
+  a.kv_group = H / H_kv;
   a.m.kv_num = bm->kv_num_blocks;
   a.m.kv_idx = bm->kv_indices;
   a.m.full_num = bm->full_kv_num_blocks;
@@ -196,12 +209,38 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
   a.m.doc = bm->document_id;
   a.m.nq = bm->num_q_blocks;
   a.m.nk = bm->num_kv_blocks;
-  a.m.kind = bm->kind;
+  const bsattn::MaskForm form = bsattn::mask_form(bm->kind, L, S);
+  a.m.kind = form.kind;
+  a.m.q_off = form.q_off;
   a.m.window = bm->window;
   a.scale = scale;
   a.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
   return hip_status(bsattn::launch_forward(dtype, a, static_cast<hipStream_t>(stream)),
                     "forward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t S, int32_t E,
+                         const int64_t* q_strides, const int64_t* k_strides,
+                         const int64_t* v_strides, const int64_t* o_strides,
+                         const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
+                         void* workspace, size_t workspace_size, void* stream) {
+  return forward_impl(q, k, v, o, lse, dtype, B, H, H, L, S, E, q_strides, k_strides, v_strides,
+                      o_strides, bm, score_mod, softcap, scale, workspace, workspace_size, stream);
+}
+
+attn_status attn_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L, int32_t S,
+                             int32_t E, const int64_t* q_strides, const int64_t* k_strides,
+                             const int64_t* v_strides, const int64_t* o_strides,
+                             const attn_block_mask* bm, int32_t score_mod, float softcap,
+                             float scale, void* workspace, size_t workspace_size, void* stream) {
+  return forward_impl(q, k, v, o, lse, dtype, B, H, H_kv, L, S, E, q_strides, k_strides, v_strides,
+                      o_strides, bm, score_mod, softcap, scale, workspace, workspace_size, stream);
 }
 
 attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,

@@ -113,13 +113,14 @@ __device__ inline float softcap_log2(float s, float two_log2e_scale_over_cap, fl
   return fmaf(-2.0f * cap_log2e, __builtin_amdgcn_rcpf(1.0f + e), cap_log2e);
 }
 
-// Query row i may see key j (both absolute positions), with j < S checked.
+// A query at rule position p (its row i plus the mask's query offset) may see
+// key j, with j < S checked; di, dj are the document ids of row i and key j.
 template <int KIND>
-__device__ inline bool pair_live(int i, int j, int S, int W, int32_t di, int32_t dj) {
+__device__ inline bool pair_live(int p, int j, int S, int W, int32_t di, int32_t dj) {
   bool ok = j < S;
-  if (KIND == ATTN_MASK_CAUSAL) ok &= j <= i;
-  if (KIND == ATTN_MASK_SLIDING_WINDOW) ok &= (j <= i) & (i - j < W);
-  if (KIND == ATTN_MASK_DOCUMENT) ok &= (j <= i) & (di == dj);
+  if (KIND == ATTN_MASK_CAUSAL) ok &= j <= p;
+  if (KIND == ATTN_MASK_SLIDING_WINDOW) ok &= (j <= p) & (p - j < W);
+  if (KIND == ATTN_MASK_DOCUMENT) ok &= (j <= p) & (di == dj);
   return ok;
 }
 
@@ -149,7 +150,7 @@ __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, in
       if (PARTIAL) {
         const int jl = t * 32 + acc_row(r, hf);
         const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? doc_k[jl] : 0;
-        if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
+        if (!pair_live<KIND>(qi + a.m.q_off, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
       }
       s[t][r] = x;
       mx = fmaxf(mx, x);
@@ -340,20 +341,6 @@ __device__ inline LanePtrs make_lane_ptrs(const Lds& lds, int lane) {
   return p;
 }
 
-// Score_mod and mask of one score of block kv0: 32-key tile t, accumulator
-// register r of this lane.
-template <int KIND, bool SOFTCAP, bool PARTIAL>
-__device__ inline float mod_mask(float x, const KStage& st, int t, int r, int hf, int qi, int kv0,
-                                 const FwdArgs& a, int32_t dq) {
-  if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
-  if (PARTIAL) {
-    const int jl = t * 32 + acc_row(r, hf);
-    const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? st.doc[jl] : 0;
-    if (!pair_live<KIND>(qi, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
-  }
-  return x;
-}
-
 // Classes of a 32 x 32 score tile in a partial block.
 enum { kTileLive = 0, kTileMixed = 1, kTileDead = 2 };
 
@@ -403,7 +390,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   // interval decides only "none live".
   int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
   if (PARTIAL) {
-    const int i0 = row0, i1 = row0 + 31;
+    const int i0 = row0 + a.m.q_off, i1 = i0 + 31;  // the rows' rule positions
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j0 = kv0 + 32 * t, j1 = min(j0 + 31, a.S - 1);
@@ -413,7 +400,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
       } else if (KIND == ATTN_MASK_NONE) {
         c = (j0 + 31 > a.S - 1) ? kTileMixed : kTileLive;
       } else {
-        const int dmin = i0 - j1, dmax = i1 - j0;  // offsets i - j of the tile
+        const int dmin = i0 - j1, dmax = i1 - j0;  // offsets p - j of the tile
         const int w = (KIND == ATTN_MASK_SLIDING_WINDOW) ? a.m.window : 0x7fffffff;
         if (dmax < 0 || dmin > w - 1)
           c = kTileDead;
@@ -428,8 +415,9 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   // Pair test of a mixed tile as an interval of the key's offset inside the
   // tile: this lane's key of register r is kv0 + 32t + 4hf + c(r), with
   // c(r) = 8(r / 4) + r % 4; it is live when lo - 32t <= c(r) <= hi - 32t.
-  // hi bounds by j <= i and j < S, lo by i - j < W (sliding windows only).
-  const int rel = qi - kv0 - 4 * hf;
+  // hi bounds by j <= p and j < S, lo by p - j < W (sliding windows only),
+  // p = qi + q_off the row's rule position.
+  const int rel = qi + a.m.q_off - kv0 - 4 * hf;
   const int hi = (KIND == ATTN_MASK_NONE) ? a.S - 1 - kv0 - 4 * hf : min(rel, a.S - 1 - kv0 - 4 * hf);
   // (A window wider than 2^30 never bites: S is far smaller.)
   const int lo = (KIND == ATTN_MASK_SLIDING_WINDOW) ? rel - min(a.m.window - 1, 1 << 30) : 0;
@@ -619,8 +607,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const int b = bh / a.H, h = bh % a.H;
 
   const T* qg = static_cast<const T*>(a.q) + b * a.q_sb + h * a.q_sh;
-  const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const int hk = h / a.kv_group;  // K/V head of query head h
+  const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + hk * a.v_sh;
   T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
 
   const int nfull = wi.nfull;
@@ -828,8 +817,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   const int b = bh / a.H, h = bh % a.H;
 
   const float* qg = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh;
-  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const int hk = h / a.kv_group;  // K/V head of query head h
+  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + hk * a.v_sh;
   float* og = static_cast<float*>(a.o) + b * a.o_sb + h * a.o_sh;
 
   const int qi = qb * kBlock + wave * 32 + lq;

@@ -8,10 +8,11 @@
 // blocks: "FlexAttention on MPS vs SDPA", data-flow section.
 //
 // Causal and sliding-window blocks are classified in closed form: all pair
-// offsets d = i - j of a block form the integer interval [q0 - k1, q1 - k0],
-// and a pair is live iff 0 <= d < W (W = infinity for causal), so the block
-// is skipped iff the two intervals are disjoint and full iff the first lies
-// inside the second. Document blocks whose queries share one id and whose
+// offsets d = p - j of a block, p = i + q_off the query position the rule
+// sees (q_off = 0, or S - L for the bottom-right kinds), form the integer
+// interval [q0 + q_off - k1, q1 + q_off - k0], and a pair is live iff
+// 0 <= d < W (W = infinity for causal), so the block is skipped iff the two
+// intervals are disjoint and full iff the first lies inside the second. Document blocks whose queries share one id and whose
 // keys share one id follow the causal rule (or are skipped when the ids
 // differ); the rest are classified exactly by evaluating every in-range pair
 // cooperatively (ids may be in any order).
@@ -41,7 +42,8 @@ __device__ inline uint8_t classify_interval(int64_t q0, int64_t q1, int64_t k0, 
 }
 
 __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
-    int32_t kind, int32_t window, const int32_t* __restrict__ doc, int32_t q_len, int32_t kv_len,
+    int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc, int32_t q_len,
+    int32_t kv_len,
     int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
     int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
   extern __shared__ uint8_t cls[];  // [nk]
@@ -73,14 +75,14 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
       const int64_t k0 = (int64_t)kb * kBlock;
       const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
       uint8_t c = kSkip;
-      if (q1 >= k0) {  // else every key comes after every query
+      if (q1 + q_off >= k0) {  // else every key comes after every query position
         const int64_t j0 = k0 + lane, j1 = k0 + lane + 64;
         const bool v0 = j0 <= k1, v1 = j1 <= k1;
         const int32_t d0 = v0 ? doc[j0] : 0, d1 = v1 ? doc[j1] : 0;
         const int32_t first = __shfl(d0, 0);  // key k0 is always in range
         const bool uni = __all((!v0 || d0 == first) && (!v1 || d1 == first));
         if (q_uniform && uni) {
-          c = (first == q_id) ? classify_interval(q0, q1, k0, k1, INT64_MAX / 4,
+          c = (first == q_id) ? classify_interval(q0 + q_off, q1 + q_off, k0, k1, INT64_MAX / 4,
                                                   q_whole && (k1 - k0 + 1) == kBlock)
                               : kSkip;
         } else {
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
           for (int il0 = 0; il0 < n_rows && !__any(any); il0 += 32) {
             const int lim = min(n_rows, il0 + 32);
             for (int il = il0; il < lim; ++il) {
-              const int64_t i = q0 + il;
+              const int64_t i = q0 + il + q_off;  // the rule's query position
               const int32_t di = doc_q[il];
               any |= (v0 & (j0 <= i) & (d0 == di)) | (v1 & (j1 <= i) & (d1 == di));
             }
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
       if (kind == ATTN_MASK_NONE)
         c = whole ? kFull : kPartial;
       else
-        c = classify_interval(q0, q1, k0, k1, w, whole);
+        c = classify_interval(q0 + q_off, q1 + q_off, k0, k1, w, whole);
       cls[kb] = c;
     }
   }
@@ -249,14 +251,14 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
 
 }  // namespace
 
-hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, int32_t q_len,
-                             int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
+hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const int32_t* doc,
+                             int32_t q_len, int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
                              int32_t* kv_idx, int32_t* full_num, int32_t* full_idx,
                              int32_t* schedule, hipStream_t stream) {
   if (nq == 0) return hipSuccess;
   const size_t lds = (size_t)((nk + 15) & ~15);
-  hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, window,
-                     doc, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
+  hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off,
+                     window, doc, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,

@@ -11,6 +11,25 @@ constexpr int kBlock = 128;   // BlockMask granularity and query/key tile size
 constexpr int kMaxChunks = 2; // work items a query block may be split into
 constexpr int kHeadDim = 64;  // the one head dimension with kernels
 
+// The kernels' form of a mask kind: one of the rule families NONE, CAUSAL,
+// SLIDING_WINDOW, DOCUMENT, evaluated at the shifted query position
+// p = i + q_off. The bottom-right kinds shift by S - L; the bidirectional
+// document kind shifts by kNoCausal, so that the causal part j <= p always
+// holds (positions stay below 2^22, so p cannot overflow).
+constexpr int32_t kNoCausal = 1 << 30;
+struct MaskForm {
+  int32_t kind;
+  int32_t q_off;
+};
+inline MaskForm mask_form(int32_t kind, int32_t q_len, int32_t kv_len) {
+  switch (kind) {
+    case 4 /* ATTN_MASK_CAUSAL_LOWER_RIGHT */: return {1, kv_len - q_len};
+    case 5 /* ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT */: return {2, kv_len - q_len};
+    case 6 /* ATTN_MASK_DOCUMENT_BIDIRECTIONAL */: return {3, kNoCausal};
+    default: return {kind, 0};
+  }
+}
+
 // Everything the forward kernels need from a BlockMask.
 struct MaskView {
   const int32_t* kv_num;
@@ -19,7 +38,10 @@ struct MaskView {
   const int32_t* full_idx;
   const int32_t* schedule;
   const int32_t* doc;
-  int32_t nq, nk, kind, window;
+  int32_t nq, nk;
+  int32_t kind;   // rule family (MaskForm::kind)
+  int32_t window;
+  int32_t q_off;  // query position offset (MaskForm::q_off)
 };
 
 // Arguments of one forward call, validated on the host.
@@ -30,6 +52,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int32_t B, H, L, S;
+  int32_t kv_group;  // query heads per K/V head (GQA); K/V head = h / kv_group
   // element strides: batch, head, sequence (the head-dim stride is 1)
   int64_t q_sb, q_sh, q_sl;
   int64_t k_sb, k_sh, k_sl;
@@ -55,17 +78,21 @@ constexpr int64_t kSplitMaxItems = 2048;
 inline bool use_split(int32_t dtype, int64_t bh, int32_t nq) {
   return dtype != 0 /* ATTN_F32 */ && nq > 0 && bh * nq <= kSplitMaxItems;
 }
-inline size_t counters_bytes(int64_t bh, int32_t nq) {
-  return ((size_t)(bh * nq) * sizeof(int32_t) + 255) & ~(size_t)255;
-}
+// The ticket counters, [query block][B*H], take a region of fixed size (the
+// most a splitting call can use), so the partial results always start at
+// the same offset: a workspace shared by calls of different shapes then
+// never sees an earlier call's partial results where a later call keeps its
+// counters, and every call leaves all counters at zero.
+constexpr size_t kCountersBytes = kSplitMaxItems * sizeof(int32_t);
 inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq) {
   if (!use_split(dtype, bh, nq)) return 0;
-  return counters_bytes(bh, nq) + (size_t)nq * kMaxChunks * (size_t)bh * kSlotFloats * sizeof(float);
+  return kCountersBytes + (size_t)nq * kMaxChunks * (size_t)bh * kSlotFloats * sizeof(float);
 }
 
 // Enqueue the block classification and the query-block schedule.
-hipError_t launch_block_mask(int32_t kind, int32_t window, const int32_t* doc, int32_t q_len,
-                             int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
+// kind is the rule family and q_off the query offset (mask_form).
+hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const int32_t* doc,
+                             int32_t q_len, int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
                              int32_t* kv_idx, int32_t* full_num, int32_t* full_idx,
                              int32_t* schedule, hipStream_t stream);
 

@@ -71,11 +71,24 @@ typedef int32_t attn_status;
  *                    keys including the query's own position)
  *   DOCUMENT         i >= j && document_id[i] == document_id[j]
  * Positions are absolute and start at 0 for both queries and keys, also
- * when q_len != kv_len (upper-left alignment). */
+ * when q_len != kv_len (upper-left alignment).
+ * Variants:
+ *   CAUSAL_LOWER_RIGHT          p >= j, with p = i + (kv_len - q_len)
+ *   SLIDING_WINDOW_LOWER_RIGHT  p >= j && p - j < window, same p
+ *   DOCUMENT_BIDIRECTIONAL      document_id[i] == document_id[j]
+ * The lower-right kinds align the causal triangle to the bottom-right corner
+ * (the last query sees every key), the form chunked or cached-key inference
+ * needs when q_len != kv_len ("SDPA replaces hand-written attention" (qiita,
+ * GeneLab_999), section 4, pitfall 3, causal_lower_right); with q_len >
+ * kv_len the first q_len - kv_len rows see no key. DOCUMENT_BIDIRECTIONAL is
+ * the block-diagonal document mask without the causal part. */
 #define ATTN_MASK_NONE 0
 #define ATTN_MASK_CAUSAL 1
 #define ATTN_MASK_SLIDING_WINDOW 2
 #define ATTN_MASK_DOCUMENT 3
+#define ATTN_MASK_CAUSAL_LOWER_RIGHT 4
+#define ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT 5
+#define ATTN_MASK_DOCUMENT_BIDIRECTIONAL 6
 
 /* score_mod applied to each scaled score s before the mask:
  *   NONE      s
@@ -143,8 +156,10 @@ int32_t attn_num_blocks(int32_t len, int32_t block_size);
 
 /*
  * Build a BlockMask for `kind` over q_len queries and kv_len keys.
- *   window        SLIDING_WINDOW: >= 1; ignored (and stored as 0) otherwise
- *   document_id   DOCUMENT: device int32[max(q_len, kv_len)]; ignored otherwise
+ *   window        the two SLIDING_WINDOW kinds: >= 1; ignored (and stored as
+ *                 0) otherwise
+ *   document_id   the two DOCUMENT kinds: device int32[max(q_len, kv_len)];
+ *                 ignored otherwise
  *   block_size    must be 128
  *   bm            host struct with the five array pointers set (non-null
  *                 unless the array has no elements)
@@ -163,7 +178,9 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
  * that is when B * H * num_q_blocks <= 2048 and dtype is ATTN_BF16 or
  * ATTN_F16; each split item then leaves fp32 partial results and takes a
  * ticket in the workspace, and the last item of a query block to finish
- * merges them.
+ * merges them. Layout: 8192 bytes of int32 ticket counters, then
+ * num_q_blocks * 2 * B * H fp32 partial slots of (4 * 32 * 64 + 2 * 128)
+ * floats each.
  * Errors: INVALID_ARGUMENT for a null bm or bytes, or B, H < 1.
  */
 attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,
@@ -190,9 +207,10 @@ attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,
  *   scale  multiplier of q.k (pass 1/sqrt(E) for the usual attention).
  *   workspace  device memory of at least attn_forward_workspace_size bytes,
  *        256-byte aligned, owned by the caller; may be NULL when that size is
- *        0. Its first use must see it zero-filled; every call leaves its
- *        counters at zero again, so it can be reused by later calls. Calls
- *        that share a workspace must not run concurrently.
+ *        0. Its first use must see it zero-filled; every call leaves the
+ *        counters at zero again, so it can be reused by later calls of any
+ *        shape (each needs it to be large enough). Calls that share a
+ *        workspace must not run concurrently.
  * A row whose every key is masked gets O = 0 and lse = -inf.
  * Arithmetic: products in fp32 (MFMA) from the input type, fp32 softmax
  * statistics and accumulation; probabilities are rounded to the input type
@@ -210,6 +228,24 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
                          const int64_t* v_strides, const int64_t* o_strides,
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_forward for grouped-query attention: H query heads share H_kv K/V
+ * heads, H a multiple of H_kv, query head h reading K/V head h / (H / H_kv)
+ * (consecutive query heads share one K/V head: "SDPA replaces hand-written
+ * attention" (qiita, GeneLab_999), section 5, enable_gqa). k and v are
+ * [B, H_kv, S, E]; everything else, including the workspace size (which
+ * depends on H, not H_kv), is as for attn_forward, which is this call with
+ * H_kv = H.
+ * Errors: those of attn_forward, and INVALID_ARGUMENT for H_kv < 1 or H not a
+ * multiple of H_kv.
+ */
+attn_status attn_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L, int32_t S,
+                             int32_t E, const int64_t* q_strides, const int64_t* k_strides,
+                             const int64_t* v_strides, const int64_t* o_strides,
+                             const attn_block_mask* bm, int32_t score_mod, float softcap,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(attn_status status);

@@ -98,6 +98,15 @@ MASK_CASES = list(wl.WORKLOADS.values()) + [
     _odd("document_ragged", "f16", 1, 1000, 1000, wl.MASK_DOCUMENT, 0, (300, 777)),
     _odd("document_L_ne_S", "f16", 1, 600, 900, wl.MASK_DOCUMENT, 0, (130, 500)),
     _odd("none_zero_kv", "bf16", 1, 256, 0, wl.MASK_NONE),
+    _odd("causal_lr_1000", "bf16", 1, 1000, 1000, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_L200_S700", "bf16", 1, 200, 700, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_L700_S200", "bf16", 1, 700, 200, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_L1_S1000", "bf16", 1, 1, 1000, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("sliding_lr_L300_S1000_w100", "bf16", 1, 300, 1000, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 100),
+    _odd("sliding_lr_L1000_S300_w50", "bf16", 1, 1000, 300, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 50),
+    _odd("document_bidir_ragged", "f16", 1, 1000, 1000, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (300, 777)),
+    _odd("document_bidir_L_ne_S", "f16", 1, 600, 900, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (130, 500)),
+    _odd("document_bidir_aligned", "f16", 1, 1024, 1024, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (256, 768)),
 ]
 
 
@@ -107,11 +116,18 @@ def test_block_mask_bit_exact(dev, w):
     _check_mask(bm, w, doc)
 
 
-def test_block_mask_unsorted_document_ids(dev):
-    w = _odd("document_random_ids", "bf16", 1, 777, 777, wl.MASK_DOCUMENT)
+@pytest.mark.parametrize("kind", [wl.MASK_DOCUMENT, wl.MASK_DOCUMENT_BIDIRECTIONAL])
+def test_block_mask_unsorted_document_ids(dev, kind):
+    w = _odd("document_random_ids", "bf16", 1, 777, 777, kind)
     doc = np.random.default_rng(4).integers(0, 3, size=777).astype(np.int32)
     bm, _ = _mask_on_gpu(w, dev, doc)
     _check_mask(bm, w, doc)
+
+
+def _expand_kv(w: wl.Workload, x: torch.Tensor) -> torch.Tensor:
+    """K or V with each K/V head repeated for its H / H_kv query heads: the
+    definition of grouped-query attention, for the oracle."""
+    return x.repeat_interleave(w.H // w.kv_heads, dim=1) if w.kv_heads != w.H else x
 
 
 def _run(w: wl.Workload, dev, seed=0, doc=None, qkv=None):
@@ -162,12 +178,36 @@ SMALL = [
     _odd("causal_4352_bf16_split", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL),
     _odd("document_4400_f16_split", "f16", 1, 4400, 4400, wl.MASK_DOCUMENT, 0, (600, 2500), 30.0),
     _odd("none_3000x4300_bf16_split", "bf16", 1, 3000, 4300, wl.MASK_NONE),
+    # mask variants and grouped-query attention
+    _odd("causal_lr_L200_S700_bf16", "bf16", 2, 200, 700, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_L700_S200_f16", "f16", 1, 700, 200, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_L1_S900_bf16", "bf16", 2, 1, 900, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_L333_S999_f32", "f32", 1, 333, 999, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("causal_lr_2048x4352_bf16_split", "bf16", 1, 2048, 4352, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("sliding_lr_L300_S1000_w100_bf16", "bf16", 2, 300, 1000,
+         wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 100),
+    _odd("sliding_lr_L1000_S300_w50_f16", "f16", 1, 1000, 300, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 50),
+    _odd("sliding_lr_f32", "f32", 1, 200, 500, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 33),
+    _odd("document_bidir_softcap_1000_f16", "f16", 2, 1000, 1000, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0,
+         (300, 777), 30.0),
+    _odd("document_bidir_600x900_bf16", "bf16", 1, 600, 900, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0,
+         (130, 500)),
+    _odd("document_bidir_f32", "f32", 1, 512, 512, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (100, 300)),
+    _odd("document_bidir_4400_f16_split", "f16", 1, 4400, 4400, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0,
+         (600, 2500), 30.0),
+    _odd("gqa_causal_h4_kv2_bf16", "bf16", 4, 640, 640, wl.MASK_CAUSAL).with_(H_kv=2),
+    _odd("gqa_sliding_h6_kv1_f16", "f16", 6, 700, 700, wl.MASK_SLIDING_WINDOW, 90).with_(H_kv=1),
+    _odd("gqa_document_h4_kv4_bf16", "bf16", 4, 500, 500, wl.MASK_DOCUMENT, 0, (200,)).with_(H_kv=4),
+    _odd("gqa_none_h4_kv2_f32", "f32", 4, 300, 200, wl.MASK_NONE).with_(H_kv=2),
+    _odd("gqa_causal_lr_B2_h8_kv2_bf16", "bf16", 8, 256, 768, wl.MASK_CAUSAL_LOWER_RIGHT,
+         B=2).with_(H_kv=2),
 ]
 
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_forward_small_full_compare(dev, w):
     (q, k, v), doc, o, lse = _run(w, dev)
+    k, v = _expand_kv(w, k), _expand_kv(w, v)
     want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(),
                                         v.double().numpy(), w.kind, w.scale, w.window, doc,
                                         w.softcap)
@@ -178,12 +218,15 @@ def test_forward_small_full_compare(dev, w):
 FULL = [wl.WORKLOADS[n] for n in ("causal_8192_bf16", "sliding_8192_w64_bf16",
                                   "sliding_8192_w256_bf16", "sliding_8192_w1024_bf16",
                                   "sliding_8192_w4096_bf16", "sliding_32768_w256_bf16",
-                                  "document_8192_f16_softcap")]
+                                  "document_8192_f16_softcap", "causal_lower_right_2048x8192_bf16",
+                                  "gqa_causal_8192_h32_kv8_bf16",
+                                  "document_bidirectional_8192_f16_softcap")]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
 def test_forward_full_size_sampled_rows(dev, w):
     (q, k, v), doc, o, lse = _run(w, dev)
+    k, v = _expand_kv(w, k), _expand_kv(w, v)
     rows = wl.sample_rows(w, 192)
     want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(),
                                         v.double().numpy(), w.kind, w.scale, w.window, doc,
@@ -236,12 +279,32 @@ def test_split_workspace_is_left_clean(dev):
     assert need > 0
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     ref = bsa.attention(q, k, v, bm)
-    n_counters = w.B * w.H * bm.num_q_blocks * 4
     for _ in range(3):
         got = bsa.attention(q, k, v, bm, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(got, ref)
-        assert int(ws[:n_counters].count_nonzero()) == 0
+        assert int(ws[:2048 * 4].count_nonzero()) == 0  # the ticket counters
+
+
+def test_workspace_shared_by_calls_of_different_shapes(dev):
+    """One zero-filled workspace serves split calls whose (B*H, query blocks)
+    differ: a call with more heads than the one before must not read the
+    earlier call's partial results as its ticket counters."""
+    small = _odd("causal_4352_h4_bf16", "bf16", 4, 4352, 4352, wl.MASK_CAUSAL)
+    big = _odd("causal_4352_h32_bf16", "bf16", 32, 4352, 4352, wl.MASK_CAUSAL)
+    bm = bsa.create_block_mask(wl.MASK_CAUSAL, 4352, 4352, device=dev)
+    qs, ks, vs = (x.to(dev) for x in wl.make_qkv(small, 6))
+    qb, kb, vb = (x.to(dev) for x in wl.make_qkv(big, 7))
+    need = max(bsa.workspace_size(qs, bm), bsa.workspace_size(qb, bm))
+    fresh = torch.zeros(bsa.workspace_size(qb, bm), dtype=torch.uint8, device=dev)
+    ref = bsa.attention(qb, kb, vb, bm, workspace=fresh)
+    shared = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        bsa.attention(qs, ks, vs, bm, workspace=shared)
+        got = bsa.attention(qb, kb, vb, bm, workspace=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+        assert int(shared[:2048 * 4].count_nonzero()) == 0
 
 
 def test_many_heads_without_split_sampled_rows(dev):

@@ -19,6 +19,16 @@ Workloads (all B=1, E=64, layout [B, H, seq, E] contiguous, i.i.d. N(0,1)):
   a tanh soft-cap of 30 ("FlexAttention on Apple Silicon: block masks",
   sections "Mask 3: document-packed" and "Bonus: a score_mod for soft-capping").
 
+Variant workloads (the mask and head-sharing variants of the same kernel):
+
+* ``causal_lower_right_2048x8192_bf16`` -- H=8, L=2048 queries at the end of
+  S=8192 keys, bottom-right aligned causal mask (chunked inference against a
+  cache: "SDPA replaces hand-written attention", section 4, pitfall 3).
+* ``gqa_causal_8192_h32_kv8_bf16`` -- 32 query heads sharing 8 K/V heads
+  (same page, section 5), L=S=8192, causal.
+* ``document_bidirectional_8192_f16_softcap`` -- the document workload's
+  shape and ids with the bidirectional (block-diagonal) document mask.
+
 Generation: ``numpy.random.default_rng(seed).standard_normal(shape, float32)``
 drawn for q, then k, then v, then rounded to the workload dtype with
 round-to-nearest-even (torch's CPU cast). Both sides read the rounded values.
@@ -37,6 +47,10 @@ MASK_NONE = 0
 MASK_CAUSAL = 1
 MASK_SLIDING_WINDOW = 2
 MASK_DOCUMENT = 3
+MASK_CAUSAL_LOWER_RIGHT = 4
+MASK_SLIDING_WINDOW_LOWER_RIGHT = 5
+MASK_DOCUMENT_BIDIRECTIONAL = 6
+DOCUMENT_KINDS = (MASK_DOCUMENT, MASK_DOCUMENT_BIDIRECTIONAL)
 
 BLOCK = 128
 
@@ -53,9 +67,14 @@ class Workload:
     E: int
     dtype: str            # "f32" | "bf16" | "f16"
     kind: int             # MASK_*
-    window: int = 0       # sliding-window size W (kind == MASK_SLIDING_WINDOW)
-    doc_bounds: tuple = ()  # document start offsets after the first (MASK_DOCUMENT)
+    window: int = 0       # sliding-window size W (the two sliding-window kinds)
+    doc_bounds: tuple = ()  # document start offsets after the first (document kinds)
     softcap: float = 0.0  # 0 = no score_mod, else c in c*tanh(s/c)
+    H_kv: int = 0         # K/V heads (grouped-query attention); 0 = H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -81,6 +100,12 @@ WORKLOADS = {
         Workload("sliding_32768_w256_bf16", 1, 8, 32768, 32768, 64, "bf16", MASK_SLIDING_WINDOW, 256),
         Workload("document_8192_f16_softcap", 1, 16, 8192, 8192, 64, "f16", MASK_DOCUMENT, 0,
                  (2048, 5000), 30.0),
+        Workload("causal_lower_right_2048x8192_bf16", 1, 8, 2048, 8192, 64, "bf16",
+                 MASK_CAUSAL_LOWER_RIGHT),
+        Workload("gqa_causal_8192_h32_kv8_bf16", 1, 32, 8192, 8192, 64, "bf16", MASK_CAUSAL,
+                 H_kv=8),
+        Workload("document_bidirectional_8192_f16_softcap", 1, 16, 8192, 8192, 64, "f16",
+                 MASK_DOCUMENT_BIDIRECTIONAL, 0, (2048, 5000), 30.0),
     ]
 }
 
@@ -94,9 +119,11 @@ def document_ids(length: int, bounds: tuple) -> np.ndarray:
 
 
 def make_qkv(w: Workload, seed: int = 0):
-    """Seeded q, k, v as CPU torch tensors of the workload dtype, [B,H,seq,E]."""
+    """Seeded q, k, v as CPU torch tensors of the workload dtype: q [B,H,L,E],
+    k and v [B,H_kv,S,E]."""
     rng = np.random.default_rng(seed)
-    shapes = [(w.B, w.H, w.L, w.E), (w.B, w.H, w.S, w.E), (w.B, w.H, w.S, w.E)]
+    hk = w.kv_heads
+    shapes = [(w.B, w.H, w.L, w.E), (w.B, hk, w.S, w.E), (w.B, hk, w.S, w.E)]
     out = []
     for shp in shapes:
         x = rng.standard_normal(shp, dtype=np.float32)
@@ -105,7 +132,7 @@ def make_qkv(w: Workload, seed: int = 0):
 
 
 def make_doc(w: Workload) -> Optional[np.ndarray]:
-    if w.kind != MASK_DOCUMENT:
+    if w.kind not in DOCUMENT_KINDS:
         return None
     return document_ids(max(w.L, w.S), w.doc_bounds)
 
