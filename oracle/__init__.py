@@ -12,6 +12,7 @@ CAUSAL_LOWER_RIGHT, SLIDING_LOWER_RIGHT (query position shifted by S - L) and
 DOCUMENT_BIDIRECTIONAL (same document, no causal part).
 
 * ``attention``   -- softmax(Q K^T * scale + mask bias) V per row, optional
+  per-batch key padding (a kept key range ANDed with the mask), optional
   tanh soft-cap on the scaled score, O = 0 and lse = -inf for a row with no
   live key.
 * ``block_mask``  -- 128x128 block classification by brute force over every
@@ -81,10 +82,10 @@ class Oracle:
         lib.oracle_block_mask.argtypes = [ctypes.c_int, i64, i32p, i64, i64, i64,
                                           i32p, i32p, i32p, i32p]
         lib.oracle_attention.restype = ctypes.c_int
+        i64p = ctypes.POINTER(ctypes.c_int64)
         lib.oracle_attention.argtypes = [f64p, f64p, f64p, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, i64, i32p, ctypes.c_double,
-                                         ctypes.c_double, ctypes.POINTER(ctypes.c_int64), i64,
-                                         f64p, f64p]
+                                         ctypes.c_double, i64p, i64p, i64p, i64, f64p, f64p]
         self._lib = lib
 
     @staticmethod
@@ -126,13 +127,15 @@ class Oracle:
         return kv_num, kv_idx, full_num, full_idx
 
     def attention(self, q, k, v, kind: int, scale: float, window: int = 0, doc=None,
-                  softcap: float = 0.0, rows=None):
+                  softcap: float = 0.0, rows=None, key_start=None, key_end=None):
         """fp64 masked softmax attention.
 
         q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev] (any float dtype; converted to
-        fp64 exactly). Returns (out, lse): for rows=None, out [B,H,L,Ev] and
-        lse [B,H,L]; otherwise out [len(rows), Ev] and lse [len(rows)] for the
-        flat row ids (b*H + h)*L + i.
+        fp64 exactly). key_start, key_end: optional per-batch [B] kept key
+        range [start, end) (key padding, ANDed with the mask). Returns
+        (out, lse): for rows=None, out [B,H,L,Ev] and lse [B,H,L]; otherwise
+        out [len(rows), Ev] and lse [len(rows)] for the flat row ids
+        (b*H + h)*L + i.
         """
         q = np.ascontiguousarray(q, dtype=np.float64)
         k = np.ascontiguousarray(k, dtype=np.float64)
@@ -143,6 +146,11 @@ class Oracle:
             raise ValueError("q/k/v shapes disagree")
         d = _doc(doc)
         self._check_doc(kind, d, L, S)
+        ks = None if key_start is None else np.ascontiguousarray(key_start, dtype=np.int64)
+        ke = None if key_end is None else np.ascontiguousarray(key_end, dtype=np.int64)
+        for a in (ks, ke):
+            if a is not None and a.shape != (B,):
+                raise ValueError("key_start / key_end need one entry per batch")
         if rows is None:
             n, rows_arr = B * H * L, None
         else:
@@ -155,6 +163,7 @@ class Oracle:
         rc = self._lib.oracle_attention(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
                                         _ptr(v, ctypes.c_double), B, H, L, S, E, Ev, kind, window,
                                         _ptr(d, ctypes.c_int32), softcap, scale,
+                                        _ptr(ks, ctypes.c_int64), _ptr(ke, ctypes.c_int64),
                                         _ptr(rows_arr, ctypes.c_int64), n,
                                         _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
         if rc != 0:
@@ -193,5 +202,6 @@ def block_mask(kind, L, S, window=0, doc=None, block=128):
     return default().block_mask(kind, L, S, window, doc, block)
 
 
-def attention(q, k, v, kind, scale, window=0, doc=None, softcap=0.0, rows=None):
-    return default().attention(q, k, v, kind, scale, window, doc, softcap, rows)
+def attention(q, k, v, kind, scale, window=0, doc=None, softcap=0.0, rows=None, key_start=None,
+              key_end=None):
+    return default().attention(q, k, v, kind, scale, window, doc, softcap, rows, key_start, key_end)

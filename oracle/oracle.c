@@ -35,6 +35,13 @@
  *    "Bonus: a score_mod for soft-capping" (score_mod changes the value, the
  *    mask decides liveness; sparsity from the mask, score_mod on survivors).
  *
+ *  - Key padding: per batch entry b, only keys in [key_start[b], key_end[b])
+ *    are kept, ANDed with the mask rule (padding keys never take weight).
+ *    Page "SDPA replaces hand-written attention" (qiita GeneLab_999),
+ *    section 4, pitfall 1 (a boolean mask's True keeps the pair; padded
+ *    keys are dropped) and section 5 (padding ANDed with the causal mask,
+ *    left padding in its test).
+ *
  *  - A row with no live key yields O = 0 and logsumexp = -inf, the
  *    fully-masked-row behaviour that the SDPA page measures (section 4,
  *    pitfall 1, the "all rows masked" aside: zeros, not NaN).
@@ -160,6 +167,8 @@ int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, i
 /*
  * Masked softmax attention, fp64, for a list of rows.
  *   q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev]: contiguous fp64.
+ *   key_start, key_end: per batch entry [B], the kept key range [start, end),
+ *   or NULL for no padding.
  *   rows: flat row ids r = (b*H + h)*L + i, or NULL for all B*H*L rows.
  *   out [nrows, Ev], lse [nrows] (natural log; -inf for a row with no live key).
  *   softcap > 0 applies s <- softcap * tanh(s / softcap) to the scaled score.
@@ -167,8 +176,9 @@ int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, i
  */
 int oracle_attention(const double* q, const double* k, const double* v, int64_t B, int64_t H,
                      int64_t L, int64_t S, int64_t E, int64_t Ev, int kind, int64_t window,
-                     const int32_t* doc, double softcap, double scale, const int64_t* rows,
-                     int64_t nrows, double* out, double* lse) {
+                     const int32_t* doc, double softcap, double scale, const int64_t* key_start,
+                     const int64_t* key_end, const int64_t* rows, int64_t nrows, double* out,
+                     double* lse) {
   if (B < 0 || H < 0 || L < 0 || S < 0 || E <= 0 || Ev <= 0) return -1;
   if (rows == NULL) nrows = B * H * L;
   int failed = 0;
@@ -181,6 +191,10 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
       if (s == NULL) continue;
       int64_t r = rows ? rows[n] : n;
       int64_t bh = r / L, i = r % L;
+      /* Kept keys of this batch entry (whole range when no padding given). */
+      const int64_t b = bh / H;
+      const int64_t kept_lo = key_start ? key_start[b] : 0;
+      const int64_t kept_hi = key_end ? key_end[b] : S;
       const double* qi = q + r * E;
       const double* kh = k + bh * S * E;
       const double* vh = v + bh * S * Ev;
@@ -193,7 +207,7 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
         for (int64_t e = 0; e < E; ++e) dot += qi[e] * kh[j * E + e];
         double sc = dot * scale;
         if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
-        if (!live(kind, window, doc, L, S, i, j)) sc = -INFINITY;
+        if (!live(kind, window, doc, L, S, i, j) || j < kept_lo || j >= kept_hi) sc = -INFINITY;
         s[j] = sc;
         if (sc > m) m = sc;
       }

@@ -423,6 +423,50 @@ def check_variant_block_masks(orc):
     assert full_idx[:, :2].tolist() == [[0, 1], [0, 1], [2, 3], [2, 3]]
 
 
+# ---------------------------------------------------------------------------
+# Key padding (a kept key range per batch entry, ANDed with the mask)
+# ---------------------------------------------------------------------------
+
+def check_key_padding_equals_truncation(orc):
+    """SDPA page, pitfall 1 and section 5: keeping keys [0, kept) equals
+    running on the truncated K/V (right padding); keeping only the padding is
+    a different result; with causal AND left padding of p tokens, rows p..
+    equal causal attention over the unpadded tokens."""
+    g = _golden("sdpa_key_padding.json")
+    L, kept = g["right_padding"]["L"], g["right_padding"]["kept"]
+    q, k, v = _rand((1, 1, L, 8), 60), _rand((1, 1, L, 8), 61), _rand((1, 1, L, 8), 62)
+    ref, ref_lse = orc.attention(q, k[:, :, :kept], v[:, :, :kept], NONE, 0.35)
+    ok, ok_lse = orc.attention(q, k, v, NONE, 0.35, key_start=[0], key_end=[kept])
+    bad, _ = orc.attention(q, k, v, NONE, 0.35, key_start=[kept], key_end=[L])
+    assert np.abs(ok - ref).max() <= 1e-15 and np.abs(ok_lse - ref_lse).max() <= 1e-15
+    assert np.abs(bad - ref).max() > 1e-2
+    L, p = g["left_padding"]["L"], g["left_padding"]["padded"]
+    q, k, v = _rand((2, 3, L, 8), 63), _rand((2, 3, L, 8), 64), _rand((2, 3, L, 8), 65)
+    full, full_lse = orc.attention(q, k, v, CAUSAL, 0.35, key_start=[p, p], key_end=[L, L])
+    trunc, trunc_lse = orc.attention(q[:, :, p:], k[:, :, p:], v[:, :, p:], CAUSAL, 0.35)
+    assert np.abs(full[:, :, p:] - trunc).max() <= 1e-15
+    assert np.abs(full_lse[:, :, p:] - trunc_lse).max() <= 1e-15
+    # the padded query rows themselves see no kept key at or before them
+    assert np.all(full[:, :, :p] == 0.0) and np.all(np.isneginf(full_lse[:, :, :p]))
+
+
+def check_key_padding_per_batch(orc):
+    """Each batch entry takes its own range: the batched result equals every
+    entry run alone, and an empty range leaves rows with no key."""
+    S = 23
+    q, k, v = _rand((3, 2, 19, 8), 66), _rand((3, 2, S, 8), 67), _rand((3, 2, S, 8), 68)
+    starts, ends = [0, 5, 9], [S, 17, 9]
+    o, lse = orc.attention(q, k, v, SLIDING, 0.3, 6, key_start=starts, key_end=ends)
+    for b in range(3):
+        ob, lb = orc.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], SLIDING, 0.3, 6,
+                               key_start=[starts[b]], key_end=[ends[b]])
+        assert np.abs(o[b:b + 1] - ob).max() <= 1e-15
+        assert np.array_equal(np.isneginf(lse[b:b + 1]), np.isneginf(lb))
+    assert np.all(o[2] == 0.0) and np.all(np.isneginf(lse[2]))
+    on, _ = orc.attention(q, k, v, SLIDING, 0.3, 6)
+    assert np.abs(o[0] - on[0]).max() <= 1e-15  # the whole range is no padding
+
+
 ALL_CHECKS = [
     check_flex_table_densities,
     check_live_pair_closed_forms,
@@ -447,4 +491,6 @@ ALL_CHECKS = [
     check_variant_live_pair_closed_forms,
     check_bidirectional_document_isolation,
     check_variant_block_masks,
+    check_key_padding_equals_truncation,
+    check_key_padding_per_batch,
 ]

@@ -31,6 +31,9 @@ MUTANTS = [
     ("max_not_subtracted_in_lse", "lse[n] = m + log(l);", "lse[n] = log(l);"),
     ("lower_right_offset_sign", "return i + (S - L) >= j;", "return i + (L - S) >= j;"),
     ("sliding_lower_right_unshifted", "const int64_t p = i + (S - L);", "const int64_t p = i;"),
+    ("padding_end_ignored", "|| j < kept_lo || j >= kept_hi)", "|| j < kept_lo)"),
+    ("padding_end_inclusive", "|| j < kept_lo || j >= kept_hi)", "|| j < kept_lo || j > kept_hi)"),
+    ("padding_start_ignored", "|| j < kept_lo || j >= kept_hi)", "|| j >= kept_hi)"),
     ("bidirectional_keeps_causal", "      return doc[i] == doc[j];\n",
      "      return i >= j && doc[i] == doc[j];\n"),
 ]
