@@ -112,6 +112,11 @@ def _load():
     lib.attn_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
                                      i32, ctypes.c_float, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.attn_forward_padded.restype = i32
+    lib.attn_forward_padded.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                        i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
+                                        i32, ctypes.c_float, ctypes.c_float, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
     lib.attn_forward_workspace_size.restype = i32
     lib.attn_forward_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(_BlockMaskStruct),
                                                 ctypes.POINTER(ctypes.c_size_t)]
@@ -249,7 +254,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
               score_mod: Optional[str] = None, softcap: float = 30.0,
               scale: Optional[float] = None, return_lse: bool = False,
               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None):
+              workspace: Optional[torch.Tensor] = None, key_start: Optional[torch.Tensor] = None,
+              key_end: Optional[torch.Tensor] = None):
     """Fused block-sparse attention forward (attn_forward, or attn_forward_gqa
     when k and v have fewer heads than q).
 
@@ -257,7 +263,10 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
     among fp32/bf16/fp16,
     head dim contiguous. ``scale`` defaults to 1/sqrt(E) ("SDPA replaces
     hand-written attention", section 1). Returns O [B,H,L,E] (and the fp32
-    natural-log logsumexp [B,H,L] when ``return_lse``). ``workspace``: a
+    natural-log logsumexp [B,H,L] when ``return_lse``). ``key_start`` /
+    ``key_end``: optional int32 GPU tensors [B], the kept key range of each
+    batch entry (key padding, ANDed with the mask; attn_forward_padded).
+    ``workspace``: a
     zero-filled uint8 GPU tensor of at least ``workspace_size(q, block_mask)``
     bytes; by default one cached per device and stream is used.
     """
@@ -289,7 +298,20 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         lse_ptr = lse.data_ptr() if lse is not None else None
-        if H_kv == H:
+        pads = []
+        for t in (key_start, key_end):
+            if t is not None:
+                if t.dtype != torch.int32 or not t.is_cuda or t.shape != (B,) or not t.is_contiguous():
+                    raise ValueError("key_start / key_end must be contiguous int32 GPU tensors [B]")
+            pads.append(t.data_ptr() if t is not None else None)
+        if key_start is not None or key_end is not None:
+            _check(_load().attn_forward_padded(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                _DTYPES[q.dtype], B, H, H_kv, L, S, E,
+                _strides(q), _strides(k), _strides(v), _strides(out),
+                ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
+                pads[0], pads[1], ws_ptr, ws_bytes, stream))
+        elif H_kv == H:
             _check(_load().attn_forward(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
                 _DTYPES[q.dtype], B, H, L, S, E,

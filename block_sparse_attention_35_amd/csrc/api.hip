@@ -127,7 +127,8 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
                          int32_t E, const int64_t* q_strides, const int64_t* k_strides,
                          const int64_t* v_strides, const int64_t* o_strides,
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
-                         void* workspace, size_t workspace_size, void* stream) {
+                         const int32_t* key_start, const int32_t* key_end, void* workspace,
+                         size_t workspace_size, void* stream) {
   g_last_error[0] = '\0';
   if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
   // A tensor with no elements may have a null pointer.
@@ -201,6 +202,8 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
   a.B = B, a.H = H, a.L = L, a.S = S;
   a.kv_group = H / H_kv;
+  a.key_start = key_start;
+  a.key_end = key_end;
   a.m.kv_num = bm->kv_num_blocks;
   a.m.kv_idx = bm->kv_indices;
   a.m.full_num = bm->full_kv_num_blocks;
@@ -230,7 +233,8 @@ attn_status attn_forward(const void* q, const void* k, const void* v, void* o, f
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
                          void* workspace, size_t workspace_size, void* stream) {
   return forward_impl(q, k, v, o, lse, dtype, B, H, H, L, S, E, q_strides, k_strides, v_strides,
-                      o_strides, bm, score_mod, softcap, scale, workspace, workspace_size, stream);
+                      o_strides, bm, score_mod, softcap, scale, nullptr, nullptr, workspace,
+                      workspace_size, stream);
 }
 
 attn_status attn_forward_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -240,7 +244,21 @@ attn_status attn_forward_gqa(const void* q, const void* k, const void* v, void* 
                              const attn_block_mask* bm, int32_t score_mod, float softcap,
                              float scale, void* workspace, size_t workspace_size, void* stream) {
   return forward_impl(q, k, v, o, lse, dtype, B, H, H_kv, L, S, E, q_strides, k_strides, v_strides,
-                      o_strides, bm, score_mod, softcap, scale, workspace, workspace_size, stream);
+                      o_strides, bm, score_mod, softcap, scale, nullptr, nullptr, workspace,
+                      workspace_size, stream);
+}
+
+attn_status attn_forward_padded(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L,
+                                int32_t S, int32_t E, const int64_t* q_strides,
+                                const int64_t* k_strides, const int64_t* v_strides,
+                                const int64_t* o_strides, const attn_block_mask* bm,
+                                int32_t score_mod, float softcap, float scale,
+                                const int32_t* key_start, const int32_t* key_end, void* workspace,
+                                size_t workspace_size, void* stream) {
+  return forward_impl(q, k, v, o, lse, dtype, B, H, H_kv, L, S, E, q_strides, k_strides, v_strides,
+                      o_strides, bm, score_mod, softcap, scale, key_start, key_end, workspace,
+                      workspace_size, stream);
 }
 
 attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,

@@ -138,7 +138,8 @@ struct RowState {
 // accumulator. kv0: absolute index of the block's first key.
 template <int KIND, bool PARTIAL, bool SOFTCAP>
 __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, int kv0, int hf,
-                                      const FwdArgs& a, int32_t dq, const int32_t* doc_k) {
+                                      const FwdArgs& a, int32_t dq, const int32_t* doc_k, int klo,
+                                      int khi) {
   const float c1 = a.scale * kLog2e;
   float mx = -INFINITY;
 #pragma unroll
@@ -150,7 +151,9 @@ __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, in
       if (PARTIAL) {
         const int jl = t * 32 + acc_row(r, hf);
         const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? doc_k[jl] : 0;
-        if (!pair_live<KIND>(qi + a.m.q_off, kv0 + jl, a.S, a.m.window, dq, dj)) x = -INFINITY;
+        // kept keys [klo, khi): the mask's own j < S, and key padding
+        if (!pair_live<KIND>(qi + a.m.q_off, kv0 + jl, khi, a.m.window, dq, dj) || kv0 + jl < klo)
+          x = -INFINITY;
       }
       s[t][r] = x;
       mx = fmaxf(mx, x);
@@ -357,11 +360,11 @@ __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 //  P. O^T += V^T P^T (MFMA i: 16-key group i / 2, head-dim tile i % 2; V
 //     fragments read four MFMAs ahead), with the probabilities of the next
 //     group.
-template <typename T, int KIND, bool SOFTCAP, bool PARTIAL>
+template <typename T, int KIND, bool SOFTCAP, bool PARTIAL, bool PADDED>
 __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
                                           const typename Vec<T>::x8 (&qop)[4], f32x16_t (&oacc)[2],
                                           float& m_ref, float& l, int qi, int row0, int kv0, int lane, const FwdArgs& a,
-                                          int32_t dq) {
+                                          int32_t dq, int klo, int khi) {
   using V = Vec<T>;
   using x8 = typename V::x8;
   typedef __attribute__((address_space(3))) const x8 lds_x8;
@@ -384,27 +387,30 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   };
   // In a partial block, each 32 x 32 tile of this wave (its rows row0 ..
   // row0 + 31 x keys kv0 + 32t .. +31) is classified in closed form, with
-  // scalar arithmetic only, from the rule's offset interval and the key range,
-  // as whole blocks are: all pairs live, none live, or mixed. Only mixed tiles
-  // test pairs, and only live tiles skip the test; for document masks the
-  // interval decides only "none live".
+  // scalar arithmetic only, from the rule's offset interval and the kept key
+  // range [klo, khi) (the whole [0, S) without padding), as whole blocks are:
+  // all pairs live, none live, or mixed. Only mixed tiles test pairs, and
+  // only live tiles skip the test; for document masks the interval decides
+  // only "none live".
   int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
   if (PARTIAL) {
     const int i0 = row0 + a.m.q_off, i1 = i0 + 31;  // the rows' rule positions
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int j0 = kv0 + 32 * t, j1 = min(j0 + 31, a.S - 1);
+      const int j0 = kv0 + 32 * t, j1 = min(j0 + 31, khi - 1);
+      const bool outside = j0 > khi - 1 || (PADDED && j0 + 31 < klo);
+      const bool edge = j0 + 31 > khi - 1 || (PADDED && j0 < klo);  // range ends inside
       int c;
-      if (j0 > a.S - 1) {
+      if (outside) {
         c = kTileDead;
       } else if (KIND == ATTN_MASK_NONE) {
-        c = (j0 + 31 > a.S - 1) ? kTileMixed : kTileLive;
+        c = edge ? kTileMixed : kTileLive;
       } else {
         const int dmin = i0 - j1, dmax = i1 - j0;  // offsets p - j of the tile
         const int w = (KIND == ATTN_MASK_SLIDING_WINDOW) ? a.m.window : 0x7fffffff;
         if (dmax < 0 || dmin > w - 1)
           c = kTileDead;
-        else if (KIND != ATTN_MASK_DOCUMENT && dmin >= 0 && dmax <= w - 1 && j0 + 31 <= a.S - 1)
+        else if (KIND != ATTN_MASK_DOCUMENT && dmin >= 0 && dmax <= w - 1 && !edge)
           c = kTileLive;
         else
           c = kTileMixed;
@@ -415,12 +421,13 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   // Pair test of a mixed tile as an interval of the key's offset inside the
   // tile: this lane's key of register r is kv0 + 32t + 4hf + c(r), with
   // c(r) = 8(r / 4) + r % 4; it is live when lo - 32t <= c(r) <= hi - 32t.
-  // hi bounds by j <= p and j < S, lo by p - j < W (sliding windows only),
-  // p = qi + q_off the row's rule position.
+  // hi bounds by j <= p and j < khi, lo by p - j < W (sliding windows) and
+  // j >= klo (padding), p = qi + q_off the row's rule position.
   const int rel = qi + a.m.q_off - kv0 - 4 * hf;
-  const int hi = (KIND == ATTN_MASK_NONE) ? a.S - 1 - kv0 - 4 * hf : min(rel, a.S - 1 - kv0 - 4 * hf);
+  const int hi = (KIND == ATTN_MASK_NONE) ? khi - 1 - kv0 - 4 * hf : min(rel, khi - 1 - kv0 - 4 * hf);
   // (A window wider than 2^30 never bites: S is far smaller.)
-  const int lo = (KIND == ATTN_MASK_SLIDING_WINDOW) ? rel - min(a.m.window - 1, 1 << 30) : 0;
+  int lo = (KIND == ATTN_MASK_SLIDING_WINDOW) ? rel - min(a.m.window - 1, 1 << 30) : -(1 << 30);
+  if (PADDED) lo = max(lo, klo - kv0 - 4 * hf);
 
   // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4), in
   // the tile's mode.
@@ -445,7 +452,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
       if (MODE == kTileMixed) {
         const int c = ((r >> 2) << 3) + (r & 3);
         bool live = c <= hi - 32 * t;
-        if (KIND == ATTN_MASK_SLIDING_WINDOW) live &= c >= lo - 32 * t;
+        if (KIND == ATTN_MASK_SLIDING_WINDOW || PADDED) live &= c >= lo - 32 * t;
         // (Read unconditionally: the four ids of a register group are one
         // 16-byte LDS read.)
         if (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
@@ -587,7 +594,7 @@ __device__ inline WorkItem work_item(const FwdArgs& a, int e) {
   return w;
 }
 
-template <typename T, int KIND, bool SOFTCAP>
+template <typename T, int KIND, bool SOFTCAP, bool PADDED>
 __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   using V = Vec<T>;
   using x8 = typename V::x8;
@@ -611,6 +618,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + hk * a.v_sh;
   T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
+  // Kept keys [klo, khi) of this batch entry (all of [0, S) without padding).
+  int klo = 0, khi = a.S;
+  if (PADDED) {
+    if (a.key_start != nullptr) klo = min(max(((const_i32_ptr)a.key_start)[b], 0), a.S);
+    if (a.key_end != nullptr) khi = max(min(((const_i32_ptr)a.key_end)[b], a.S), klo);
+  }
 
   const int nfull = wi.nfull;
   const int npart = wi.npart;
@@ -700,7 +713,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
       if (m + 2 < m_end) kv_after = kv_start(m + 2);
     }
-    fwd_block<T, KIND, SOFTCAP, PARTIAL>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0, lane, a, dq);
+    if (PADDED) {
+      // A block with no kept key is skipped; a full block that a padding
+      // boundary cuts runs the per-tile pair tests of a partial block.
+      if (kv0 + kBlock <= klo || kv0 >= khi) return;
+      if (!PARTIAL && (kv0 < klo || kv0 + kBlock > khi)) {
+        fwd_block<T, KIND, SOFTCAP, true, true>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0,
+                                                lane, a, dq, klo, khi);
+        return;
+      }
+    }
+    fwd_block<T, KIND, SOFTCAP, PARTIAL, PADDED>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0,
+                                                 lane, a, dq, klo, khi);
   };
   int m = m_begin;
   for (; m < min(m_end, nfull); ++m) block(std::false_type{}, m);
@@ -821,6 +845,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + hk * a.v_sh;
   float* og = static_cast<float*>(a.o) + b * a.o_sb + h * a.o_sh;
+  // Kept keys [klo, khi) of this batch entry (all of [0, S) without padding).
+  int klo = 0, khi = a.S;
+  if (a.key_start != nullptr) klo = min(max(a.key_start[b], 0), a.S);
+  if (a.key_end != nullptr) khi = max(min(a.key_end[b], a.S), klo);
 
   const int qi = qb * kBlock + wave * 32 + lq;
   // Contraction step j of lane half hf covers head dim e = 32*hf + j.
@@ -849,9 +877,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   const int32_t* part_list = a.m.kv_idx + (int64_t)qb * a.m.nk;
 
   for (int n = 0; n < nfull + npart; ++n) {
-    const bool partial = n >= nfull;
-    const int kb = partial ? part_list[n - nfull] : full_list[n];
+    const int kb = n >= nfull ? part_list[n - nfull] : full_list[n];
     const int kv0 = kb * kBlock;
+    // Skip blocks with no kept key; a padding boundary inside a full block
+    // makes it partial.
+    if (kv0 + kBlock <= klo || kv0 >= khi) continue;
+    const bool partial = n >= nfull || kv0 < klo || kv0 + kBlock > khi;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -881,9 +912,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
 
     float alpha;
     if (partial)
-      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
+      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi);
     else
-      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k);
+      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi);
 
     float psum = 0.0f;
 #pragma unroll
@@ -929,7 +960,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   }
 }
 
-template <int KIND, bool SOFTCAP>
+template <int KIND, bool SOFTCAP, bool PADDED>
 hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   // Up to kMaxChunks work items per query block; items past the plan's end
   // return at once.
@@ -937,10 +968,10 @@ hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   const dim3 block(kThreads);
   switch (dtype) {
     case ATTN_BF16:
-      hipLaunchKernelGGL((fwd16_kernel<__bf16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd16_kernel<__bf16, KIND, SOFTCAP, PADDED>), grid, block, 0, stream, a);
       break;
     case ATTN_F16:
-      hipLaunchKernelGGL((fwd16_kernel<_Float16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd16_kernel<_Float16, KIND, SOFTCAP, PADDED>), grid, block, 0, stream, a);
       break;
     case ATTN_F32:
       hipLaunchKernelGGL((fwd32_kernel<KIND, SOFTCAP>), grid, block, 0, stream, a);
@@ -951,10 +982,18 @@ hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, bool PADDED>
 hipError_t launch_softcap(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
-  return a.softcap > 0.0f ? launch_kind<KIND, true>(dtype, a, stream)
-                          : launch_kind<KIND, false>(dtype, a, stream);
+  return a.softcap > 0.0f ? launch_kind<KIND, true, PADDED>(dtype, a, stream)
+                          : launch_kind<KIND, false, PADDED>(dtype, a, stream);
+}
+
+// Key padding has kernels of its own, so the unpadded ones carry no range
+// tests.
+template <int KIND>
+hipError_t launch_padded(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  return (a.key_start != nullptr || a.key_end != nullptr) ? launch_softcap<KIND, true>(dtype, a, stream)
+                                                          : launch_softcap<KIND, false>(dtype, a, stream);
 }
 
 }  // namespace
@@ -962,10 +1001,10 @@ hipError_t launch_softcap(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_forward(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   if ((int64_t)a.B * a.H * a.m.nq == 0) return hipSuccess;
   switch (a.m.kind) {
-    case ATTN_MASK_NONE: return launch_softcap<ATTN_MASK_NONE>(dtype, a, stream);
-    case ATTN_MASK_CAUSAL: return launch_softcap<ATTN_MASK_CAUSAL>(dtype, a, stream);
-    case ATTN_MASK_SLIDING_WINDOW: return launch_softcap<ATTN_MASK_SLIDING_WINDOW>(dtype, a, stream);
-    case ATTN_MASK_DOCUMENT: return launch_softcap<ATTN_MASK_DOCUMENT>(dtype, a, stream);
+    case ATTN_MASK_NONE: return launch_padded<ATTN_MASK_NONE>(dtype, a, stream);
+    case ATTN_MASK_CAUSAL: return launch_padded<ATTN_MASK_CAUSAL>(dtype, a, stream);
+    case ATTN_MASK_SLIDING_WINDOW: return launch_padded<ATTN_MASK_SLIDING_WINDOW>(dtype, a, stream);
+    case ATTN_MASK_DOCUMENT: return launch_padded<ATTN_MASK_DOCUMENT>(dtype, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

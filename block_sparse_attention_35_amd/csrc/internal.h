@@ -53,6 +53,10 @@ struct FwdArgs {
   float* lse;
   int32_t B, H, L, S;
   int32_t kv_group;  // query heads per K/V head (GQA); K/V head = h / kv_group
+  // Key padding: batch entry b keeps keys [key_start[b], key_end[b]) (device
+  // int32 [B], clamped to [0, S]); a null array means 0, respectively S.
+  const int32_t* key_start;
+  const int32_t* key_end;
   // element strides: batch, head, sequence (the head-dim stride is 1)
   int64_t q_sb, q_sh, q_sl;
   int64_t k_sb, k_sh, k_sl;

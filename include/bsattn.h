@@ -247,6 +247,29 @@ attn_status attn_forward_gqa(const void* q, const void* k, const void* v, void* 
                              const attn_block_mask* bm, int32_t score_mod, float softcap,
                              float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_forward_gqa with key padding: batch entry b keeps only keys
+ * key_start[b] <= j < key_end[b], ANDed with the mask rule (the padded keys of
+ * a batch take no weight; a row left with no key gets O = 0, lse = -inf).
+ * "SDPA replaces hand-written attention" (qiita, GeneLab_999), section 4,
+ * pitfall 1 (a boolean mask's True keeps the pair, so padding is dropped) and
+ * section 5 (the padding mask ANDed with the causal mask; left padding).
+ *   key_start, key_end  device int32[B], or NULL for 0, respectively S;
+ *        entries are clamped to [0, S] (and key_end to >= key_start). Read by
+ *        the kernels; the caller keeps them valid until the call completes.
+ * Blocks of the BlockMask with no kept key are skipped; blocks a padding
+ * boundary cuts take the per-element test. Everything else, and the errors,
+ * as for attn_forward_gqa (with both pointers NULL it is attn_forward_gqa).
+ */
+attn_status attn_forward_padded(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L,
+                                int32_t S, int32_t E, const int64_t* q_strides,
+                                const int64_t* k_strides, const int64_t* v_strides,
+                                const int64_t* o_strides, const attn_block_mask* bm,
+                                int32_t score_mod, float softcap, float scale,
+                                const int32_t* key_start, const int32_t* key_end, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(attn_status status);
 

@@ -242,6 +242,58 @@ def test_forward_full_size_sampled_rows(dev, w):
     assert torch.isfinite(lse).all()  # no empty rows in these workloads
 
 
+# Key padding: (workload, per-batch kept key ranges [start, end); None = 0 / S)
+PADDED = [
+    (_odd("pad_causal_700_bf16", "bf16", 2, 700, 700, wl.MASK_CAUSAL, B=3),
+     ([0, 100, 300], [700, 650, 300])),                 # none, both ends, empty
+    (_odd("pad_sliding_900_f16_right", "f16", 2, 900, 900, wl.MASK_SLIDING_WINDOW, 150, B=2),
+     (None, [900, 517])),
+    (_odd("pad_document_softcap_800_bf16_left", "bf16", 1, 800, 800, wl.MASK_DOCUMENT, 0, (250, 600),
+          30.0, B=2), ([3, 129], None)),
+    (_odd("pad_none_300x500_f32", "f32", 2, 300, 500, wl.MASK_NONE, B=2), ([10, 0], [400, 128])),
+    (_odd("pad_causal_4352_bf16_split", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL, B=2),
+     ([0, 1000], [3000, 4352])),
+    (_odd("pad_gqa_causal_lr_bf16", "bf16", 4, 256, 900, wl.MASK_CAUSAL_LOWER_RIGHT, B=2).with_(H_kv=2),
+     ([128, 0], [900, 700])),
+    (_odd("pad_bidir_doc_f16", "f16", 2, 640, 640, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (200, 500), B=2),
+     ([64, 0], [640, 300])),
+]
+
+
+def _run_padded(w, ranges, dev):
+    starts, ends = ranges
+    q, k, v = wl.make_qkv(w, 8)
+    bm, doc = _mask_on_gpu(w, dev)
+    ks = None if starts is None else torch.tensor(starts, dtype=torch.int32, device=dev)
+    ke = None if ends is None else torch.tensor(ends, dtype=torch.int32, device=dev)
+    o, lse = bsa.attention(q.to(dev), k.to(dev), v.to(dev), bm,
+                           score_mod="softcap" if w.softcap else None, softcap=w.softcap or 30.0,
+                           scale=w.scale, return_lse=True, key_start=ks, key_end=ke)
+    torch.cuda.synchronize()
+    return (q, k, v), doc, o, lse
+
+
+@pytest.mark.parametrize("w,ranges", PADDED, ids=[c[0].name for c in PADDED])
+def test_forward_key_padding(dev, w, ranges):
+    (q, k, v), doc, o, lse = _run_padded(w, ranges, dev)
+    starts, ends = ranges
+    want_o, want_lse = oracle.attention(q.double().numpy(), _expand_kv(w, k).double().numpy(),
+                                        _expand_kv(w, v).double().numpy(), w.kind, w.scale,
+                                        w.window, doc, w.softcap, key_start=starts, key_end=ends)
+    _compare(w, o.float().cpu().numpy(), lse.cpu().numpy().astype(np.float64), want_o, want_lse,
+             w.name)
+
+
+def test_key_padding_whole_range_matches_unpadded(dev):
+    """Ranges covering every key run the padded kernel with nothing to drop:
+    bit-identical to the unpadded kernel."""
+    w = _odd("pad_full_range_bf16", "bf16", 2, 1000, 1000, wl.MASK_SLIDING_WINDOW, 300, B=2)
+    (q, k, v), _, o_pad, l_pad = _run_padded(w, ([0, 0], [1000, 1000]), dev)
+    bm, _ = _mask_on_gpu(w, dev)
+    o, l = bsa.attention(q.to(dev), k.to(dev), v.to(dev), bm, scale=w.scale, return_lse=True)
+    assert torch.equal(o, o_pad) and torch.equal(l, l_pad)
+
+
 def test_window_one_is_identity_bit_exact(dev):
     w = _odd("sliding_w1_bf16", "bf16", 2, 1000, 1000, wl.MASK_SLIDING_WINDOW, 1)
     (q, k, v), _, o, lse = _run(w, dev)
