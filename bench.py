@@ -10,7 +10,7 @@ kernel is also timed alone with events on the stream it runs on (batches of
 back-to-back launches), for the roofline figure. The second headline workload (sliding window 256
 over S=32768) is measured the same way and reported in the same line, and so
 are the mask and head-sharing variants (bottom-right causal, grouped-query
-heads, bidirectional documents) under "workloads".
+heads, bidirectional documents, key padding) under "workloads".
 
 Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
 (4 * E flops per unmasked (query, key) pair); ``forward_only`` has the
@@ -43,12 +43,24 @@ HEADLINE = "causal_8192_bf16"
 SECOND = "sliding_32768_w256_bf16"
 # Mask and head-sharing variants of the same kernel, reported in "workloads".
 VARIANTS = ("causal_lower_right_2048x8192_bf16", "gqa_causal_8192_h32_kv8_bf16",
-            "document_bidirectional_8192_f16_softcap")
+            "document_bidirectional_8192_f16_softcap", "causal_8192_keypad_b2_bf16")
+
+
+def padded_causal_pairs(L: int, start: int, end: int) -> int:
+    """Causal pairs (j <= i) of L queries whose keys are limited to
+    [start, end): query i has max(0, min(i, end - 1) - start + 1) keys."""
+    i = np.arange(L, dtype=np.int64)
+    return int(np.maximum(0, np.minimum(i, end - 1) - start + 1).sum())
 
 
 def live_pairs(w: wl.Workload) -> int:
-    """Live (query, key) pairs of one head from the closed forms of the rules."""
+    """Live (query, key) pairs of one head (averaged over the batch when
+    the key padding differs per entry) from the closed forms of the rules."""
     L, S = w.L, w.S
+    if w.key_ranges:
+        if w.kind != wl.MASK_CAUSAL or L != S:
+            raise ValueError("no closed form for this padded workload")
+        return sum(padded_causal_pairs(L, a, b) for a, b in w.key_ranges) // w.B
     if w.kind == wl.MASK_CAUSAL and L == S:
         return S * (S + 1) // 2
     if w.kind == wl.MASK_SLIDING_WINDOW and L == S and w.window <= S:
@@ -87,11 +99,15 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None, document_id=doc_t,
                                device=dev)
     score_mod = "softcap" if w.softcap else None
+    ks = ke = None
+    if w.key_ranges:
+        ks = torch.tensor([a for a, _ in w.key_ranges], dtype=torch.int32, device=dev)
+        ke = torch.tensor([b for _, b in w.key_ranges], dtype=torch.int32, device=dev)
 
     def step():
         bm.rebuild()
         bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
-                      scale=w.scale, out=o, lse=lse)
+                      scale=w.scale, out=o, lse=lse, key_start=ks, key_end=ke)
 
     for _ in range(warmup):
         step()
@@ -117,7 +133,7 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     mask_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     def fwd():
         bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
-                      scale=w.scale, out=o, lse=lse)
+                      scale=w.scale, out=o, lse=lse, key_start=ks, key_end=ke)
 
     # Each timed batch is queued behind two untimed launches, so the host
     # stays ahead of the GPU and no host-side pause lands between the events;

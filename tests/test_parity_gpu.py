@@ -284,6 +284,22 @@ def test_forward_key_padding(dev, w, ranges):
              w.name)
 
 
+def test_key_padding_full_size_sampled_rows(dev):
+    """The benchmark's padded workload (B=2, H=8, causal 8192, entry 1 keeps
+    keys [2048, 7168)), in its launch configuration, on sampled rows."""
+    w = wl.WORKLOADS["causal_8192_keypad_b2_bf16"]
+    ranges = ([a for a, _ in w.key_ranges], [b for _, b in w.key_ranges])
+    (q, k, v), doc, o, lse = _run_padded(w, ranges, dev)
+    rows = wl.sample_rows(w, 160)
+    want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                        w.kind, w.scale, rows=rows, key_start=ranges[0],
+                                        key_end=ranges[1])
+    idx = torch.from_numpy(rows).to(dev)
+    got = o.float().reshape(-1, w.E)[idx].cpu().numpy()
+    got_lse = lse.reshape(-1)[idx].cpu().numpy().astype(np.float64)
+    _compare(w, got, got_lse, want_o, want_lse, w.name)
+
+
 def test_key_padding_whole_range_matches_unpadded(dev):
     """Ranges covering every key run the padded kernel with nothing to drop:
     bit-identical to the unpadded kernel."""

@@ -28,6 +28,10 @@ Variant workloads (the mask and head-sharing variants of the same kernel):
   (same page, section 5), L=S=8192, causal.
 * ``document_bidirectional_8192_f16_softcap`` -- the document workload's
   shape and ids with the bidirectional (block-diagonal) document mask.
+* ``causal_8192_keypad_b2_bf16`` -- B=2, H=8, L=S=8192 causal with key
+  padding: batch entry 0 keeps every key, entry 1 keys [2048, 7168) (left
+  and right padding ANDed with the causal mask; SDPA page, section 4,
+  pitfall 1 and section 5).
 
 Generation: ``numpy.random.default_rng(seed).standard_normal(shape, float32)``
 drawn for q, then k, then v, then rounded to the workload dtype with
@@ -71,6 +75,7 @@ class Workload:
     doc_bounds: tuple = ()  # document start offsets after the first (document kinds)
     softcap: float = 0.0  # 0 = no score_mod, else c in c*tanh(s/c)
     H_kv: int = 0         # K/V heads (grouped-query attention); 0 = H
+    key_ranges: tuple = ()  # per batch entry (start, end) kept keys; () = no padding
 
     @property
     def kv_heads(self) -> int:
@@ -106,6 +111,8 @@ WORKLOADS = {
                  H_kv=8),
         Workload("document_bidirectional_8192_f16_softcap", 1, 16, 8192, 8192, 64, "f16",
                  MASK_DOCUMENT_BIDIRECTIONAL, 0, (2048, 5000), 30.0),
+        Workload("causal_8192_keypad_b2_bf16", 2, 8, 8192, 8192, 64, "bf16", MASK_CAUSAL,
+                 key_ranges=((0, 8192), (2048, 7168))),
     ]
 }
 
