@@ -10,7 +10,8 @@ kernel is also timed alone with events on the stream it runs on (batches of
 back-to-back launches), for the roofline figure. The second headline workload (sliding window 256
 over S=32768) is measured the same way and reported in the same line, and so
 are the mask and head-sharing variants (bottom-right causal, grouped-query
-heads, bidirectional documents, key padding) under "workloads".
+heads, bidirectional documents, key padding, and split-KV decode) under
+"workloads".
 
 Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
 (4 * E flops per unmasked (query, key) pair); ``forward_only`` has the
@@ -43,7 +44,8 @@ HEADLINE = "causal_8192_bf16"
 SECOND = "sliding_32768_w256_bf16"
 # Mask and head-sharing variants of the same kernel, reported in "workloads".
 VARIANTS = ("causal_lower_right_2048x8192_bf16", "gqa_causal_8192_h32_kv8_bf16",
-            "document_bidirectional_8192_f16_softcap", "causal_8192_keypad_b2_bf16")
+            "document_bidirectional_8192_f16_softcap", "causal_8192_keypad_b2_bf16",
+            "decode_gqa_b8_h32_kv8_s8192_bf16")
 
 
 def padded_causal_pairs(L: int, start: int, end: int) -> int:
@@ -179,7 +181,7 @@ def summarize(w: wl.Workload, r):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                "fwd16_causal_8192_sliding_32768_w256_hbm_traffic.md")
-FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_35_amd", "csrc", "attn_fwd.hip")
+FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_35_amd", "csrc", "fwd_kernels.h")
 
 
 def measured_traffic(workload: str):

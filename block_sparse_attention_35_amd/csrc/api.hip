@@ -187,14 +187,16 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
                 (long long)kMaxSeqStride);
   if ((int64_t)B * H * bm->num_q_blocks * 2 > 0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "too many work items");
-  const size_t need = bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks);
+  const size_t need =
+      bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks, bm->num_kv_blocks);
   if (need > 0) {
     if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
         workspace_size < need)
       return fail(ATTN_ERR_INVALID_ARGUMENT,
                   "workspace must be 256-byte aligned and hold %zu bytes (got %zu)", need,
                   workspace == nullptr ? (size_t)0 : workspace_size);
-    a.split = 1;
+    a.kv_split = bsattn::kv_split_count(dtype, (int64_t)B * H, bm->num_q_blocks, bm->num_kv_blocks);
+    a.split = a.kv_split > 0 ? 0 : 1;
     a.counters = static_cast<int32_t*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + bsattn::kCountersBytes);
   }
@@ -267,7 +269,7 @@ attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,
   if (bm == nullptr || bytes == nullptr)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask and bytes must be non-null");
   if (B < 1 || H < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d", B, H);
-  *bytes = bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks);
+  *bytes = bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks, bm->num_kv_blocks);
   return ATTN_OK;
 }
 

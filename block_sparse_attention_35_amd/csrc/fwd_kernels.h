@@ -1,0 +1,1114 @@
+// Fused block-sparse attention forward for gfx950: the kernels, and the
+// launch templates instantiated by one translation unit per mask family
+// (fwd_*.hip), so the instantiations compile in parallel.
+//
+// O = softmax(Q K^T * scale + mask bias [+ soft-cap score_mod]) V and the
+// per-row logsumexp, without writing the L x S score table anywhere: a
+// workgroup owns one work item (128 query rows of one batch*head, all of
+// their live kv blocks or one chunk of them), walks the item's full kv
+// blocks and then its partial kv blocks from the BlockMask, and keeps a
+// running row max and row sum (online softmax) while accumulating P V.
+// Definition: "SDPA replaces hand-written attention", section 1 (Attention
+// equation and its four steps); running max / running sum instead of the
+// score table: same page, section 2, and "FlashAttention" (service-dock),
+// tiled softmax is exact; tiles kept in on-chip memory with only the result
+// written back: "Flash Attention 2 and the IO bottleneck" (tcdigital),
+// section on tiling. Skipped / partial / full blocks: "FlexAttention on Apple
+// Silicon: block masks", closing section; soft-cap: same page, "Bonus".
+//
+// Work layout (4 waves of 64 lanes, each wave owns 32 query rows):
+//  * S^T = K_j Q^T is computed with 32x32 MFMA tiles, kv along M and queries
+//    along N, so each lane holds one query (lane % 32) and 16 kv values per
+//    32x32 tile. Row max / row sum are then in-lane reductions plus one swap
+//    between the two 32-lane halves.
+//  * The S^T accumulator layout (lane = query, registers = kv) is exactly the
+//    B operand layout of O^T = V^T P^T once probabilities are packed to
+//    16 bits, because the contraction index may be permuted freely as long as
+//    both operands use the same permutation; the matching V^T operand comes
+//    from transposed LDS reads (ds_read_b64_tr_b16) of the row-major V tile.
+//  * K and V tiles go from global memory straight to LDS (double buffered,
+//    16-byte chunks XOR-swizzled); each block is two phases of MFMA chunks
+//    with the vector work of the softmax placed between the MFMAs.
+//  * Long query blocks are split into two work items whose partial results
+//    the later one merges (see the work plan of the block-mask builder).
+//
+// bf16/fp16 use v_mfma_f32_32x32x16_{bf16,f16}; fp32 uses v_mfma_f32_32x32x2_f32
+// and keeps probabilities in fp32.
+#pragma once
+
+#include <cmath>
+#include <type_traits>
+
+#include "bsattn.h"
+#include "internal.h"
+
+namespace bsattn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<__bf16> {
+  using x8 = bf16x8_t;
+  using x4 = bf16x4_t;
+  using x2 = bf16x2_t;
+  static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // acc + a.x + a.y in fp32 (v_dot2c_f32_bf16 against (1, 1)). Written as
+  // volatile asm so it stays in the chunk that produces `a` (a plain builtin
+  // is only ordered by its data and gets sunk to the end of the phase, where
+  // the sum is used).
+  static __device__ inline float add_pair(x2 a, float acc) {
+    asm volatile("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(a));
+    return acc;
+  }
+};
+template <>
+struct Vec<_Float16> {
+  using x8 = f16x8_t;
+  using x4 = f16x4_t;
+  using x2 = f16x2_t;
+  static __device__ inline f32x16_t mma(x8 a, x8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // acc + a.x + a.y in fp32 (v_dot2c_f32_f16 against (1, 1)), volatile asm
+  // for the same reason as the bf16 form.
+  static __device__ inline float add_pair(x2 a, float acc) {
+    asm volatile("v_dot2c_f32_f16 %0, 0x3c003c00, %1" : "+v"(acc) : "v"(a));
+    return acc;
+  }
+};
+
+// Other half's value combined with ours: v_permlane32_swap exchanges lanes
+// l and l^32 between its two operands; with both operands equal, the two
+// results of each lane are {x_l, x_(l^32)} in some order.
+__device__ inline float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// c * tanh(y), y = s * scale / c, in base-2 units of the result, from
+// c tanh(y) = c - 2c / (e^(2y) + 1): one multiply, exp, add, reciprocal and
+// FMA. It saturates to +-c for large |y| (e = inf or 0); near y = 0 the
+// cancellation costs at most an absolute 2^-23 c, far below the rounding of
+// the probabilities.
+__device__ inline float softcap_log2(float s, float two_log2e_scale_over_cap, float cap_log2e) {
+  const float e = fast_exp2(s * two_log2e_scale_over_cap);
+  return fmaf(-2.0f * cap_log2e, __builtin_amdgcn_rcpf(1.0f + e), cap_log2e);
+}
+
+// A query at rule position p (its row i plus the mask's query offset) may see
+// key j, with j < S checked; di, dj are the document ids of row i and key j.
+template <int KIND>
+__device__ inline bool pair_live(int p, int j, int S, int W, int32_t di, int32_t dj) {
+  bool ok = j < S;
+  if (KIND == ATTN_MASK_CAUSAL) ok &= j <= p;
+  if (KIND == ATTN_MASK_SLIDING_WINDOW) ok &= (j <= p) & (p - j < W);
+  if (KIND == ATTN_MASK_DOCUMENT) ok &= (j <= p) & (di == dj);
+  return ok;
+}
+
+// Row of the 32x32 MFMA accumulator held in register r by lane half hf.
+__device__ inline int acc_row(int r, int hf) { return ((r >> 2) << 3) + (hf << 2) + (r & 3); }
+
+// Per-lane online-softmax state for one query row (half of its kv values).
+struct RowState {
+  float m;  // running max in log2 units (-inf before the first live key)
+  float l;  // running sum of this lane half's probabilities
+};
+
+// Turn four S^T tiles (raw q.k) into probabilities in place and update the
+// running statistics. Returns alpha, the factor that rescales the previous
+// accumulator. kv0: absolute index of the block's first key.
+template <int KIND, bool PARTIAL, bool SOFTCAP>
+__device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, int kv0, int hf,
+                                      const FwdArgs& a, int32_t dq, const int32_t* doc_k, int klo,
+                                      int khi) {
+  const float c1 = a.scale * kLog2e;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[t][r];
+      if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
+      if (PARTIAL) {
+        const int jl = t * 32 + acc_row(r, hf);
+        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? doc_k[jl] : 0;
+        // kept keys [klo, khi): the mask's own j < S, and key padding
+        if (!pair_live<KIND>(qi + a.m.q_off, kv0 + jl, khi, a.m.window, dq, dj) || kv0 + jl < klo)
+          x = -INFINITY;
+      }
+      s[t][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = half_max(mx);
+  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
+  const float m_blk = SOFTCAP ? mx : mx * c1;
+  const float m_new = fmaxf(st.m, m_blk);
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = s[t][r];
+      s[t][r] = SOFTCAP ? fast_exp2(x - m_use) : fast_exp2(fmaf(x, c1, -m_use));
+    }
+  }
+  st.m = m_new;
+  return alpha;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 kernel
+// ---------------------------------------------------------------------------
+// LDS holds two K tiles and two V tiles (128 rows x 128 bytes each, row-major)
+// plus the document ids of each K tile. Rows are split in eight 16-byte
+// chunks stored XOR-swizzled: K chunk c of row r sits in slot c ^ (r & 7)
+// (conflict-free 16-byte reads of 8 consecutive rows); V chunk c sits in slot
+// c ^ 2(r & 3) (conflict-free transposed reads of 4 rows x 32 bytes by each
+// 16-lane group).
+struct alignas(16) KStage {
+  uint8_t k[kBlock * 128];
+  int32_t doc[kBlock];
+};
+struct alignas(16) VStage {
+  uint8_t v[kBlock * 128];
+};
+
+// The running max only moves when a block's max exceeds it by more than this
+// many powers of two, so probabilities stay <= 2^8 and the accumulator rescale
+// is skipped for most blocks. The result is algebraically the same: numerator
+// and normaliser share the reference.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Workgroup barrier without memory fences: the caller waits for exactly the
+// memory operations it needs first (the fences of __syncthreads would also
+// wait for the next tile's in-flight copies). The signal fences only keep the
+// compiler from moving memory accesses across the barrier.
+__device__ inline void barrier_only() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]
+// | vmcnt[5:4] << 14), leaving the other counters unconstrained.
+__device__ inline void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ inline void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Block index lists are read through the constant address space so the loads
+// are scalar (they never change during a launch).
+typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+
+// Global -> LDS copies (global_load_lds_dword{x4}): lane l writes bytes
+// [size*l, size*(l+1)) after the wave-uniform base in M0. They are issued as
+// inline asm so that the compiler's own wait insertion, which cannot tell
+// these LDS writes from the tiles being read, adds no wait for the copies in
+// flight before every LDS read; every wait on them is explicit (wait_vm_zero,
+// then a barrier). The instructions have no result registers and their
+// address registers are read at issue. The first form takes a 64-bit
+// address per lane; the second a wave-uniform base in SGPRs plus a 32-bit
+// byte offset per lane, which keeps the per-tile address arithmetic scalar.
+__device__ inline uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ inline void lds_copy16(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
+}
+__device__ inline void lds_copy16_base(const void* sbase, uint32_t lane_off, uint32_t lds_wave_base) {
+  // readfirstlane returns int: widen through uint32_t so the low word is
+  // zero-extended (a sign extension would set the high word's bits).
+  const uint64_t p = (uint64_t)(uintptr_t)sbase;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"((const void*)(uintptr_t)(lo | (hi << 32))),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
+}
+__device__ inline void lds_copy4(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
+}
+
+// One wave's share of a tile copy: tile rows 32w .. 32w+31 (4 KiB), four
+// copies of 8 rows. Lane l of copy i fills slot l & 7 of tile row
+// 32w + 8i + l/8 and fetches the global chunk that the swizzle puts there;
+// that chunk depends only on the lane, so the per-lane byte offset (relative
+// to the copy's first row) is fixed for the whole launch. Rows past the end
+// are clamped to the last key (their scores are masked); that only happens on
+// a ragged last tile.
+template <typename T, bool IS_V>
+__device__ inline void issue_rows(const T* g, int64_t sl, uint32_t lane_off, int kv0, int S,
+                                  uint8_t* tile, int wave, int lane) {
+  const int row0 = kv0 + wave * 32;  // first key of this wave's rows
+  const uint32_t lds0 = lds_offset(tile) + (uint32_t)wave * 4096u;
+  if (kv0 + kBlock <= S) {
+    // One 64-bit multiply per tile; copy i starts 8 i rows further on.
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(g + (int64_t)row0 * sl);
+    const int64_t step = sl * (int64_t)(8 * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16_base(base + i * step, lane_off, lds0 + 1024u * i);
+  } else {
+    const int chunk = IS_V ? ((lane & 7) ^ (((lane >> 3) & 3) << 1)) : ((lane & 7) ^ (lane >> 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(row0 + 8 * i + (lane >> 3), S - 1);
+      lds_copy16(g + (int64_t)key * sl + chunk * 8, lds0 + 1024u * i);
+    }
+  }
+}
+
+template <typename T, int KIND>
+__device__ inline void issue_k(const T* kg, int64_t k_sl, uint32_t k_off, const int32_t* doc, int kv0,
+                               int S, KStage& st, int wave, int lane) {
+  issue_rows<T, false>(kg, k_sl, k_off, kv0, S, st.k, wave, lane);
+  if (KIND == ATTN_MASK_DOCUMENT) {
+    // ids of keys 32*wave .. 32*wave+31 of the tile, 4 bytes per lane
+    if (lane < 32) {
+      const int64_t j = min(kv0 + wave * 32 + lane, S - 1);
+      lds_copy4(doc + j, lds_offset(st.doc) + (uint32_t)wave * 128u);
+    }
+  }
+}
+
+typedef __attribute__((address_space(3))) const uint8_t* lds_u8;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// All LDS of a workgroup: two K stages and two V stages.
+struct alignas(16) Lds {
+  KStage k[2];
+  VStage v[2];
+};
+
+// Per-lane LDS read addresses into stage 0; stage 1 is a constant away, and
+// every read of a step is one of these plus a constant that fits the
+// instruction's offset field.
+//  * k[c]: K operand of contraction step c (head dims 16c + 8hf .. +7) of
+//    key lq of the tile's first 32-key tile: row lq, chunk 2c + hf, stored
+//    in slot (2c + hf) ^ (lq & 7). Tile t adds 4096 bytes.
+//  * v[te]: V^T operand of head-dim tile te. For 16-key group g, lane half
+//    hf holds keys 16g + 4hf + {0..3} and 16g + 8 + 4hf + {0..3} of P^T; the
+//    matching V^T operand comes from two transposed LDS reads: in each
+//    16-lane group, lane i16 supplies the address of row (key)
+//    r0 + i16/4, head dims eb + 4(i16%4) .. +3 (16-byte chunk eb/8 + ...,
+//    swizzled by 2(row & 3)), and receives head dim eb + i16 of rows
+//    r0 .. r0+3. Group g adds 2048 bytes; the second read adds 1024.
+struct LanePtrs {
+  lds_u8 k[4];
+  lds_u8 v[2];
+};
+
+__device__ inline LanePtrs make_lane_ptrs(const Lds& lds, int lane) {
+  LanePtrs p;
+  const int lq = lane & 31, hf = lane >> 5;
+  const lds_u8 kb = (lds_u8)lds.k[0].k;
+  const lds_u8 vb = (lds_u8)lds.v[0].v;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) p.k[c] = kb + lq * 128 + (((2 * c + hf) ^ (lq & 7)) << 4);
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int r1 = hf * 4 + (i16 >> 2);  // row of group 0
+#pragma unroll
+  for (int te = 0; te < 2; ++te) {
+    const int e = te * 32 + (g16 & 1) * 16 + (i16 & 3) * 4;
+    const int c16 = e >> 3, half = (e >> 2) & 1;
+    p.v[te] = vb + r1 * 128 + ((c16 ^ ((r1 & 3) << 1)) << 4) + half * 8;
+  }
+  return p;
+}
+
+// Classes of a 32 x 32 score tile in a partial block.
+enum { kTileLive = 0, kTileMixed = 1, kTileDead = 2 };
+
+// Keeps the compiler's schedulers from moving any instruction across this
+// point, so the source order of the chunks below is the issue order.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One KV block for this wave's 32 query rows, in two phases of 16 chunks,
+// each chunk one MFMA plus a slice of vector work that does not depend on
+// it, so LDS latency is covered and the matrix and vector units overlap:
+//  Q. S^T = K Q^T (MFMA j: 32-key tile j / 4, contraction step j % 4; K
+//     fragments read four MFMAs ahead), with the score_mod, mask and max of
+//     the tile finished before.
+//  P. O^T += V^T P^T (MFMA i: 16-key group i / 2, head-dim tile i % 2; V
+//     fragments read four MFMAs ahead), with the probabilities of the next
+//     group.
+template <typename T, int KIND, bool SOFTCAP, bool PARTIAL, bool PADDED>
+__device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
+                                          const typename Vec<T>::x8 (&qop)[4], f32x16_t (&oacc)[2],
+                                          float& m_ref, float& l, int qi, int row0, int kv0, int lane, const FwdArgs& a,
+                                          int32_t dq, int klo, int khi) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  typedef __attribute__((address_space(3))) const x8 lds_x8;
+  const int hf = lane >> 5;
+  const float c1 = a.scale * kLog2e;
+
+  // K operand of QK MFMA j: head dims 16c + 8hf .. +7 of key 32t + lq.
+  auto k_frag = [&](int j) -> x8 {
+    const int t = j >> 2, c = j & 3;
+    return *reinterpret_cast<const lds_x8*>(kp[c] + t * 4096);
+  };
+  // V^T operand of PV MFMA i: two transposed reads, 8 rows apart (see
+  // LanePtrs).
+  auto v_frag = [&](int i) -> x8 {
+    const int g = i >> 1, te = i & 1;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[te] + g * 2048));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp[te] + g * 2048 + 1024));
+    const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(x8, both);
+  };
+  // In a partial block, each 32 x 32 tile of this wave (its rows row0 ..
+  // row0 + 31 x keys kv0 + 32t .. +31) is classified in closed form, with
+  // scalar arithmetic only, from the rule's offset interval and the kept key
+  // range [klo, khi) (the whole [0, S) without padding), as whole blocks are:
+  // all pairs live, none live, or mixed. Only mixed tiles test pairs, and
+  // only live tiles skip the test; for document masks the interval decides
+  // only "none live".
+  int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
+  if (PARTIAL) {
+    const int i0 = row0 + a.m.q_off, i1 = i0 + 31;  // the rows' rule positions
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j0 = kv0 + 32 * t, j1 = min(j0 + 31, khi - 1);
+      const bool outside = j0 > khi - 1 || (PADDED && j0 + 31 < klo);
+      const bool edge = j0 + 31 > khi - 1 || (PADDED && j0 < klo);  // range ends inside
+      int c;
+      if (outside) {
+        c = kTileDead;
+      } else if (KIND == ATTN_MASK_NONE) {
+        c = edge ? kTileMixed : kTileLive;
+      } else {
+        const int dmin = i0 - j1, dmax = i1 - j0;  // offsets p - j of the tile
+        const int w = (KIND == ATTN_MASK_SLIDING_WINDOW) ? a.m.window : 0x7fffffff;
+        if (dmax < 0 || dmin > w - 1)
+          c = kTileDead;
+        else if (KIND != ATTN_MASK_DOCUMENT && dmin >= 0 && dmax <= w - 1 && !edge)
+          c = kTileLive;
+        else
+          c = kTileMixed;
+      }
+      tile_cls[t] = c;
+    }
+  }
+  // Pair test of a mixed tile as an interval of the key's offset inside the
+  // tile: this lane's key of register r is kv0 + 32t + 4hf + c(r), with
+  // c(r) = 8(r / 4) + r % 4; it is live when lo - 32t <= c(r) <= hi - 32t.
+  // hi bounds by j <= p and j < khi, lo by p - j < W (sliding windows) and
+  // j >= klo (padding), p = qi + q_off the row's rule position.
+  const int rel = qi + a.m.q_off - kv0 - 4 * hf;
+  const int hi = (KIND == ATTN_MASK_NONE) ? khi - 1 - kv0 - 4 * hf : min(rel, khi - 1 - kv0 - 4 * hf);
+  // (A window wider than 2^30 never bites: S is far smaller.)
+  int lo = (KIND == ATTN_MASK_SLIDING_WINDOW) ? rel - min(a.m.window - 1, 1 << 30) : -(1 << 30);
+  if (PADDED) lo = max(lo, klo - kv0 - 4 * hf);
+
+  // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4), in
+  // the tile's mode.
+  float mx = -INFINITY;
+  f32x16_t s[4];
+  auto mask_chunk = [&](auto mode_c, int k) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
+    const int t = k >> 2;
+#pragma unroll
+    for (int e = 4 * k; e < 4 * k + 4; ++e) {
+      const int r = e & 15;
+      if (MODE == kTileDead) {
+        // Written here, in the dead tile's own path (a constant would be
+        // materialised before the branch, on every path).
+        float ninf;
+        asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
+        s[t][r] = ninf;
+        continue;
+      }
+      float x = s[t][r];
+      if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
+      if (MODE == kTileMixed) {
+        const int c = ((r >> 2) << 3) + (r & 3);
+        bool live = c <= hi - 32 * t;
+        if (KIND == ATTN_MASK_SLIDING_WINDOW || PADDED) live &= c >= lo - 32 * t;
+        // (Read unconditionally: the four ids of a register group are one
+        // 16-byte LDS read.)
+        if (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
+        x = live ? x : -INFINITY;
+      }
+      s[t][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  };
+  // Runs f with the mode of tile t as a compile-time constant (one scalar
+  // branch per tile).
+  auto with_mode = [&](int t, auto&& f) __attribute__((always_inline)) {
+    if (!PARTIAL || tile_cls[t] == kTileLive)
+      f(std::integral_constant<int, kTileLive>{});
+    else if (tile_cls[t] == kTileDead)
+      f(std::integral_constant<int, kTileDead>{});
+    else
+      f(std::integral_constant<int, kTileMixed>{});
+  };
+
+  // Phase Q. Tile t is complete after chunk 4t + 3; its scores are
+  // processed in chunks 4t + 4 .. 4t + 7 (tile 3 after the phase).
+  x8 kf[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kf[j] = k_frag(j);
+  sched_fence();
+  auto q_chunk = [&](int j) __attribute__((always_inline)) {
+    if (j + 4 < 16) kf[j + 4] = k_frag(j + 4);
+    const int t = j >> 2, c = j & 3;
+    s[t] = V::mma(kf[j], qop[c], c == 0 ? f32x16_t{} : s[t]);
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    q_chunk(j);
+    sched_fence();
+  }
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    with_mode(t, [&](auto mode_c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 4 * t + 4; j < 4 * t + 8; ++j) {
+        q_chunk(j);
+        mask_chunk(mode_c, j - 4);
+        sched_fence();
+      }
+    });
+  }
+  x8 vf[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vf[i] = v_frag(i);
+  with_mode(3, [&](auto mode_c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 12; k < 16; ++k) mask_chunk(mode_c, k);
+  });
+  mx = half_max(mx);
+  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
+  const float m_blk = SOFTCAP ? mx : mx * c1;
+
+  // Lazy rescale (wave-uniform branch).
+  const bool grow = m_blk > m_ref + kRescaleLog2;
+  if (__ballot(grow) != 0) {
+    const float alpha = grow ? fast_exp2(m_ref - m_blk) : 1.0f;
+    l *= alpha;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
+  }
+  if (grow) m_ref = m_blk;
+  const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+
+  // Probabilities of scores 4k .. 4k+3 (group k / 2, entries 4(k % 2) ..),
+  // rounded to T (nearest even) for P V; the normaliser sums the rounded
+  // values.
+  x8 pk[8];
+  float psum[2] = {0.0f, 0.0f};
+  auto prob_chunk = [&](int k) {
+    const int g = k >> 1;
+#pragma unroll
+    for (int u = (k & 1) * 4; u < (k & 1) * 4 + 4; u += 2) {
+      const float x0 = s[g >> 1][(g & 1) * 8 + u], x1 = s[g >> 1][(g & 1) * 8 + u + 1];
+      const float p0 = SOFTCAP ? fast_exp2(x0 - m_use) : fast_exp2(fmaf(x0, c1, -m_use));
+      const float p1 = SOFTCAP ? fast_exp2(x1 - m_use) : fast_exp2(fmaf(x1, c1, -m_use));
+      const typename V::x2 pr = {(T)p0, (T)p1};
+      psum[(u >> 1) & 1] = V::add_pair(pr, psum[(u >> 1) & 1]);
+      pk[g][u] = pr[0];
+      pk[g][u + 1] = pr[1];
+    }
+  };
+
+  // Phase P. Group g's probabilities are made in chunks 2g - 2 and 2g - 1
+  // (group 0 before the phase) and used by MFMAs 2g and 2g + 1. The phase
+  // runs at raised wave priority: it is bound by the vector unit, and when
+  // the other wave on the SIMD is in its MFMA-bound phase Q, issuing this
+  // wave's vector work first keeps both units busy.
+  __builtin_amdgcn_s_setprio(1);
+  prob_chunk(0);
+  prob_chunk(1);
+  sched_fence();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i + 4 < 16) vf[i + 4] = v_frag(i + 4);
+    oacc[i & 1] = V::mma(vf[i], pk[i >> 1], oacc[i & 1]);
+    if (i + 2 < 16) prob_chunk(i + 2);
+    sched_fence();
+  }
+  l += psum[0] + psum[1];
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One work item of the plan written by the mask builder (a 16-byte
+// descriptor, one scalar load): query block qb, which of its k chunks of kv
+// blocks the item visits, the block counts of qb and the item's first block.
+struct WorkItem {
+  int qb, chunk, k;
+  int nfull, npart;  // full and partial kv blocks of qb
+  int first_kb;      // kv block index of the item's first visited block
+  bool split;        // the item is one of k > 1 chunks whose results are merged
+  bool skip;         // no work (past the end of the plan, or a later chunk when
+                     // splitting is off: then the first item visits every block)
+};
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const i32x4_t* const_i32x4_ptr;
+
+__device__ inline WorkItem work_item(const FwdArgs& a, int e) {
+  const i32x4_t d = ((const_i32x4_ptr)(a.m.schedule + 4))[e];
+  WorkItem w;
+  w.skip = d[0] < 0;
+  w.qb = d[0] & 0xFFFFF;
+  w.chunk = (d[0] >> 20) & 3;
+  w.k = ((d[0] >> 22) & 3) + 1;
+  w.nfull = d[1];
+  w.npart = d[2];
+  w.first_kb = d[3];
+  w.split = a.split && w.k > 1;
+  w.skip = w.skip || (w.chunk > 0 && !w.split);
+  if (w.skip) w.qb = w.chunk = w.nfull = w.npart = w.first_kb = 0;
+  return w;
+}
+
+template <typename T, int KIND, bool SOFTCAP, bool PADDED, bool KVSPLIT>
+__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  using x4 = typename V::x4;
+  __shared__ Lds lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = a.B * a.H;
+  const int item = blockIdx.x;
+  WorkItem wi;
+  int b, h;
+  if (KVSPLIT) {
+    // Split-KV item (query block qb, chunk c of kv_split, batch b, K/V head
+    // hk, query head h = hk * G + g). The batch*K/V-head index varies
+    // fastest, so (with B*H_kv a multiple of 8) every item that reads one
+    // K/V head lands on one XCD and shares its L2.
+    const int G = a.kv_group, BHk = a.B * (a.H / G), k = a.kv_split;
+    const int bk = item % BHk, rest = item / BHk;
+    const int c = rest % k, rest2 = rest / k;
+    const int g = rest2 % G;
+    b = bk / (a.H / G);
+    h = (bk % (a.H / G)) * G + g;
+    wi.qb = rest2 / G;
+    wi.chunk = c;
+    wi.k = k;
+    wi.nfull = ((const_i32_ptr)a.m.full_num)[wi.qb];
+    wi.npart = ((const_i32_ptr)a.m.kv_num)[wi.qb];
+    wi.split = true;
+    wi.skip = false;
+    wi.first_kb = 0;  // set below, once the item's range is known
+  } else {
+    wi = work_item(a, item / BH);
+    if (wi.skip) return;
+    b = (item % BH) / a.H;
+    h = (item % BH) % a.H;
+  }
+  const int qb = wi.qb;
+  const int bh = b * a.H + h;
+
+  const T* qg = static_cast<const T*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const int hk = h / a.kv_group;  // K/V head of query head h
+  const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + hk * a.v_sh;
+  T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
+  // Kept keys [klo, khi) of this batch entry (all of [0, S) without padding).
+  int klo = 0, khi = a.S;
+  if (PADDED) {
+    if (a.key_start != nullptr) klo = min(max(((const_i32_ptr)a.key_start)[b], 0), a.S);
+    if (a.key_end != nullptr) khi = max(min(((const_i32_ptr)a.key_end)[b], a.S), klo);
+  }
+
+  const int nfull = wi.nfull;
+  const int npart = wi.npart;
+  const int nblk = nfull + npart;
+  const const_i32_ptr full_list = (const_i32_ptr)(a.m.full_idx + (int64_t)qb * a.m.nk);
+  const const_i32_ptr part_list = (const_i32_ptr)(a.m.kv_idx + (int64_t)qb * a.m.nk);
+  // First key of the n-th visited block: full blocks first, then partial.
+  auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
+  // This item visits blocks [m_begin, m_end) of that order: a split query
+  // block's first chunk is its first C blocks (C from the plan), the second
+  // the rest; split-KV chunk c of k takes blocks [c n / k, (c + 1) n / k).
+  int m_begin, m_end;
+  if (KVSPLIT) {
+    m_begin = (int)((int64_t)wi.chunk * nblk / wi.k);
+    m_end = (int)((int64_t)(wi.chunk + 1) * nblk / wi.k);
+    if (m_end > m_begin) wi.first_kb = kv_start(m_begin) / kBlock;
+  } else {
+    const int split_len = a.m.schedule[1];
+    m_begin = (wi.split && wi.chunk == 1) ? split_len : 0;
+    m_end = (wi.split && wi.chunk == 0) ? split_len : nblk;
+  }
+  // Per-lane byte offsets of the tile copies (see issue_rows).
+  const uint32_t k_off =
+      (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  const uint32_t v_off = (uint32_t)((lane >> 3) * a.v_sl * (int64_t)sizeof(T)) +
+                         (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+
+  // Block m's K and V tiles live in stage (m - m_begin) % 2. The index of
+  // the block after the next one is loaded a block ahead, so no block waits
+  // on a scalar load before issuing its copies.
+  int kv_next = 0;   // first key of the next block to copy
+  int kv_after = 0;  // first key of the block after it
+  if (m_end > m_begin) {
+    kv_next = wi.first_kb * kBlock;
+    if (m_begin + 1 < m_end) kv_after = kv_start(m_begin + 1);
+    issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[0], wave, lane);
+    issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[0].v, wave, lane);
+  }
+
+  const int row0 = qb * kBlock + wave * 32;  // this wave's first query row
+  const int qi = row0 + lq;                   // this lane's query row
+  x8 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (qi < a.L)
+      qop[c] = *reinterpret_cast<const x8*>(qg + (int64_t)qi * a.q_sl + c * 16 + hf * 8);
+    else
+      qop[c] = x8{};
+  }
+  const int32_t dq = (KIND == ATTN_MASK_DOCUMENT && qi < a.L) ? a.m.doc[qi] : -1;
+  // Q, dq and tile 0 have landed: no load the compiler tracks is still in
+  // flight inside the loop, so it adds no wait there (such a wait would also
+  // drain the next tile's copies, which share the in-order counter).
+  wait_vm_zero();
+
+  // Per-lane LDS read addresses of each stage.
+  const LanePtrs lp = make_lane_ptrs(lds, lane);
+
+  f32x16_t oacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
+  float m_ref = -INFINITY, l = 0.0f;
+
+  // Two stages and one barrier per block: once every wave's copies of block
+  // m have landed and every wave has finished block m-1, the copies of block
+  // m+1 go into the stage block m-1 used, and block m is computed. Full and
+  // partial blocks run in separate loops, so each loop body has a single
+  // definition of the accumulators and they stay in place.
+  auto block = [&](auto partial_c, int m) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_c)::value;
+    const int par = (m - m_begin) & 1;
+    lds_u8 kp[4], vp[2];
+    // Computed once per block; the empty asm keeps the compiler from
+    // recomputing each address before every read instead of holding it.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kp[c] = lp.k[c] + par * (int)sizeof(KStage);
+      asm volatile("" : "+v"(kp[c]));
+    }
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+      vp[te] = lp.v[te] + par * (int)sizeof(VStage);
+      asm volatile("" : "+v"(vp[te]));
+    }
+    const int kv0 = kv_next;
+    wait_vm_zero();    // this wave's copies of block m
+    wait_lgkm_zero();  // this wave's reads of block m-1
+    barrier_only();
+    if (m + 1 < m_end) {
+      kv_next = kv_after;
+      issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[1 - par], wave, lane);
+      issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
+      if (m + 2 < m_end) kv_after = kv_start(m + 2);
+    }
+    if (PADDED) {
+      // A block with no kept key is skipped; a full block that a padding
+      // boundary cuts runs the per-tile pair tests of a partial block.
+      if (kv0 + kBlock <= klo || kv0 >= khi) return;
+      if (!PARTIAL && (kv0 < klo || kv0 + kBlock > khi)) {
+        fwd_block<T, KIND, SOFTCAP, true, true>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0,
+                                                lane, a, dq, klo, khi);
+        return;
+      }
+    }
+    fwd_block<T, KIND, SOFTCAP, PARTIAL, PADDED>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0,
+                                                 lane, a, dq, klo, khi);
+  };
+  int m = m_begin;
+  for (; m < min(m_end, nfull); ++m) block(std::false_type{}, m);
+  for (; m < m_end; ++m) block(std::true_type{}, m);
+
+  float lt = half_sum(l);  // the row's sum of (rounded) probabilities
+
+  if (KVSPLIT) {
+    // Split-KV: leave this chunk's unnormalised O (row-major [row][64]), its
+    // reference max and its sum for the query rows in range; the merge kernel,
+    // launched next on the stream, combines the chunks.
+    if (qi < a.L) {
+      float* slot = a.partials + (((int64_t)qb * a.kv_split + wi.chunk) * BH + bh) * kSlotFloats;
+      float* orow = slot + (wave * 32 + lq) * 64;
+#pragma unroll
+      for (int te = 0; te < 2; ++te)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4 o4;
+          o4.x = oacc[te][r4 * 4 + 0];
+          o4.y = oacc[te][r4 * 4 + 1];
+          o4.z = oacc[te][r4 * 4 + 2];
+          o4.w = oacc[te][r4 * 4 + 3];
+          *reinterpret_cast<float4*>(orow + te * 32 + r4 * 8 + hf * 4) = o4;
+        }
+      if (hf == 0) {
+        slot[4 * 32 * 64 + wave * 32 + lq] = m_ref;
+        slot[4 * 32 * 64 + kBlock + wave * 32 + lq] = lt;
+      }
+    }
+    return;
+  }
+
+  if (wi.split) {
+    // Leave this chunk's partial result, then take a ticket; the last of the
+    // k chunks to finish merges them all. The partials are written and read
+    // with device-scope (sc1) accesses, and every write has completed before
+    // the ticket is taken, so the chunks may run on different XCDs; this
+    // avoids device-scope fences, which would write back and invalidate the
+    // whole L2 of the XCD (and with it the K/V tiles other workgroups reuse).
+    const int64_t bhn = (int64_t)a.B * a.H;
+    auto slot = [&](int c) { return a.partials + (((int64_t)qb * kMaxChunks + c) * bhn + bh) * kSlotFloats; };
+    auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto get = [](float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    float* mine = slot(wi.chunk);
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) put(mine + (wave * 32 + te * 16 + r) * 64 + lane, oacc[te][r]);
+    if (hf == 0) {
+      put(mine + 4 * 32 * 64 + wave * 32 + lq, m_ref);
+      put(mine + 4 * 32 * 64 + kBlock + wave * 32 + lq, lt);
+    }
+    wait_vm_zero();  // this wave's partial writes have completed
+    __syncthreads();
+    __shared__ int ticket;
+    int32_t* counter = a.counters + (int64_t)qb * bhn + bh;
+    if (tid == 0) ticket = atomicAdd(counter, 1);
+    __syncthreads();
+    if (ticket != wi.k - 1) return;  // a later chunk merges
+    if (tid == 0) atomicExch(counter, 0);  // ready for the next call
+    // Merge in chunk order (the same operations whichever chunk merges):
+    // weights w_c = 2^(m_c - max m), O = sum_c w_c O_c, l = sum_c w_c l_c.
+    float mc[kMaxChunks], lc[kMaxChunks], wc[kMaxChunks];
+    float m_new = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c < wi.k) {
+        mc[c] = (c == wi.chunk) ? m_ref : get(slot(c) + 4 * 32 * 64 + wave * 32 + lq);
+        lc[c] = (c == wi.chunk) ? lt : get(slot(c) + 4 * 32 * 64 + kBlock + wave * 32 + lq);
+        m_new = fmaxf(m_new, mc[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < wi.k) wc[c] = (mc[c] == -INFINITY) ? 0.0f : fast_exp2(mc[c] - m_new);
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+          if (c < wi.k) {
+            const float ov = (c == wi.chunk) ? oacc[te][r] : get(slot(c) + (wave * 32 + te * 16 + r) * 64 + lane);
+            acc = (c == 0) ? wc[0] * ov : fmaf(wc[c], ov, acc);
+          }
+        }
+        oacc[te][r] = acc;
+      }
+    float lsum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < wi.k) lsum = (c == 0) ? wc[0] * lc[0] : fmaf(wc[c], lc[c], lsum);
+    lt = lsum;
+    m_ref = m_new;
+  }
+
+  // Epilogue: O = O^T / l (0 for a row without live keys), lse = ln(sum exp).
+  const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+  if (qi < a.L) {
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int e0 = te * 32 + r4 * 8 + hf * 4;
+        x4 outv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) outv[u] = (T)(oacc[te][r4 * 4 + u] * inv);
+        *reinterpret_cast<x4*>(og + (int64_t)qi * a.o_sl + e0) = outv;
+      }
+    }
+    if (a.lse != nullptr && hf == 0)
+      a.lse[(int64_t)bh * a.L + qi] = (lt > 0.0f) ? (m_ref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: same structure with v_mfma_f32_32x32x2_f32 (one element of the
+// contraction per lane and step), probabilities kept in fp32.
+// ---------------------------------------------------------------------------
+constexpr int kF32RowStride = 68;  // floats per LDS row (64 + 4 padding)
+
+template <int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float k_lds[kBlock * kF32RowStride];
+  __shared__ __attribute__((aligned(16))) float v_lds[kBlock * kF32RowStride];
+  __shared__ int32_t doc_k[kBlock];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = a.B * a.H;
+  const int item = blockIdx.x;
+  // fp32 never splits (no workspace): a first item visits every block.
+  const WorkItem wi = work_item(a, item / BH);
+  if (wi.skip) return;
+  const int qb = wi.qb;
+  const int bh = item % BH;
+  const int b = bh / a.H, h = bh % a.H;
+
+  const float* qg = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const int hk = h / a.kv_group;  // K/V head of query head h
+  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + hk * a.v_sh;
+  float* og = static_cast<float*>(a.o) + b * a.o_sb + h * a.o_sh;
+  // Kept keys [klo, khi) of this batch entry (all of [0, S) without padding).
+  int klo = 0, khi = a.S;
+  if (a.key_start != nullptr) klo = min(max(a.key_start[b], 0), a.S);
+  if (a.key_end != nullptr) khi = max(min(a.key_end[b], a.S), klo);
+
+  const int qi = qb * kBlock + wave * 32 + lq;
+  // Contraction step j of lane half hf covers head dim e = 32*hf + j.
+  float qv[32];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qi < a.L) x = *reinterpret_cast<const float4*>(qg + (int64_t)qi * a.q_sl + hf * 32 + c * 4);
+    qv[4 * c + 0] = x.x;
+    qv[4 * c + 1] = x.y;
+    qv[4 * c + 2] = x.z;
+    qv[4 * c + 3] = x.w;
+  }
+  const int32_t dq = (KIND == ATTN_MASK_DOCUMENT && qi < a.L) ? a.m.doc[qi] : -1;
+
+  f32x16_t oacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
+  RowState st{-INFINITY, 0.0f};
+
+  const int nfull = a.m.full_num[qb];
+  const int npart = a.m.kv_num[qb];
+  const int32_t* full_list = a.m.full_idx + (int64_t)qb * a.m.nk;
+  const int32_t* part_list = a.m.kv_idx + (int64_t)qb * a.m.nk;
+
+  for (int n = 0; n < nfull + npart; ++n) {
+    const int kb = n >= nfull ? part_list[n - nfull] : full_list[n];
+    const int kv0 = kb * kBlock;
+    // Skip blocks with no kept key; a padding boundary inside a full block
+    // makes it partial.
+    if (kv0 + kBlock <= klo || kv0 >= khi) continue;
+    const bool partial = n >= nfull || kv0 < klo || kv0 + kBlock > khi;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int cidx = tid + u * kThreads;  // 2048 float4 chunks per tile
+      const int row = cidx >> 4, ch = cidx & 15;
+      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+      if (kv0 + row < a.S) {
+        kx = *reinterpret_cast<const float4*>(kg + (int64_t)(kv0 + row) * a.k_sl + ch * 4);
+        vx = *reinterpret_cast<const float4*>(vg + (int64_t)(kv0 + row) * a.v_sl + ch * 4);
+      }
+      *reinterpret_cast<float4*>(k_lds + row * kF32RowStride + ch * 4) = kx;
+      *reinterpret_cast<float4*>(v_lds + row * kF32RowStride + ch * 4) = vx;
+    }
+    if (KIND == ATTN_MASK_DOCUMENT && partial && tid < kBlock)
+      doc_k[tid] = (kv0 + tid < a.S) ? a.m.doc[kv0 + tid] : -1;
+    __syncthreads();
+
+    f32x16_t s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+      const float* krow = k_lds + (t * 32 + lq) * kF32RowStride + hf * 32;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) s[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[j], qv[j], s[t], 0, 0, 0);
+    }
+
+    float alpha;
+    if (partial)
+      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi);
+    else
+      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi);
+
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) psum += s[t][r];
+    st.l = st.l * alpha + psum;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
+
+    // O^T += V^T P^T: step (t, r) pairs lane half 0's key acc_row(r,0) with
+    // lane half 1's key acc_row(r,1) of tile t; A = V[key][e], B = p.
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float va = v_lds[(t * 32 + acc_row(r, hf)) * kF32RowStride + te * 32 + lq];
+          oacc[te] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, s[t][r], oacc[te], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float l = half_sum(st.l);
+  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+  if (qi < a.L) {
+#pragma unroll
+    for (int te = 0; te < 2; ++te) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int e0 = te * 32 + r4 * 8 + hf * 4;
+        float4 outv = make_float4(oacc[te][r4 * 4 + 0] * inv, oacc[te][r4 * 4 + 1] * inv,
+                                  oacc[te][r4 * 4 + 2] * inv, oacc[te][r4 * 4 + 3] * inv);
+        *reinterpret_cast<float4*>(og + (int64_t)qi * a.o_sl + e0) = outv;
+      }
+    }
+    if (a.lse != nullptr && hf == 0)
+      a.lse[(int64_t)bh * a.L + qi] = (l > 0.0f) ? (st.m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// Merge of split-KV chunks: one workgroup per (query block, batch*head), one
+// thread per (row, head dim) of four rows at a time; for each row, weights
+// w_c = 2^(m_c - max m) over the chunks in chunk order, O = sum w_c O_c /
+// sum w_c l_c (0 without any live key), lse = (max m + log2 sum w_c l_c) ln 2.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void kv_merge_kernel(FwdArgs a) {
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH, qb = blockIdx.x / BH;
+  const int b = bh / a.H, h = bh % a.H;
+  const int k = a.kv_split;
+  const int rows = min(kBlock, a.L - qb * kBlock);
+  const float* slot0 = a.partials + ((int64_t)qb * k * BH + bh) * kSlotFloats;
+  const int64_t cstride = (int64_t)BH * kSlotFloats;  // next chunk's slot
+  T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
+  for (int r0 = 0; r0 < rows; r0 += kThreads / kHeadDim) {
+    const int row = r0 + threadIdx.x / kHeadDim, e = threadIdx.x % kHeadDim;
+    if (row >= rows) break;
+    float m_new = -INFINITY;
+    for (int c = 0; c < k; ++c) m_new = fmaxf(m_new, slot0[c * cstride + 4 * 32 * 64 + row]);
+    float acc = 0.0f, lsum = 0.0f;
+    for (int c = 0; c < k; ++c) {
+      const float* sl = slot0 + c * cstride;
+      const float mc = sl[4 * 32 * 64 + row];
+      const float w = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - m_new);
+      acc = (c == 0) ? w * sl[row * kHeadDim + e] : fmaf(w, sl[row * kHeadDim + e], acc);
+      lsum = (c == 0) ? w * sl[4 * 32 * 64 + kBlock + row] : fmaf(w, sl[4 * 32 * 64 + kBlock + row], lsum);
+    }
+    const int qi = qb * kBlock + row;
+    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+    og[(int64_t)qi * a.o_sl + e] = (T)(acc * inv);
+    if (a.lse != nullptr && e == 0)
+      a.lse[(int64_t)bh * a.L + qi] = (lsum > 0.0f) ? (m_new + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int KIND, bool SOFTCAP, bool PADDED, bool KVSPLIT>
+hipError_t launch_split(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  // Up to kMaxChunks work items per query block (items past the plan's end
+  // return at once), or kv_split split-KV chunks followed by their merge.
+  const int64_t chunks = a.kv_split > 0 ? a.kv_split : kMaxChunks;
+  const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * chunks));
+  const dim3 block(kThreads);
+  const dim3 merge_grid((unsigned)((int64_t)a.B * a.H * a.m.nq));
+  switch (dtype) {
+    case ATTN_BF16:
+      hipLaunchKernelGGL((fwd16_kernel<__bf16, KIND, SOFTCAP, PADDED, KVSPLIT>), grid, block, 0, stream, a);
+      if (KVSPLIT) hipLaunchKernelGGL(kv_merge_kernel<__bf16>, merge_grid, block, 0, stream, a);
+      break;
+    case ATTN_F16:
+      hipLaunchKernelGGL((fwd16_kernel<_Float16, KIND, SOFTCAP, PADDED, KVSPLIT>), grid, block, 0, stream, a);
+      if (KVSPLIT) hipLaunchKernelGGL(kv_merge_kernel<_Float16>, merge_grid, block, 0, stream, a);
+      break;
+    case ATTN_F32:
+      hipLaunchKernelGGL((fwd32_kernel<KIND, SOFTCAP>), grid, block, 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Split-KV items have kernels of their own, so the others keep their code.
+template <int KIND, bool SOFTCAP, bool PADDED>
+hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  return (a.kv_split > 0 && dtype != ATTN_F32) ? launch_split<KIND, SOFTCAP, PADDED, true>(dtype, a, stream)
+                                               : launch_split<KIND, SOFTCAP, PADDED, false>(dtype, a, stream);
+}
+
+template <int KIND, bool PADDED>
+hipError_t launch_softcap(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  return a.softcap > 0.0f ? launch_kind<KIND, true, PADDED>(dtype, a, stream)
+                          : launch_kind<KIND, false, PADDED>(dtype, a, stream);
+}
+
+// Key padding has kernels of its own, so the unpadded ones carry no range
+// tests.
+template <int KIND>
+hipError_t launch_padded(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  return (a.key_start != nullptr || a.key_end != nullptr) ? launch_softcap<KIND, true>(dtype, a, stream)
+                                                          : launch_softcap<KIND, false>(dtype, a, stream);
+}
+
+}  // namespace
+
+// Launch of the forward for one mask family (defined in fwd_<family>.hip).
+template <int KIND>
+hipError_t launch_family(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  return launch_padded<KIND>(dtype, a, stream);
+}
+
+}  // namespace bsattn

@@ -70,11 +70,16 @@ struct FwdArgs {
   int32_t split;
   int32_t* counters;
   float* partials;
+  // Split-KV (kv_split_count > 0): every query block's visit list is cut into
+  // kv_split contiguous chunks, one work item each; the items leave row-major
+  // partial results and a second kernel merges them.
+  int32_t kv_split;
 };
 
 // Partial result of one split item: the 4 waves' O^T accumulators in
-// register order ([wave][32 registers][64 lanes]), then the running max and
-// the sum of each of the 128 rows. Slots are [query block][chunk][B*H].
+// register order ([wave][32 registers][64 lanes]) -- for split-KV items the
+// rows' O row-major ([128 rows][64]) -- then the running max and the sum of
+// each of the 128 rows. Slots are [query block][chunk][B*H].
 constexpr int64_t kSlotFloats = 4 * 32 * 64 + 2 * kBlock;
 // Long query blocks are split only when there are few work items.
 constexpr int64_t kSplitMaxItems = 2048;
@@ -88,7 +93,23 @@ inline bool use_split(int32_t dtype, int64_t bh, int32_t nq) {
 // never sees an earlier call's partial results where a later call keeps its
 // counters, and every call leaves all counters at zero.
 constexpr size_t kCountersBytes = kSplitMaxItems * sizeof(int32_t);
-inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq) {
+// Split-KV for shapes with few query blocks (decode: a few queries against a
+// long key sequence): with B*H*nq items the GPU would idle, so each query
+// block's kv blocks are cut into k chunks, k chosen from the shape alone
+// (about kKvSplitTarget items, at least two kv blocks per chunk, at most
+// kKvSplitMax), when that gives more than the two-way split of the plan.
+constexpr int64_t kKvSplitTarget = 1024;
+constexpr int32_t kKvSplitMax = 64;
+inline int32_t kv_split_count(int32_t dtype, int64_t bh, int32_t nq, int32_t nk) {
+  if (dtype == 0 /* ATTN_F32 */ || nq <= 0 || bh <= 0) return 0;
+  int64_t k = (kKvSplitTarget + bh * nq - 1) / (bh * nq);
+  k = k < kKvSplitMax ? k : kKvSplitMax;
+  k = k < nk / 2 ? k : nk / 2;
+  return k >= 3 ? (int32_t)k : 0;
+}
+inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq, int32_t nk) {
+  const int32_t ks = kv_split_count(dtype, bh, nq, nk);
+  if (ks > 0) return kCountersBytes + (size_t)nq * ks * (size_t)bh * kSlotFloats * sizeof(float);
   if (!use_split(dtype, bh, nq)) return 0;
   return kCountersBytes + (size_t)nq * kMaxChunks * (size_t)bh * kSlotFloats * sizeof(float);
 }

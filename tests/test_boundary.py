@@ -232,6 +232,11 @@ def test_workspace_size():
     assert _ws_size(1, 1, 32, 8192) == counters + 64 * 2 * 32 * slot  # 2048 items
     assert _ws_size(1, 1, 33, 8192) == 0           # many items: no split
     assert _ws_size(1, 1, 8, 0) == 0               # no query blocks
+    # decode (one query block, many kv blocks): split-KV, k = min(64,
+    # ceil(1024 / (B*H*nq)), nk / 2) chunks of one slot each
+    assert _ws_size(1, 1, 8, 1, 8192) == counters + 1 * 32 * 8 * slot      # k = 32
+    assert _ws_size(2, 4, 32, 16, 8192) == counters + 1 * 8 * 128 * slot   # k = 8
+    assert _ws_size(1, 1, 8, 1, 640) == counters + 1 * 2 * 8 * slot        # nk = 5: two-way split
 
 
 @no_gpu

@@ -178,6 +178,18 @@ SMALL = [
     _odd("causal_4352_bf16_split", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL),
     _odd("document_4400_f16_split", "f16", 1, 4400, 4400, wl.MASK_DOCUMENT, 0, (600, 2500), 30.0),
     _odd("none_3000x4300_bf16_split", "bf16", 1, 3000, 4300, wl.MASK_NONE),
+    # 34 query blocks x 16 heads: the plan's two-way split (fewer heads split
+    # the kv range instead, below)
+    _odd("causal_4352_h16_bf16_plan_split", "bf16", 16, 4352, 4352, wl.MASK_CAUSAL),
+    # decode and other few-query-block shapes: split-KV chunks and their merge
+    _odd("decode_L1_S8192_lr_bf16", "bf16", 8, 1, 8192, wl.MASK_CAUSAL_LOWER_RIGHT, B=2),
+    _odd("decode_L16_S5000_lr_f16", "f16", 4, 16, 5000, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("decode_L64_S3000_none_bf16", "bf16", 2, 64, 3000, wl.MASK_NONE, B=3),
+    _odd("decode_L1_S9000_window_bf16", "bf16", 4, 1, 9000, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 1000),
+    _odd("decode_L3_S4000_doc_softcap_f16", "f16", 2, 3, 4000, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0,
+         (1000, 3500), 30.0),
+    _odd("decode_gqa_L1_S6000_bf16", "bf16", 16, 1, 6000, wl.MASK_CAUSAL_LOWER_RIGHT, B=2).with_(H_kv=4),
+    _odd("causal_2000_h1_bf16_kv_split", "bf16", 1, 2000, 2000, wl.MASK_CAUSAL),
     # mask variants and grouped-query attention
     _odd("causal_lr_L200_S700_bf16", "bf16", 2, 200, 700, wl.MASK_CAUSAL_LOWER_RIGHT),
     _odd("causal_lr_L700_S200_f16", "f16", 1, 700, 200, wl.MASK_CAUSAL_LOWER_RIGHT),
@@ -220,7 +232,8 @@ FULL = [wl.WORKLOADS[n] for n in ("causal_8192_bf16", "sliding_8192_w64_bf16",
                                   "sliding_8192_w4096_bf16", "sliding_32768_w256_bf16",
                                   "document_8192_f16_softcap", "causal_lower_right_2048x8192_bf16",
                                   "gqa_causal_8192_h32_kv8_bf16",
-                                  "document_bidirectional_8192_f16_softcap")]
+                                  "document_bidirectional_8192_f16_softcap",
+                                  "decode_gqa_b8_h32_kv8_s8192_bf16")]
 
 
 @pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
@@ -257,6 +270,8 @@ PADDED = [
      ([128, 0], [900, 700])),
     (_odd("pad_bidir_doc_f16", "f16", 2, 640, 640, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (200, 500), B=2),
      ([64, 0], [640, 300])),
+    (_odd("pad_decode_L1_S7000_bf16", "bf16", 4, 1, 7000, wl.MASK_CAUSAL_LOWER_RIGHT, B=3),
+     ([0, 2500, 0], [7000, 6000, 900])),
 ]
 
 

@@ -28,6 +28,10 @@ Variant workloads (the mask and head-sharing variants of the same kernel):
   (same page, section 5), L=S=8192, causal.
 * ``document_bidirectional_8192_f16_softcap`` -- the document workload's
   shape and ids with the bidirectional (block-diagonal) document mask.
+* ``decode_gqa_b8_h32_kv8_s8192_bf16`` -- decode: one new query per sequence
+  (L=1) against S=8192 cached keys, B=8 sequences, 32 query heads sharing 8
+  K/V heads, bottom-right causal (the query sees every key: SDPA page,
+  section 4, pitfall 3, KV-cache inference; section 5, GQA).
 * ``causal_8192_keypad_b2_bf16`` -- B=2, H=8, L=S=8192 causal with key
   padding: batch entry 0 keeps every key, entry 1 keys [2048, 7168) (left
   and right padding ANDed with the causal mask; SDPA page, section 4,
@@ -113,6 +117,8 @@ WORKLOADS = {
                  MASK_DOCUMENT_BIDIRECTIONAL, 0, (2048, 5000), 30.0),
         Workload("causal_8192_keypad_b2_bf16", 2, 8, 8192, 8192, 64, "bf16", MASK_CAUSAL,
                  key_ranges=((0, 8192), (2048, 7168))),
+        Workload("decode_gqa_b8_h32_kv8_s8192_bf16", 8, 32, 1, 8192, 64, "bf16",
+                 MASK_CAUSAL_LOWER_RIGHT, H_kv=8),
     ]
 }
 
