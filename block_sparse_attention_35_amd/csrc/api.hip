@@ -200,6 +200,11 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
     a.counters = static_cast<int32_t*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + bsattn::kCountersBytes);
   }
+  if (bsattn::use_packed(dtype, L, H / H_kv)) {
+    a.pack_split = bsattn::packed_split_count((int64_t)B * H_kv, bm->num_kv_blocks, need);
+    a.kv_split = 0;
+    a.split = 0;
+  }
 
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
   a.B = B, a.H = H, a.L = L, a.S = S;

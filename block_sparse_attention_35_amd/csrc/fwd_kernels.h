@@ -218,6 +218,12 @@ __device__ inline void barrier_only() {
 // | vmcnt[5:4] << 14), leaving the other counters unconstrained.
 __device__ inline void wait_vm_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Wait until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Block index lists are read through the constant address space so the loads
 // are scalar (they never change during a launch).
@@ -330,7 +336,8 @@ struct LanePtrs {
   lds_u8 v[2];
 };
 
-__device__ inline LanePtrs make_lane_ptrs(const Lds& lds, int lane) {
+template <class LdsT>
+__device__ inline LanePtrs make_lane_ptrs(const LdsT& lds, int lane) {
   LanePtrs p;
   const int lq = lane & 31, hf = lane >> 5;
   const lds_u8 kb = (lds_u8)lds.k[0].k;
@@ -1021,39 +1028,376 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   }
 }
 
-// Merge of split-KV chunks: one workgroup per (query block, batch*head), one
-// thread per (row, head dim) of four rows at a time; for each row, weights
-// w_c = 2^(m_c - max m) over the chunks in chunk order, O = sum w_c O_c /
-// sum w_c l_c (0 without any live key), lse = (max m + log2 sum w_c l_c) ln 2.
+// Merge of one output row over the k <= 64 chunks of a split visit list.
+// Chunk c's partial result sits at slot0 + c * cstride: the row's
+// unnormalised O (64 floats) at o_off, its max (log2 units) at m_off and its
+// sum at l_off. Thread t takes chunk t / 4 and head dims 16 (t % 4) .. +15,
+// so every load is in flight at once; with w_c = 2^(m_c - max m) (0 for a
+// chunk without live keys), O = sum w_c O_c / sum w_c l_c (0 when the sum is
+// 0) and lse = (max m + log2 sum w_c l_c) ln 2, the sums taken in chunk
+// order through LDS.
+template <typename T>
+__device__ inline void merge_row(const float* slot0, int64_t cstride, int o_off, int m_off, int l_off, int k,
+                                 T* out, float* lse) {
+  static_assert(kThreads == 4 * kKvSplitMax, "one thread per (chunk, quarter row)");
+  __shared__ float s_m[kKvSplitMax], s_wl[kKvSplitMax];
+  __shared__ float s_o[kKvSplitMax][kHeadDim + 4];
+  const int t = threadIdx.x, c = t >> 2, e0 = (t & 3) * 16;
+  float m = -INFINITY, lc = 0.0f;
+  float4 o[4];
+  if (c < k) {
+    const float* sl = slot0 + c * cstride;
+    m = sl[m_off];
+    lc = sl[l_off];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = *reinterpret_cast<const float4*>(sl + o_off + e0 + 4 * u);
+    if ((t & 3) == 0) s_m[c] = m;
+  }
+  __syncthreads();
+  float mmax = -INFINITY;
+  for (int cc = 0; cc < k; ++cc) mmax = fmaxf(mmax, s_m[cc]);
+  if (c < k) {
+    const float w = (m == -INFINITY) ? 0.0f : fast_exp2(m - mmax);
+    if ((t & 3) == 0) s_wl[c] = w * lc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s_o[c][e0 + 4 * u + 0] = w * o[u].x;
+      s_o[c][e0 + 4 * u + 1] = w * o[u].y;
+      s_o[c][e0 + 4 * u + 2] = w * o[u].z;
+      s_o[c][e0 + 4 * u + 3] = w * o[u].w;
+    }
+  }
+  __syncthreads();
+  if (t < kHeadDim) {
+    float acc = 0.0f, lsum = 0.0f;
+    for (int cc = 0; cc < k; ++cc) {
+      acc += s_o[cc][t];
+      lsum += s_wl[cc];
+    }
+    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+    out[t] = (T)(acc * inv);
+    if (lse != nullptr && t == 0)
+      *lse = (lsum > 0.0f) ? (mmax + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+// Merge of split-KV chunks: one workgroup per output row (query block qb,
+// row r of it, batch*head bh); slots are [qb][chunk][B*H].
 template <typename T>
 __global__ __launch_bounds__(kThreads) void kv_merge_kernel(FwdArgs a) {
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH, qb = blockIdx.x / BH;
+  const int bh = blockIdx.x % BH, rq = blockIdx.x / BH;
+  const int qi = rq, qb = rq / kBlock, row = rq % kBlock;
+  if (qi >= a.L) return;
   const int b = bh / a.H, h = bh % a.H;
   const int k = a.kv_split;
-  const int rows = min(kBlock, a.L - qb * kBlock);
   const float* slot0 = a.partials + ((int64_t)qb * k * BH + bh) * kSlotFloats;
-  const int64_t cstride = (int64_t)BH * kSlotFloats;  // next chunk's slot
-  T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
-  for (int r0 = 0; r0 < rows; r0 += kThreads / kHeadDim) {
-    const int row = r0 + threadIdx.x / kHeadDim, e = threadIdx.x % kHeadDim;
-    if (row >= rows) break;
-    float m_new = -INFINITY;
-    for (int c = 0; c < k; ++c) m_new = fmaxf(m_new, slot0[c * cstride + 4 * 32 * 64 + row]);
-    float acc = 0.0f, lsum = 0.0f;
-    for (int c = 0; c < k; ++c) {
-      const float* sl = slot0 + c * cstride;
-      const float mc = sl[4 * 32 * 64 + row];
-      const float w = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - m_new);
-      acc = (c == 0) ? w * sl[row * kHeadDim + e] : fmaf(w, sl[row * kHeadDim + e], acc);
-      lsum = (c == 0) ? w * sl[4 * 32 * 64 + kBlock + row] : fmaf(w, sl[4 * 32 * 64 + kBlock + row], lsum);
-    }
-    const int qi = qb * kBlock + row;
-    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
-    og[(int64_t)qi * a.o_sl + e] = (T)(acc * inv);
-    if (a.lse != nullptr && e == 0)
-      a.lse[(int64_t)bh * a.L + qi] = (lsum > 0.0f) ? (m_new + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+  merge_row<T>(slot0, (int64_t)BH * kSlotFloats, row * kHeadDim, 4 * 32 * 64 + row, 4 * 32 * 64 + kBlock + row, k,
+               static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl,
+               a.lse == nullptr ? nullptr : a.lse + (int64_t)bh * a.L + qi);
+}
+
+// ---------------------------------------------------------------------------
+// Packed-row kernel: few query rows per K/V head (decode, short queries)
+// ---------------------------------------------------------------------------
+// When the L queries of the G query heads that share one K/V head number at
+// most 32 rows, they fill the N side of one 32 x 32 MFMA tile: packed row
+// r = g L + l (query head hk G + g, query l). A work item is one (batch, K/V
+// head, chunk of the visit list), so K and V are read once per K/V head and
+// no MFMA column goes to rows past L, as it would in a 128-row query tile.
+// Each wave takes its own 32 keys of every 128-key block (keys 32w .. 32w+31),
+// copies exactly those K and V rows into its part of each LDS stage and keeps
+// its own running max and sum: inside the loop the waves never wait on each
+// other, and each keeps kPackStages - 1 blocks of copies in flight. At the
+// end the four waves' (max, sum, O) combine through LDS: into the output when
+// the item holds the whole visit list, else into the item's partial slot,
+// which packed_merge_kernel combines over the chunks.
+constexpr int kPackStages = 2;
+
+template <int NS>
+struct alignas(16) PackLds {
+  KStage k[NS];
+  VStage v[NS];
+  uint8_t q[kPackRows * 128];  // the packed rows' Q, row-major
+  int32_t doc_q[kPackRows];    // document id of each packed row's query
+};
+// Row stride (floats) of each wave's O in the combine area: 4 floats of
+// padding spread the rows over the LDS banks.
+constexpr int kPackORow = kHeadDim + 4;
+static_assert(sizeof(float) * 4 * kPackRows * (kPackORow + 2) <=
+                  (sizeof(KStage) + sizeof(VStage)) * kPackStages,
+              "the combine area fits in the stages");
+
+template <typename T, int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void packed_kernel(FwdArgs a) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  typedef __attribute__((address_space(3))) const x8 lds_x8;
+  constexpr int NS = kPackStages;
+  // vector memory operations one wave issues per block: 4 K, 4 V copies (and
+  // the keys' document ids)
+  constexpr int kPerBlock = (KIND == ATTN_MASK_DOCUMENT) ? 9 : 8;
+  static_assert((NS - 1) * kPerBlock < 64, "copies in flight fit vmcnt");
+  __shared__ PackLds<NS> lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int G = a.kv_group, Hk = a.H / G, k = a.pack_split;
+  const int R = a.L * G;  // packed rows in use (<= 32)
+  const int bk = blockIdx.x % (a.B * Hk), chunk = blockIdx.x / (a.B * Hk);
+  const int b = bk / Hk, hk = bk % Hk;
+  const float c1 = a.scale * kLog2e;
+
+  const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + hk * a.v_sh;
+  // Kept keys [klo, khi) of this batch entry (all of [0, S) without padding).
+  int klo = 0, khi = a.S;
+  if (a.key_start != nullptr) klo = min(max(((const_i32_ptr)a.key_start)[b], 0), a.S);
+  if (a.key_end != nullptr) khi = max(min(((const_i32_ptr)a.key_end)[b], a.S), klo);
+
+  // The one query block's visit list (full blocks first), cut into k chunks.
+  const int nfull = ((const_i32_ptr)a.m.full_num)[0];
+  const int nblk = nfull + ((const_i32_ptr)a.m.kv_num)[0];
+  const const_i32_ptr full_list = (const_i32_ptr)a.m.full_idx;
+  const const_i32_ptr part_list = (const_i32_ptr)a.m.kv_idx;
+  auto kv_start = [&](int n) { return (n < nfull ? full_list[n] : part_list[n - nfull]) * kBlock; };
+  const int m_begin = (int)((int64_t)chunk * nblk / k);
+  const int m_end = (int)((int64_t)(chunk + 1) * nblk / k);
+
+  // Q of the packed rows, 8 rows per wave (rows past R repeat row 0; their
+  // results are never stored), and the rows' document ids.
+  {
+    const int r = wave * 8 + (lane >> 3);
+    const int rr = r < R ? r : 0;
+    const T* src = static_cast<const T*>(a.q) + b * a.q_sb + (hk * G + rr / a.L) * a.q_sh +
+                   (int64_t)(rr % a.L) * a.q_sl + (lane & 7) * 8;
+    lds_copy16(src, lds_offset(lds.q) + (uint32_t)wave * 1024u);
+    if (KIND == ATTN_MASK_DOCUMENT && wave == 0 && lane < 32)
+      lds_copy4(a.m.doc + (lq < R ? lq % a.L : 0), lds_offset(lds.doc_q));
   }
+  const uint32_t k_off =
+      (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  const uint32_t v_off = (uint32_t)((lane >> 3) * a.v_sl * (int64_t)sizeof(T)) +
+                         (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+  auto issue = [&](int kv0, int st) __attribute__((always_inline)) {
+    issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv0, a.S, lds.k[st], wave, lane);
+    issue_rows<T, true>(vg, a.v_sl, v_off, kv0, a.S, lds.v[st].v, wave, lane);
+  };
+  // Blocks m_begin .. m_begin + NS - 2 go out first; block m then refills the
+  // stage of block m - 1 with block m + NS - 1. The first key of the block
+  // to copy next is loaded one block ahead.
+  const int nb = m_end - m_begin;
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nb) issue(kv_start(m_begin + i), i);
+  int kv_issue = (nb > NS - 1) ? kv_start(m_begin + NS - 1) : 0;
+  // Wait for Q (issued before every block copy), then share it.
+  const int pro = min(NS - 1, nb);
+  switch (pro) {  // blocks issued after Q
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<kPerBlock>(); break;
+    case 2: wait_vm<2 * kPerBlock>(); break;
+    default: wait_vm<3 * kPerBlock>(); break;
+  }
+  barrier_only();
+  x8 qop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qop[c] = *reinterpret_cast<const lds_x8*>((lds_u8)lds.q + lq * 128 + (2 * c + hf) * 16);
+  const int lrow = lq % a.L;                   // this lane's query
+  const int p = lrow + a.m.q_off;              // its rule position
+  const int32_t dq = (KIND == ATTN_MASK_DOCUMENT) ? lds.doc_q[lq] : 0;
+
+  const LanePtrs lp = make_lane_ptrs(lds, lane);
+  f32x16_t oacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[te][r] = 0.0f;
+  float m_ref = -INFINITY, l = 0.0f;
+
+  int st = 0;  // stage of block m
+  for (int m = m_begin; m < m_end; ++m) {
+    const int kv0 = kv_start(m);
+    wait_lgkm_zero();  // this wave's reads of block m - 1, and the list loads
+    switch (min(NS - 2, m_end - 1 - m)) {  // blocks issued after block m
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<kPerBlock>(); break;
+      default: wait_vm<2 * kPerBlock>(); break;
+    }
+    if (m + NS - 1 < m_end) {
+      issue(kv_issue, st == 0 ? NS - 1 : st - 1);
+      if (m + NS < m_end) kv_issue = kv_start(m + NS);
+    }
+    const bool full = m < nfull && kv0 >= klo && kv0 + kBlock <= khi;
+    if (kv0 + kBlock <= klo || kv0 >= khi) {  // no kept key
+      st = (st + 1 == NS) ? 0 : st + 1;
+      continue;
+    }
+    // S^T = K Q^T for this wave's 32 keys (tile `wave` of the block).
+    f32x16_t s = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const x8 kf = *reinterpret_cast<const lds_x8*>(lp.k[c] + st * (int)sizeof(KStage) + wave * 4096);
+      s = V::mma(kf, qop[c], s);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[r];
+      if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
+      if (!full) {
+        const int jl = wave * 32 + acc_row(r, hf);
+        const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? lds.k[st].doc[jl] : 0;
+        if (!pair_live<KIND>(p, kv0 + jl, khi, a.m.window, dq, dj) || kv0 + jl < klo) x = -INFINITY;
+      }
+      s[r] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = half_max(mx);
+    const float m_blk = SOFTCAP ? mx : mx * c1;
+    const bool grow = m_blk > m_ref + kRescaleLog2;
+    if (__ballot(grow) != 0) {
+      const float alpha = grow ? fast_exp2(m_ref - m_blk) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int te = 0; te < 2; ++te)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[te][r] *= alpha;
+    }
+    if (grow) m_ref = m_blk;
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    // Probabilities, rounded to T for P V; the sum takes the rounded values.
+    x8 pk[2];
+    float psum[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        const float x0 = s[gi * 8 + u], x1 = s[gi * 8 + u + 1];
+        const float p0 = SOFTCAP ? fast_exp2(x0 - m_use) : fast_exp2(fmaf(x0, c1, -m_use));
+        const float p1 = SOFTCAP ? fast_exp2(x1 - m_use) : fast_exp2(fmaf(x1, c1, -m_use));
+        const typename V::x2 pr = {(T)p0, (T)p1};
+        psum[(u >> 1) & 1] = V::add_pair(pr, psum[(u >> 1) & 1]);
+        pk[gi][u] = pr[0];
+        pk[gi][u + 1] = pr[1];
+      }
+    l += psum[0] + psum[1];
+    // O^T += V^T P^T over the wave's two 16-key groups (2 wave, 2 wave + 1).
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int te = 0; te < 2; ++te) {
+        const lds_u8 vb = lp.v[te] + st * (int)sizeof(VStage) + (2 * wave + gi) * 2048;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 1024));
+        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[te] = V::mma(__builtin_bit_cast(x8, both), pk[gi], oacc[te]);
+      }
+    st = (st + 1 == NS) ? 0 : st + 1;
+  }
+  const float lt = half_sum(l);
+
+  // Combine the four waves: every copy has landed (the last block waited for
+  // all), so once every wave's reads are done the stages hold each wave's
+  // max, sum and O (row r, head dims te 32 + 8q + 4hf .. +3 in registers
+  // 4q .. 4q+3 of tile te).
+  wait_lgkm_zero();
+  barrier_only();
+  float* cm = reinterpret_cast<float*>(&lds);       // [4][32] maxima
+  float* cl = cm + 4 * kPackRows;                   // [4][32] sums
+  float* co = cl + 4 * kPackRows;                   // [4][32][kPackORow] O
+  if (hf == 0) {
+    cm[wave * kPackRows + lq] = m_ref;
+    cl[wave * kPackRows + lq] = lt;
+  }
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 o4 = {oacc[te][4 * q4], oacc[te][4 * q4 + 1], oacc[te][4 * q4 + 2], oacc[te][4 * q4 + 3]};
+      *reinterpret_cast<float4*>(co + (wave * kPackRows + lq) * kPackORow + te * 32 + 8 * q4 + 4 * hf) = o4;
+    }
+  wait_lgkm_zero();
+  barrier_only();
+  // Thread: packed row tid / 8, head dims 8 (tid % 8) .. +7; waves in order.
+  const int row = tid >> 3, e0 = (tid & 7) * 8;
+  if (row >= R) return;
+  float mw[4], wt[4];
+  float mmax = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = cm[w * kPackRows + row];
+    mmax = fmaxf(mmax, mw[w]);
+  }
+  float lsum = 0.0f;
+  float o8[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = (mw[w] == -INFINITY) ? 0.0f : fast_exp2(mw[w] - mmax);
+    lsum = (w == 0) ? wt[0] * cl[row] : fmaf(wt[w], cl[w * kPackRows + row], lsum);
+    const float* orow = co + (w * kPackRows + row) * kPackORow + e0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o8[u] = (w == 0) ? wt[0] * orow[u] : fmaf(wt[w], orow[u], o8[u]);
+  }
+  if (k > 1) {
+    float* slot = a.partials + ((int64_t)bk * k + chunk) * kPackSlotFloats;
+#pragma unroll
+    for (int u = 0; u < 8; u += 4)
+      *reinterpret_cast<float4*>(slot + row * kHeadDim + e0 + u) = {o8[u], o8[u + 1], o8[u + 2], o8[u + 3]};
+    if (e0 == 0) {
+      slot[kPackRows * kHeadDim + row] = mmax;
+      slot[kPackRows * kHeadDim + kPackRows + row] = lsum;
+    }
+    return;
+  }
+  const int h = hk * G + row / a.L, qi = row % a.L;
+  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+  x8 outv;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) outv[u] = (T)(o8[u] * inv);
+  *reinterpret_cast<x8*>(static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl + e0) = outv;
+  if (a.lse != nullptr && e0 == 0)
+    a.lse[((int64_t)b * a.H + h) * a.L + qi] =
+        (lsum > 0.0f) ? (mmax + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+}
+
+// Merge of the packed kernel's chunks: one workgroup per (batch, K/V head,
+// packed row); slots are [batch * K/V head][chunk].
+template <typename T>
+__global__ __launch_bounds__(kThreads) void packed_merge_kernel(FwdArgs a) {
+  const int G = a.kv_group, Hk = a.H / G, R = a.L * G;
+  const int bk = blockIdx.x / R, row = blockIdx.x % R;
+  const int b = bk / Hk, hk = bk % Hk;
+  const int h = hk * G + row / a.L, qi = row % a.L;
+  const float* slot0 = a.partials + (int64_t)bk * a.pack_split * kPackSlotFloats;
+  merge_row<T>(slot0, kPackSlotFloats, row * kHeadDim, kPackRows * kHeadDim + row,
+               kPackRows * kHeadDim + kPackRows + row, a.pack_split,
+               static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl,
+               a.lse == nullptr ? nullptr : a.lse + ((int64_t)b * a.H + h) * a.L + qi);
+}
+
+template <int KIND, bool SOFTCAP>
+hipError_t launch_packed(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  const int64_t bhk = (int64_t)a.B * (a.H / a.kv_group);
+  const dim3 grid((unsigned)(bhk * a.pack_split)), merge_grid((unsigned)(bhk * a.L * a.kv_group)),
+      block(kThreads);
+  const bool merge = a.pack_split > 1;
+  switch (dtype) {
+    case ATTN_BF16:
+      hipLaunchKernelGGL((packed_kernel<__bf16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      if (merge) hipLaunchKernelGGL(packed_merge_kernel<__bf16>, merge_grid, block, 0, stream, a);
+      break;
+    case ATTN_F16:
+      hipLaunchKernelGGL((packed_kernel<_Float16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      if (merge) hipLaunchKernelGGL(packed_merge_kernel<_Float16>, merge_grid, block, 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int KIND, bool SOFTCAP, bool PADDED, bool KVSPLIT>
@@ -1063,7 +1407,7 @@ hipError_t launch_split(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   const int64_t chunks = a.kv_split > 0 ? a.kv_split : kMaxChunks;
   const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * chunks));
   const dim3 block(kThreads);
-  const dim3 merge_grid((unsigned)((int64_t)a.B * a.H * a.m.nq));
+  const dim3 merge_grid((unsigned)((int64_t)a.B * a.H * a.L));  // one workgroup per output row
   switch (dtype) {
     case ATTN_BF16:
       hipLaunchKernelGGL((fwd16_kernel<__bf16, KIND, SOFTCAP, PADDED, KVSPLIT>), grid, block, 0, stream, a);
@@ -1085,6 +1429,7 @@ hipError_t launch_split(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
 // Split-KV items have kernels of their own, so the others keep their code.
 template <int KIND, bool SOFTCAP, bool PADDED>
 hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  if (a.pack_split > 0) return launch_packed<KIND, SOFTCAP>(dtype, a, stream);
   return (a.kv_split > 0 && dtype != ATTN_F32) ? launch_split<KIND, SOFTCAP, PADDED, true>(dtype, a, stream)
                                                : launch_split<KIND, SOFTCAP, PADDED, false>(dtype, a, stream);
 }

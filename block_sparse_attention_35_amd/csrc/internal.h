@@ -74,6 +74,10 @@ struct FwdArgs {
   // kv_split contiguous chunks, one work item each; the items leave row-major
   // partial results and a second kernel merges them.
   int32_t kv_split;
+  // Packed rows (pack_split > 0): the L x G query rows of each K/V head form
+  // one 32-row tile; the visit list is cut into pack_split chunks, merged
+  // from partial results when there is more than one.
+  int32_t pack_split;
 };
 
 // Partial result of one split item: the 4 waves' O^T accumulators in
@@ -112,6 +116,32 @@ inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq, int32_t nk)
   if (ks > 0) return kCountersBytes + (size_t)nq * ks * (size_t)bh * kSlotFloats * sizeof(float);
   if (!use_split(dtype, bh, nq)) return 0;
   return kCountersBytes + (size_t)nq * kMaxChunks * (size_t)bh * kSlotFloats * sizeof(float);
+}
+
+// Packed rows: when the L queries of the G = H / H_kv query heads sharing a
+// K/V head number at most kPackRows, one work item per (batch, K/V head,
+// chunk) computes them all from one read of the K/V head. The chunk count
+// aims at kPackTarget work items (one per CU: longer chunks beat more of
+// them, and one chunk needs no merge) with at least two kv blocks each, and
+// is capped by the partial slots that fit in the workspace the shape asks
+// for (the formula above, which does not depend on H_kv or L); with one chunk
+// the items write the output directly. Slot: O [32][64] row-major, then the
+// rows' maxima [32] and sums [32].
+constexpr int kPackRows = 32;
+constexpr int64_t kPackSlotFloats = kPackRows * kHeadDim + 2 * kPackRows;
+constexpr int64_t kPackTarget = 256;
+inline bool use_packed(int32_t dtype, int32_t L, int32_t G) {
+  return dtype != 0 /* ATTN_F32 */ && L >= 1 && G >= 1 && (int64_t)L * G <= kPackRows;
+}
+inline int32_t packed_split_count(int64_t bhk, int32_t nk, size_t ws_bytes) {
+  int64_t k = (kPackTarget + bhk - 1) / bhk;
+  k = k < kKvSplitMax ? k : kKvSplitMax;
+  k = k < nk / 2 ? k : nk / 2;
+  const int64_t slots = ws_bytes > kCountersBytes
+                            ? (int64_t)((ws_bytes - kCountersBytes) / sizeof(float)) / kPackSlotFloats
+                            : 0;
+  k = k < slots / bhk ? k : slots / bhk;
+  return k >= 2 ? (int32_t)k : 1;
 }
 
 // Enqueue the block classification and the query-block schedule.

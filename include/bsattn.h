@@ -173,14 +173,21 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
 
 /*
  * Bytes of device workspace attn_forward needs for this problem (0 when it
- * needs none). The forward splits long query blocks into two work items
- * (see the work plan) when there are few query blocks for the GPU,
- * that is when B * H * num_q_blocks <= 2048 and dtype is ATTN_BF16 or
- * ATTN_F16; each split item then leaves fp32 partial results and takes a
- * ticket in the workspace, and the last item of a query block to finish
- * merges them. Layout: 8192 bytes of int32 ticket counters, then
- * num_q_blocks * 2 * B * H fp32 partial slots of (4 * 32 * 64 + 2 * 128)
- * floats each.
+ * needs none, and always for ATTN_F32). It depends on dtype, B * H and the
+ * mask's block counts nq = num_q_blocks, nk = num_kv_blocks only:
+ *   with k = min(64, ceil(1024 / (B * H * nq)), nk / 2) >= 3: split-KV, every
+ *     query block's visit list cut into k chunks whose partial results a
+ *     second kernel merges: 8192 + nq * k * B * H * 8448 * 4 bytes;
+ *   else, with B * H * nq <= 2048: long query blocks split into two work
+ *     items, the later of which merges (ticket counters):
+ *     8192 + nq * 2 * B * H * 8448 * 4 bytes;
+ *   else 0.
+ * Layout: 8192 bytes of int32 ticket counters, then fp32 partial slots.
+ * When the L queries of the H / H_kv query heads sharing a K/V head number
+ * at most 32 (decode), the forward instead packs them into one tile per K/V
+ * head and cuts the visit list into as many chunks (of 32 * 64 + 64 floats
+ * each) as the same area holds, up to its own target; with one chunk it
+ * writes the output directly.
  * Errors: INVALID_ARGUMENT for a null bm or bytes, or B, H < 1.
  */
 attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,

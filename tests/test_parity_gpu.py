@@ -190,6 +190,23 @@ SMALL = [
          (1000, 3500), 30.0),
     _odd("decode_gqa_L1_S6000_bf16", "bf16", 16, 1, 6000, wl.MASK_CAUSAL_LOWER_RIGHT, B=2).with_(H_kv=4),
     _odd("causal_2000_h1_bf16_kv_split", "bf16", 1, 2000, 2000, wl.MASK_CAUSAL),
+    # packed rows (L x G <= 32 query rows per K/V head in one tile): exactly
+    # 32 rows, a group of 5, one chunk per item (many K/V heads; few kv
+    # blocks), top-left causal at L = 1, no keys at all, document masks
+    _odd("packed_L4_G8_R32_lr_bf16", "bf16", 16, 4, 3000, wl.MASK_CAUSAL_LOWER_RIGHT, B=2).with_(H_kv=2),
+    _odd("packed_L6_G5_R30_window_f16", "f16", 10, 6, 2500, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT,
+         300).with_(H_kv=2),
+    _odd("packed_L32_G1_none_bf16", "bf16", 2, 32, 1500, wl.MASK_NONE, B=2),
+    _odd("packed_direct_1024_heads_bf16", "bf16", 128, 1, 700, wl.MASK_CAUSAL_LOWER_RIGHT, B=8),
+    _odd("packed_direct_S200_softcap_f16", "f16", 8, 2, 200, wl.MASK_NONE, 0, (), 20.0).with_(H_kv=2),
+    _odd("packed_causal_top_left_L1_S700_bf16", "bf16", 4, 1, 700, wl.MASK_CAUSAL, B=2),
+    _odd("packed_L1_S0_bf16", "bf16", 4, 1, 0, wl.MASK_NONE),
+    # 64 chunks, the most either merge takes: packed rows, and split-KV
+    _odd("packed_64_chunks_L1_S17000_bf16", "bf16", 1, 1, 17000, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("kv_split_64_chunks_L100_S17000_f16", "f16", 1, 100, 17000, wl.MASK_CAUSAL_LOWER_RIGHT),
+    _odd("packed_doc_L8_S2000_f16", "f16", 4, 8, 2000, wl.MASK_DOCUMENT, 0, (5, 700, 1500)).with_(H_kv=1),
+    _odd("packed_doc_bidir_L2_S3000_softcap_bf16", "bf16", 8, 2, 3000, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0,
+         (1, 1200), 30.0).with_(H_kv=4),
     # mask variants and grouped-query attention
     _odd("causal_lr_L200_S700_bf16", "bf16", 2, 200, 700, wl.MASK_CAUSAL_LOWER_RIGHT),
     _odd("causal_lr_L700_S200_f16", "f16", 1, 700, 200, wl.MASK_CAUSAL_LOWER_RIGHT),
@@ -272,6 +289,10 @@ PADDED = [
      ([64, 0], [640, 300])),
     (_odd("pad_decode_L1_S7000_bf16", "bf16", 4, 1, 7000, wl.MASK_CAUSAL_LOWER_RIGHT, B=3),
      ([0, 2500, 0], [7000, 6000, 900])),
+    (_odd("pad_packed_gqa_L2_S5000_bf16", "bf16", 8, 2, 5000, wl.MASK_CAUSAL_LOWER_RIGHT, B=3).with_(H_kv=2),
+     ([0, 1000, 4999], [5000, 3333, 5000])),
+    (_odd("pad_packed_window_L1_f16", "f16", 4, 1, 4000, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 700, B=2),
+     ([3500, 0], [4000, 2000])),
 ]
 
 
