@@ -173,31 +173,38 @@ def summarize(w: wl.Workload, r):
         "forward_tflops": flops / (fwd_avg * 1e-3) / 1e12,
         "forward_frac_bf16_peak": flops / (fwd_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "forward_gbs": nbytes / (fwd_avg * 1e-3) / 1e9,
+        "forward_frac_hbm_peak": nbytes / (fwd_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "dominant_kernel_traffic": measured_traffic(w.name),
         "mask_build_ms": {"mean": float(r["mask_ms"].mean()), "median": float(np.median(r["mask_ms"]))},
         "live_gflop": flops / 1e9,
         "algorithmic_bytes": nbytes,
     }
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
-                               "fwd16_causal_8192_sliding_32768_w256_hbm_traffic.md")
+TRAFFIC_PROFILES = [os.path.join(ROOT, "profiles", f) for f in (
+    "fwd16_causal_8192_sliding_32768_w256_hbm_traffic.md",
+    "packed_decode_gqa_b8_h32_kv8_s8192_hbm_traffic.md")]
 FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_35_amd", "csrc", "fwd_kernels.h")
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per forward launch from the committed rocprofv3 counter
-    summary, or None when the forward source has changed since it was taken."""
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 counter summaries, or None when the forward source has
+    changed since they were taken."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
         src_hash = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()[:16]
     except OSError:
         return None
-    for line in text.splitlines():
-        if line.startswith("traffic-bytes "):
-            fields = dict(f.split("=", 1) for f in line.split()[1:])
-            if fields.get("source") != src_hash or workload not in fields:
-                return None
-            return int(fields[workload])
+    for path in TRAFFIC_PROFILES:
+        try:
+            text = open(path).read()
+        except OSError:
+            continue
+        for line in text.splitlines():
+            if line.startswith("traffic-bytes "):
+                fields = dict(f.split("=", 1) for f in line.split()[1:])
+                if fields.get("source") == src_hash and workload in fields:
+                    return int(fields[workload])
     return None
 
 
