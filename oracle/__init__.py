@@ -9,7 +9,8 @@ the passages they follow are cited in ``oracle.c``:
 
 Mask kinds: NONE, CAUSAL, SLIDING, DOCUMENT, and the variants
 CAUSAL_LOWER_RIGHT, SLIDING_LOWER_RIGHT (query position shifted by S - L) and
-DOCUMENT_BIDIRECTIONAL (same document, no causal part).
+DOCUMENT_BIDIRECTIONAL (same document, no causal part); DENSE reads a
+user-supplied L x S boolean mask (True keeps the pair).
 
 * ``attention``   -- softmax(Q K^T * scale + mask bias) V per row, optional
   per-batch key padding (a kept key range ANDed with the mask), optional
@@ -18,6 +19,8 @@ DOCUMENT_BIDIRECTIONAL (same document, no causal part).
 * ``block_mask``  -- 128x128 block classification by brute force over every
   in-range pair: skip / partial / full, with ascending index lists padded by 0.
 * ``count_live``  -- number of live (query, key) pairs of a mask.
+* ``pack_mask``   -- bit-packed form of a dense boolean mask: row i is
+  4 * ceil(S / 128) uint32 words, bit b of word w is M[i, 32 w + b].
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against values the
 pages print, closed forms, invariances and library routines.
@@ -37,6 +40,7 @@ _LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
 
 NONE, CAUSAL, SLIDING, DOCUMENT = 0, 1, 2, 3
 CAUSAL_LOWER_RIGHT, SLIDING_LOWER_RIGHT, DOCUMENT_BIDIRECTIONAL = 4, 5, 6
+DENSE = 7
 _DOC_KINDS = (DOCUMENT, DOCUMENT_BIDIRECTIONAL)
 
 
@@ -66,6 +70,18 @@ def _doc(doc) -> Optional[np.ndarray]:
     return None if doc is None else np.ascontiguousarray(doc, dtype=np.int32)
 
 
+def _dense(kind, mask, L, S) -> Optional[np.ndarray]:
+    """The DENSE kind's mask as contiguous bytes [L, S] (None for other kinds)."""
+    if kind != DENSE:
+        return None
+    if mask is None:
+        raise ValueError("the DENSE kind needs a mask")
+    m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    if m.shape != (L, S):
+        raise ValueError(f"mask shape {m.shape} is not (L, S) = ({L}, {S})")
+    return m
+
+
 class Oracle:
     """ctypes front end over one compiled copy of the oracle."""
 
@@ -73,18 +89,21 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         i64, i32p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
         f64p = ctypes.POINTER(ctypes.c_double)
+        u8p, u32p = ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_uint32)
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_live.restype = ctypes.c_int
-        lib.oracle_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64, i64, i64]
+        lib.oracle_live.argtypes = [ctypes.c_int, i64, i32p, u8p, i64, i64, i64, i64]
         lib.oracle_count_live.restype = i64
-        lib.oracle_count_live.argtypes = [ctypes.c_int, i64, i32p, i64, i64]
+        lib.oracle_count_live.argtypes = [ctypes.c_int, i64, i32p, u8p, i64, i64]
         lib.oracle_block_mask.restype = ctypes.c_int
-        lib.oracle_block_mask.argtypes = [ctypes.c_int, i64, i32p, i64, i64, i64,
+        lib.oracle_block_mask.argtypes = [ctypes.c_int, i64, i32p, u8p, i64, i64, i64,
                                           i32p, i32p, i32p, i32p]
+        lib.oracle_pack_mask.restype = ctypes.c_int
+        lib.oracle_pack_mask.argtypes = [u8p, i64, i64, u32p]
         lib.oracle_attention.restype = ctypes.c_int
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.oracle_attention.argtypes = [f64p, f64p, f64p, i64, i64, i64, i64, i64, i64,
-                                         ctypes.c_int, i64, i32p, ctypes.c_double,
+                                         ctypes.c_int, i64, i32p, u8p, ctypes.c_double,
                                          ctypes.c_double, i64p, i64p, i64p, i64, f64p, f64p]
         self._lib = lib
 
@@ -97,28 +116,47 @@ class Oracle:
         return int(self._lib.oracle_num_threads())
 
     def live(self, kind: int, i: int, j: int, window: int = 0, doc=None, L: int = 0,
-             S: int = 0) -> bool:
+             S: int = 0, mask=None) -> bool:
         """The predicate for query i and key j (L and S matter only to the
-        lower-right kinds)."""
+        lower-right kinds and DENSE)."""
         d = _doc(doc)
-        return bool(self._lib.oracle_live(kind, window, _ptr(d, ctypes.c_int32), L, S, i, j))
+        m = _dense(kind, mask, L, S)
+        if m is not None and not (0 <= i < L and 0 <= j < S):
+            raise ValueError("pair outside the mask")
+        return bool(self._lib.oracle_live(kind, window, _ptr(d, ctypes.c_int32),
+                                          _ptr(m, ctypes.c_uint8), L, S, i, j))
 
-    def count_live(self, kind: int, L: int, S: int, window: int = 0, doc=None) -> int:
+    def count_live(self, kind: int, L: int, S: int, window: int = 0, doc=None, mask=None) -> int:
         d = _doc(doc)
         self._check_doc(kind, d, L, S)
-        return int(self._lib.oracle_count_live(kind, window, _ptr(d, ctypes.c_int32), L, S))
+        m = _dense(kind, mask, L, S)
+        return int(self._lib.oracle_count_live(kind, window, _ptr(d, ctypes.c_int32),
+                                               _ptr(m, ctypes.c_uint8), L, S))
 
-    def block_mask(self, kind: int, L: int, S: int, window: int = 0, doc=None, block: int = 128):
+    def pack_mask(self, mask) -> np.ndarray:
+        """Bit-packed mask: uint32 [L, 4 * ceil(S / 128)], bit b of word w of
+        row i = mask[i, 32 w + b] (0 past S)."""
+        m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+        L, S = m.shape
+        bits = np.zeros((L, 4 * (-(-S // 128))), np.uint32)
+        if self._lib.oracle_pack_mask(_ptr(m, ctypes.c_uint8), L, S, _ptr(bits, ctypes.c_uint32)) != 0:
+            raise ValueError("oracle_pack_mask rejected its arguments")
+        return bits
+
+    def block_mask(self, kind: int, L: int, S: int, window: int = 0, doc=None, block: int = 128,
+                   mask=None):
         """(kv_num_blocks [nq], kv_indices [nq,nk], full_kv_num_blocks [nq],
         full_kv_indices [nq,nk]) as int32 arrays."""
         d = _doc(doc)
         self._check_doc(kind, d, L, S)
+        m = _dense(kind, mask, L, S)
         nq, nk = -(-L // block), -(-S // block)
         kv_num = np.zeros(nq, np.int32)
         kv_idx = np.zeros((nq, nk), np.int32)
         full_num = np.zeros(nq, np.int32)
         full_idx = np.zeros((nq, nk), np.int32)
-        rc = self._lib.oracle_block_mask(kind, window, _ptr(d, ctypes.c_int32), L, S, block,
+        rc = self._lib.oracle_block_mask(kind, window, _ptr(d, ctypes.c_int32),
+                                         _ptr(m, ctypes.c_uint8), L, S, block,
                                          _ptr(kv_num, ctypes.c_int32), _ptr(kv_idx, ctypes.c_int32),
                                          _ptr(full_num, ctypes.c_int32),
                                          _ptr(full_idx, ctypes.c_int32))
@@ -127,12 +165,13 @@ class Oracle:
         return kv_num, kv_idx, full_num, full_idx
 
     def attention(self, q, k, v, kind: int, scale: float, window: int = 0, doc=None,
-                  softcap: float = 0.0, rows=None, key_start=None, key_end=None):
+                  softcap: float = 0.0, rows=None, key_start=None, key_end=None, mask=None):
         """fp64 masked softmax attention.
 
         q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev] (any float dtype; converted to
         fp64 exactly). key_start, key_end: optional per-batch [B] kept key
-        range [start, end) (key padding, ANDed with the mask). Returns
+        range [start, end) (key padding, ANDed with the mask). mask: the
+        DENSE kind's boolean [L, S]. Returns
         (out, lse): for rows=None, out [B,H,L,Ev] and lse [B,H,L]; otherwise
         out [len(rows), Ev] and lse [len(rows)] for the flat row ids
         (b*H + h)*L + i.
@@ -146,6 +185,7 @@ class Oracle:
             raise ValueError("q/k/v shapes disagree")
         d = _doc(doc)
         self._check_doc(kind, d, L, S)
+        m = _dense(kind, mask, L, S)
         ks = None if key_start is None else np.ascontiguousarray(key_start, dtype=np.int64)
         ke = None if key_end is None else np.ascontiguousarray(key_end, dtype=np.int64)
         for a in (ks, ke):
@@ -162,7 +202,8 @@ class Oracle:
         lse = np.zeros(n, np.float64)
         rc = self._lib.oracle_attention(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
                                         _ptr(v, ctypes.c_double), B, H, L, S, E, Ev, kind, window,
-                                        _ptr(d, ctypes.c_int32), softcap, scale,
+                                        _ptr(d, ctypes.c_int32), _ptr(m, ctypes.c_uint8),
+                                        softcap, scale,
                                         _ptr(ks, ctypes.c_int64), _ptr(ke, ctypes.c_int64),
                                         _ptr(rows_arr, ctypes.c_int64), n,
                                         _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
@@ -190,18 +231,23 @@ def num_threads() -> int:
     return default().num_threads()
 
 
-def live(kind, i, j, window=0, doc=None, L=0, S=0):
-    return default().live(kind, i, j, window, doc, L, S)
+def live(kind, i, j, window=0, doc=None, L=0, S=0, mask=None):
+    return default().live(kind, i, j, window, doc, L, S, mask)
 
 
-def count_live(kind, L, S, window=0, doc=None):
-    return default().count_live(kind, L, S, window, doc)
+def count_live(kind, L, S, window=0, doc=None, mask=None):
+    return default().count_live(kind, L, S, window, doc, mask)
 
 
-def block_mask(kind, L, S, window=0, doc=None, block=128):
-    return default().block_mask(kind, L, S, window, doc, block)
+def pack_mask(mask):
+    return default().pack_mask(mask)
+
+
+def block_mask(kind, L, S, window=0, doc=None, block=128, mask=None):
+    return default().block_mask(kind, L, S, window, doc, block, mask)
 
 
 def attention(q, k, v, kind, scale, window=0, doc=None, softcap=0.0, rows=None, key_start=None,
-              key_end=None):
-    return default().attention(q, k, v, kind, scale, window, doc, softcap, rows, key_start, key_end)
+              key_end=None, mask=None):
+    return default().attention(q, k, v, kind, scale, window, doc, softcap, rows, key_start, key_end,
+                               mask)

@@ -35,6 +35,16 @@
  *    "Bonus: a score_mod for soft-capping" (score_mod changes the value, the
  *    mask decides liveness; sparsity from the mask, score_mod on survivors).
  *
+ *  - A user-supplied dense boolean mask M [L][S] (kind DENSE): the pair is
+ *    live exactly when M[i][j] is true, the boolean attn_mask convention of
+ *    page "SDPA replaces hand-written attention" (qiita GeneLab_999),
+ *    section 4, pitfall 1 (True keeps the pair); the pages build such masks
+ *    densely for SDPA and skip blocks from them for FlexAttention (page
+ *    "FlexAttention on MPS vs SDPA" (qiita kiarina), setup notes on the
+ *    32768 x 32768 boolean mask). Its bit-packed form (oracle_pack_mask):
+ *    row i holds W = 4 * ceil(S / 128) 32-bit words, bit b of word w is
+ *    M[i][32 w + b], and bits at 32 w + b >= S are 0.
+ *
  *  - Key padding: per batch entry b, only keys in [key_start[b], key_end[b])
  *    are kept, ANDed with the mask rule (padding keys never take weight).
  *    Page "SDPA replaces hand-written attention" (qiita GeneLab_999),
@@ -75,12 +85,16 @@
 #define ORACLE_CAUSAL_LOWER_RIGHT 4
 #define ORACLE_SLIDING_LOWER_RIGHT 5
 #define ORACLE_DOCUMENT_BIDIRECTIONAL 6
+#define ORACLE_DENSE 7
 
 /* The mask predicate: 1 when query i may attend to key j, for L queries and
- * S keys (the lower-right kinds shift the query position by S - L). */
-static int live(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S, int64_t i,
-                int64_t j) {
+ * S keys (the lower-right kinds shift the query position by S - L; DENSE
+ * reads the L x S byte mask, nonzero = live). */
+static int live(int kind, int64_t window, const int32_t* doc, const uint8_t* dense, int64_t L,
+                int64_t S, int64_t i, int64_t j) {
   switch (kind) {
+    case ORACLE_DENSE:
+      return dense[i * S + j] != 0;
     case ORACLE_NONE:
       return 1;
     case ORACLE_CAUSAL:
@@ -111,18 +125,19 @@ int oracle_num_threads(void) {
 }
 
 /* Evaluate the predicate itself (used by the tests to count live pairs). */
-int oracle_live(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S, int64_t i,
-                int64_t j) {
-  return live(kind, window, doc, L, S, i, j);
+int oracle_live(int kind, int64_t window, const int32_t* doc, const uint8_t* dense, int64_t L,
+                int64_t S, int64_t i, int64_t j) {
+  return live(kind, window, doc, dense, L, S, i, j);
 }
 
 /* Number of live pairs over [0,L) x [0,S). */
-int64_t oracle_count_live(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S) {
+int64_t oracle_count_live(int kind, int64_t window, const int32_t* doc, const uint8_t* dense,
+                          int64_t L, int64_t S) {
   int64_t total = 0;
 #pragma omp parallel for reduction(+ : total) schedule(dynamic, 16)
   for (int64_t i = 0; i < L; ++i) {
     int64_t c = 0;
-    for (int64_t j = 0; j < S; ++j) c += live(kind, window, doc, L, S, i, j);
+    for (int64_t j = 0; j < S; ++j) c += live(kind, window, doc, dense, L, S, i, j);
     total += c;
   }
   return total;
@@ -135,8 +150,8 @@ int64_t oracle_count_live(int kind, int64_t window, const int32_t* doc, int64_t 
  * with nq = ceil(L/bs), nk = ceil(S/bs). A block is full only when all
  * bs*bs of its pairs are in range and live. Returns 0, or -1 on bad sizes.
  */
-int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, int64_t S,
-                      int64_t bs, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
+int oracle_block_mask(int kind, int64_t window, const int32_t* doc, const uint8_t* dense, int64_t L,
+                      int64_t S, int64_t bs, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
                       int32_t* full_idx) {
   if (L < 0 || S < 0 || bs <= 0) return -1;
   int64_t nq = (L + bs - 1) / bs, nk = (S + bs - 1) / bs;
@@ -151,7 +166,7 @@ int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, i
       int64_t count = 0;
       for (int64_t i = qb * bs; i < (qb + 1) * bs && i < L; ++i)
         for (int64_t j = kb * bs; j < (kb + 1) * bs && j < S; ++j)
-          count += live(kind, window, doc, L, S, i, j);
+          count += live(kind, window, doc, dense, L, S, i, j);
       if (count == 0) continue;
       if (count == bs * bs)
         full_idx[qb * nk + nf++] = (int32_t)kb;
@@ -165,10 +180,32 @@ int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, i
 }
 
 /*
+ * Bit-packed form of a dense L x S byte mask (nonzero = live): row i is
+ * W = 4 * ceil(S / 128) words, bit b of word w = (dense[i][32 w + b] != 0),
+ * 0 past S. bits: caller-allocated uint32 [L * W]. Returns 0, or -1 on bad
+ * sizes.
+ */
+int oracle_pack_mask(const uint8_t* dense, int64_t L, int64_t S, uint32_t* bits) {
+  if (L < 0 || S < 0) return -1;
+  const int64_t W = 4 * ((S + 127) / 128);
+  for (int64_t i = 0; i < L; ++i)
+    for (int64_t w = 0; w < W; ++w) {
+      uint32_t word = 0;
+      for (int64_t b = 0; b < 32; ++b) {
+        const int64_t j = 32 * w + b;
+        if (j < S && dense[i * S + j] != 0) word |= (uint32_t)1 << b;
+      }
+      bits[i * W + w] = word;
+    }
+  return 0;
+}
+
+/*
  * Masked softmax attention, fp64, for a list of rows.
  *   q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev]: contiguous fp64.
  *   key_start, key_end: per batch entry [B], the kept key range [start, end),
- *   or NULL for no padding.
+ *   or NULL for no padding. dense: the L x S byte mask of kind DENSE (NULL
+ *   otherwise).
  *   rows: flat row ids r = (b*H + h)*L + i, or NULL for all B*H*L rows.
  *   out [nrows, Ev], lse [nrows] (natural log; -inf for a row with no live key).
  *   softcap > 0 applies s <- softcap * tanh(s / softcap) to the scaled score.
@@ -176,7 +213,8 @@ int oracle_block_mask(int kind, int64_t window, const int32_t* doc, int64_t L, i
  */
 int oracle_attention(const double* q, const double* k, const double* v, int64_t B, int64_t H,
                      int64_t L, int64_t S, int64_t E, int64_t Ev, int kind, int64_t window,
-                     const int32_t* doc, double softcap, double scale, const int64_t* key_start,
+                     const int32_t* doc, const uint8_t* dense, double softcap, double scale,
+                     const int64_t* key_start,
                      const int64_t* key_end, const int64_t* rows, int64_t nrows, double* out,
                      double* lse) {
   if (B < 0 || H < 0 || L < 0 || S < 0 || E <= 0 || Ev <= 0) return -1;
@@ -207,7 +245,7 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
         for (int64_t e = 0; e < E; ++e) dot += qi[e] * kh[j * E + e];
         double sc = dot * scale;
         if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
-        if (!live(kind, window, doc, L, S, i, j) || j < kept_lo || j >= kept_hi) sc = -INFINITY;
+        if (!live(kind, window, doc, dense, L, S, i, j) || j < kept_lo || j >= kept_hi) sc = -INFINITY;
         s[j] = sc;
         if (sc > m) m = sc;
       }

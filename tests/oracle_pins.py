@@ -21,6 +21,7 @@ import workloads as wl
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 NONE, CAUSAL, SLIDING, DOCUMENT = 0, 1, 2, 3
 CAUSAL_LR, SLIDING_LR, DOCUMENT_BIDIR = 4, 5, 6
+DENSE = 7
 
 
 def _golden(name):
@@ -467,6 +468,109 @@ def check_key_padding_per_batch(orc):
     assert np.abs(o[0] - on[0]).max() <= 1e-15  # the whole range is no padding
 
 
+# ---------------------------------------------------------------------------
+# User-supplied dense masks
+# ---------------------------------------------------------------------------
+
+def _band(L, S, lo, hi):
+    """Boolean [L, S] with True where lo <= i - j <= hi (an input mask)."""
+    d = np.arange(L)[:, None] - np.arange(S)[None, :]
+    return (d >= lo) & (d <= hi)
+
+
+def check_dense_mask_table_densities(orc):
+    """The FlexAttention-on-MPS densities again, now from the patterns given
+    as dense boolean masks (the form SDPA takes them in): token and block
+    densities of the S = 8192 rows, to the printed 2 decimals."""
+    g = _golden("flex_mps_densities.json")
+    for row in g["rows"]:
+        S, W = row["S"], row["W"]
+        if S != 8192 or (W or 0) > 1024:
+            continue
+        m = _band(S, S, 0, S) if row["pattern"] == "causal" else _band(S, S, 0, W - 1)
+        live = orc.count_live(DENSE, S, S, mask=m)
+        assert round(100.0 * live / (S * S), 2) == row["token_pct"], (row, live)
+        kv_num, _, full_num, _ = orc.block_mask(DENSE, S, S, block=g["block"], mask=m)
+        nb = -(-S // g["block"])
+        assert round(100.0 * int(kv_num.sum() + full_num.sum()) / (nb * nb), 2) == row["block_pct"], row
+
+
+def check_pack_mask_worked_example(orc):
+    """The bit layout on a hand-worked example (tests/golden/dense_mask_bits.json)."""
+    g = _golden("dense_mask_bits.json")
+    m = np.zeros((g["L"], g["S"]), bool)
+    for i, kept in enumerate(g["kept"]):
+        if kept == "all":
+            m[i, :] = True
+        else:
+            m[i, kept] = True
+    want = np.array([[int(w, 16) for w in row] for row in g["words"]], np.uint32)
+    assert np.array_equal(orc.pack_mask(m), want)
+
+
+def check_pack_mask_numpy(orc):
+    """Bit packing equals numpy.packbits (little bit order) of the mask padded
+    with False to a multiple of 128 keys, read as little-endian 32-bit words."""
+    rng = np.random.default_rng(70)
+    for L, S in ((3, 1), (5, 127), (4, 128), (7, 300), (2, 1000)):
+        m = rng.random((L, S)) < 0.4
+        padded = np.zeros((L, 128 * (-(-S // 128))), bool)
+        padded[:, :S] = m
+        want = np.packbits(padded, axis=1, bitorder="little").view("<u4")
+        assert np.array_equal(orc.pack_mask(m), want), (L, S)
+
+
+def check_dense_mask_matches_sdpa(orc):
+    """Attention under a random dense boolean mask equals torch's
+    scaled_dot_product_attention with that mask as attn_mask (True = take
+    part), fp64 on the CPU, with and without the soft-cap written as a float
+    bias; every row keeps at least one key."""
+    rng = np.random.default_rng(71)
+    B, H, L, S, E = 2, 3, 37, 53, 8
+    q, k, v = _rand((B, H, L, E), 72), _rand((B, H, S, E), 73), _rand((B, H, S, E), 74)
+    m = rng.random((L, S)) < 0.3
+    m[np.arange(L), rng.integers(0, S, L)] = True
+    o, lse = orc.attention(q, k, v, DENSE, 0.3, mask=m)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(m),
+                                                           scale=0.3).numpy()
+    assert np.abs(o - ref).max() <= 1e-13
+    sc = (tq @ tk.transpose(-2, -1).contiguous()) * 0.3
+    sc = sc.masked_fill(~torch.from_numpy(m), float("-inf"))
+    assert np.abs(lse - torch.logsumexp(sc, dim=-1).numpy()).max() <= 1e-13
+
+
+def check_dense_mask_empty_rows(orc):
+    """A row whose mask keeps nothing gives O = 0 and lse = -inf; the others
+    are unchanged by it."""
+    q, k, v = _rand((1, 2, 6, 4), 75), _rand((1, 2, 9, 4), 76), _rand((1, 2, 9, 4), 77)
+    m = np.ones((6, 9), bool)
+    m[2] = False
+    o, lse = orc.attention(q, k, v, DENSE, 0.5, mask=m)
+    on, ln = orc.attention(q, k, v, NONE, 0.5)
+    assert np.all(o[:, :, 2] == 0.0) and np.all(np.isneginf(lse[:, :, 2]))
+    keep = [0, 1, 3, 4, 5]
+    assert np.array_equal(o[:, :, keep], on[:, :, keep]) and np.array_equal(lse[:, :, keep], ln[:, :, keep])
+
+
+def check_dense_mask_equals_rules(orc):
+    """A rule written out as a dense mask gives the rule's result exactly
+    (bottom-right causal with L < S, a sliding window, documents)."""
+    q, k, v = _rand((1, 2, 40, 8), 78), _rand((1, 2, 70, 8), 79), _rand((1, 2, 70, 8), 80)
+    cases = [(CAUSAL_LR, 0, None, _band(40, 70, -30, 70)),
+             (SLIDING, 9, None, _band(40, 70, 0, 8))]
+    doc = np.repeat([0, 1, 2], [25, 30, 15]).astype(np.int32)
+    same = doc[:40, None] == doc[None, :70]
+    cases.append((DOCUMENT, 0, doc, same & _band(40, 70, 0, 70)))
+    for kind, win, d, m in cases:
+        o1, l1 = orc.attention(q, k, v, kind, 0.4, win, d, softcap=5.0)
+        o2, l2 = orc.attention(q, k, v, DENSE, 0.4, softcap=5.0, mask=m)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), kind
+        a = orc.block_mask(kind, 40, 70, win, d, block=16)
+        b = orc.block_mask(DENSE, 40, 70, block=16, mask=m)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b)), kind
+
+
 ALL_CHECKS = [
     check_flex_table_densities,
     check_live_pair_closed_forms,
@@ -493,4 +597,10 @@ ALL_CHECKS = [
     check_variant_block_masks,
     check_key_padding_equals_truncation,
     check_key_padding_per_batch,
+    check_dense_mask_table_densities,
+    check_pack_mask_worked_example,
+    check_pack_mask_numpy,
+    check_dense_mask_matches_sdpa,
+    check_dense_mask_empty_rows,
+    check_dense_mask_equals_rules,
 ]

@@ -34,6 +34,10 @@ MUTANTS = [
     ("padding_end_ignored", "|| j < kept_lo || j >= kept_hi)", "|| j < kept_lo)"),
     ("padding_end_inclusive", "|| j < kept_lo || j >= kept_hi)", "|| j < kept_lo || j > kept_hi)"),
     ("padding_start_ignored", "|| j < kept_lo || j >= kept_hi)", "|| j >= kept_hi)"),
+    ("dense_transposed", "return dense[i * S + j] != 0;", "return dense[j * L + i] != 0;"),
+    ("dense_inverted", "return dense[i * S + j] != 0;", "return dense[i * S + j] == 0;"),
+    ("pack_bit_order", "word |= (uint32_t)1 << b;", "word |= (uint32_t)1 << (31 - b);"),
+    ("pack_words_per_row", "const int64_t W = 4 * ((S + 127) / 128);", "const int64_t W = (S + 31) / 32;"),
     ("bidirectional_keeps_causal", "      return doc[i] == doc[j];\n",
      "      return i >= j && doc[i] == doc[j];\n"),
 ]
