@@ -10,8 +10,8 @@ kernel is also timed alone with events on the stream it runs on (batches of
 back-to-back launches), for the roofline figure. The second headline workload (sliding window 256
 over S=32768) is measured the same way and reported in the same line, and so
 are the mask and head-sharing variants (bottom-right causal, grouped-query
-heads, bidirectional documents, key padding, and split-KV decode) under
-"workloads".
+heads, bidirectional documents, key padding, split-KV / packed-row decode,
+and a user-supplied dense mask) under "workloads".
 
 Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
 (4 * E flops per unmasked (query, key) pair); ``forward_only`` has the
@@ -45,7 +45,7 @@ SECOND = "sliding_32768_w256_bf16"
 # Mask and head-sharing variants of the same kernel, reported in "workloads".
 VARIANTS = ("causal_lower_right_2048x8192_bf16", "gqa_causal_8192_h32_kv8_bf16",
             "document_bidirectional_8192_f16_softcap", "causal_8192_keypad_b2_bf16",
-            "decode_gqa_b8_h32_kv8_s8192_bf16")
+            "decode_gqa_b8_h32_kv8_s8192_bf16", "custom_blocks_8192_bf16")
 
 
 def padded_causal_pairs(L: int, start: int, end: int) -> int:
@@ -81,6 +81,8 @@ def live_pairs(w: wl.Workload) -> int:
     if w.kind == wl.MASK_DOCUMENT_BIDIRECTIONAL and L == S:
         edges = [0, *w.doc_bounds, S]
         return sum((b - a) ** 2 for a, b in zip(edges[:-1], edges[1:]))
+    if w.kind == wl.MASK_CUSTOM:
+        return int(wl.make_mask(w).sum())  # the pairs the user mask keeps
     raise ValueError("no closed form for this workload")
 
 
@@ -98,8 +100,12 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     doc_t = torch.from_numpy(doc).to(dev) if doc is not None else None
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.L, dtype=torch.float32, device=dev)
-    bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None, document_id=doc_t,
-                               device=dev)
+    if w.kind == wl.MASK_CUSTOM:
+        # the user mask is packed once; a step rebuilds the BlockMask from its bits
+        bm = bsa.create_block_mask_from_dense(torch.from_numpy(wl.make_mask(w)).to(dev))
+    else:
+        bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None, document_id=doc_t,
+                                   device=dev)
     score_mod = "softcap" if w.softcap else None
     ks = ke = None
     if w.key_ranges:

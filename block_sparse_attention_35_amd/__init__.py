@@ -30,7 +30,8 @@ from typing import Optional, Union
 import torch
 
 __all__ = [
-    "BlockMask", "BsattnError", "create_block_mask", "attention", "num_blocks", "library_path",
+    "BlockMask", "BsattnError", "create_block_mask", "create_block_mask_from_dense",
+    "create_block_mask_from_bits", "pack_mask", "mask_words", "attention", "num_blocks", "library_path",
     "workspace_size",
     "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
     "MASK_CAUSAL_LOWER_RIGHT", "MASK_SLIDING_WINDOW_LOWER_RIGHT", "MASK_DOCUMENT_BIDIRECTIONAL",
@@ -44,6 +45,7 @@ ATTN_OK = 0
 F32, BF16, F16 = 0, 1, 2
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
 MASK_CAUSAL_LOWER_RIGHT, MASK_SLIDING_WINDOW_LOWER_RIGHT, MASK_DOCUMENT_BIDIRECTIONAL = 4, 5, 6
+MASK_CUSTOM = 7
 _WINDOWED = (MASK_SLIDING_WINDOW, MASK_SLIDING_WINDOW_LOWER_RIGHT)
 _DOCUMENTS = (MASK_DOCUMENT, MASK_DOCUMENT_BIDIRECTIONAL)
 SCORE_NONE, SCORE_SOFTCAP = 0, 1
@@ -78,6 +80,7 @@ class _BlockMaskStruct(ctypes.Structure):
         ("kind", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("document_id", ctypes.c_void_p),
+        ("mask_bits", ctypes.c_void_p),
     ]
 
 
@@ -104,6 +107,12 @@ def _load():
     lib.attn_build_block_mask.restype = i32
     lib.attn_build_block_mask.argtypes = [i32, i32, vp, i32, i32, i32,
                                           ctypes.POINTER(_BlockMaskStruct), vp]
+    lib.attn_mask_words.restype = i32
+    lib.attn_mask_words.argtypes = [i32]
+    lib.attn_pack_mask.restype = i32
+    lib.attn_pack_mask.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp]
+    lib.attn_build_block_mask_custom.restype = i32
+    lib.attn_build_block_mask_custom.argtypes = [vp, i32, i32, i32, ctypes.POINTER(_BlockMaskStruct), vp]
     lib.attn_forward.restype = i32
     lib.attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
@@ -158,11 +167,13 @@ class BlockMask:
     """
 
     def __init__(self, kind: int, q_len: int, kv_len: int, window: int,
-                 document_id: Optional[torch.Tensor], device: torch.device):
+                 document_id: Optional[torch.Tensor], device: torch.device,
+                 mask_bits: Optional[torch.Tensor] = None):
         nq, nk = num_blocks(q_len), num_blocks(kv_len)
         opt = dict(dtype=torch.int32, device=device)
         self.kind, self.q_len, self.kv_len, self.window = kind, q_len, kv_len, window
         self.document_id = document_id
+        self.mask_bits = mask_bits  # CUSTOM: int32 [q_len, 4 nk] bit-packed mask
         self.device = device
         self.kv_num_blocks = torch.empty(nq, **opt)
         self.kv_indices = torch.empty(nq, nk, **opt)
@@ -187,12 +198,17 @@ class BlockMask:
 
     def rebuild(self):
         """Enqueue the library's mask build on the current stream."""
-        doc = self.document_id.data_ptr() if self.document_id is not None else None
         with torch.cuda.device(self.device):
-            _check(_load().attn_build_block_mask(self.kind, self.window, doc, self.q_len,
-                                                 self.kv_len, BLOCK_SIZE,
-                                                 ctypes.byref(self._struct),
-                                                 _stream_handle(self.device)))
+            if self.kind == MASK_CUSTOM:
+                _check(_load().attn_build_block_mask_custom(
+                    self.mask_bits.data_ptr(), self.q_len, self.kv_len, BLOCK_SIZE,
+                    ctypes.byref(self._struct), _stream_handle(self.device)))
+            else:
+                doc = self.document_id.data_ptr() if self.document_id is not None else None
+                _check(_load().attn_build_block_mask(self.kind, self.window, doc, self.q_len,
+                                                     self.kv_len, BLOCK_SIZE,
+                                                     ctypes.byref(self._struct),
+                                                     _stream_handle(self.device)))
         return self
 
 
@@ -201,6 +217,8 @@ def create_block_mask(kind: Union[str, int], q_len: int, kv_len: int, window: Op
                       device: Union[str, torch.device] = "cuda") -> BlockMask:
     """Build a BlockMask with attn_build_block_mask (asynchronous on the
     current stream of ``device``)."""
+    if kind in ("custom", MASK_CUSTOM):
+        raise ValueError("custom masks: create_block_mask_from_dense or create_block_mask_from_bits")
     k = _KINDS[kind] if isinstance(kind, str) else int(kind)
     device = torch.device(device)
     if device.type != "cuda":
@@ -221,6 +239,52 @@ def create_block_mask(kind: Union[str, int], q_len: int, kv_len: int, window: Op
             raise ValueError("document_id must cover max(q_len, kv_len) positions")
         doc = document_id.to(device=device, dtype=torch.int32).contiguous()
     return BlockMask(k, q_len, kv_len, w, doc, device).rebuild()
+
+
+def mask_words(kv_len: int) -> int:
+    """uint32 words per row of a bit-packed mask: 4 * ceil(kv_len / 128)."""
+    n = _load().attn_mask_words(kv_len)
+    if n < 0:
+        raise BsattnError(-1, f"bad kv_len {kv_len}")
+    return n
+
+
+def pack_mask(mask: torch.Tensor) -> torch.Tensor:
+    """Bit-pack a dense boolean mask [q_len, kv_len] (True keeps the pair) on
+    its GPU with attn_pack_mask: int32 [q_len, mask_words(kv_len)], bit b of
+    word w of row i = mask[i, 32 w + b]."""
+    if mask.dim() != 2 or mask.device.type != "cuda":
+        raise ValueError("mask must be a 2-D tensor on a cuda device")
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise ValueError("mask must be torch.bool or torch.uint8")
+    L, S = mask.shape
+    if S > 0 and mask.stride(1) != 1:
+        mask = mask.contiguous()
+    stride = mask.stride(0) if L > 1 else S
+    bits = torch.empty(L, mask_words(S), dtype=torch.int32, device=mask.device)
+    with torch.cuda.device(mask.device):
+        _check(_load().attn_pack_mask(mask.data_ptr() if mask.numel() else None, stride, L, S,
+                                      bits.data_ptr() if bits.numel() else None,
+                                      _stream_handle(mask.device)))
+    return bits
+
+
+def create_block_mask_from_bits(bits: torch.Tensor, q_len: int, kv_len: int) -> BlockMask:
+    """BlockMask of kind CUSTOM from a bit-packed mask (int32 [q_len,
+    mask_words(kv_len)] on a cuda device, kept by the BlockMask)."""
+    if bits.device.type != "cuda" or bits.dtype != torch.int32:
+        raise ValueError("bits must be an int32 tensor on a cuda device")
+    if tuple(bits.shape) != (q_len, mask_words(kv_len)) or not bits.is_contiguous():
+        raise ValueError(f"bits must be contiguous [{q_len}, {mask_words(kv_len)}]")
+    return BlockMask(MASK_CUSTOM, q_len, kv_len, 0, None, bits.device, mask_bits=bits).rebuild()
+
+
+def create_block_mask_from_dense(mask: torch.Tensor) -> BlockMask:
+    """BlockMask of kind CUSTOM from a dense boolean mask [q_len, kv_len] on a
+    cuda device (True keeps the pair): the mask is bit-packed on the GPU, and
+    only the packed form is kept."""
+    L, S = mask.shape
+    return create_block_mask_from_bits(pack_mask(mask), L, S)
 
 
 _workspaces = {}

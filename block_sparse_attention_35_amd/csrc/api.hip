@@ -75,13 +75,17 @@ int32_t attn_num_blocks(int32_t len, int32_t block_size) {
   return (int32_t)(((int64_t)len + block_size - 1) / block_size);
 }
 
-attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* document_id,
-                                  int32_t q_len, int32_t kv_len, int32_t block_size,
-                                  attn_block_mask* bm, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two builders: validates, fills bm's fields and enqueues
+// the classification and the work plan.
+attn_status build_impl(int32_t kind, int32_t window, const int32_t* document_id,
+                       const uint32_t* bits, int32_t q_len, int32_t kv_len, int32_t block_size,
+                       attn_block_mask* bm, void* stream) {
   g_last_error[0] = '\0';
   if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask struct is null");
-  if (kind < ATTN_MASK_NONE || kind > ATTN_MASK_DOCUMENT_BIDIRECTIONAL)
-    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask kind %d", kind);
   if (q_len < 0 || kv_len < 0)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "negative length (q_len=%d, kv_len=%d)", q_len, kv_len);
   if (block_size != ATTN_BLOCK_SIZE)
@@ -89,10 +93,15 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
                 ATTN_BLOCK_SIZE);
   const bool windowed = kind == ATTN_MASK_SLIDING_WINDOW || kind == ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT;
   const bool documents = kind == ATTN_MASK_DOCUMENT || kind == ATTN_MASK_DOCUMENT_BIDIRECTIONAL;
+  const bool custom = kind == ATTN_MASK_CUSTOM;
   if (windowed && window < 1)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "sliding window must be >= 1 (got %d)", window);
   if (documents && document_id == nullptr)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "document mask needs document_id");
+  if (custom && bits == nullptr && (int64_t)q_len * kv_len > 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "custom mask needs its bits");
+  if (custom && (reinterpret_cast<uintptr_t>(bits) & 15u) != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "custom mask bits must be 16-byte aligned");
   const int32_t nq = attn_num_blocks(q_len, block_size);
   const int32_t nk = attn_num_blocks(kv_len, block_size);
   if (!arrays_present(bm, nq, nk))
@@ -108,13 +117,55 @@ attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* d
   bm->kind = kind;
   bm->window = windowed ? window : 0;
   bm->document_id = documents ? document_id : nullptr;
+  bm->mask_bits = custom ? bits : nullptr;
   const bsattn::MaskForm form = bsattn::mask_form(kind, q_len, kv_len);
   return hip_status(bsattn::launch_block_mask(form.kind, form.q_off, bm->window, bm->document_id,
-                                              q_len, kv_len, nq, nk, bm->kv_num_blocks,
-                                              bm->kv_indices, bm->full_kv_num_blocks,
-                                              bm->full_kv_indices, bm->schedule,
-                                              static_cast<hipStream_t>(stream)),
+                                              bm->mask_bits, q_len, kv_len, nq, nk,
+                                              bm->kv_num_blocks, bm->kv_indices,
+                                              bm->full_kv_num_blocks, bm->full_kv_indices,
+                                              bm->schedule, static_cast<hipStream_t>(stream)),
                     "block mask launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* document_id,
+                                  int32_t q_len, int32_t kv_len, int32_t block_size,
+                                  attn_block_mask* bm, void* stream) {
+  if (kind < ATTN_MASK_NONE || kind > ATTN_MASK_DOCUMENT_BIDIRECTIONAL) {
+    g_last_error[0] = '\0';
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown mask kind %d%s", kind,
+                kind == ATTN_MASK_CUSTOM ? " (custom masks: attn_build_block_mask_custom)" : "");
+  }
+  return build_impl(kind, window, document_id, nullptr, q_len, kv_len, block_size, bm, stream);
+}
+
+int32_t attn_mask_words(int32_t kv_len) {
+  if (kv_len < 0) return -1;
+  return 4 * attn_num_blocks(kv_len, ATTN_BLOCK_SIZE);
+}
+
+attn_status attn_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_len, int32_t kv_len,
+                           uint32_t* bits, void* stream) {
+  g_last_error[0] = '\0';
+  if (q_len < 0 || kv_len < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "negative length (q_len=%d, kv_len=%d)", q_len, kv_len);
+  if (row_stride < kv_len)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "row_stride %lld < kv_len %d", (long long)row_stride, kv_len);
+  if ((int64_t)q_len * kv_len > 0 && (dense == nullptr || bits == nullptr))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "dense and bits must be non-null");
+  if ((reinterpret_cast<uintptr_t>(bits) & 15u) != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "bits must be 16-byte aligned");
+  return hip_status(bsattn::launch_pack_mask(dense, row_stride, q_len, kv_len, bits,
+                                             static_cast<hipStream_t>(stream)),
+                    "mask pack launch");
+}
+
+attn_status attn_build_block_mask_custom(const uint32_t* bits, int32_t q_len, int32_t kv_len,
+                                         int32_t block_size, attn_block_mask* bm, void* stream) {
+  return build_impl(ATTN_MASK_CUSTOM, 0, nullptr, bits, q_len, kv_len, block_size, bm, stream);
 }
 
 }  // extern "C"
@@ -155,11 +206,14 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
       bm->num_kv_blocks != attn_num_blocks(S, ATTN_BLOCK_SIZE) ||
       !arrays_present(bm, bm->num_q_blocks, bm->num_kv_blocks))
     return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is not built");
-  if (bm->kind < ATTN_MASK_NONE || bm->kind > ATTN_MASK_DOCUMENT_BIDIRECTIONAL ||
+  if (bm->kind < ATTN_MASK_NONE || bm->kind > ATTN_MASK_CUSTOM ||
       ((bm->kind == ATTN_MASK_SLIDING_WINDOW || bm->kind == ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT) &&
        bm->window < 1) ||
       ((bm->kind == ATTN_MASK_DOCUMENT || bm->kind == ATTN_MASK_DOCUMENT_BIDIRECTIONAL) &&
-       bm->document_id == nullptr))
+       bm->document_id == nullptr) ||
+      (bm->kind == ATTN_MASK_CUSTOM &&
+       ((bm->mask_bits == nullptr && (int64_t)L * S > 0) ||
+        (reinterpret_cast<uintptr_t>(bm->mask_bits) & 15u) != 0)))
     return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask fields are inconsistent");
   if (score_mod != ATTN_SCORE_NONE && score_mod != ATTN_SCORE_SOFTCAP)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown score_mod %d", score_mod);
@@ -217,6 +271,8 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
   a.m.full_idx = bm->full_kv_indices;
   a.m.schedule = bm->schedule;
   a.m.doc = bm->document_id;
+  a.m.bits = bm->mask_bits;
+  a.m.bits_w = 4 * bm->num_kv_blocks;
   a.m.nq = bm->num_q_blocks;
   a.m.nk = bm->num_kv_blocks;
   const bsattn::MaskForm form = bsattn::mask_form(bm->kind, L, S);

@@ -17,10 +17,16 @@
 // differ); the rest are classified exactly by evaluating every in-range pair
 // cooperatively (ids may be in any order).
 //
+// CUSTOM blocks are classified from the bit-packed user mask: a block is
+// skipped when none of its in-range bits is set and full when all 128 x 128
+// are in range and set.
+//
 // Kernel 1 (one workgroup per query block) writes the classes to LDS, then
 // compacts them in ascending kb order with wave ballots and writes the counts,
 // the index lists and the zero padding. Kernel 2 ranks query blocks by their
 // number of live kv blocks, descending, ties by index, and writes the order.
+#include <algorithm>
+
 #include "internal.h"
 
 #include "bsattn.h"
@@ -42,8 +48,8 @@ __device__ inline uint8_t classify_interval(int64_t q0, int64_t q1, int64_t k0, 
 }
 
 __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
-    int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc, int32_t q_len,
-    int32_t kv_len,
+    int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc,
+    const uint32_t* __restrict__ bits, int32_t q_len, int32_t kv_len,
     int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
     int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
   extern __shared__ uint8_t cls[];  // [nk]
@@ -100,6 +106,36 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
         }
       }
       if (lane == 0) cls[kb] = c;
+    }
+  } else if (kind == ATTN_MASK_CUSTOM) {
+    // One wave per kv block: lane l holds rows q0 + l and q0 + l + 64 (when
+    // in range) and reads each one's four words of the block.
+    const int64_t W = 4 * (int64_t)nk;
+    const int n_rows = (int)(q1 - q0 + 1);
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int kb = wave; kb < nk; kb += kWaves) {
+      const int nvalid = (int)min<int64_t>(kBlock, kv_len - (int64_t)kb * kBlock);
+      uint32_t vm[4];  // in-range keys of each word
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = nvalid - 32 * t;
+        vm[t] = n >= 32 ? ~0u : (n <= 0 ? 0u : ((1u << n) - 1u));
+      }
+      bool any = false, all = nvalid == kBlock;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = lane + 64 * h;
+        if (r < n_rows) {
+          const uint4 w = *reinterpret_cast<const uint4*>(bits + (q0 + r) * W + 4 * kb);
+          any |= ((w.x & vm[0]) | (w.y & vm[1]) | (w.z & vm[2]) | (w.w & vm[3])) != 0u;
+          all &= (w.x & w.y & w.z & w.w) == ~0u;
+        } else {
+          all = false;  // the block is not whole
+        }
+      }
+      any = __any(any);
+      all = __all(all);
+      if (lane == 0) cls[kb] = !any ? kSkip : (all ? kFull : kPartial);
     }
   } else {
     const int64_t w = (kind == ATTN_MASK_SLIDING_WINDOW) ? (int64_t)window : INT64_MAX / 4;
@@ -249,16 +285,60 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
   }
 }
 
+// Dense byte mask -> CUSTOM bits. One wave per (row, 512-key chunk): lane l
+// reads byte 64 u + l of the chunk for u = 0..7 (64 consecutive bytes per
+// load instruction), and ballot u is words 16 c + 2 u and 16 c + 2 u + 1 of
+// the row (bit l of the ballot = key 64 u + l of the chunk).
+__global__ __launch_bounds__(kThreads) void pack_mask_kernel(const uint8_t* __restrict__ dense,
+                                                             int64_t row_stride, int32_t q_len,
+                                                             int32_t kv_len, int32_t W,
+                                                             uint32_t* __restrict__ bits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t chunks = (W + 15) / 16;
+  const int64_t tasks = (int64_t)q_len * chunks;
+  for (int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); t < tasks;
+       t += (int64_t)gridDim.x * kWaves) {
+    const int64_t i = t / chunks, c = t % chunks;
+    const uint8_t* row = dense + i * row_stride;
+    uint8_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = c * 512 + 64 * u + lane;
+      v[u] = j < kv_len ? row[j] : 0;
+    }
+    uint64_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t m = __ballot(v[u] != 0);
+      if (lane == u) mine = m;
+    }
+    const int64_t w0 = c * 16 + 2 * lane;
+    if (lane < 8 && w0 < W)
+      *reinterpret_cast<uint2*>(bits + i * W + w0) = make_uint2((uint32_t)mine, (uint32_t)(mine >> 32));
+  }
+}
+
 }  // namespace
 
+hipError_t launch_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_len, int32_t kv_len,
+                            uint32_t* bits, hipStream_t stream) {
+  const int32_t W = 4 * (int32_t)(((int64_t)kv_len + kBlock - 1) / kBlock);
+  if (q_len == 0 || W == 0) return hipSuccess;
+  const int64_t tasks = (int64_t)q_len * ((W + 15) / 16);
+  const int64_t blocks = std::min<int64_t>((tasks + kWaves - 1) / kWaves, 16384);
+  hipLaunchKernelGGL(pack_mask_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, dense, row_stride,
+                     q_len, kv_len, W, bits);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const int32_t* doc,
-                             int32_t q_len, int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
-                             int32_t* kv_idx, int32_t* full_num, int32_t* full_idx,
-                             int32_t* schedule, hipStream_t stream) {
+                             const uint32_t* bits, int32_t q_len, int32_t kv_len, int32_t nq,
+                             int32_t nk, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
+                             int32_t* full_idx, int32_t* schedule, hipStream_t stream) {
   if (nq == 0) return hipSuccess;
   const size_t lds = (size_t)((nk + 15) & ~15);
   hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off,
-                     window, doc, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
+                     window, doc, bits, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,

@@ -15,6 +15,9 @@
 // written back: "Flash Attention 2 and the IO bottleneck" (tcdigital),
 // section on tiling. Skipped / partial / full blocks: "FlexAttention on Apple
 // Silicon: block masks", closing section; soft-cap: same page, "Bonus".
+// User-supplied masks (kind CUSTOM) arrive bit-packed, four words per (query
+// row, kv block); each block's words are staged with its K tile and read by
+// the pair test of partial blocks only.
 //
 // Work layout (4 waves of 64 lanes, each wave owns 32 query rows):
 //  * S^T = K_j Q^T is computed with 32x32 MFMA tiles, kv along M and queries
@@ -119,6 +122,7 @@ __device__ inline float softcap_log2(float s, float two_log2e_scale_over_cap, fl
 
 // A query at rule position p (its row i plus the mask's query offset) may see
 // key j, with j < S checked; di, dj are the document ids of row i and key j.
+// (CUSTOM checks j < S here; its bit is tested by the caller.)
 template <int KIND>
 __device__ inline bool pair_live(int p, int j, int S, int W, int32_t di, int32_t dj) {
   bool ok = j < S;
@@ -143,7 +147,7 @@ struct RowState {
 template <int KIND, bool PARTIAL, bool SOFTCAP>
 __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, int kv0, int hf,
                                       const FwdArgs& a, int32_t dq, const int32_t* doc_k, int klo,
-                                      int khi) {
+                                      int khi, uint4 mw) {
   const float c1 = a.scale * kLog2e;
   float mx = -INFINITY;
 #pragma unroll
@@ -156,8 +160,12 @@ __device__ inline float softmax_tiles(f32x16_t (&s)[4], RowState& st, int qi, in
         const int jl = t * 32 + acc_row(r, hf);
         const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? doc_k[jl] : 0;
         // kept keys [klo, khi): the mask's own j < S, and key padding
-        if (!pair_live<KIND>(qi + a.m.q_off, kv0 + jl, khi, a.m.window, dq, dj) || kv0 + jl < klo)
-          x = -INFINITY;
+        bool ok = pair_live<KIND>(qi + a.m.q_off, kv0 + jl, khi, a.m.window, dq, dj) && kv0 + jl >= klo;
+        if (KIND == ATTN_MASK_CUSTOM) {
+          const uint32_t w = t == 0 ? mw.x : t == 1 ? mw.y : t == 2 ? mw.z : mw.w;
+          ok &= (w >> acc_row(r, hf)) & 1u;
+        }
+        if (!ok) x = -INFINITY;
       }
       s[t][r] = x;
       mx = fmaxf(mx, x);
@@ -317,6 +325,22 @@ struct alignas(16) Lds {
   KStage k[2];
   VStage v[2];
 };
+// For CUSTOM masks, also each stage's mask words: [query row][4].
+struct alignas(16) LdsBits {
+  KStage k[2];
+  VStage v[2];
+  uint32_t bits[2][kBlock * 4];
+};
+
+// Mask words of this wave's 32 query rows (row0 .. row0 + 31; rows past L
+// repeat row L - 1) for kv block kb: 16 bytes per row, lanes 0..31.
+__device__ inline void issue_bits(const uint32_t* bits, int W, int row0, int L, int kb, uint32_t* stage,
+                                  int wave, int lane) {
+  if (lane < 32) {
+    const int r = min(row0 + lane, L - 1);
+    lds_copy16(bits + (int64_t)r * W + 4 * kb, lds_offset(stage) + (uint32_t)wave * 512u);
+  }
+}
 
 // Per-lane LDS read addresses into stage 0; stage 1 is a constant away, and
 // every read of a step is one of these plus a constant that fits the
@@ -375,7 +399,7 @@ template <typename T, int KIND, bool SOFTCAP, bool PARTIAL, bool PADDED>
 __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
                                           const typename Vec<T>::x8 (&qop)[4], f32x16_t (&oacc)[2],
                                           float& m_ref, float& l, int qi, int row0, int kv0, int lane, const FwdArgs& a,
-                                          int32_t dq, int klo, int khi) {
+                                          int32_t dq, int klo, int khi, const uint32_t* mbits) {
   using V = Vec<T>;
   using x8 = typename V::x8;
   typedef __attribute__((address_space(3))) const x8 lds_x8;
@@ -404,6 +428,14 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   // only live tiles skip the test; for document masks the interval decides
   // only "none live".
   int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
+  // CUSTOM: this lane's row's mask words of the block (word t = tile t).
+  uint32_t mw[4] = {0u, 0u, 0u, 0u};
+  if (PARTIAL && KIND == ATTN_MASK_CUSTOM) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+    const u32x4_t w4 = *reinterpret_cast<lds_u32x4*>((lds_u8)mbits + ((row0 % kBlock) + (lane & 31)) * 16);
+    mw[0] = w4[0], mw[1] = w4[1], mw[2] = w4[2], mw[3] = w4[3];
+  }
   if (PARTIAL) {
     const int i0 = row0 + a.m.q_off, i1 = i0 + 31;  // the rows' rule positions
 #pragma unroll
@@ -414,6 +446,14 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
       int c;
       if (outside) {
         c = kTileDead;
+      } else if (KIND == ATTN_MASK_CUSTOM) {
+        // from the words of the wave's 32 rows: none set, all set, or mixed
+        if (__ballot(mw[t] != 0u) == 0)
+          c = kTileDead;
+        else if (!edge && __ballot(mw[t] != ~0u) == 0)
+          c = kTileLive;
+        else
+          c = kTileMixed;
       } else if (KIND == ATTN_MASK_NONE) {
         c = edge ? kTileMixed : kTileLive;
       } else {
@@ -435,7 +475,8 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   // hi bounds by j <= p and j < khi, lo by p - j < W (sliding windows) and
   // j >= klo (padding), p = qi + q_off the row's rule position.
   const int rel = qi + a.m.q_off - kv0 - 4 * hf;
-  const int hi = (KIND == ATTN_MASK_NONE) ? khi - 1 - kv0 - 4 * hf : min(rel, khi - 1 - kv0 - 4 * hf);
+  const int hi = (KIND == ATTN_MASK_NONE || KIND == ATTN_MASK_CUSTOM) ? khi - 1 - kv0 - 4 * hf
+                                                                      : min(rel, khi - 1 - kv0 - 4 * hf);
   // (A window wider than 2^30 never bites: S is far smaller.)
   int lo = (KIND == ATTN_MASK_SLIDING_WINDOW) ? rel - min(a.m.window - 1, 1 << 30) : -(1 << 30);
   if (PADDED) lo = max(lo, klo - kv0 - 4 * hf);
@@ -467,6 +508,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
         // (Read unconditionally: the four ids of a register group are one
         // 16-byte LDS read.)
         if (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
+        if (KIND == ATTN_MASK_CUSTOM) live &= (mw[t] >> (c + 4 * hf)) & 1u;
         x = live ? x : -INFINITY;
       }
       s[t][r] = x;
@@ -610,7 +652,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   using V = Vec<T>;
   using x8 = typename V::x8;
   using x4 = typename V::x4;
-  __shared__ Lds lds;
+  constexpr bool BITS = KIND == ATTN_MASK_CUSTOM;
+  __shared__ std::conditional_t<BITS, LdsBits, Lds> lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -696,6 +739,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
     if (m_begin + 1 < m_end) kv_after = kv_start(m_begin + 1);
     issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[0], wave, lane);
     issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[0].v, wave, lane);
+    if constexpr (BITS)
+      issue_bits(a.m.bits, a.m.bits_w, qb * kBlock + wave * 32, a.L, kv_next / kBlock, lds.bits[0], wave, lane);
   }
 
   const int row0 = qb * kBlock + wave * 32;  // this wave's first query row
@@ -753,20 +798,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       kv_next = kv_after;
       issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv_next, a.S, lds.k[1 - par], wave, lane);
       issue_rows<T, true>(vg, a.v_sl, v_off, kv_next, a.S, lds.v[1 - par].v, wave, lane);
+      if constexpr (BITS)
+        issue_bits(a.m.bits, a.m.bits_w, qb * kBlock + wave * 32, a.L, kv_next / kBlock, lds.bits[1 - par],
+                   wave, lane);
       if (m + 2 < m_end) kv_after = kv_start(m + 2);
     }
+    const uint32_t* mb = nullptr;
+    if constexpr (BITS) mb = lds.bits[par];
     if (PADDED) {
       // A block with no kept key is skipped; a full block that a padding
       // boundary cuts runs the per-tile pair tests of a partial block.
       if (kv0 + kBlock <= klo || kv0 >= khi) return;
       if (!PARTIAL && (kv0 < klo || kv0 + kBlock > khi)) {
         fwd_block<T, KIND, SOFTCAP, true, true>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0,
-                                                lane, a, dq, klo, khi);
+                                                lane, a, dq, klo, khi, mb);
         return;
       }
     }
     fwd_block<T, KIND, SOFTCAP, PARTIAL, PADDED>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0,
-                                                 lane, a, dq, klo, khi);
+                                                 lane, a, dq, klo, khi, mb);
   };
   int m = m_begin;
   for (; m < min(m_end, nfull); ++m) block(std::false_type{}, m);
@@ -966,6 +1016,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
     }
     if (KIND == ATTN_MASK_DOCUMENT && partial && tid < kBlock)
       doc_k[tid] = (kv0 + tid < a.S) ? a.m.doc[kv0 + tid] : -1;
+    // CUSTOM: this lane's row's mask words of the block
+    uint4 mw = make_uint4(0u, 0u, 0u, 0u);
+    if (KIND == ATTN_MASK_CUSTOM && partial)
+      mw = *reinterpret_cast<const uint4*>(a.m.bits + (int64_t)min(qi, a.L - 1) * a.m.bits_w + 4 * kb);
     __syncthreads();
 
     f32x16_t s[4];
@@ -980,9 +1034,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
 
     float alpha;
     if (partial)
-      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi);
+      alpha = softmax_tiles<KIND, true, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi, mw);
     else
-      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi);
+      alpha = softmax_tiles<KIND, false, SOFTCAP>(s, st, qi, kv0, hf, a, dq, doc_k, klo, khi, mw);
 
     float psum = 0.0f;
 #pragma unroll
@@ -1114,12 +1168,14 @@ __global__ __launch_bounds__(kThreads) void kv_merge_kernel(FwdArgs a) {
 // which packed_merge_kernel combines over the chunks.
 constexpr int kPackStages = 2;
 
-template <int NS>
+template <int NS, bool BITS>
 struct alignas(16) PackLds {
   KStage k[NS];
   VStage v[NS];
   uint8_t q[kPackRows * 128];  // the packed rows' Q, row-major
   int32_t doc_q[kPackRows];    // document id of each packed row's query
+  // CUSTOM: per stage and wave, each packed row's mask word of the wave's keys
+  uint32_t bits[BITS ? NS : 1][4][kPackRows];
 };
 // Row stride (floats) of each wave's O in the combine area: 4 floats of
 // padding spread the rows over the LDS banks.
@@ -1134,11 +1190,12 @@ __global__ __launch_bounds__(kThreads, 2) void packed_kernel(FwdArgs a) {
   using x8 = typename V::x8;
   typedef __attribute__((address_space(3))) const x8 lds_x8;
   constexpr int NS = kPackStages;
+  constexpr bool BITS = KIND == ATTN_MASK_CUSTOM;
   // vector memory operations one wave issues per block: 4 K, 4 V copies (and
-  // the keys' document ids)
-  constexpr int kPerBlock = (KIND == ATTN_MASK_DOCUMENT) ? 9 : 8;
+  // the keys' document ids, or the rows' mask words)
+  constexpr int kPerBlock = (KIND == ATTN_MASK_DOCUMENT || BITS) ? 9 : 8;
   static_assert((NS - 1) * kPerBlock < 64, "copies in flight fit vmcnt");
-  __shared__ PackLds<NS> lds;
+  __shared__ PackLds<NS, BITS> lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1184,6 +1241,12 @@ __global__ __launch_bounds__(kThreads, 2) void packed_kernel(FwdArgs a) {
   auto issue = [&](int kv0, int st) __attribute__((always_inline)) {
     issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv0, a.S, lds.k[st], wave, lane);
     issue_rows<T, true>(vg, a.v_sl, v_off, kv0, a.S, lds.v[st].v, wave, lane);
+    if constexpr (BITS) {
+      // word `wave` (this wave's 32 keys) of each packed row's query
+      if (lane < 32)
+        lds_copy4(a.m.bits + (int64_t)(lq % a.L) * a.m.bits_w + 4 * (kv0 / kBlock) + wave,
+                  lds_offset(lds.bits[st][wave]));
+    }
   };
   // Blocks m_begin .. m_begin + NS - 2 go out first; block m then refills the
   // stage of block m - 1 with block m + NS - 1. The first key of the block
@@ -1251,7 +1314,9 @@ __global__ __launch_bounds__(kThreads, 2) void packed_kernel(FwdArgs a) {
       if (!full) {
         const int jl = wave * 32 + acc_row(r, hf);
         const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? lds.k[st].doc[jl] : 0;
-        if (!pair_live<KIND>(p, kv0 + jl, khi, a.m.window, dq, dj) || kv0 + jl < klo) x = -INFINITY;
+        bool ok = pair_live<KIND>(p, kv0 + jl, khi, a.m.window, dq, dj) && kv0 + jl >= klo;
+        if constexpr (BITS) ok &= (lds.bits[st][wave][lq] >> acc_row(r, hf)) & 1u;
+        if (!ok) x = -INFINITY;
       }
       s[r] = x;
       mx = fmaxf(mx, x);

@@ -12,7 +12,8 @@ constexpr int kMaxChunks = 2; // work items a query block may be split into
 constexpr int kHeadDim = 64;  // the one head dimension with kernels
 
 // The kernels' form of a mask kind: one of the rule families NONE, CAUSAL,
-// SLIDING_WINDOW, DOCUMENT, evaluated at the shifted query position
+// SLIDING_WINDOW, DOCUMENT (or CUSTOM, a bit-packed user mask), evaluated at
+// the shifted query position
 // p = i + q_off. The bottom-right kinds shift by S - L; the bidirectional
 // document kind shifts by kNoCausal, so that the causal part j <= p always
 // holds (positions stay below 2^22, so p cannot overflow).
@@ -26,6 +27,7 @@ inline MaskForm mask_form(int32_t kind, int32_t q_len, int32_t kv_len) {
     case 4 /* ATTN_MASK_CAUSAL_LOWER_RIGHT */: return {1, kv_len - q_len};
     case 5 /* ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT */: return {2, kv_len - q_len};
     case 6 /* ATTN_MASK_DOCUMENT_BIDIRECTIONAL */: return {3, kNoCausal};
+    // 7, ATTN_MASK_CUSTOM: its own family (the pair test reads the bits)
     default: return {kind, 0};
   }
 }
@@ -38,6 +40,8 @@ struct MaskView {
   const int32_t* full_idx;
   const int32_t* schedule;
   const int32_t* doc;
+  const uint32_t* bits;  // CUSTOM: [L][bits_w] bit-packed mask
+  int32_t bits_w;        // words per mask row, 4 * nk
   int32_t nq, nk;
   int32_t kind;   // rule family (MaskForm::kind)
   int32_t window;
@@ -146,10 +150,15 @@ inline int32_t packed_split_count(int64_t bhk, int32_t nk, size_t ws_bytes) {
 
 // Enqueue the block classification and the query-block schedule.
 // kind is the rule family and q_off the query offset (mask_form).
+// bits: the CUSTOM kind's bit-packed mask ([q_len][4 nk] words).
 hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const int32_t* doc,
-                             int32_t q_len, int32_t kv_len, int32_t nq, int32_t nk, int32_t* kv_num,
-                             int32_t* kv_idx, int32_t* full_num, int32_t* full_idx,
-                             int32_t* schedule, hipStream_t stream);
+                             const uint32_t* bits, int32_t q_len, int32_t kv_len, int32_t nq,
+                             int32_t nk, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
+                             int32_t* full_idx, int32_t* schedule, hipStream_t stream);
+
+// Enqueue the packing of a dense byte mask into the CUSTOM bit layout.
+hipError_t launch_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_len, int32_t kv_len,
+                            uint32_t* bits, hipStream_t stream);
 
 // Enqueue the fused forward. dtype is ATTN_F32 / ATTN_BF16 / ATTN_F16.
 hipError_t launch_forward(int32_t dtype, const FwdArgs& a, hipStream_t stream);

@@ -89,6 +89,16 @@ typedef int32_t attn_status;
 #define ATTN_MASK_CAUSAL_LOWER_RIGHT 4
 #define ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT 5
 #define ATTN_MASK_DOCUMENT_BIDIRECTIONAL 6
+/* CUSTOM: a user-supplied boolean mask M [q_len][kv_len], live iff M[i][j]
+ * (True keeps the pair: the boolean attn_mask convention of "SDPA replaces
+ * hand-written attention" (qiita, GeneLab_999), section 4, pitfall 1; the
+ * dense form the pages hand to SDPA, "FlexAttention on MPS vs SDPA" (qiita,
+ * kiarina), setup notes), held bit-packed on the device: row i is
+ * attn_mask_words(kv_len) = 4 * ceil(kv_len / 128) uint32 words, bit b of
+ * word w is M[i][32 w + b] (so one 16-byte group of a row covers one 128-key
+ * block); bits past kv_len are ignored. Built with
+ * attn_build_block_mask_custom, not attn_build_block_mask. */
+#define ATTN_MASK_CUSTOM 7
 
 /* score_mod applied to each scaled score s before the mask:
  *   NONE      s
@@ -149,6 +159,7 @@ typedef struct attn_block_mask {
   int32_t kind;
   int32_t window;
   const int32_t* document_id; /* device, borrowed: must stay valid while the mask is used */
+  const uint32_t* mask_bits;  /* CUSTOM: device bit-packed mask, borrowed likewise */
 } attn_block_mask;
 
 /* ceil(len / block_size) for len >= 0 and block_size == 128; -1 otherwise. */
@@ -164,12 +175,49 @@ int32_t attn_num_blocks(int32_t len, int32_t block_size);
  *   bm            host struct with the five array pointers set (non-null
  *                 unless the array has no elements)
  * Errors: INVALID_ARGUMENT for a null bm/array, q_len or kv_len < 0, a bad
- * window, a missing document_id or an unknown kind; UNSUPPORTED for
- * block_size != 128 or more than ATTN_MAX_KV_BLOCKS kv blocks.
+ * window, a missing document_id or an unknown kind (CUSTOM included: it has
+ * its own builder); UNSUPPORTED for block_size != 128 or more than
+ * ATTN_MAX_KV_BLOCKS kv blocks.
  */
 attn_status attn_build_block_mask(int32_t kind, int32_t window, const int32_t* document_id,
                                   int32_t q_len, int32_t kv_len, int32_t block_size,
                                   attn_block_mask* bm, void* stream);
+
+/* 32-bit words per row of a bit-packed CUSTOM mask: 4 * ceil(kv_len / 128)
+ * for kv_len >= 0; -1 otherwise. */
+int32_t attn_mask_words(int32_t kv_len);
+
+/*
+ * Pack a dense boolean mask into the CUSTOM bit layout (asynchronous on
+ * `stream`).
+ *   dense       device bytes, row i at dense + i * row_stride, byte j nonzero
+ *               = the pair (i, j) is live (a torch.bool or uint8 tensor)
+ *   row_stride  bytes between rows, >= kv_len
+ *   bits        device uint32 [q_len * attn_mask_words(kv_len)], 16-byte
+ *               aligned, written in full (bits past kv_len are 0)
+ * Errors: INVALID_ARGUMENT for null pointers with a non-empty mask, negative
+ * sizes, row_stride < kv_len or misaligned bits; HIP for a failed launch.
+ */
+attn_status attn_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_len, int32_t kv_len,
+                           uint32_t* bits, void* stream);
+
+/*
+ * Build a BlockMask of kind CUSTOM from a bit-packed mask (asynchronous on
+ * `stream`). Every 128 x 128 block is classified from its bits: no live
+ * in-range pair -> skipped, all 128 x 128 pairs in range and live -> full,
+ * else partial ("FlexAttention on Apple Silicon: block masks", closing
+ * section: only fully masked blocks can be skipped). The work plan is the
+ * same as attn_build_block_mask's.
+ *   bits   device uint32 [q_len * attn_mask_words(kv_len)], 16-byte
+ *          aligned; stored in
+ *          bm->mask_bits and read again by attn_forward, so it must stay
+ *          valid and unchanged while the mask is used
+ *   q_len, kv_len, block_size, bm  as for attn_build_block_mask
+ * Errors: those of attn_build_block_mask, and INVALID_ARGUMENT for null bits
+ * with q_len * kv_len > 0 or misaligned bits.
+ */
+attn_status attn_build_block_mask_custom(const uint32_t* bits, int32_t q_len, int32_t kv_len,
+                                         int32_t block_size, attn_block_mask* bm, void* stream);
 
 /*
  * Bytes of device workspace attn_forward needs for this problem (0 when it

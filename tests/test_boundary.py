@@ -75,7 +75,8 @@ def _build(kind=1, window=0, doc=None, q_len=256, kv_len=256, block=128, bm=None
 
 
 BUILD_CASES = [
-    ("unknown_kind", dict(kind=7), INVALID, "kind"),
+    ("custom_kind_needs_its_builder", dict(kind=7), INVALID, "attn_build_block_mask_custom"),
+    ("unknown_kind", dict(kind=8), INVALID, "kind"),
     ("negative_kind", dict(kind=-1), INVALID, "kind"),
     ("lower_right_window_zero", dict(kind=5, window=0), INVALID, "window"),
     ("bidirectional_document_without_ids", dict(kind=6, doc=None), INVALID, "document"),
@@ -135,7 +136,8 @@ FWD_CASES = [
      "inconsistent"),
     ("bidirectional_mask_without_ids", dict(bm=_built_mask(256, 256, kind=6)), INVALID,
      "inconsistent"),
-    ("unknown_mask_kind", dict(bm=_built_mask(256, 256, kind=7)), INVALID, "inconsistent"),
+    ("custom_mask_without_bits", dict(bm=_built_mask(256, 256, kind=7)), INVALID, "inconsistent"),
+    ("unknown_mask_kind", dict(bm=_built_mask(256, 256, kind=8)), INVALID, "inconsistent"),
     ("unknown_score_mod", dict(score_mod=4), INVALID, "score_mod"),
     ("softcap_zero", dict(score_mod=1, softcap=0.0), INVALID, "soft-cap"),
     ("softcap_nan", dict(score_mod=1, softcap=float("nan")), INVALID, "soft-cap"),
@@ -259,3 +261,56 @@ def test_binding_rejects_float64():
     q = torch.zeros(1, 1, 128, 64, dtype=torch.float64)
     with pytest.raises(ValueError):
         bsa.attention(q, q, q, block_mask=None)
+
+
+def test_mask_words():
+    lib = bsa._load()
+    assert [lib.attn_mask_words(n) for n in (0, 1, 128, 129, 8192)] == [0, 4, 4, 8, 256]
+    assert lib.attn_mask_words(-1) == -1
+    assert bsa.mask_words(1000) == 32
+
+
+def _build_custom(bits=FAKE, q_len=256, kv_len=256, block=128, bm=None):
+    lib = bsa._load()
+    bm = _bm() if bm is None else bm
+    return lib.attn_build_block_mask_custom(bits, q_len, kv_len, block, ctypes.byref(bm), None)
+
+
+CUSTOM_BUILD_CASES = [
+    ("null_bits", dict(bits=None), INVALID, "bits"),
+    ("misaligned_bits", dict(bits=FAKE + 4), INVALID, "aligned"),
+    ("negative_len", dict(kv_len=-3), INVALID, "negative"),
+    ("block_64", dict(block=64), UNSUPPORTED, "block_size"),
+    ("null_array", dict(bm=_bm(schedule=None)), INVALID, "null"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code,words", CUSTOM_BUILD_CASES, ids=[c[0] for c in CUSTOM_BUILD_CASES])
+def test_build_block_mask_custom_validation(name, kw, code, words):
+    assert _build_custom(**kw) == code
+    assert words in bsa._load().attn_last_error().decode()
+
+
+PACK_CASES = [
+    ("negative_len", dict(q_len=-1), INVALID, "negative"),
+    ("short_row_stride", dict(row_stride=99), INVALID, "row_stride"),
+    ("null_dense", dict(dense=None), INVALID, "non-null"),
+    ("null_bits", dict(bits=None), INVALID, "non-null"),
+    ("misaligned_bits", dict(bits=FAKE + 8), INVALID, "aligned"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code,words", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_pack_mask_validation(name, kw, code, words):
+    a = dict(dense=FAKE, row_stride=100, q_len=10, kv_len=100, bits=FAKE)
+    a.update(kw)
+    lib = bsa._load()
+    assert lib.attn_pack_mask(a["dense"], a["row_stride"], a["q_len"], a["kv_len"], a["bits"], None) == code
+    assert words in lib.attn_last_error().decode()
+
+
+def test_binding_custom_kind_needs_its_own_constructor():
+    with pytest.raises(ValueError, match="create_block_mask_from_dense"):
+        bsa.create_block_mask("custom", 128, 128)

@@ -87,7 +87,8 @@ def _odd(name, dtype, H, L, S, kind, window=0, bounds=(), softcap=0.0, B=1):
     return wl.Workload(name, B, H, L, S, 64, dtype, kind, window, bounds, softcap)
 
 
-MASK_CASES = list(wl.WORKLOADS.values()) + [
+# (user-supplied masks have their own tests: test_custom_mask_gpu.py)
+MASK_CASES = [w for w in wl.WORKLOADS.values() if w.kind != wl.MASK_CUSTOM] + [
     _odd("none_300x200", "bf16", 1, 300, 200, wl.MASK_NONE),
     _odd("causal_1000", "bf16", 1, 1000, 1000, wl.MASK_CAUSAL),
     _odd("causal_L200_S700", "bf16", 1, 200, 700, wl.MASK_CAUSAL),

@@ -36,6 +36,16 @@ Variant workloads (the mask and head-sharing variants of the same kernel):
   padding: batch entry 0 keeps every key, entry 1 keys [2048, 7168) (left
   and right padding ANDed with the causal mask; SDPA page, section 4,
   pitfall 1 and section 5).
+* ``custom_blocks_8192_bf16`` -- H=8, L=S=8192 with a user-supplied dense
+  boolean mask (the form SDPA takes masks in: "FlexAttention on MPS vs SDPA",
+  setup notes; True keeps the pair: SDPA page, section 4, pitfall 1): each
+  128 x 128 block is all True with probability 0.08, holds i.i.d. pairs kept
+  with probability 0.5 with probability 0.06, and is all False otherwise
+  (about 14% of the blocks live, like the table's W=1024 row), seed 11.
+
+User masks (``block_structured_mask``): per 128 x 128 block one uniform draw
+picks full / partial / empty, then the partial blocks' pairs are drawn
+i.i.d.; both from ``numpy.random.default_rng(seed)``.
 
 Generation: ``numpy.random.default_rng(seed).standard_normal(shape, float32)``
 drawn for q, then k, then v, then rounded to the workload dtype with
@@ -58,6 +68,7 @@ MASK_DOCUMENT = 3
 MASK_CAUSAL_LOWER_RIGHT = 4
 MASK_SLIDING_WINDOW_LOWER_RIGHT = 5
 MASK_DOCUMENT_BIDIRECTIONAL = 6
+MASK_CUSTOM = 7
 DOCUMENT_KINDS = (MASK_DOCUMENT, MASK_DOCUMENT_BIDIRECTIONAL)
 
 BLOCK = 128
@@ -80,6 +91,7 @@ class Workload:
     softcap: float = 0.0  # 0 = no score_mod, else c in c*tanh(s/c)
     H_kv: int = 0         # K/V heads (grouped-query attention); 0 = H
     key_ranges: tuple = ()  # per batch entry (start, end) kept keys; () = no padding
+    mask_recipe: tuple = ()  # CUSTOM: (p_full, p_partial, density, seed) of block_structured_mask
 
     @property
     def kv_heads(self) -> int:
@@ -119,6 +131,8 @@ WORKLOADS = {
                  key_ranges=((0, 8192), (2048, 7168))),
         Workload("decode_gqa_b8_h32_kv8_s8192_bf16", 8, 32, 1, 8192, 64, "bf16",
                  MASK_CAUSAL_LOWER_RIGHT, H_kv=8),
+        Workload("custom_blocks_8192_bf16", 1, 8, 8192, 8192, 64, "bf16", MASK_CUSTOM,
+                 mask_recipe=(0.08, 0.06, 0.5, 11)),
     ]
 }
 
@@ -142,6 +156,27 @@ def make_qkv(w: Workload, seed: int = 0):
         x = rng.standard_normal(shp, dtype=np.float32)
         out.append(torch.from_numpy(x).to(w.torch_dtype))
     return tuple(out)
+
+
+def block_structured_mask(L: int, S: int, seed: int, p_full: float = 0.1, p_partial: float = 0.1,
+                          density: float = 0.5) -> np.ndarray:
+    """Seeded boolean [L, S]: each 128 x 128 block (ragged at the ends) is all
+    True with probability p_full, i.i.d. pairs kept with probability
+    `density` with probability p_partial, all False otherwise."""
+    rng = np.random.default_rng(seed)
+    nq, nk = -(-L // BLOCK), -(-S // BLOCK)
+    u = rng.random((nq, nk))
+    full = np.repeat(np.repeat(u < p_full, BLOCK, 0), BLOCK, 1)[:L, :S]
+    part = np.repeat(np.repeat((u >= p_full) & (u < p_full + p_partial), BLOCK, 0), BLOCK, 1)[:L, :S]
+    return full | (part & (rng.random((L, S), dtype=np.float32) < density))
+
+
+def make_mask(w: Workload) -> Optional[np.ndarray]:
+    """The user mask of a CUSTOM workload (None for the rule kinds)."""
+    if w.kind != MASK_CUSTOM:
+        return None
+    p_full, p_partial, density, seed = w.mask_recipe
+    return block_structured_mask(w.L, w.S, seed, p_full, p_partial, density)
 
 
 def make_doc(w: Workload) -> Optional[np.ndarray]:
