@@ -19,6 +19,8 @@ user-supplied L x S boolean mask (True keeps the pair).
 * ``block_mask``  -- 128x128 block classification by brute force over every
   in-range pair: skip / partial / full, with ascending index lists padded by 0.
 * ``count_live``  -- number of live (query, key) pairs of a mask.
+* ``attention_backward`` -- dq, dk, dv of sum(dO * O) by the chain rule, the
+  attention matrix recomputed per row.
 * ``pack_mask``   -- bit-packed form of a dense boolean mask: row i is
   4 * ceil(S / 128) uint32 words, bit b of word w is M[i, 32 w + b].
 
@@ -105,6 +107,10 @@ class Oracle:
         lib.oracle_attention.argtypes = [f64p, f64p, f64p, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, i64, i32p, u8p, ctypes.c_double,
                                          ctypes.c_double, i64p, i64p, i64p, i64, f64p, f64p]
+        lib.oracle_attention_backward.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = [f64p, f64p, f64p, f64p, i64, i64, i64, i64, i64,
+                                                  ctypes.c_int, i64, i32p, u8p, ctypes.c_double,
+                                                  ctypes.c_double, i64p, i64p, f64p, f64p, f64p]
         self._lib = lib
 
     @staticmethod
@@ -217,6 +223,34 @@ class Oracle:
 _default: Optional[Oracle] = None
 
 
+def _attention_backward(self, q, k, v, dout, kind: int, scale: float, window: int = 0, doc=None,
+                        softcap: float = 0.0, key_start=None, key_end=None, mask=None):
+    """fp64 gradients (dq, dk, dv) of sum(dout * O) for O = attention(q, k, v,
+    ...): q, dout [B,H,L,E], k, v [B,H,S,E] (K/V heads expanded to H)."""
+    q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, H, L, E = q.shape
+    S = k.shape[2]
+    if k.shape != (B, H, S, E) or v.shape != (B, H, S, E) or dout.shape != q.shape:
+        raise ValueError("q/k/v/dout shapes disagree (the backward takes E = Ev)")
+    d = _doc(doc)
+    self._check_doc(kind, d, L, S)
+    m = _dense(kind, mask, L, S)
+    ks = None if key_start is None else np.ascontiguousarray(key_start, dtype=np.int64)
+    ke = None if key_end is None else np.ascontiguousarray(key_end, dtype=np.int64)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    rc = self._lib.oracle_attention_backward(
+        _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+        _ptr(dout, ctypes.c_double), B, H, L, S, E, kind, window, _ptr(d, ctypes.c_int32),
+        _ptr(m, ctypes.c_uint8), softcap, scale, _ptr(ks, ctypes.c_int64), _ptr(ke, ctypes.c_int64),
+        _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_backward failed")
+    return dq, dk, dv
+
+
+Oracle.attention_backward = _attention_backward
+
+
 def default() -> Oracle:
     """The oracle built from oracle.c (built on first use if missing or stale)."""
     global _default
@@ -251,3 +285,9 @@ def attention(q, k, v, kind, scale, window=0, doc=None, softcap=0.0, rows=None, 
               key_end=None, mask=None):
     return default().attention(q, k, v, kind, scale, window, doc, softcap, rows, key_start, key_end,
                                mask)
+
+
+def attention_backward(q, k, v, dout, kind, scale, window=0, doc=None, softcap=0.0, key_start=None,
+                       key_end=None, mask=None):
+    return default().attention_backward(q, k, v, dout, kind, scale, window, doc, softcap, key_start,
+                                        key_end, mask)

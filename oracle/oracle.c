@@ -65,6 +65,20 @@
  *    Here each block is classified by brute force: every in-range pair is
  *    evaluated with the predicate and counted.
  *
+ *  - The backward: gradients of the scalar sum(dO * O) with respect to q, k
+ *    and v, with the attention matrix recomputed instead of stored (page
+ *    "Flash Attention 2 and the IO bottleneck" (tcdigital), section on
+ *    recomputation in backpropagation). Written out by the chain rule from
+ *    the forward definition: with P the row softmax of the masked scores
+ *    s' = mod(scale * q.k) (mod = identity, or c * tanh(. / c)),
+ *      dV_j  = sum_i P_ij dO_i
+ *      dP_ij = dO_i . v_j,   D_i = sum_j P_ij dP_ij
+ *      dS'_ij = P_ij (dP_ij - D_i)
+ *      dS_ij = dS'_ij * scale * mod'(scale q_i.k_j),  mod' = 1 - (s'/c)^2 or 1
+ *      dQ_i = sum_j dS_ij k_j,   dK_j = sum_i dS_ij q_i
+ *    Masked pairs have P = 0 and so no gradient; a row with no live key has
+ *    P = 0 and contributes nothing.
+ *
  * Arithmetic is fp64 throughout (libm exp, tanh, log). Rows are independent;
  * OpenMP spreads whole rows over threads and changes no arithmetic order
  * inside a row.
@@ -201,6 +215,29 @@ int oracle_pack_mask(const uint8_t* dense, int64_t L, int64_t S, uint32_t* bits)
 }
 
 /*
+ * Steps 1-3 for query row i of one (batch, head): s[j] = the scaled score
+ * q_i.k_j * scale, soft-capped when softcap > 0, and -inf where the mask or
+ * the kept key range [kept_lo, kept_hi) drops the pair. Returns the row max
+ * (-inf when no key is live).
+ */
+static double row_scores(const double* qi, const double* kh, int64_t L, int64_t S, int64_t E,
+                         int64_t i, int kind, int64_t window, const int32_t* doc,
+                         const uint8_t* dense, double softcap, double scale, int64_t kept_lo,
+                         int64_t kept_hi, double* s) {
+  double m = -INFINITY;
+  for (int64_t j = 0; j < S; ++j) {
+    double dot = 0.0;
+    for (int64_t e = 0; e < E; ++e) dot += qi[e] * kh[j * E + e];
+    double sc = dot * scale;
+    if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
+    if (!live(kind, window, doc, dense, L, S, i, j) || j < kept_lo || j >= kept_hi) sc = -INFINITY;
+    s[j] = sc;
+    if (sc > m) m = sc;
+  }
+  return m;
+}
+
+/*
  * Masked softmax attention, fp64, for a list of rows.
  *   q [B,H,L,E], k [B,H,S,E], v [B,H,S,Ev]: contiguous fp64.
  *   key_start, key_end: per batch entry [B], the kept key range [start, end),
@@ -239,16 +276,8 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
       double* o = out + n * Ev;
 
       /* Step 1-3: scores, scale, score_mod, mask. */
-      double m = -INFINITY;
-      for (int64_t j = 0; j < S; ++j) {
-        double dot = 0.0;
-        for (int64_t e = 0; e < E; ++e) dot += qi[e] * kh[j * E + e];
-        double sc = dot * scale;
-        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);
-        if (!live(kind, window, doc, dense, L, S, i, j) || j < kept_lo || j >= kept_hi) sc = -INFINITY;
-        s[j] = sc;
-        if (sc > m) m = sc;
-      }
+      const double m = row_scores(qi, kh, L, S, E, i, kind, window, doc, dense, softcap, scale,
+                                  kept_lo, kept_hi, s);
       /* Step 4: softmax, then mix V. */
       for (int64_t e = 0; e < Ev; ++e) o[e] = 0.0;
       if (m == -INFINITY) {
@@ -266,6 +295,77 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
       lse[n] = m + log(l);
     }
     free(s);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Backward of oracle_attention (all rows): q [B,H,L,E], k, v [B,H,S,E], dout
+ * [B,H,L,E] contiguous fp64 (K/V heads already expanded to H); outputs dq
+ * [B,H,L,E], dk, dv [B,H,S,E]. Same mask arguments as oracle_attention.
+ * Returns 0, or -1 on bad sizes / allocation failure.
+ */
+int oracle_attention_backward(const double* q, const double* k, const double* v, const double* dout,
+                              int64_t B, int64_t H, int64_t L, int64_t S, int64_t E, int kind,
+                              int64_t window, const int32_t* doc, const uint8_t* dense, double softcap,
+                              double scale, const int64_t* key_start, const int64_t* key_end,
+                              double* dq, double* dk, double* dv) {
+  if (B < 0 || H < 0 || L < 0 || S < 0 || E <= 0) return -1;
+  memset(dq, 0, sizeof(double) * (size_t)(B * H * L * E));
+  memset(dk, 0, sizeof(double) * (size_t)(B * H * S * E));
+  memset(dv, 0, sizeof(double) * (size_t)(B * H * S * E));
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    double* sp = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));  /* scores s' */
+    double* p = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));   /* P */
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));  /* dP */
+    if (sp == NULL || p == NULL || dp == NULL) {
+      failed = 1;
+      free(sp), free(p), free(dp);
+      continue;
+    }
+    const int64_t b = bh / H;
+    const int64_t kept_lo = key_start ? key_start[b] : 0;
+    const int64_t kept_hi = key_end ? key_end[b] : S;
+    const double* kh = k + bh * S * E;
+    const double* vh = v + bh * S * E;
+    double* dkh = dk + bh * S * E;
+    double* dvh = dv + bh * S * E;
+    for (int64_t i = 0; i < L; ++i) {
+      const double* qi = q + (bh * L + i) * E;
+      const double* doi = dout + (bh * L + i) * E;
+      double* dqi = dq + (bh * L + i) * E;
+      /* forward: masked scores and their softmax */
+      const double m = row_scores(qi, kh, L, S, E, i, kind, window, doc, dense, softcap, scale,
+                                  kept_lo, kept_hi, sp);
+      if (m == -INFINITY) continue; /* no live key: P = 0, no gradient */
+      double l = 0.0;
+      for (int64_t j = 0; j < S; ++j) {
+        p[j] = exp(sp[j] - m);
+        l += p[j];
+      }
+      for (int64_t j = 0; j < S; ++j) p[j] /= l;
+      /* dP and D */
+      double D = 0.0;
+      for (int64_t j = 0; j < S; ++j) {
+        double t = 0.0;
+        for (int64_t e = 0; e < E; ++e) t += doi[e] * vh[j * E + e];
+        dp[j] = t;
+        D += p[j] * t;
+      }
+      for (int64_t j = 0; j < S; ++j) {
+        if (p[j] == 0.0) continue;
+        double ds = p[j] * (dp[j] - D) * scale;
+        if (softcap > 0.0) ds *= 1.0 - (sp[j] / softcap) * (sp[j] / softcap);
+        for (int64_t e = 0; e < E; ++e) {
+          dqi[e] += ds * kh[j * E + e];
+          dkh[j * E + e] += ds * qi[e];
+          dvh[j * E + e] += p[j] * doi[e];
+        }
+      }
+    }
+    free(sp), free(p), free(dp);
   }
   return failed ? -1 : 0;
 }

@@ -571,6 +571,105 @@ def check_dense_mask_equals_rules(orc):
         assert all(np.array_equal(x, y) for x, y in zip(a, b)), kind
 
 
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+def _torch_attention(q, k, v, keep, scale, softcap=0.0):
+    """Masked softmax attention composed of torch ops (fp64, CPU), for
+    autograd: keep [L, S] or [B, 1, L, S] boolean."""
+    sc = (q @ k.transpose(-2, -1).contiguous()) * scale
+    if softcap > 0.0:
+        sc = softcap * torch.tanh(sc / softcap)
+    sc = sc.masked_fill(~keep, float("-inf"))
+    return torch.softmax(sc, dim=-1) @ v
+
+
+def check_backward_matches_autograd(orc):
+    """dq, dk, dv of sum(dO * O) equal torch autograd through the composed
+    attention (fp64), for the rule kinds, a dense mask, the soft-cap, key
+    padding and grouped K/V heads (the gradient of a shared head is the sum
+    over the query heads that read it)."""
+    B, H, Hk, L, S, E = 2, 4, 2, 23, 31, 8
+    rng = np.random.default_rng(81)
+    doc = np.repeat([0, 1, 2], [9, 12, 10]).astype(np.int32)
+    dense = rng.random((L, S)) < 0.4
+    dense[np.arange(L), rng.integers(0, S, L)] = True
+    i, j = np.arange(L)[:, None], np.arange(S)[None, :]
+    cases = [
+        (NONE, 0, None, None, np.ones((L, S), bool), 0.0, None),
+        (CAUSAL_LR, 0, None, None, j <= i + (S - L), 0.0, None),
+        (SLIDING, 5, None, None, (j <= i) & (i - j < 5), 7.0, None),
+        (DOCUMENT_BIDIR, 0, doc, None, doc[:L, None] == doc[None, :S], 0.0, None),
+        (DENSE, 0, None, dense, dense, 3.0, None),
+        (CAUSAL_LR, 0, None, None, j <= i + (S - L), 0.0, ([2, 0], [31, 20])),
+    ]
+    q, dout = _rand((B, H, L, E), 82), _rand((B, H, L, E), 85)
+    kk, vv = _rand((B, Hk, S, E), 83), _rand((B, Hk, S, E), 84)
+    for kind, win, d, m, keep, cap, pad in cases:
+        ke, ve = (np.repeat(x, H // Hk, axis=1) for x in (kk, vv))
+        keep_b = np.broadcast_to(keep, (B, 1, L, S)).copy()
+        if pad is not None:
+            for b in range(B):
+                keep_b[b, :, :, :pad[0][b]] = False
+                keep_b[b, :, :, pad[1][b]:] = False
+        dq, dk, dv = orc.attention_backward(q, ke, ve, dout, kind, 0.3, win, d, cap,
+                                            key_start=None if pad is None else pad[0],
+                                            key_end=None if pad is None else pad[1], mask=m)
+        dk = dk.reshape(B, Hk, H // Hk, S, E).sum(2)
+        dv = dv.reshape(B, Hk, H // Hk, S, E).sum(2)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, kk, vv))
+        o = _torch_attention(tq, tk.repeat_interleave(H // Hk, 1), tv.repeat_interleave(H // Hk, 1),
+                             torch.from_numpy(keep_b), 0.3, cap)
+        (o * torch.from_numpy(dout)).sum().backward()
+        for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+            assert np.abs(got - t.grad.numpy()).max() <= 1e-12, kind
+
+
+def check_backward_finite_differences(orc):
+    """Gradients against central differences of the oracle's own forward
+    (f = sum(dO * O)) on sampled elements of q, k and v, with the soft-cap
+    and a sliding window."""
+    rng = np.random.default_rng(86)
+    q, k, v, dout = _rand((1, 2, 9, 4), 87), _rand((1, 2, 13, 4), 88), _rand((1, 2, 13, 4), 89), \
+        _rand((1, 2, 9, 4), 90)
+    args = dict(kind=SLIDING_LR, scale=0.45, window=6, softcap=2.5)
+    dq, dk, dv = orc.attention_backward(q, k, v, dout, args["kind"], args["scale"], args["window"],
+                                        softcap=args["softcap"])
+
+    def f(q_, k_, v_):
+        o, _ = orc.attention(q_, k_, v_, args["kind"], args["scale"], args["window"],
+                             softcap=args["softcap"])
+        return float((o * dout).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = (q, k, v)
+            pos = {"q": 0, "k": 1, "v": 2}[name]
+            fp = f(*[xp if t == pos else a[t] for t in range(3)])
+            fm = f(*[xm if t == pos else a[t] for t in range(3)])
+            assert abs((fp - fm) / (2 * h) - g[idx]) <= 1e-7, (name, idx)
+
+
+def check_backward_empty_rows_and_unseen_keys(orc):
+    """A query row with no live key gets dq = 0; a key no query sees gets
+    dk = dv = 0."""
+    q, k, v, dout = _rand((1, 1, 6, 4), 91), _rand((1, 1, 8, 4), 92), _rand((1, 1, 8, 4), 93), \
+        _rand((1, 1, 6, 4), 94)
+    m = np.ones((6, 8), bool)
+    m[3] = False
+    m[:, 5] = False
+    dq, dk, dv = orc.attention_backward(q, k, v, dout, DENSE, 0.5, mask=m)
+    assert np.all(dq[0, 0, 3] == 0.0) and np.any(dq[0, 0, 2] != 0.0)
+    assert np.all(dk[0, 0, 5] == 0.0) and np.all(dv[0, 0, 5] == 0.0)
+    assert np.any(dk[0, 0, 4] != 0.0) and np.any(dv[0, 0, 4] != 0.0)
+
+
 ALL_CHECKS = [
     check_flex_table_densities,
     check_live_pair_closed_forms,
@@ -603,4 +702,7 @@ ALL_CHECKS = [
     check_dense_mask_matches_sdpa,
     check_dense_mask_empty_rows,
     check_dense_mask_equals_rules,
+    check_backward_matches_autograd,
+    check_backward_finite_differences,
+    check_backward_empty_rows_and_unseen_keys,
 ]

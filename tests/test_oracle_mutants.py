@@ -16,12 +16,12 @@ MUTANTS = [
     ("document_without_causal", "return i >= j && doc[i] == doc[j];", "return doc[i] == doc[j];"),
     ("dropped_scale", "double sc = dot * scale;", "double sc = dot;"),
     ("softcap_before_scale",
-     "double sc = dot * scale;\n        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);",
-     "double sc = dot;\n        if (softcap > 0.0) sc = softcap * tanh(sc / softcap);\n"
-     "        sc *= scale;"),
+     "double sc = dot * scale;\n    if (softcap > 0.0) sc = softcap * tanh(sc / softcap);",
+     "double sc = dot;\n    if (softcap > 0.0) sc = softcap * tanh(sc / softcap);\n"
+     "    sc *= scale;"),
     ("lse_log2", "lse[n] = m + log(l);", "lse[n] = m + log2(l);"),
     ("missing_normalisation", "for (int64_t e = 0; e < Ev; ++e) o[e] /= l;", ""),
-    ("transposed_k", "kh[j * E + e]", "kh[e * S + j]"),
+    ("transposed_k", "dot += qi[e] * kh[j * E + e]", "dot += qi[e] * kh[e * S + j]"),
     ("reversed_v", "vh[j * Ev + e]", "vh[(S - 1 - j) * Ev + e]"),
     ("full_threshold", "if (count == bs * bs)", "if (count * 2 >= bs * bs)"),
     ("pad_minus_one", "      kv_idx[qb * nk + t] = 0;", "      kv_idx[qb * nk + t] = -1;"),
@@ -38,6 +38,12 @@ MUTANTS = [
     ("dense_inverted", "return dense[i * S + j] != 0;", "return dense[i * S + j] == 0;"),
     ("pack_bit_order", "word |= (uint32_t)1 << b;", "word |= (uint32_t)1 << (31 - b);"),
     ("pack_words_per_row", "const int64_t W = 4 * ((S + 127) / 128);", "const int64_t W = (S + 31) / 32;"),
+    ("bwd_drops_row_term", "double ds = p[j] * (dp[j] - D) * scale;", "double ds = p[j] * dp[j] * scale;"),
+    ("bwd_drops_scale", "double ds = p[j] * (dp[j] - D) * scale;", "double ds = p[j] * (dp[j] - D);"),
+    ("bwd_drops_softcap_derivative",
+     "if (softcap > 0.0) ds *= 1.0 - (sp[j] / softcap) * (sp[j] / softcap);", ""),
+    ("bwd_dv_from_ds", "dvh[j * E + e] += p[j] * doi[e];", "dvh[j * E + e] += ds * doi[e];"),
+    ("bwd_dk_from_dout", "dkh[j * E + e] += ds * qi[e];", "dkh[j * E + e] += ds * doi[e];"),
     ("bidirectional_keeps_causal", "      return doc[i] == doc[j];\n",
      "      return i >= j && doc[i] == doc[j];\n"),
 ]
