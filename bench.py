@@ -13,6 +13,9 @@ are the mask and head-sharing variants (bottom-right causal, grouped-query
 heads, bidirectional documents, key padding, split-KV / packed-row decode,
 and a user-supplied dense mask) under "workloads".
 
+The backward (dq, dk, dv after one forward) of the causal workload is timed
+the same way and reported under "backward" (10 E flops per live pair).
+
 Prints one JSON line. ``value`` is live-pair TFLOPS of the whole step
 (4 * E flops per unmasked (query, key) pair); ``forward_only`` has the
 forward kernel alone, which is what the FlexAttention-on-MPS table times.
@@ -166,6 +169,54 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     return dict(wall_ms=wall_ms, mask_ms=mask_ms, fwd_ms=fwd_ms)
 
 
+def run_backward(w: wl.Workload, steps: int, warmup: int, dev):
+    """Per-call time of the backward (attn_backward: D and the transposed mask,
+    then the dK/dV and dQ kernels) after one forward, in batches of back-to-back
+    launches timed with events on the stream they run on."""
+    q, k, v = (x.to(dev) for x in wl.make_qkv(w, 0))
+    dout = torch.from_numpy(np.random.default_rng(99).standard_normal(
+        (w.B, w.H, w.L, w.E), dtype=np.float32)).to(w.torch_dtype).to(dev)
+    doc = wl.make_doc(w)
+    bm = bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None,
+                               document_id=None if doc is None else torch.from_numpy(doc).to(dev),
+                               device=dev)
+    sm = "softcap" if w.softcap else None
+    o, lse = bsa.attention(q, k, v, bm, score_mod=sm, softcap=w.softcap or 30.0, scale=w.scale,
+                           return_lse=True)
+
+    def bwd():
+        bsa.attention_backward(q, k, v, o, lse, dout, bm, score_mod=sm, softcap=w.softcap or 30.0,
+                               scale=w.scale)
+
+    for _ in range(max(1, warmup // 4)):
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    batch, times = 5, []
+    gc.disable()
+    try:
+        events = []
+        for _ in range(max(1, steps // (2 * batch))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            bwd()
+            e0.record(stream)
+            for _ in range(batch):
+                bwd()
+            e1.record(stream)
+            events.append((e0, e1))
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) / batch for a, b in events]
+    finally:
+        gc.enable()
+    ms = float(np.mean(times))
+    # 5 products of 2 E flops per live pair (S, dP, dV, dK, dQ; the second
+    # score product of the dQ kernel is recomputation, not counted)
+    flops = 10.0 * w.E * live_pairs(w) * w.B * w.H
+    return {"workload": w.name, "ms": ms, "min_ms": float(np.min(times)),
+            "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def summarize(w: wl.Workload, r):
     flops = 4.0 * w.E * live_pairs(w) * w.B * w.H
     fwd_avg = float(r["fwd_ms"].mean())
@@ -258,6 +309,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workloads", default=",".join((HEADLINE, SECOND) + VARIANTS))
+    ap.add_argument("--backward", default=HEADLINE,
+                    help="workloads whose backward is timed too (comma list; empty for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel that scales HBM traffic counters in profiler runs)")
@@ -288,6 +341,13 @@ def main():
         print(f"bench: {n} forward {results[n]['forward_ms']['mean']:.4f} ms "
               f"{results[n]['forward_tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
 
+    backward = {}
+    for n in [x for x in args.backward.split(",") if x]:
+        print(f"bench: {n} backward ...", file=sys.stderr, flush=True)
+        backward[n] = run_backward(wl.WORKLOADS[n], args.steps, args.warmup, dev)
+        print(f"bench: {n} backward {backward[n]['ms']:.4f} ms {backward[n]['tflops']:.1f} TFLOPS",
+              file=sys.stderr, flush=True)
+
     head = results[names[0]]
     w = wl.WORKLOADS[names[0]]
     line = {
@@ -317,6 +377,7 @@ def main():
                      "per_launch_flop": head["live_gflop"] * 1e9,
                      "launch_ms": head["forward_ms"]["mean"]},
         "workloads": results,
+        "backward": backward,
     }
     if SECOND in results:
         s = results[SECOND]

@@ -31,7 +31,8 @@ import torch
 
 __all__ = [
     "BlockMask", "BsattnError", "create_block_mask", "create_block_mask_from_dense",
-    "create_block_mask_from_bits", "pack_mask", "mask_words", "attention", "num_blocks", "library_path",
+    "create_block_mask_from_bits", "pack_mask", "mask_words", "attention", "attention_backward",
+    "num_blocks", "library_path",
     "workspace_size",
     "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
     "MASK_CAUSAL_LOWER_RIGHT", "MASK_SLIDING_WINDOW_LOWER_RIGHT", "MASK_DOCUMENT_BIDIRECTIONAL",
@@ -113,6 +114,13 @@ def _load():
     lib.attn_pack_mask.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp]
     lib.attn_build_block_mask_custom.restype = i32
     lib.attn_build_block_mask_custom.argtypes = [vp, i32, i32, i32, ctypes.POINTER(_BlockMaskStruct), vp]
+    lib.attn_backward.restype = i32
+    lib.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                  ctypes.POINTER(_BlockMaskStruct), i32, ctypes.c_float, ctypes.c_float,
+                                  vp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_backward_workspace_size.restype = i32
+    lib.attn_backward_workspace_size.argtypes = [i32, i32, ctypes.POINTER(_BlockMaskStruct),
+                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_forward.restype = i32
     lib.attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                  i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
@@ -390,3 +398,52 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
                 ctypes.byref(block_mask._struct), sm, float(softcap), float(scale),
                 ws_ptr, ws_bytes, stream))
     return (out, lse) if return_lse else out
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor, dout: torch.Tensor, block_mask: BlockMask,
+                       score_mod: Optional[str] = None, softcap: float = 30.0,
+                       scale: Optional[float] = None, key_start: Optional[torch.Tensor] = None,
+                       key_end: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(dout * out) through ``attention`` (bf16
+    or fp16), with the attention matrix recomputed from ``lse`` (the forward's
+    logsumexp) by attn_backward. ``out`` and ``lse`` are the forward's outputs
+    for the same arguments; k and v may have fewer heads (grouped-query
+    attention), and dk, dv then sum over the query heads that share a K/V head.
+    Tensors are made contiguous; the call is asynchronous on the current
+    stream."""
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("the backward takes bfloat16 or float16")
+    for t in (k, v, out, dout):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, out and dout must share dtype and device")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a cuda device")
+    B, H, L, E = q.shape
+    Hk, S = k.shape[1], k.shape[2]
+    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[0] != B:
+        raise ValueError("shape mismatch")
+    if lse.shape != (B, H, L) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, L]")
+    q, k, v, out, dout, lse = (t.contiguous() for t in (q, k, v, out, dout, lse))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    lib = _load()
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.attn_backward_workspace_size(B, H, ctypes.byref(block_mask._struct), ctypes.byref(nbytes)))
+    ws = torch.empty(max(nbytes.value, 1) + 256, dtype=torch.uint8, device=q.device)
+    ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+    sm = SCORE_SOFTCAP if score_mod == "softcap" else SCORE_NONE
+    if score_mod not in (None, "softcap"):
+        raise ValueError(f"unknown score_mod {score_mod!r}")
+    sc = 1.0 / math.sqrt(E) if scale is None else float(scale)
+    ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
+    for t in (key_start, key_end):
+        if t is not None and (t.dtype != torch.int32 or t.shape != (B,) or t.device != q.device):
+            raise ValueError("key_start / key_end must be int32 [B] on the tensors' device")
+    with torch.cuda.device(q.device):
+        _check(lib.attn_backward(ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), ptr(dout), ptr(dq), ptr(dk),
+                                 ptr(dv), _DTYPES[q.dtype], B, H, Hk, L, S, E,
+                                 ctypes.byref(block_mask._struct), sm, float(softcap), sc,
+                                 ptr(key_start), ptr(key_end), ws_ptr, nbytes.value,
+                                 _stream_handle(q.device)))
+    return dq, dk, dv

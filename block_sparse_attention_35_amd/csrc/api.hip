@@ -324,6 +324,112 @@ attn_status attn_forward_padded(const void* q, const void* k, const void* v, voi
                       workspace_size, stream);
 }
 
+attn_status attn_backward_workspace_size(int32_t B, int32_t H, const attn_block_mask* bm,
+                                         size_t* bytes) {
+  g_last_error[0] = '\0';
+  if (bm == nullptr || bytes == nullptr)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask and bytes must be non-null");
+  if (B < 1 || H < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d", B, H);
+  *bytes = bsattn::bwd_workspace_bytes((int64_t)B * H, bm->q_len, bm->num_q_blocks, bm->num_kv_blocks);
+  return ATTN_OK;
+}
+
+attn_status attn_backward(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L, int32_t S,
+                          int32_t E, const attn_block_mask* bm, int32_t score_mod, float softcap,
+                          float scale, const int32_t* key_start, const int32_t* key_end,
+                          void* workspace, size_t workspace_size, void* stream) {
+  g_last_error[0] = '\0';
+  if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
+  if (dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "the backward takes bf16 or fp16");
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (B < 1 || H < 1 || L < 0 || S < 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d L=%d S=%d", B, H, L, S);
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "H=%d query heads cannot share H_kv=%d K/V heads", H, H_kv);
+  if (E != bsattn::kHeadDim)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dim %d: only %d is supported", E, bsattn::kHeadDim);
+  if ((L > 0 && (!q || !o || !lse || !dout || !dq)) || (S > 0 && (!k || !v || !dk || !dv)))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "q, k, v, o, lse, dout, dq, dk and dv must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+  if (bm->q_len != L || bm->kv_len != S || bm->block_size != ATTN_BLOCK_SIZE)
+    return fail(ATTN_ERR_INVALID_ARGUMENT,
+                "block mask was built for q_len=%d kv_len=%d block=%d, tensors have L=%d S=%d",
+                bm->q_len, bm->kv_len, bm->block_size, L, S);
+  if (bm->num_q_blocks != attn_num_blocks(L, ATTN_BLOCK_SIZE) ||
+      bm->num_kv_blocks != attn_num_blocks(S, ATTN_BLOCK_SIZE) ||
+      !arrays_present(bm, bm->num_q_blocks, bm->num_kv_blocks))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is not built");
+  if (bm->kind < ATTN_MASK_NONE || bm->kind > ATTN_MASK_CUSTOM ||
+      ((bm->kind == ATTN_MASK_SLIDING_WINDOW || bm->kind == ATTN_MASK_SLIDING_WINDOW_LOWER_RIGHT) &&
+       bm->window < 1) ||
+      ((bm->kind == ATTN_MASK_DOCUMENT || bm->kind == ATTN_MASK_DOCUMENT_BIDIRECTIONAL) &&
+       bm->document_id == nullptr) ||
+      (bm->kind == ATTN_MASK_CUSTOM && ((bm->mask_bits == nullptr && (int64_t)L * S > 0) ||
+                                        (reinterpret_cast<uintptr_t>(bm->mask_bits) & 15u) != 0)))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask fields are inconsistent");
+  if (score_mod != ATTN_SCORE_NONE && score_mod != ATTN_SCORE_SOFTCAP)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "unknown score_mod %d", score_mod);
+  if (score_mod == ATTN_SCORE_SOFTCAP && !(std::isfinite(softcap) && softcap > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "soft-cap must be finite and > 0");
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if ((int64_t)B * H * (bm->num_q_blocks > bm->num_kv_blocks ? bm->num_q_blocks : bm->num_kv_blocks) >
+      0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "too many work items");
+  const size_t need =
+      bsattn::bwd_workspace_bytes((int64_t)B * H, L, bm->num_q_blocks, bm->num_kv_blocks);
+  if (need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+                   workspace_size < need))
+    return fail(ATTN_ERR_INVALID_ARGUMENT,
+                "workspace must be 256-byte aligned and hold %zu bytes (got %zu)", need,
+                workspace == nullptr ? (size_t)0 : workspace_size);
+
+  bsattn::BwdArgs a{};
+  bsattn::FwdArgs& f = a.f;
+  f.q = q, f.k = k, f.v = v, f.o = const_cast<void*>(o), f.lse = const_cast<float*>(lse);
+  f.B = B, f.H = H, f.L = L, f.S = S;
+  f.kv_group = H / H_kv;
+  f.key_start = key_start;
+  f.key_end = key_end;
+  // contiguous [B, heads, len, E]
+  f.q_sl = f.o_sl = E, f.q_sh = f.o_sh = (int64_t)L * E, f.q_sb = f.o_sb = (int64_t)H * L * E;
+  f.k_sl = f.v_sl = E, f.k_sh = f.v_sh = (int64_t)S * E, f.k_sb = f.v_sb = (int64_t)H_kv * S * E;
+  f.m.kv_num = bm->kv_num_blocks;
+  f.m.kv_idx = bm->kv_indices;
+  f.m.full_num = bm->full_kv_num_blocks;
+  f.m.full_idx = bm->full_kv_indices;
+  f.m.schedule = bm->schedule;
+  f.m.doc = bm->document_id;
+  f.m.bits = bm->mask_bits;
+  f.m.bits_w = 4 * bm->num_kv_blocks;
+  f.m.nq = bm->num_q_blocks;
+  f.m.nk = bm->num_kv_blocks;
+  const bsattn::MaskForm form = bsattn::mask_form(bm->kind, L, S);
+  f.m.kind = form.kind;
+  f.m.q_off = form.q_off;
+  f.m.window = bm->window;
+  f.scale = scale;
+  f.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
+  a.dout = dout, a.dq = dq, a.dk = dk, a.dv = dv;
+  char* w = static_cast<char*>(workspace);
+  const size_t rows = bsattn::bwd_align((size_t)B * H * L * sizeof(float));
+  const size_t nums = bsattn::bwd_align((size_t)bm->num_kv_blocks * sizeof(int32_t));
+  a.D = reinterpret_cast<float*>(w);
+  a.lse2 = reinterpret_cast<float*>(w + rows);
+  a.tq_num = reinterpret_cast<int32_t*>(w + 2 * rows);
+  a.tf_num = reinterpret_cast<int32_t*>(w + 2 * rows + nums);
+  a.tq_idx = reinterpret_cast<int32_t*>(w + 2 * rows + 2 * nums);
+  a.tf_idx = reinterpret_cast<int32_t*>(
+      w + 2 * rows + 2 * nums +
+      bsattn::bwd_align((size_t)bm->num_kv_blocks * bm->num_q_blocks * sizeof(int32_t)));
+  return hip_status(bsattn::launch_backward(dtype, a, static_cast<hipStream_t>(stream)),
+                    "backward launch");
+}
+
 attn_status attn_forward_workspace_size(int32_t dtype, int32_t B, int32_t H,
                                         const attn_block_mask* bm, size_t* bytes) {
   g_last_error[0] = '\0';

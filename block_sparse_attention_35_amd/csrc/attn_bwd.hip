@@ -1,0 +1,38 @@
+// Backward dispatch: D and the logsumexp in log2 units, the transposed
+// BlockMask, then the dK/dV and dQ kernels of the mask family (instantiated
+// in bwd_none.hip, bwd_causal.hip, bwd_sliding.hip, bwd_document.hip and
+// bwd_custom.hip).
+#include "bwd_kernels.h"
+
+namespace bsattn {
+
+hipError_t launch_backward_none(int32_t dtype, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_causal(int32_t dtype, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_sliding(int32_t dtype, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_document(int32_t dtype, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_custom(int32_t dtype, const BwdArgs& a, hipStream_t stream);
+
+hipError_t launch_backward(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
+  const dim3 block(kThreads);
+  const int64_t rows = (int64_t)a.f.B * a.f.H * a.f.L;
+  if (rows > 0) {
+    const dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)));
+    if (dtype == ATTN_BF16)
+      hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, grid, block, 0, stream, a);
+  }
+  if (a.f.m.nk > 0) hipLaunchKernelGGL(bwd_transpose_kernel, dim3(a.f.m.nk), block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (a.f.m.kind) {
+    case ATTN_MASK_NONE: return launch_backward_none(dtype, a, stream);
+    case ATTN_MASK_CAUSAL: return launch_backward_causal(dtype, a, stream);
+    case ATTN_MASK_SLIDING_WINDOW: return launch_backward_sliding(dtype, a, stream);
+    case ATTN_MASK_DOCUMENT: return launch_backward_document(dtype, a, stream);
+    case ATTN_MASK_CUSTOM: return launch_backward_custom(dtype, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bsattn

@@ -1,0 +1,10 @@
+// Backward kernels of the document mask family (see bwd_kernels.h).
+#include "bwd_kernels.h"
+
+namespace bsattn {
+
+hipError_t launch_backward_document(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
+  return launch_backward_family<ATTN_MASK_DOCUMENT>(dtype, a, stream);
+}
+
+}  // namespace bsattn

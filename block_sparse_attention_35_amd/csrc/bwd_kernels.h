@@ -1,0 +1,510 @@
+// Block-sparse attention backward for gfx950: dQ, dK, dV of sum(dO * O)
+// with the attention matrix recomputed from the saved logsumexp instead of
+// stored ("Flash Attention 2 and the IO bottleneck" (tcdigital), section on
+// recomputation in backpropagation). With P = exp(s' - lse) for the masked,
+// scaled (and soft-capped) scores s' of the forward:
+//   dV_j = sum_i P_ij dO_i,  dP_ij = dO_i . v_j,  D_i = dO_i . O_i,
+//   dS_ij = P_ij (dP_ij - D_i) mod'_ij,  dQ_i = scale sum_j dS_ij k_j,
+//   dK_j = scale sum_i dS_ij q_i,
+// mod' = 1 - (s'/c)^2 with the soft-cap (1 without). D uses the forward's
+// output O (sum_j P_ij dP_ij = dO_i . O_i).
+//
+// Two kernels, no atomics (deterministic): dK/dV per (batch, K/V head, kv
+// block), looping over the query heads that share the K/V head and over the
+// query blocks that see the kv block (the BlockMask transposed); dQ per
+// (batch, query head, query block), over the kv blocks the forward visits.
+// Both skip dead blocks, run full blocks without a per-pair test and test
+// every pair of a partial block. Products on v_mfma_f32_32x32x16 from the
+// input type, P and dS rounded to the input type for their products, fp32
+// accumulation.
+//
+// Layouts (each wave owns 32 rows of the item's fixed block, as in the
+// forward; the permuted-contraction trick is the forward's):
+//  * dK/dV: S = Q K^T and dP = dO V^T with queries along M (Q and dO rows
+//    read from LDS) and the wave's 32 keys along N (K and V rows held in
+//    registers), so each lane holds one key. P and dS in that accumulator
+//    layout are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//    operands are transposed LDS reads of the dO and Q tiles.
+//  * dQ: S^T = K Q^T and dP^T = V dO^T with the wave's 32 queries along N
+//    (Q and dO rows in registers), so each lane holds one query; dS^T is the
+//    B operand of dQ^T += K^T dS^T, whose A operand is a transposed LDS read
+//    of the K tile.
+#pragma once
+
+#include "fwd_kernels.h"
+
+namespace bsattn {
+
+namespace {
+
+// Per-lane LDS pointers of one 128 x 128-byte tile.
+//  * plain_k / plain_v: A-operand rows (row lq, head dims 16c + 8hf .. +7,
+//    16-byte chunk 2c + hf) of a K-swizzled (slot c ^ (r & 7)) or V-swizzled
+//    (slot c ^ 2(r & 3)) tile; rows 32t + lq add t * 4096.
+//  * tr: the transposed-read address of the forward's V operand (see
+//    LanePtrs) for head-dim tile te of a V-swizzled tile; 16-row group g adds
+//    2048 bytes, the second read 1024.
+__device__ inline lds_u8 plain_k(lds_u8 tile, int lane, int c) {
+  const int lq = lane & 31, hf = lane >> 5;
+  return tile + lq * 128 + (((2 * c + hf) ^ (lq & 7)) << 4);
+}
+__device__ inline lds_u8 plain_v(lds_u8 tile, int lane, int c) {
+  const int lq = lane & 31, hf = lane >> 5;
+  return tile + lq * 128 + (((2 * c + hf) ^ ((lq & 3) << 1)) << 4);
+}
+__device__ inline lds_u8 tr_v(lds_u8 tile, int lane, int te) {
+  const int hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
+  const int r1 = hf * 4 + (i16 >> 2);
+  const int e = te * 32 + (g16 & 1) * 16 + (i16 & 3) * 4;
+  const int c16 = e >> 3, half = (e >> 2) & 1;
+  return tile + r1 * 128 + ((c16 ^ ((r1 & 3) << 1)) << 4) + half * 8;
+}
+template <typename T>
+__device__ inline typename Vec<T>::x8 read16(lds_u8 p) {
+  typedef __attribute__((address_space(3))) const typename Vec<T>::x8 lds_x8;
+  return *reinterpret_cast<const lds_x8*>(p);
+}
+template <typename T>
+__device__ inline typename Vec<T>::x8 read_tr(lds_u8 p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
+  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename Vec<T>::x8, both);
+}
+
+// Liveness of pair (query i, key j) in a partial block: the forward's rule,
+// the kept key range [klo, khi) and, for CUSTOM, the pair's bit.
+template <int KIND>
+__device__ inline bool bwd_live(const FwdArgs& a, int i, int j, int klo, int khi, int32_t di, int32_t dj,
+                                uint32_t word, int bit) {
+  bool ok = (i < a.L) & (j >= klo) & pair_live<KIND>(i + a.m.q_off, j, khi, a.m.window, di, dj);
+  if (KIND == ATTN_MASK_CUSTOM) ok &= (word >> bit) & 1u;
+  return ok;
+}
+
+// P and the factor of dS from a raw score x = q.k: returns P, sets mod' (the
+// soft-cap derivative, 1 without it).
+template <bool SOFTCAP>
+__device__ inline float bwd_prob(float x, float lse2, const FwdArgs& a, float& dmod) {
+  if (SOFTCAP) {
+    const float cap2 = a.softcap * kLog2e;
+    const float y2 = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, cap2);  // s' log2 e
+    const float t = y2 / cap2;                                                   // tanh
+    dmod = 1.0f - t * t;
+    return fast_exp2(y2 - lse2);
+  }
+  dmod = 1.0f;
+  return fast_exp2(fmaf(x, a.scale * kLog2e, -lse2));
+}
+
+// ---------------------------------------------------------------------------
+// D = dO . O and the logsumexp in log2 units, one row per 8 threads.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
+  const int64_t rows = (int64_t)a.f.B * a.f.H * a.f.L;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 8) + threadIdx.x / 8;
+  const int part = threadIdx.x % 8;
+  float acc = 0.0f;
+  if (row < rows) {
+    const auto* o = static_cast<const typename Vec<T>::x8*>(a.f.o) + row * 8 + part;
+    const auto* d = static_cast<const typename Vec<T>::x8*>(a.dout) + row * 8 + part;
+    const typename Vec<T>::x8 ov = *o, dv = *d;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = fmaf((float)ov[u], (float)dv[u], acc);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && part == 0) {
+    a.D[row] = acc;
+    const float l = a.f.lse[row];
+    a.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The BlockMask transposed: for kv block kb, its partial and full query
+// blocks in ascending order (one workgroup per kv block; binary search in
+// each query block's ascending lists, then a ballot compaction).
+// ---------------------------------------------------------------------------
+__device__ inline bool sorted_has(const int32_t* row, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] < x)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo < n && row[lo] == x;
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_transpose_kernel(BwdArgs a) {
+  __shared__ int32_t wave_counts[2][kThreads / 64];
+  const int kb = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nq = a.f.m.nq, nk = a.f.m.nk;
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t base_p = 0, base_f = 0;
+  for (int c0 = 0; c0 < nq; c0 += kThreads) {
+    const int qb = c0 + tid;
+    bool part = false, full = false;
+    if (qb < nq) {
+      full = sorted_has(a.f.m.full_idx + (int64_t)qb * nk, a.f.m.full_num[qb], kb);
+      part = !full && sorted_has(a.f.m.kv_idx + (int64_t)qb * nk, a.f.m.kv_num[qb], kb);
+    }
+    const uint64_t bp = __ballot(part), bf = __ballot(full);
+    if (lane == 0) {
+      wave_counts[0][wave] = __popcll(bp);
+      wave_counts[1][wave] = __popcll(bf);
+    }
+    __syncthreads();
+    int32_t off_p = base_p, off_f = base_f, tot_p = 0, tot_f = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      if (w < wave) {
+        off_p += wave_counts[0][w];
+        off_f += wave_counts[1][w];
+      }
+      tot_p += wave_counts[0][w];
+      tot_f += wave_counts[1][w];
+    }
+    if (part) a.tq_idx[(int64_t)kb * nq + off_p + __popcll(bp & lower)] = qb;
+    if (full) a.tf_idx[(int64_t)kb * nq + off_f + __popcll(bf & lower)] = qb;
+    base_p += tot_p;
+    base_f += tot_f;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.tq_num[kb] = base_p;
+    a.tf_num[kb] = base_f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+// One stage of the query side: Q and dO tiles (V-swizzled), the rows' lse2
+// and D, their document ids and, for CUSTOM, word 4 kb + w of each row for
+// wave w.
+struct alignas(16) BwdQStage {
+  uint8_t q[kBlock * 128];
+  uint8_t dout[kBlock * 128];
+  float lse2[kBlock];
+  float D[kBlock];
+  int32_t doc[kBlock];
+  uint32_t bits[4][kBlock];
+};
+
+template <typename T, int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  using x4 = typename V::x4;
+  __shared__ BwdQStage st[2];
+  const FwdArgs& f = a.f;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int G = f.kv_group, Hk = f.H / G;
+  const int bk = blockIdx.x % (f.B * Hk), kb = blockIdx.x / (f.B * Hk);
+  const int b = bk / Hk, hk = bk % Hk;
+  const int kv0 = kb * kBlock;
+  const int key = kv0 + wave * 32 + lq;  // this lane's key
+  int klo = 0, khi = f.S;
+  if (f.key_start != nullptr) klo = min(max(((const_i32_ptr)f.key_start)[b], 0), f.S);
+  if (f.key_end != nullptr) khi = max(min(((const_i32_ptr)f.key_end)[b], f.S), klo);
+
+  // This lane's K and V rows as B operands (head dims 16c + 8hf .. +7).
+  const T* kg = static_cast<const T*>(f.k) + b * f.k_sb + hk * f.k_sh;
+  const T* vg = static_cast<const T*>(f.v) + b * f.v_sb + hk * f.v_sh;
+  x8 kreg[4], vreg[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    kreg[c] = key < f.S ? *reinterpret_cast<const x8*>(kg + (int64_t)key * f.k_sl + c * 16 + hf * 8) : x8{};
+    vreg[c] = key < f.S ? *reinterpret_cast<const x8*>(vg + (int64_t)key * f.v_sl + c * 16 + hf * 8) : x8{};
+  }
+  const int32_t dj = (KIND == ATTN_MASK_DOCUMENT && key < f.S) ? f.m.doc[key] : -1;
+
+  const int nfull = ((const_i32_ptr)a.tf_num)[kb], npart = ((const_i32_ptr)a.tq_num)[kb];
+  const int nblk = nfull + npart;
+  const const_i32_ptr flist = (const_i32_ptr)(a.tf_idx + (int64_t)kb * f.m.nq);
+  const const_i32_ptr plist = (const_i32_ptr)(a.tq_idx + (int64_t)kb * f.m.nq);
+  // No kept key in the block: nothing to do (the gradients are zero).
+  const bool keys_dead = kv0 >= khi || kv0 + kBlock <= klo;
+  const bool keys_cut = kv0 < klo || kv0 + kBlock > khi;  // padding cuts the block
+  const int total = keys_dead ? 0 : G * nblk;              // (query head, query block) pairs
+  auto qblock = [&](int n) { const int m = n % nblk; return m < nfull ? flist[m] : plist[m - nfull]; };
+
+  const uint32_t lane_off = (uint32_t)((lane >> 3) * f.q_sl * (int64_t)sizeof(T)) +
+                            (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+  auto issue = [&](int n, BwdQStage& s) __attribute__((always_inline)) {
+    const int g = n / nblk, qb = qblock(n);
+    const int h = hk * G + g;
+    const int q0 = qb * kBlock;
+    const T* qg = static_cast<const T*>(f.q) + b * f.q_sb + h * f.q_sh;
+    const T* dg = static_cast<const T*>(a.dout) + b * f.q_sb + h * f.q_sh;
+    issue_rows<T, true>(qg, f.q_sl, lane_off, q0, f.L, s.q, wave, lane);
+    issue_rows<T, true>(dg, f.q_sl, lane_off, q0, f.L, s.dout, wave, lane);
+    const int64_t rb = ((int64_t)b * f.H + h) * f.L;
+    const int r = min(q0 + wave * 32 + lq, f.L - 1);
+    if (lane < 32) {
+      lds_copy4(a.lse2 + rb + r, lds_offset(s.lse2) + (uint32_t)wave * 128u);
+      lds_copy4(a.D + rb + r, lds_offset(s.D) + (uint32_t)wave * 128u);
+      if (KIND == ATTN_MASK_DOCUMENT) lds_copy4(f.m.doc + r, lds_offset(s.doc) + (uint32_t)wave * 128u);
+    }
+    if (KIND == ATTN_MASK_CUSTOM) {
+      // word 4 kb + wave (this wave's keys) of rows q0 .. q0 + 127
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rr = min(q0 + hh * 64 + lane, f.L - 1);
+        lds_copy4(f.m.bits + (int64_t)rr * f.m.bits_w + 4 * kb + wave,
+                  lds_offset(s.bits[wave]) + (uint32_t)hh * 256u);
+      }
+    }
+  };
+
+  f32x16_t dkacc[2], dvacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkacc[te][r] = dvacc[te][r] = 0.0f;
+
+  if (total > 0) issue(0, st[0]);
+  wait_vm_zero();  // K/V rows and the first stage (no compiler-tracked load stays in flight)
+  for (int n = 0; n < total; ++n) {
+    BwdQStage& s = st[n & 1];
+    const int m = n % nblk;
+    const int qb = qblock(n);
+    const int q0 = qb * kBlock;
+    wait_vm_zero();
+    wait_lgkm_zero();
+    barrier_only();
+    if (n + 1 < total) issue(n + 1, st[(n + 1) & 1]);
+    const bool partial = m >= nfull || keys_cut;
+    const lds_u8 qt_base = (lds_u8)s.q, dt_base = (lds_u8)s.dout;
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      f32x16_t sacc = {}, dpacc = {};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sacc = V::mma(read16<T>(plain_v(qt_base, lane, c) + qt * 4096), kreg[c], sacc);
+        dpacc = V::mma(read16<T>(plain_v(dt_base, lane, c) + qt * 4096), vreg[c], dpacc);
+      }
+      x8 pk[2], dsk[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rl = qt * 32 + 8 * q4 + 4 * hf;  // block row of registers 4 q4 .. 4 q4 + 3
+        typedef __attribute__((address_space(3))) const f32x4_t lds_f4;
+        const f32x4_t l4 = *reinterpret_cast<lds_f4*>((lds_u8)s.lse2 + rl * 4);
+        const f32x4_t d4 = *reinterpret_cast<lds_f4*>((lds_u8)s.D + rl * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * q4 + u;
+          float dmod;
+          float p = bwd_prob<SOFTCAP>(sacc[r], l4[u], f, dmod);
+          if (partial) {
+            const int32_t di = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[rl + u] : 0;
+            const uint32_t word = (KIND == ATTN_MASK_CUSTOM) ? s.bits[wave][rl + u] : 0u;
+            if (!bwd_live<KIND>(f, q0 + rl + u, key, klo, khi, di, dj, word, lq)) p = 0.0f;
+          }
+          const float ds = p * (dpacc[r] - d4[u]) * dmod;
+          pk[r >> 3][r & 7] = (T)p;
+          dsk[r >> 3][r & 7] = (T)ds;
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int te = 0; te < 2; ++te) {
+          const int g16 = qt * 2 + gi;
+          dvacc[te] = V::mma(read_tr<T>(tr_v(dt_base, lane, te) + g16 * 2048), pk[gi], dvacc[te]);
+          dkacc[te] = V::mma(read_tr<T>(tr_v(qt_base, lane, te) + g16 * 2048), dsk[gi], dkacc[te]);
+        }
+    }
+  }
+
+  // dK = scale * dK^T, dV = dV^T: lane = key, registers 4 q4 .. +3 of tile te
+  // = head dims te 32 + 8 q4 + 4 hf .. +3.
+  if (key < f.S) {
+    T* dkg = static_cast<T*>(a.dk) + b * f.k_sb + hk * f.k_sh + (int64_t)key * f.k_sl;
+    T* dvg = static_cast<T*>(a.dv) + b * f.v_sb + hk * f.v_sh + (int64_t)key * f.v_sl;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int e0 = te * 32 + q4 * 8 + hf * 4;
+        x4 kv, vv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kv[u] = (T)(dkacc[te][q4 * 4 + u] * f.scale);
+          vv[u] = (T)dvacc[te][q4 * 4 + u];
+        }
+        *reinterpret_cast<x4*>(dkg + e0) = kv;
+        *reinterpret_cast<x4*>(dvg + e0) = vv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+// One stage of the key side: K (V-swizzled, read plain and transposed), V
+// (K-swizzled, read plain), the keys' document ids and, for CUSTOM, the
+// wave's 32 rows' words of the block.
+struct alignas(16) BwdKStage {
+  uint8_t k[kBlock * 128];
+  uint8_t v[kBlock * 128];
+  int32_t doc[kBlock];
+  uint32_t bits[kBlock * 4];
+};
+
+template <typename T, int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  using x4 = typename V::x4;
+  __shared__ BwdKStage st[2];
+  const FwdArgs& f = a.f;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = f.B * f.H;
+  const int bh = blockIdx.x % BH, qb = f.m.nq - 1 - blockIdx.x / BH;  // longest rows first
+  const int b = bh / f.H, h = bh % f.H, hk = h / f.kv_group;
+  const int q0 = qb * kBlock;
+  const int qi = q0 + wave * 32 + lq;  // this lane's query
+  int klo = 0, khi = f.S;
+  if (f.key_start != nullptr) klo = min(max(((const_i32_ptr)f.key_start)[b], 0), f.S);
+  if (f.key_end != nullptr) khi = max(min(((const_i32_ptr)f.key_end)[b], f.S), klo);
+
+  const T* qg = static_cast<const T*>(f.q) + b * f.q_sb + h * f.q_sh;
+  const T* dg = static_cast<const T*>(a.dout) + b * f.q_sb + h * f.q_sh;
+  const T* kg = static_cast<const T*>(f.k) + b * f.k_sb + hk * f.k_sh;
+  const T* vg = static_cast<const T*>(f.v) + b * f.v_sb + hk * f.v_sh;
+  x8 qop[4], doop[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qop[c] = qi < f.L ? *reinterpret_cast<const x8*>(qg + (int64_t)qi * f.q_sl + c * 16 + hf * 8) : x8{};
+    doop[c] = qi < f.L ? *reinterpret_cast<const x8*>(dg + (int64_t)qi * f.q_sl + c * 16 + hf * 8) : x8{};
+  }
+  const int64_t row = (int64_t)bh * f.L + min(qi, f.L - 1);
+  const float lse2 = a.lse2[row], Dq = a.D[row];
+  const int32_t di = (KIND == ATTN_MASK_DOCUMENT && qi < f.L) ? f.m.doc[qi] : -1;
+
+  const int nfull = ((const_i32_ptr)f.m.full_num)[qb], npart = ((const_i32_ptr)f.m.kv_num)[qb];
+  const int nblk = nfull + npart;
+  const const_i32_ptr flist = (const_i32_ptr)(f.m.full_idx + (int64_t)qb * f.m.nk);
+  const const_i32_ptr plist = (const_i32_ptr)(f.m.kv_idx + (int64_t)qb * f.m.nk);
+  auto kvblock = [&](int m) { return m < nfull ? flist[m] : plist[m - nfull]; };
+  // K uses the V swizzle (it is also read transposed), V the K swizzle.
+  const uint32_t k_off = (uint32_t)((lane >> 3) * f.k_sl * (int64_t)sizeof(T)) +
+                         (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+  const uint32_t v_off =
+      (uint32_t)((lane >> 3) * f.v_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  auto issue = [&](int m, BwdKStage& s) __attribute__((always_inline)) {
+    const int kb = kvblock(m), kv0 = kb * kBlock;
+    issue_rows<T, true>(kg, f.k_sl, k_off, kv0, f.S, s.k, wave, lane);
+    issue_rows<T, false>(vg, f.v_sl, v_off, kv0, f.S, s.v, wave, lane);
+    if (KIND == ATTN_MASK_DOCUMENT && lane < 32)
+      lds_copy4(f.m.doc + min(kv0 + wave * 32 + lane, f.S - 1), lds_offset(s.doc) + (uint32_t)wave * 128u);
+    if (KIND == ATTN_MASK_CUSTOM) issue_bits(f.m.bits, f.m.bits_w, q0 + wave * 32, f.L, kb, s.bits, wave, lane);
+  };
+
+  f32x16_t dqacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[te][r] = 0.0f;
+
+  if (nblk > 0) issue(0, st[0]);
+  wait_vm_zero();
+  for (int m = 0; m < nblk; ++m) {
+    BwdKStage& s = st[m & 1];
+    const int kv0 = kvblock(m) * kBlock;
+    wait_vm_zero();
+    wait_lgkm_zero();
+    barrier_only();
+    if (m + 1 < nblk) issue(m + 1, st[(m + 1) & 1]);
+    if (kv0 >= khi || kv0 + kBlock <= klo) continue;  // no kept key
+    const bool partial = m >= nfull || kv0 < klo || kv0 + kBlock > khi;
+    uint32_t mw[4] = {0u, 0u, 0u, 0u};
+    if (KIND == ATTN_MASK_CUSTOM && partial) {
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+      const u32x4_t w4 = *reinterpret_cast<lds_u32x4*>((lds_u8)s.bits + (wave * 32 + lq) * 16);
+      mw[0] = w4[0], mw[1] = w4[1], mw[2] = w4[2], mw[3] = w4[3];
+    }
+    const lds_u8 kt_base = (lds_u8)s.k, vt_base = (lds_u8)s.v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x16_t sacc = {}, dpacc = {};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sacc = V::mma(read16<T>(plain_v(kt_base, lane, c) + t * 4096), qop[c], sacc);
+        dpacc = V::mma(read16<T>(plain_k(vt_base, lane, c) + t * 4096), doop[c], dpacc);
+      }
+      x8 dsk[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jl = t * 32 + acc_row(r, hf);
+        float dmod;
+        float p = bwd_prob<SOFTCAP>(sacc[r], lse2, f, dmod);
+        if (partial) {
+          const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[jl] : 0;
+          if (!bwd_live<KIND>(f, qi, kv0 + jl, klo, khi, di, dj, mw[t], acc_row(r, hf))) p = 0.0f;
+        }
+        dsk[r >> 3][r & 7] = (T)(p * (dpacc[r] - Dq) * dmod);
+      }
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int te = 0; te < 2; ++te)
+          dqacc[te] = V::mma(read_tr<T>(tr_v(kt_base, lane, te) + (t * 2 + gi) * 2048), dsk[gi], dqacc[te]);
+    }
+  }
+
+  if (qi < f.L) {
+    T* dqg = static_cast<T*>(a.dq) + b * f.q_sb + h * f.q_sh + (int64_t)qi * f.q_sl;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        x4 outv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) outv[u] = (T)(dqacc[te][q4 * 4 + u] * f.scale);
+        *reinterpret_cast<x4*>(dqg + te * 32 + q4 * 8 + hf * 4) = outv;
+      }
+  }
+}
+
+template <int KIND, bool SOFTCAP>
+hipError_t launch_bwd_kernels(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
+  const int64_t Hk = a.f.H / a.f.kv_group;
+  const dim3 block(kThreads);
+  const dim3 g_dkdv((unsigned)((int64_t)a.f.B * Hk * a.f.m.nk));
+  const dim3 g_dq((unsigned)((int64_t)a.f.B * a.f.H * a.f.m.nq));
+  switch (dtype) {
+    case ATTN_BF16:
+      if (a.f.m.nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<__bf16, KIND, SOFTCAP>), g_dkdv, block, 0, stream, a);
+      if (a.f.m.nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<__bf16, KIND, SOFTCAP>), g_dq, block, 0, stream, a);
+      break;
+    case ATTN_F16:
+      if (a.f.m.nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<_Float16, KIND, SOFTCAP>), g_dkdv, block, 0, stream, a);
+      if (a.f.m.nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<_Float16, KIND, SOFTCAP>), g_dq, block, 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The dK/dV and dQ kernels of one mask family (defined in bwd_<family>.hip).
+template <int KIND>
+hipError_t launch_backward_family(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
+  return a.f.softcap > 0.0f ? launch_bwd_kernels<KIND, true>(dtype, a, stream)
+                            : launch_bwd_kernels<KIND, false>(dtype, a, stream);
+}
+
+}  // namespace bsattn

@@ -163,4 +163,34 @@ hipError_t launch_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_
 // Enqueue the fused forward. dtype is ATTN_F32 / ATTN_BF16 / ATTN_F16.
 hipError_t launch_forward(int32_t dtype, const FwdArgs& a, hipStream_t stream);
 
+// Everything the backward kernels take (host-validated; every tensor
+// contiguous [B, heads, len, 64]).
+struct BwdArgs {
+  FwdArgs f;          // q, k, v, o, lse, sizes, strides, mask, scale, soft-cap, padding
+  const void* dout;   // [B, H, L, E], q's strides
+  void* dq;           // [B, H, L, E], q's strides
+  void* dk;           // [B, H_kv, S, E], k's strides
+  void* dv;           // [B, H_kv, S, E], v's strides
+  float* D;           // [B*H, L]: dO . O
+  float* lse2;        // [B*H, L]: lse * log2 e (+inf for rows without a live key)
+  int32_t* tq_num;    // [nk]: partial query blocks of kv block kb
+  int32_t* tq_idx;    // [nk][nq]: their indices, ascending
+  int32_t* tf_num;    // [nk]: full query blocks of kv block kb
+  int32_t* tf_idx;    // [nk][nq]
+};
+
+// Backward workspace: D and lse2 ([B*H*L] floats each), then the transposed
+// BlockMask (tq_num, tf_num [nk]; tq_idx, tf_idx [nk*nq]), each region
+// starting on a 256-byte boundary.
+inline size_t bwd_align(size_t n) { return (n + 255) & ~(size_t)255; }
+inline size_t bwd_workspace_bytes(int64_t bh, int32_t L, int32_t nq, int32_t nk) {
+  const size_t rows = (size_t)bh * (size_t)L * sizeof(float);
+  const size_t nums = (size_t)nk * sizeof(int32_t), idx = (size_t)nk * (size_t)nq * sizeof(int32_t);
+  return 2 * bwd_align(rows) + 2 * bwd_align(nums) + 2 * bwd_align(idx);
+}
+
+// Enqueue the backward (bf16 / fp16): D and lse2, the transposed BlockMask,
+// then the dK/dV and dQ kernels.
+hipError_t launch_backward(int32_t dtype, const BwdArgs& a, hipStream_t stream);
+
 }  // namespace bsattn

@@ -107,6 +107,10 @@ class Oracle:
         lib.oracle_attention.argtypes = [f64p, f64p, f64p, i64, i64, i64, i64, i64, i64,
                                          ctypes.c_int, i64, i32p, u8p, ctypes.c_double,
                                          ctypes.c_double, i64p, i64p, i64p, i64, f64p, f64p]
+        lib.oracle_attention_backward_dq_rows.restype = ctypes.c_int
+        lib.oracle_attention_backward_dq_rows.argtypes = [
+            f64p, f64p, f64p, f64p, i64, i64, i64, i64, i64, ctypes.c_int, i64, i32p, u8p,
+            ctypes.c_double, ctypes.c_double, i64p, i64p, i64p, i64, f64p]
         lib.oracle_attention_backward.restype = ctypes.c_int
         lib.oracle_attention_backward.argtypes = [f64p, f64p, f64p, f64p, i64, i64, i64, i64, i64,
                                                   ctypes.c_int, i64, i32p, u8p, ctypes.c_double,
@@ -251,6 +255,32 @@ def _attention_backward(self, q, k, v, dout, kind: int, scale: float, window: in
 Oracle.attention_backward = _attention_backward
 
 
+def _attention_backward_dq_rows(self, q, k, v, dout, kind: int, scale: float, rows, window: int = 0,
+                                doc=None, softcap: float = 0.0, mask=None):
+    """dq of attention_backward for flat rows (b*H + h)*L + i only: [len(rows), E]."""
+    q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, H, L, E = q.shape
+    S = k.shape[2]
+    d = _doc(doc)
+    self._check_doc(kind, d, L, S)
+    m = _dense(kind, mask, L, S)
+    rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows_arr.size and (rows_arr.min() < 0 or rows_arr.max() >= B * H * L):
+        raise ValueError("row id out of range")
+    out = np.zeros((rows_arr.size, E), np.float64)
+    rc = self._lib.oracle_attention_backward_dq_rows(
+        _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+        _ptr(dout, ctypes.c_double), B, H, L, S, E, kind, window, _ptr(d, ctypes.c_int32),
+        _ptr(m, ctypes.c_uint8), softcap, scale, None, None, _ptr(rows_arr, ctypes.c_int64),
+        rows_arr.size, _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_backward_dq_rows failed")
+    return out
+
+
+Oracle.attention_backward_dq_rows = _attention_backward_dq_rows
+
+
 def default() -> Oracle:
     """The oracle built from oracle.c (built on first use if missing or stale)."""
     global _default
@@ -291,3 +321,9 @@ def attention_backward(q, k, v, dout, kind, scale, window=0, doc=None, softcap=0
                        key_end=None, mask=None):
     return default().attention_backward(q, k, v, dout, kind, scale, window, doc, softcap, key_start,
                                         key_end, mask)
+
+
+def attention_backward_dq_rows(q, k, v, dout, kind, scale, rows, window=0, doc=None, softcap=0.0,
+                               mask=None):
+    return default().attention_backward_dq_rows(q, k, v, dout, kind, scale, rows, window, doc, softcap,
+                                                mask)

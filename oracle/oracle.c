@@ -299,6 +299,14 @@ int oracle_attention(const double* q, const double* k, const double* v, int64_t 
   return failed ? -1 : 0;
 }
 
+/* dS_ij = P_ij (dP_ij - D_i) * scale * mod', with mod' = 1 - (s'/c)^2 the
+ * soft-cap's derivative at the capped score s' (1 without the soft-cap). */
+static double dscore(double p, double dp, double D, double sp, double softcap, double scale) {
+  double ds = p * (dp - D) * scale;
+  if (softcap > 0.0) ds *= 1.0 - (sp / softcap) * (sp / softcap);
+  return ds;
+}
+
 /*
  * Backward of oracle_attention (all rows): q [B,H,L,E], k, v [B,H,S,E], dout
  * [B,H,L,E] contiguous fp64 (K/V heads already expanded to H); outputs dq
@@ -356,13 +364,67 @@ int oracle_attention_backward(const double* q, const double* k, const double* v,
       }
       for (int64_t j = 0; j < S; ++j) {
         if (p[j] == 0.0) continue;
-        double ds = p[j] * (dp[j] - D) * scale;
-        if (softcap > 0.0) ds *= 1.0 - (sp[j] / softcap) * (sp[j] / softcap);
+        const double ds = dscore(p[j], dp[j], D, sp[j], softcap, scale);
         for (int64_t e = 0; e < E; ++e) {
           dqi[e] += ds * kh[j * E + e];
           dkh[j * E + e] += ds * qi[e];
           dvh[j * E + e] += p[j] * doi[e];
         }
+      }
+    }
+    free(sp), free(p), free(dp);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * dq of oracle_attention_backward for a list of flat rows r = (b*H + h)*L + i
+ * only (each needs just its own row of P): dq_rows [nrows, E]. Returns 0, or
+ * -1 on bad sizes / allocation failure.
+ */
+int oracle_attention_backward_dq_rows(const double* q, const double* k, const double* v,
+                                      const double* dout, int64_t B, int64_t H, int64_t L, int64_t S,
+                                      int64_t E, int kind, int64_t window, const int32_t* doc,
+                                      const uint8_t* dense, double softcap, double scale,
+                                      const int64_t* key_start, const int64_t* key_end,
+                                      const int64_t* rows, int64_t nrows, double* dq_rows) {
+  if (B < 0 || H < 0 || L <= 0 || S < 0 || E <= 0 || nrows < 0) return -1;
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* sp = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (sp == NULL || p == NULL || dp == NULL) failed = 1;
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < nrows; ++n) {
+      double* dqi = dq_rows + n * E;
+      for (int64_t e = 0; e < E; ++e) dqi[e] = 0.0;
+      if (sp == NULL || p == NULL || dp == NULL) continue;
+      const int64_t r = rows[n], bh = r / L, i = r % L, b = bh / H;
+      const double* qi = q + r * E;
+      const double* doi = dout + r * E;
+      const double* kh = k + bh * S * E;
+      const double* vh = v + bh * S * E;
+      const double m = row_scores(qi, kh, L, S, E, i, kind, window, doc, dense, softcap, scale,
+                                  key_start ? key_start[b] : 0, key_end ? key_end[b] : S, sp);
+      if (m == -INFINITY) continue;
+      double l = 0.0, D = 0.0;
+      for (int64_t j = 0; j < S; ++j) {
+        p[j] = exp(sp[j] - m);
+        l += p[j];
+      }
+      for (int64_t j = 0; j < S; ++j) {
+        p[j] /= l;
+        double t = 0.0;
+        for (int64_t e = 0; e < E; ++e) t += doi[e] * vh[j * E + e];
+        dp[j] = t;
+        D += p[j] * t;
+      }
+      for (int64_t j = 0; j < S; ++j) {
+        if (p[j] == 0.0) continue;
+        const double ds = dscore(p[j], dp[j], D, sp[j], softcap, scale);
+        for (int64_t e = 0; e < E; ++e) dqi[e] += ds * kh[j * E + e];
       }
     }
     free(sp), free(p), free(dp);

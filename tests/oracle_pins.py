@@ -656,6 +656,16 @@ def check_backward_finite_differences(orc):
             assert abs((fp - fm) / (2 * h) - g[idx]) <= 1e-7, (name, idx)
 
 
+def check_backward_dq_rows(orc):
+    """The rows form of dq equals those rows of the whole backward."""
+    q, k, v, dout = _rand((2, 2, 11, 4), 95), _rand((2, 2, 17, 4), 96), _rand((2, 2, 17, 4), 97), \
+        _rand((2, 2, 11, 4), 98)
+    dq, _, _ = orc.attention_backward(q, k, v, dout, CAUSAL_LR, 0.4, softcap=3.0)
+    rows = np.array([0, 5, 11, 30, 43])
+    got = orc.attention_backward_dq_rows(q, k, v, dout, CAUSAL_LR, 0.4, rows, softcap=3.0)
+    assert np.abs(got - dq.reshape(-1, 4)[rows]).max() <= 1e-15
+
+
 def check_backward_empty_rows_and_unseen_keys(orc):
     """A query row with no live key gets dq = 0; a key no query sees gets
     dk = dv = 0."""
@@ -705,4 +715,5 @@ ALL_CHECKS = [
     check_backward_matches_autograd,
     check_backward_finite_differences,
     check_backward_empty_rows_and_unseen_keys,
+    check_backward_dq_rows,
 ]

@@ -1,0 +1,140 @@
+"""GPU parity of the backward (attn_backward), through the C ABI.
+
+dq, dk, dv of sum(dO * O) against the fp64 oracle on the same inputs (the
+forward's O and logsumexp come from the GPU forward, as in training). Every
+product term passes through one rounding to the input type (P for dV, dS for
+dK and dQ, and O in D = dO . O), relative error u = 2^-9 (bf16) or 2^-12
+(fp16), and the result is rounded once more to the input type, so the error
+of each output is a few u times the magnitude of its terms: the test bounds
+the max-abs error by 8 u and the mean-abs error by 2 u, relative to the
+reference's max-abs (resp. mean-abs) value (measured: at most 2.7 u and
+1.3 u over the cases below). At full size (the benchmark's
+shapes) dq is compared on sampled rows, and dk, dv through identities that
+hold exactly: sum_j dV_j = sum_i dO_i over the rows with a live key, and
+sum_j dK_j = 0 without the soft-cap (each row of dS sums to zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_35_amd as bsa
+import oracle
+import workloads as wl
+from test_parity_gpu import _expand_kv
+
+pytestmark = pytest.mark.gpu
+
+U = {"bf16": 2.0 ** -9, "f16": 2.0 ** -12}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda", 0)
+
+
+def _odd(name, dtype, H, L, S, kind, window=0, bounds=(), softcap=0.0, B=1, H_kv=0):
+    return wl.Workload(name, B, H, L, S, 64, dtype, kind, window, bounds, softcap, H_kv=H_kv)
+
+
+def _mask(w, dev, m=None):
+    if w.kind == wl.MASK_CUSTOM:
+        return bsa.create_block_mask_from_dense(torch.from_numpy(m).to(dev)), None
+    doc = wl.make_doc(w)
+    return bsa.create_block_mask(w.kind, w.L, w.S, window=w.window or None,
+                                 document_id=None if doc is None else torch.from_numpy(doc).to(dev),
+                                 device=dev), doc
+
+
+def _run(w, dev, m=None, ranges=None, seed=0):
+    q, k, v = wl.make_qkv(w, seed)
+    dout = torch.from_numpy(np.random.default_rng(seed + 99).standard_normal(
+        (w.B, w.H, w.L, w.E), dtype=np.float32)).to(w.torch_dtype)
+    bm, doc = _mask(w, dev, m)
+    ks = ke = None
+    if ranges is not None:
+        ks = torch.tensor(ranges[0], dtype=torch.int32, device=dev)
+        ke = torch.tensor(ranges[1], dtype=torch.int32, device=dev)
+    qd, kd, vd, dd = (x.to(dev) for x in (q, k, v, dout))
+    sm = "softcap" if w.softcap else None
+    o, lse = bsa.attention(qd, kd, vd, bm, score_mod=sm, softcap=w.softcap or 30.0, scale=w.scale,
+                           return_lse=True, key_start=ks, key_end=ke)
+    dq, dk, dv = bsa.attention_backward(qd, kd, vd, o, lse, dd, bm, score_mod=sm,
+                                        softcap=w.softcap or 30.0, scale=w.scale, key_start=ks,
+                                        key_end=ke)
+    torch.cuda.synchronize()
+    return (q, k, v, dout), doc, (dq, dk, dv)
+
+
+def _reduce_kv(w, g):
+    """Gradient of a shared K/V head: the sum over its query heads."""
+    G = w.H // w.kv_heads
+    return g.reshape(w.B, w.kv_heads, G, w.S, w.E).sum(2) if G > 1 else g
+
+
+def _compare(w, got, want, what):
+    u = U[w.dtype]
+    got = got.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite"
+    err = np.abs(got - want)
+    scale_max, scale_mean = max(np.abs(want).max(), 1e-6), max(np.abs(want).mean(), 1e-6)
+    assert err.max() <= 8 * u * scale_max, f"{what}: max-abs {err.max():.3g} vs {8 * u * scale_max:.3g}"
+    assert err.mean() <= 2 * u * scale_mean, f"{what}: mean-abs {err.mean():.3g} vs {2 * u * scale_mean:.3g}"
+
+
+CASES = [
+    (_odd("causal_1000_bf16", "bf16", 2, 1000, 1000, wl.MASK_CAUSAL), None, None),
+    (_odd("sliding_w200_1000_f16", "f16", 2, 1000, 1000, wl.MASK_SLIDING_WINDOW, 200), None, None),
+    (_odd("document_softcap_1000_f16", "f16", 2, 1000, 1000, wl.MASK_DOCUMENT, 0, (300, 777), 30.0), None, None),
+    (_odd("none_300x200_bf16", "bf16", 2, 300, 200, wl.MASK_NONE), None, None),
+    (_odd("causal_lr_gqa_200x700_bf16", "bf16", 4, 200, 700, wl.MASK_CAUSAL_LOWER_RIGHT, H_kv=2), None, None),
+    (_odd("bidir_document_gqa_softcap_bf16", "bf16", 6, 640, 640, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (200, 500),
+          20.0, H_kv=2), None, None),
+    (_odd("sliding_empty_rows_bf16", "bf16", 1, 400, 130, wl.MASK_SLIDING_WINDOW, 20), None, None),
+    (_odd("ragged_causal_333x555_f16", "f16", 3, 333, 555, wl.MASK_CAUSAL, B=2), None, None),
+    (_odd("decode_lr_L1_S3000_bf16", "bf16", 8, 1, 3000, wl.MASK_CAUSAL_LOWER_RIGHT, H_kv=2), None, None),
+    (_odd("custom_blocks_700_bf16", "bf16", 2, 700, 900, wl.MASK_CUSTOM),
+     wl.block_structured_mask(700, 900, 21, 0.3, 0.3, 0.4), None),
+    (_odd("padded_causal_600_bf16", "bf16", 2, 600, 600, wl.MASK_CAUSAL, B=3), None, ([0, 100, 300], [600, 450, 300])),
+]
+
+
+@pytest.mark.parametrize("w,m,ranges", CASES, ids=[c[0].name for c in CASES])
+def test_backward_against_oracle(dev, w, m, ranges):
+    (q, k, v, dout), doc, (dq, dk, dv) = _run(w, dev, m, ranges)
+    want = oracle.attention_backward(q.double().numpy(), _expand_kv(w, k).double().numpy(),
+                                     _expand_kv(w, v).double().numpy(), dout.double().numpy(), w.kind,
+                                     w.scale, w.window, doc, w.softcap,
+                                     key_start=None if ranges is None else ranges[0],
+                                     key_end=None if ranges is None else ranges[1], mask=m)
+    _compare(w, dq, want[0], w.name + " dq")
+    _compare(w, dk, _reduce_kv(w, want[1]), w.name + " dk")
+    _compare(w, dv, _reduce_kv(w, want[2]), w.name + " dv")
+
+
+def test_backward_is_deterministic(dev):
+    w = _odd("det_causal_gqa_bf16", "bf16", 4, 777, 777, wl.MASK_CAUSAL, H_kv=2)
+    _, _, g1 = _run(w, dev)
+    _, _, g2 = _run(w, dev)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+def test_backward_full_size_causal_8192(dev):
+    """The benchmark's backward shape: dq on sampled rows against the oracle;
+    dk and dv through the exact identities; everything finite."""
+    w = wl.WORKLOADS["causal_8192_bf16"]
+    (q, k, v, dout), _, (dq, dk, dv) = _run(w, dev)
+    rows = wl.sample_rows(w, 48)
+    want = oracle.attention_backward_dq_rows(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                             dout.double().numpy(), w.kind, w.scale, rows)
+    got = dq.reshape(-1, w.E)[torch.from_numpy(rows).to(dev)]
+    _compare(w, got, want, "dq rows")
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all()
+    # sum over keys of dV = sum over rows of dO (every causal row has a live key)
+    sv = dv.double().sum(2).cpu().numpy()
+    so = dout.double().sum(2).numpy()
+    assert np.abs(sv - so).max() <= 16 * U["bf16"] * np.abs(dout.double().numpy()).sum(2).max()
+    # sum over keys of dK = 0
+    sk = dk.double().sum(2).cpu().numpy()
+    assert np.abs(sk).max() <= 16 * U["bf16"] * dk.double().abs().sum(2).max().item()

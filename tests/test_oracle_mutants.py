@@ -38,10 +38,10 @@ MUTANTS = [
     ("dense_inverted", "return dense[i * S + j] != 0;", "return dense[i * S + j] == 0;"),
     ("pack_bit_order", "word |= (uint32_t)1 << b;", "word |= (uint32_t)1 << (31 - b);"),
     ("pack_words_per_row", "const int64_t W = 4 * ((S + 127) / 128);", "const int64_t W = (S + 31) / 32;"),
-    ("bwd_drops_row_term", "double ds = p[j] * (dp[j] - D) * scale;", "double ds = p[j] * dp[j] * scale;"),
-    ("bwd_drops_scale", "double ds = p[j] * (dp[j] - D) * scale;", "double ds = p[j] * (dp[j] - D);"),
+    ("bwd_drops_row_term", "double ds = p * (dp - D) * scale;", "double ds = p * dp * scale;"),
+    ("bwd_drops_scale", "double ds = p * (dp - D) * scale;", "double ds = p * (dp - D);"),
     ("bwd_drops_softcap_derivative",
-     "if (softcap > 0.0) ds *= 1.0 - (sp[j] / softcap) * (sp[j] / softcap);", ""),
+     "if (softcap > 0.0) ds *= 1.0 - (sp / softcap) * (sp / softcap);", ""),
     ("bwd_dv_from_ds", "dvh[j * E + e] += p[j] * doi[e];", "dvh[j * E + e] += ds * doi[e];"),
     ("bwd_dk_from_dout", "dkh[j * E + e] += ds * qi[e];", "dkh[j * E + e] += ds * doi[e];"),
     ("bidirectional_keeps_causal", "      return doc[i] == doc[j];\n",
