@@ -314,3 +314,49 @@ def test_pack_mask_validation(name, kw, code, words):
 def test_binding_custom_kind_needs_its_own_constructor():
     with pytest.raises(ValueError, match="create_block_mask_from_dense"):
         bsa.create_block_mask("custom", 128, 128)
+
+
+def _bwd(dtype=1, B=1, H=2, H_kv=2, L=256, S=256, E=64, bm=None, score_mod=0, softcap=0.0, scale=0.125,
+         ws=FAKE, ws_bytes=1 << 30, ptrs=None):
+    lib = bsa._load()
+    bm = _built_mask(L, S) if bm is None else bm
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
+    p.update(ptrs or {})
+    return lib.attn_backward(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"], p["dv"],
+                             dtype, B, H, H_kv, L, S, E, ctypes.byref(bm), score_mod, softcap, scale,
+                             None, None, ws, ws_bytes, None)
+
+
+BWD_CASES = [
+    ("fp32_unsupported", dict(dtype=0), UNSUPPORTED, "bf16 or fp16"),
+    ("unknown_dtype", dict(dtype=9), UNSUPPORTED, "dtype"),
+    ("head_dim_128", dict(E=128), UNSUPPORTED, "head dim"),
+    ("kv_heads_not_dividing", dict(H=3, H_kv=2), INVALID, "share"),
+    ("null_dout", dict(ptrs=dict(dout=None)), INVALID, "non-null"),
+    ("null_lse", dict(ptrs=dict(lse=None)), INVALID, "non-null"),
+    ("misaligned_dq", dict(ptrs=dict(dq=FAKE + 2)), INVALID, "aligned"),
+    ("mask_for_other_lengths", dict(bm=_built_mask(128, 256)), INVALID, "q_len"),
+    ("bad_score_mod", dict(score_mod=5), INVALID, "score_mod"),
+    ("softcap_zero", dict(score_mod=1, softcap=0.0), INVALID, "soft-cap"),
+    ("bad_scale", dict(scale=float("nan")), INVALID, "scale"),
+    ("workspace_too_small", dict(ws_bytes=16), INVALID, "workspace"),
+    ("workspace_misaligned", dict(ws=FAKE + 16), INVALID, "workspace"),
+    ("custom_mask_without_bits", dict(bm=_built_mask(256, 256, kind=7)), INVALID, "inconsistent"),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,kw,code,words", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_validation(name, kw, code, words):
+    assert _bwd(**kw) == code
+    assert words in bsa._load().attn_last_error().decode()
+
+
+def test_backward_workspace_size():
+    lib = bsa._load()
+    n = ctypes.c_size_t(0)
+    bm = _built_mask(300, 700)  # nq = 3, nk = 6
+    assert lib.attn_backward_workspace_size(2, 4, ctypes.byref(bm), ctypes.byref(n)) == OK
+    al = lambda x: (x + 255) // 256 * 256
+    assert n.value == 2 * al(2 * 4 * 300 * 4) + 2 * al(6 * 4) + 2 * al(6 * 3 * 4)
+    assert lib.attn_backward_workspace_size(0, 4, ctypes.byref(bm), ctypes.byref(n)) == INVALID
