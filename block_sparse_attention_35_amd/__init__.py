@@ -119,7 +119,7 @@ def _load():
                                   ctypes.POINTER(_BlockMaskStruct), i32, ctypes.c_float, ctypes.c_float,
                                   vp, vp, vp, ctypes.c_size_t, vp]
     lib.attn_backward_workspace_size.restype = i32
-    lib.attn_backward_workspace_size.argtypes = [i32, i32, ctypes.POINTER(_BlockMaskStruct),
+    lib.attn_backward_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(_BlockMaskStruct),
                                                  ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_forward.restype = i32
     lib.attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -298,10 +298,12 @@ def create_block_mask_from_dense(mask: torch.Tensor) -> BlockMask:
 _workspaces = {}
 
 
-def _workspace(nbytes: int, device: torch.device, stream: int) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes, one per (device, stream),
-    kept for later calls (the library leaves its counters at zero again)."""
-    key = (device.index, stream)
+def _workspace(nbytes: int, device: torch.device, stream: int, role: str = "forward") -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes, one per (device, stream,
+    role), kept for later calls (the library leaves its counters at zero
+    again; the forward and the backward lay theirs out differently, so each
+    has its own)."""
+    key = (device.index, stream, role)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
@@ -429,9 +431,9 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     lib = _load()
     nbytes = ctypes.c_size_t(0)
-    _check(lib.attn_backward_workspace_size(B, H, ctypes.byref(block_mask._struct), ctypes.byref(nbytes)))
-    ws = torch.empty(max(nbytes.value, 1) + 256, dtype=torch.uint8, device=q.device)
-    ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+    _check(lib.attn_backward_workspace_size(B, H, Hk, ctypes.byref(block_mask._struct), ctypes.byref(nbytes)))
+    stream = _stream_handle(q.device)
+    ws = _workspace(nbytes.value, q.device, stream, role="backward")
     sm = SCORE_SOFTCAP if score_mod == "softcap" else SCORE_NONE
     if score_mod not in (None, "softcap"):
         raise ValueError(f"unknown score_mod {score_mod!r}")
@@ -444,6 +446,5 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
         _check(lib.attn_backward(ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), ptr(dout), ptr(dq), ptr(dk),
                                  ptr(dv), _DTYPES[q.dtype], B, H, Hk, L, S, E,
                                  ctypes.byref(block_mask._struct), sm, float(softcap), sc,
-                                 ptr(key_start), ptr(key_end), ws_ptr, nbytes.value,
-                                 _stream_handle(q.device)))
+                                 ptr(key_start), ptr(key_end), ws.data_ptr(), ws.numel(), stream))
     return dq, dk, dv

@@ -324,13 +324,15 @@ attn_status attn_forward_padded(const void* q, const void* k, const void* v, voi
                       workspace_size, stream);
 }
 
-attn_status attn_backward_workspace_size(int32_t B, int32_t H, const attn_block_mask* bm,
+attn_status attn_backward_workspace_size(int32_t B, int32_t H, int32_t H_kv, const attn_block_mask* bm,
                                          size_t* bytes) {
   g_last_error[0] = '\0';
   if (bm == nullptr || bytes == nullptr)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask and bytes must be non-null");
-  if (B < 1 || H < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d", B, H);
-  *bytes = bsattn::bwd_workspace_bytes((int64_t)B * H, bm->q_len, bm->num_q_blocks, bm->num_kv_blocks);
+  if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0)
+    return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d H_kv=%d", B, H, H_kv);
+  *bytes = bsattn::bwd_workspace_bytes((int64_t)B * H, (int64_t)B * H_kv, bm->q_len, bm->num_q_blocks,
+                                       bm->num_kv_blocks);
   return ATTN_OK;
 }
 
@@ -380,8 +382,9 @@ attn_status attn_backward(const void* q, const void* k, const void* v, const voi
   if ((int64_t)B * H * (bm->num_q_blocks > bm->num_kv_blocks ? bm->num_q_blocks : bm->num_kv_blocks) >
       0x7fffffffLL)
     return fail(ATTN_ERR_UNSUPPORTED, "too many work items");
-  const size_t need =
-      bsattn::bwd_workspace_bytes((int64_t)B * H, L, bm->num_q_blocks, bm->num_kv_blocks);
+  const bsattn::BwdLayout lay =
+      bsattn::bwd_layout((int64_t)B * H, (int64_t)B * H_kv, L, bm->num_q_blocks, bm->num_kv_blocks);
+  const size_t need = lay.total;
   if (need > 0 && (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
                    workspace_size < need))
     return fail(ATTN_ERR_INVALID_ARGUMENT,
@@ -416,16 +419,19 @@ attn_status attn_backward(const void* q, const void* k, const void* v, const voi
   f.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
   a.dout = dout, a.dq = dq, a.dk = dk, a.dv = dv;
   char* w = static_cast<char*>(workspace);
-  const size_t rows = bsattn::bwd_align((size_t)B * H * L * sizeof(float));
-  const size_t nums = bsattn::bwd_align((size_t)bm->num_kv_blocks * sizeof(int32_t));
-  a.D = reinterpret_cast<float*>(w);
-  a.lse2 = reinterpret_cast<float*>(w + rows);
-  a.tq_num = reinterpret_cast<int32_t*>(w + 2 * rows);
-  a.tf_num = reinterpret_cast<int32_t*>(w + 2 * rows + nums);
-  a.tq_idx = reinterpret_cast<int32_t*>(w + 2 * rows + 2 * nums);
-  a.tf_idx = reinterpret_cast<int32_t*>(
-      w + 2 * rows + 2 * nums +
-      bsattn::bwd_align((size_t)bm->num_kv_blocks * bm->num_q_blocks * sizeof(int32_t)));
+  a.D = reinterpret_cast<float*>(w + lay.D);
+  a.lse2 = reinterpret_cast<float*>(w + lay.lse2);
+  a.tq_num = reinterpret_cast<int32_t*>(w + lay.tq_num);
+  a.tf_num = reinterpret_cast<int32_t*>(w + lay.tf_num);
+  a.tq_idx = reinterpret_cast<int32_t*>(w + lay.tq_idx);
+  a.tf_idx = reinterpret_cast<int32_t*>(w + lay.tf_idx);
+  a.tplan = reinterpret_cast<int32_t*>(w + lay.tplan);
+  a.split_kv = lay.split_kv ? 1 : 0;
+  f.split = lay.split_q ? 1 : 0;
+  a.counters_kv = reinterpret_cast<int32_t*>(w + lay.counters_kv);
+  a.counters_q = reinterpret_cast<int32_t*>(w + lay.counters_q);
+  a.part_kv = reinterpret_cast<float*>(w + lay.part_kv);
+  a.part_q = reinterpret_cast<float*>(w + lay.part_q);
   return hip_status(bsattn::launch_backward(dtype, a, static_cast<hipStream_t>(stream)),
                     "backward launch");
 }

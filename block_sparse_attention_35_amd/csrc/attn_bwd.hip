@@ -1,5 +1,5 @@
 // Backward dispatch: D and the logsumexp in log2 units, the transposed
-// BlockMask, then the dK/dV and dQ kernels of the mask family (instantiated
+// BlockMask and its work plan, then the dK/dV and dQ kernels of the mask family (instantiated
 // in bwd_none.hip, bwd_causal.hip, bwd_sliding.hip, bwd_document.hip and
 // bwd_custom.hip).
 #include "bwd_kernels.h"
@@ -24,6 +24,9 @@ hipError_t launch_backward(int32_t dtype, const BwdArgs& a, hipStream_t stream) 
   }
   if (a.f.m.nk > 0) hipLaunchKernelGGL(bwd_transpose_kernel, dim3(a.f.m.nk), block, 0, stream, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the dK/dV work plan over kv blocks and their query-block lists
+  e = launch_plan(a.f.m.nk, a.f.m.nq, a.tq_num, a.tq_idx, a.tf_num, a.tf_idx, a.tplan, stream);
   if (e != hipSuccess) return e;
   switch (a.f.m.kind) {
     case ATTN_MASK_NONE: return launch_backward_none(dtype, a, stream);

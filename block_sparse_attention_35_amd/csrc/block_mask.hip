@@ -331,6 +331,14 @@ hipError_t launch_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_
   return hipGetLastError();
 }
 
+hipError_t launch_plan(int32_t nrows, int32_t ncols, const int32_t* part_num, const int32_t* part_idx,
+                       const int32_t* full_num, const int32_t* full_idx, int32_t* plan, hipStream_t stream) {
+  if (nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nrows + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, nrows, ncols, part_num, part_idx, full_num, full_idx, plan);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const int32_t* doc,
                              const uint32_t* bits, int32_t q_len, int32_t kv_len, int32_t nq,
                              int32_t nk, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,

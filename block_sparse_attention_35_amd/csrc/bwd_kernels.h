@@ -180,6 +180,35 @@ __global__ __launch_bounds__(kThreads) void bwd_transpose_kernel(BwdArgs a) {
   }
 }
 
+// Two-way split items: each chunk leaves its fp32 accumulators (N tiles of
+// 16 registers, register order [wave][tile*16 + r][lane]) in its slot with
+// device-scope stores, all writes complete before the ticket; the later of
+// the two adds the other chunk's partial (two terms: the sum does not depend
+// on which finishes last) and resets the counter for the next call. Returns
+// false in the chunk that exits.
+template <int N>
+__device__ inline bool merge_two(f32x16_t (&acc)[N], float* mine, float* other, int32_t* counter, int wave,
+                                 int lane) {
+  auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto get = [](float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+#pragma unroll
+  for (int t = 0; t < N; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) put(mine + ((wave * N + t) * 16 + r) * 64 + lane, acc[t][r]);
+  wait_vm_zero();
+  __syncthreads();
+  __shared__ int ticket;
+  if (threadIdx.x == 0) ticket = atomicAdd(counter, 1);
+  __syncthreads();
+  if (ticket != 1) return false;
+  if (threadIdx.x == 0) atomicExch(counter, 0);
+#pragma unroll
+  for (int t = 0; t < N; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] += get(other + ((wave * N + t) * 16 + r) * 64 + lane);
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
@@ -205,8 +234,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
-  const int G = f.kv_group, Hk = f.H / G;
-  const int bk = blockIdx.x % (f.B * Hk), kb = blockIdx.x / (f.B * Hk);
+  const int G = f.kv_group, Hk = f.H / G, BHk = f.B * Hk;
+  // Item from the dK/dV plan (the forward plan's format over kv blocks):
+  // kv block kb, chunk `chunk` of k; up to two items per kv block.
+  const i32x4_t desc = ((const_i32x4_ptr)(a.tplan + 4))[blockIdx.x / BHk];
+  if (desc[0] < 0) return;
+  const int kb = desc[0] & 0xFFFFF, chunk = (desc[0] >> 20) & 3;
+  const bool split = a.split_kv && ((desc[0] >> 22) & 3) > 0;
+  if (chunk > 0 && !split) return;
+  const int bk = blockIdx.x % BHk;
   const int b = bk / Hk, hk = bk % Hk;
   const int kv0 = kb * kBlock;
   const int key = kv0 + wave * 32 + lq;  // this lane's key
@@ -225,20 +261,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const int32_t dj = (KIND == ATTN_MASK_DOCUMENT && key < f.S) ? f.m.doc[key] : -1;
 
-  const int nfull = ((const_i32_ptr)a.tf_num)[kb], npart = ((const_i32_ptr)a.tq_num)[kb];
+  const int nfull = desc[1], npart = desc[2];
   const int nblk = nfull + npart;
+  // chunk 0 visits the first C blocks (C from the plan), chunk 1 the rest
+  const int split_len = ((const_i32_ptr)a.tplan)[1];
+  const int m_begin = (split && chunk == 1) ? split_len : 0;
+  const int m_end = (split && chunk == 0) ? split_len : nblk;
+  const int span = m_end - m_begin;
   const const_i32_ptr flist = (const_i32_ptr)(a.tf_idx + (int64_t)kb * f.m.nq);
   const const_i32_ptr plist = (const_i32_ptr)(a.tq_idx + (int64_t)kb * f.m.nq);
   // No kept key in the block: nothing to do (the gradients are zero).
   const bool keys_dead = kv0 >= khi || kv0 + kBlock <= klo;
   const bool keys_cut = kv0 < klo || kv0 + kBlock > khi;  // padding cuts the block
-  const int total = keys_dead ? 0 : G * nblk;              // (query head, query block) pairs
-  auto qblock = [&](int n) { const int m = n % nblk; return m < nfull ? flist[m] : plist[m - nfull]; };
+  const int total = keys_dead ? 0 : G * span;              // (query head, query block) pairs
+  auto qblock = [&](int n) { const int m = m_begin + n % span; return m < nfull ? flist[m] : plist[m - nfull]; };
 
   const uint32_t lane_off = (uint32_t)((lane >> 3) * f.q_sl * (int64_t)sizeof(T)) +
                             (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
   auto issue = [&](int n, BwdQStage& s) __attribute__((always_inline)) {
-    const int g = n / nblk, qb = qblock(n);
+    const int g = n / span, qb = qblock(n);
     const int h = hk * G + g;
     const int q0 = qb * kBlock;
     const T* qg = static_cast<const T*>(f.q) + b * f.q_sb + h * f.q_sh;
@@ -273,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   wait_vm_zero();  // K/V rows and the first stage (no compiler-tracked load stays in flight)
   for (int n = 0; n < total; ++n) {
     BwdQStage& s = st[n & 1];
-    const int m = n % nblk;
+    const int m = m_begin + n % span;
     const int qb = qblock(n);
     const int q0 = qb * kBlock;
     wait_vm_zero();
@@ -323,6 +364,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  if (split) {
+    f32x16_t acc[4] = {dkacc[0], dkacc[1], dvacc[0], dvacc[1]};
+    float* base = a.part_kv + ((int64_t)kb * 2 * BHk + bk) * kBwdKvSlot;
+    if (!merge_two<4>(acc, base + (int64_t)chunk * BHk * kBwdKvSlot, base + (int64_t)(1 - chunk) * BHk * kBwdKvSlot,
+                      a.counters_kv + (int64_t)kb * BHk + bk, wave, lane))
+      return;
+    dkacc[0] = acc[0], dkacc[1] = acc[1], dvacc[0] = acc[2], dvacc[1] = acc[3];
+  }
+
   // dK = scale * dK^T, dV = dV^T: lane = key, registers 4 q4 .. +3 of tile te
   // = head dims te 32 + 8 q4 + 4 hf .. +3.
   if (key < f.S) {
@@ -369,7 +419,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const int BH = f.B * f.H;
-  const int bh = blockIdx.x % BH, qb = f.m.nq - 1 - blockIdx.x / BH;  // longest rows first
+  // Item from the forward's plan: query block qb, chunk of k (f.split
+  // enables the two-way split).
+  const WorkItem wi = work_item(f, blockIdx.x / BH);
+  if (wi.skip) return;
+  const int qb = wi.qb;
+  const int bh = blockIdx.x % BH;
   const int b = bh / f.H, h = bh % f.H, hk = h / f.kv_group;
   const int q0 = qb * kBlock;
   const int qi = q0 + wave * 32 + lq;  // this lane's query
@@ -396,6 +451,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const const_i32_ptr flist = (const_i32_ptr)(f.m.full_idx + (int64_t)qb * f.m.nk);
   const const_i32_ptr plist = (const_i32_ptr)(f.m.kv_idx + (int64_t)qb * f.m.nk);
   auto kvblock = [&](int m) { return m < nfull ? flist[m] : plist[m - nfull]; };
+  const int split_len = f.m.schedule[1];
+  const int m_begin = (wi.split && wi.chunk == 1) ? split_len : 0;
+  const int m_end = (wi.split && wi.chunk == 0) ? split_len : nblk;
   // K uses the V swizzle (it is also read transposed), V the K swizzle.
   const uint32_t k_off = (uint32_t)((lane >> 3) * f.k_sl * (int64_t)sizeof(T)) +
                          (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
@@ -416,15 +474,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[te][r] = 0.0f;
 
-  if (nblk > 0) issue(0, st[0]);
+  if (m_end > m_begin) issue(m_begin, st[0]);
   wait_vm_zero();
-  for (int m = 0; m < nblk; ++m) {
-    BwdKStage& s = st[m & 1];
+  for (int m = m_begin; m < m_end; ++m) {
+    BwdKStage& s = st[(m - m_begin) & 1];
     const int kv0 = kvblock(m) * kBlock;
     wait_vm_zero();
     wait_lgkm_zero();
     barrier_only();
-    if (m + 1 < nblk) issue(m + 1, st[(m + 1) & 1]);
+    if (m + 1 < m_end) issue(m + 1, st[(m + 1 - m_begin) & 1]);
     if (kv0 >= khi || kv0 + kBlock <= klo) continue;  // no kept key
     const bool partial = m >= nfull || kv0 < klo || kv0 + kBlock > khi;
     uint32_t mw[4] = {0u, 0u, 0u, 0u};
@@ -463,6 +521,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
+  if (wi.split) {
+    float* base = a.part_q + ((int64_t)qb * 2 * BH + bh) * kBwdQSlot;
+    if (!merge_two<2>(dqacc, base + (int64_t)wi.chunk * BH * kBwdQSlot, base + (int64_t)(1 - wi.chunk) * BH * kBwdQSlot,
+                      a.counters_q + (int64_t)qb * BH + bh, wave, lane))
+      return;
+  }
+
   if (qi < f.L) {
     T* dqg = static_cast<T*>(a.dq) + b * f.q_sb + h * f.q_sh + (int64_t)qi * f.q_sl;
 #pragma unroll
@@ -481,8 +546,9 @@ template <int KIND, bool SOFTCAP>
 hipError_t launch_bwd_kernels(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
   const int64_t Hk = a.f.H / a.f.kv_group;
   const dim3 block(kThreads);
-  const dim3 g_dkdv((unsigned)((int64_t)a.f.B * Hk * a.f.m.nk));
-  const dim3 g_dq((unsigned)((int64_t)a.f.B * a.f.H * a.f.m.nq));
+  // up to two items per kv block / query block (items past a plan's end exit)
+  const dim3 g_dkdv((unsigned)((int64_t)a.f.B * Hk * a.f.m.nk * kMaxChunks));
+  const dim3 g_dq((unsigned)((int64_t)a.f.B * a.f.H * a.f.m.nq * kMaxChunks));
   switch (dtype) {
     case ATTN_BF16:
       if (a.f.m.nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<__bf16, KIND, SOFTCAP>), g_dkdv, block, 0, stream, a);

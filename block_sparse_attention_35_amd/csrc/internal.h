@@ -177,17 +177,62 @@ struct BwdArgs {
   int32_t* tq_idx;    // [nk][nq]: their indices, ascending
   int32_t* tf_num;    // [nk]: full query blocks of kv block kb
   int32_t* tf_idx;    // [nk][nq]
+  // Work plan of the dK/dV kernel ([4 + 8 nk], the forward plan's format
+  // over kv blocks and their query-block lists); the dQ kernel follows the
+  // forward's plan (f.m.schedule). A split item leaves its fp32 partial
+  // accumulators, and the later of the two merges (ticket counters).
+  int32_t* tplan;
+  int32_t split_kv;      // dK/dV items may split (f.split for dQ)
+  int32_t* counters_kv;  // [nk][B*H_kv]
+  float* part_kv;        // [nk][2][B*H_kv] x kBwdKvSlot
+  int32_t* counters_q;   // [nq][B*H]
+  float* part_q;         // [nq][2][B*H] x kBwdQSlot
 };
 
-// Backward workspace: D and lse2 ([B*H*L] floats each), then the transposed
-// BlockMask (tq_num, tf_num [nk]; tq_idx, tf_idx [nk*nq]), each region
-// starting on a 256-byte boundary.
+// Backward workspace, each region on a 256-byte boundary: the dK/dV and dQ
+// ticket counters first, at fixed offsets (kSplitMaxItems int32 each, so a
+// workspace shared by calls of different shapes always finds its counters
+// where the previous call left them at zero), then D and lse2 ([B*H*L]
+// floats each), the transposed BlockMask (tq_num, tf_num [nk]; tq_idx,
+// tf_idx [nk*nq]), the dK/dV plan [4 + 8 nk], and, when items may split (at
+// most kSplitMaxItems items), the partial slots: dK/dV [nk][2][B*H_kv] of
+// kBwdKvSlot floats, dQ [nq][2][B*H] of kBwdQSlot floats (the 4 waves'
+// accumulators in register order).
+constexpr int64_t kBwdQSlot = 4 * 32 * 64;
+constexpr int64_t kBwdKvSlot = 2 * 4 * 32 * 64;
 inline size_t bwd_align(size_t n) { return (n + 255) & ~(size_t)255; }
-inline size_t bwd_workspace_bytes(int64_t bh, int32_t L, int32_t nq, int32_t nk) {
-  const size_t rows = (size_t)bh * (size_t)L * sizeof(float);
-  const size_t nums = (size_t)nk * sizeof(int32_t), idx = (size_t)nk * (size_t)nq * sizeof(int32_t);
-  return 2 * bwd_align(rows) + 2 * bwd_align(nums) + 2 * bwd_align(idx);
+struct BwdLayout {
+  size_t counters_kv, counters_q, D, lse2, tq_num, tf_num, tq_idx, tf_idx, tplan, part_kv, part_q, total;
+  bool split_kv, split_q;
+};
+inline BwdLayout bwd_layout(int64_t bh, int64_t bhk, int32_t L, int32_t nq, int32_t nk) {
+  BwdLayout w{};
+  size_t o = 0;
+  auto take = [&](size_t n) { const size_t at = o; o += bwd_align(n); return at; };
+  w.counters_kv = take(kCountersBytes);
+  w.counters_q = take(kCountersBytes);
+  w.D = take((size_t)bh * L * sizeof(float));
+  w.lse2 = take((size_t)bh * L * sizeof(float));
+  w.tq_num = take((size_t)nk * sizeof(int32_t));
+  w.tf_num = take((size_t)nk * sizeof(int32_t));
+  w.tq_idx = take((size_t)nk * nq * sizeof(int32_t));
+  w.tf_idx = take((size_t)nk * nq * sizeof(int32_t));
+  w.tplan = take((size_t)(4 + 8 * (int64_t)nk) * sizeof(int32_t));
+  w.split_kv = bhk * nk <= kSplitMaxItems;
+  w.split_q = bh * nq <= kSplitMaxItems;
+  w.part_kv = take(w.split_kv ? (size_t)nk * 2 * bhk * kBwdKvSlot * sizeof(float) : 0);
+  w.part_q = take(w.split_q ? (size_t)nq * 2 * bh * kBwdQSlot * sizeof(float) : 0);
+  w.total = o;
+  return w;
 }
+inline size_t bwd_workspace_bytes(int64_t bh, int64_t bhk, int32_t L, int32_t nq, int32_t nk) {
+  return bwd_layout(bh, bhk, L, nq, nk).total;
+}
+
+// Enqueue the work plan (plan_kernel) over n_rows rows of blocks whose
+// partial / full block lists have n_cols columns.
+hipError_t launch_plan(int32_t nrows, int32_t ncols, const int32_t* part_num, const int32_t* part_idx,
+                       const int32_t* full_num, const int32_t* full_idx, int32_t* plan, hipStream_t stream);
 
 // Enqueue the backward (bf16 / fp16): D and lse2, the transposed BlockMask,
 // then the dK/dV and dQ kernels.

@@ -325,6 +325,57 @@ attn_status attn_forward_padded(const void* q, const void* k, const void* v, voi
                                 const int32_t* key_start, const int32_t* key_end, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace attn_backward needs (always > 0): two fixed 8 KiB
+ * regions of ticket counters, D and lse2 (B*H*q_len floats each), the
+ * BlockMask transposed ([nk] counts and [nk * nq] indices, twice), the dK/dV
+ * work plan (4 + 8 nk ints), and, when there are few work items (B*H_kv*nk
+ * <= 2048, resp. B*H*nq <= 2048), fp32 partial slots for the two-way split
+ * of long items (nk * 2 * B*H_kv slots of 16384 floats, nq * 2 * B*H slots
+ * of 8192 floats); each region 256-byte aligned.
+ * Errors: INVALID_ARGUMENT for a null bm or bytes, B, H, H_kv < 1 or H not a
+ * multiple of H_kv.
+ */
+attn_status attn_backward_workspace_size(int32_t B, int32_t H, int32_t H_kv, const attn_block_mask* bm,
+                                         size_t* bytes);
+
+/*
+ * Backward of attn_forward_padded (bf16 / fp16): the gradients dq, dk, dv of
+ * sum(dout * o) with respect to q, k and v, the attention matrix recomputed
+ * from the forward's logsumexp instead of stored ("Flash Attention 2 and the
+ * IO bottleneck" (tcdigital), section on recomputation in backpropagation).
+ * With P the forward's probabilities and s' its (soft-capped) scaled scores:
+ *   dv_j = sum_i P_ij dout_i;  dS_ij = P_ij (dout_i . v_j - dout_i . o_i) mod'
+ *   dq_i = scale sum_j dS_ij k_j;  dk_j = scale sum_i dS_ij q_i
+ * with mod' = 1 - (s'/softcap)^2 under the soft-cap (1 otherwise); a K/V head
+ * shared by several query heads gets the sum over them. Masked pairs, padded
+ * keys and rows without a live key contribute nothing.
+ *   q, o, dout, dq  device [B, H, L, E];  k, v, dk, dv  device [B, H_kv, S, E];
+ *        all contiguous, 16-byte aligned, element type dtype (ATTN_BF16 or
+ *        ATTN_F16); dq, dk, dv are written in full.
+ *   lse  device fp32 [B, H, L]: the forward's logsumexp for these arguments
+ *        (o too must be the forward's output).
+ *   bm, score_mod, softcap, scale, key_start, key_end: as for the forward.
+ *   workspace  device memory of at least attn_backward_workspace_size bytes,
+ *        256-byte aligned, owned by the caller; its first use must see it
+ *        zero-filled, and every call leaves its counters at zero, so it can be
+ *        reused by later calls of any shape. Calls sharing a workspace must
+ *        not run concurrently.
+ * Arithmetic: products on MFMA from the input type, P and dS rounded to the
+ * input type for their products, fp32 accumulation; deterministic (no
+ * atomics on the gradients: the same inputs give the same bits).
+ * Errors: INVALID_ARGUMENT as for the forward (null pointers, sizes, a mask
+ * built for other lengths, score_mod/softcap/scale, workspace); UNSUPPORTED
+ * for ATTN_F32 or another dtype, E != 64, or too many work items; HIP for a
+ * failed launch.
+ */
+attn_status attn_backward(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L, int32_t S,
+                          int32_t E, const attn_block_mask* bm, int32_t score_mod, float softcap,
+                          float scale, const int32_t* key_start, const int32_t* key_end,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(attn_status status);
 

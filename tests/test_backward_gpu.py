@@ -96,6 +96,10 @@ CASES = [
     (_odd("custom_blocks_700_bf16", "bf16", 2, 700, 900, wl.MASK_CUSTOM),
      wl.block_structured_mask(700, 900, 21, 0.3, 0.3, 0.4), None),
     (_odd("padded_causal_600_bf16", "bf16", 2, 600, 600, wl.MASK_CAUSAL, B=3), None, ([0, 100, 300], [600, 450, 300])),
+    # more than 16 live blocks per row: dQ and dK/dV items split in two and merge
+    (_odd("split_causal_4352_bf16", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL), None, None),
+    (_odd("split_gqa_causal_2304_f16", "f16", 4, 2304, 2304, wl.MASK_CAUSAL, H_kv=2), None, None),
+    (_odd("split_padded_none_2560_bf16", "bf16", 1, 2560, 2560, wl.MASK_NONE, B=2), None, ([100, 0], [2560, 2200])),
 ]
 
 
@@ -117,6 +121,18 @@ def test_backward_is_deterministic(dev):
     _, _, g1 = _run(w, dev)
     _, _, g2 = _run(w, dev)
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+def test_backward_workspace_shared_by_shapes(dev):
+    """One cached workspace serves calls of different shapes in turn (split
+    and unsplit items): every call gives the bits of a call on its own."""
+    ws = [_odd("ws_a_causal_2304_bf16", "bf16", 2, 2304, 2304, wl.MASK_CAUSAL),
+          _odd("ws_b_sliding_700_bf16", "bf16", 3, 700, 700, wl.MASK_SLIDING_WINDOW, 90),
+          _odd("ws_c_gqa_4352_bf16", "bf16", 4, 640, 4352, wl.MASK_CAUSAL_LOWER_RIGHT, H_kv=1)]
+    first = [_run(w, dev)[2] for w in ws]
+    again = [_run(w, dev)[2] for w in reversed(ws)][::-1]
+    for w, g1, g2 in zip(ws, first, again):
+        assert all(torch.equal(a, b) for a, b in zip(g1, g2)), w.name
 
 
 def test_backward_full_size_causal_8192(dev):

@@ -356,7 +356,10 @@ def test_backward_workspace_size():
     lib = bsa._load()
     n = ctypes.c_size_t(0)
     bm = _built_mask(300, 700)  # nq = 3, nk = 6
-    assert lib.attn_backward_workspace_size(2, 4, ctypes.byref(bm), ctypes.byref(n)) == OK
+    assert lib.attn_backward_workspace_size(2, 4, 2, ctypes.byref(bm), ctypes.byref(n)) == OK
     al = lambda x: (x + 255) // 256 * 256
-    assert n.value == 2 * al(2 * 4 * 300 * 4) + 2 * al(6 * 4) + 2 * al(6 * 3 * 4)
-    assert lib.attn_backward_workspace_size(0, 4, ctypes.byref(bm), ctypes.byref(n)) == INVALID
+    fixed = 2 * 8192 + 2 * al(2 * 4 * 300 * 4) + 2 * al(6 * 4) + 2 * al(6 * 3 * 4) + al((4 + 8 * 6) * 4)
+    # few items: partial slots for split dK/dV (6 kv blocks x 2 x B*H_kv) and dQ (3 x 2 x B*H)
+    assert n.value == fixed + al(6 * 2 * 4 * 16384 * 4) + al(3 * 2 * 8 * 8192 * 4)
+    assert lib.attn_backward_workspace_size(0, 4, 2, ctypes.byref(bm), ctypes.byref(n)) == INVALID
+    assert lib.attn_backward_workspace_size(2, 4, 3, ctypes.byref(bm), ctypes.byref(n)) == INVALID
