@@ -37,39 +37,78 @@ namespace bsattn {
 
 namespace {
 
-// Per-lane LDS pointers of one 128 x 128-byte tile.
-//  * plain_k / plain_v: A-operand rows (row lq, head dims 16c + 8hf .. +7,
-//    16-byte chunk 2c + hf) of a K-swizzled (slot c ^ (r & 7)) or V-swizzled
-//    (slot c ^ 2(r & 3)) tile; rows 32t + lq add t * 4096.
-//  * tr: the transposed-read address of the forward's V operand (see
-//    LanePtrs) for head-dim tile te of a V-swizzled tile; 16-row group g adds
-//    2048 bytes, the second read 1024.
+// A-operand rows of a K-swizzled tile (slot c ^ (r & 7)): row lq, head dims
+// 16c + 8hf .. +7 (16-byte chunk 2c + hf); rows 32t + lq add t * 4096.
 __device__ inline lds_u8 plain_k(lds_u8 tile, int lane, int c) {
   const int lq = lane & 31, hf = lane >> 5;
   return tile + lq * 128 + (((2 * c + hf) ^ (lq & 7)) << 4);
 }
-__device__ inline lds_u8 plain_v(lds_u8 tile, int lane, int c) {
+
+// Tiles read both plain and transposed use one swizzle: 16-byte chunk c of
+// row r sits in slot c ^ u(r), u(r) = 4 ((r >> 1) & 1) | ((r >> 2) & 3). With
+// 64 banks of 4 bytes, a 16-byte slot of row r lands in bank group
+// (8 r + slot) mod 16, so (a) the plain reads of 16 consecutive rows (one
+// chunk each) hit 16 distinct groups: u takes 8 distinct values over the even
+// rows and over the odd rows; (b) a transposed read of 4 aligned rows x up to
+// 4 consecutive chunks does too: rows r and r + 2 differ in bit 2 of u, so
+// their chunk sets are disjoint, and odd rows use the other half of the
+// groups. u depends on row bits 1..3 only, so 32-row tiles and 16-row groups
+// keep the pattern.
+__device__ inline int uswz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+__device__ inline lds_u8 plain_u(lds_u8 tile, int lane, int c) {
   const int lq = lane & 31, hf = lane >> 5;
-  return tile + lq * 128 + (((2 * c + hf) ^ ((lq & 3) << 1)) << 4);
+  return tile + lq * 128 + (((2 * c + hf) ^ uswz(lq)) << 4);
 }
-__device__ inline lds_u8 tr_v(lds_u8 tile, int lane, int te) {
+// Transposed-read addresses (the forward's V-operand layout, see LanePtrs)
+// of the first (rows r1) and
+// second (rows r1 + 8) read of head-dim tile te in a u-swizzled tile.
+__device__ inline lds_u8 tr_u(lds_u8 tile, int lane, int te, int second) {
   const int hf = lane >> 5, g16 = lane >> 4, i16 = lane & 15;
-  const int r1 = hf * 4 + (i16 >> 2);
+  const int r1 = hf * 4 + (i16 >> 2) + 8 * second;
   const int e = te * 32 + (g16 & 1) * 16 + (i16 & 3) * 4;
   const int c16 = e >> 3, half = (e >> 2) & 1;
-  return tile + r1 * 128 + ((c16 ^ ((r1 & 3) << 1)) << 4) + half * 8;
+  return tile + r1 * 128 + ((c16 ^ uswz(r1)) << 4) + half * 8;
 }
+// Per-lane byte offsets of the u-swizzled tile copies: lane l fills slot
+// l & 7 of row l / 8 of an 8-row copy; copies 0 and 2 (rows with bit 3
+// clear) and 1 and 3 (bit 3 set) need different chunks.
+__device__ inline uint32_t u_off(int64_t sl_bytes, int lane, int odd) {
+  const int r = (lane >> 3) + 8 * odd;
+  return (uint32_t)((lane >> 3) * sl_bytes) + (uint32_t)(((lane & 7) ^ uswz(r)) * 16);
+}
+// One wave's share (rows 32 wave .. +31) of a u-swizzled 128-row tile copy
+// from rows row0 .. of g (rows past n clamp to n - 1).
+template <typename T>
+__device__ inline void issue_rows_u(const T* g, int64_t sl, uint32_t off_even, uint32_t off_odd, int row0, int n,
+                                    uint8_t* tile, int wave, int lane) {
+  const int r0 = row0 + wave * 32;
+  const uint32_t lds0 = lds_offset(tile) + (uint32_t)wave * 4096u;
+  if (row0 + kBlock <= n) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(g + (int64_t)r0 * sl);
+    const int64_t step = sl * (int64_t)(8 * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16_base(base + i * step, (i & 1) ? off_odd : off_even, lds0 + 1024u * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rt = wave * 32 + 8 * i + (lane >> 3);  // row in the tile
+      const int row = min(r0 + 8 * i + (lane >> 3), n - 1);
+      lds_copy16(g + (int64_t)row * sl + ((lane & 7) ^ uswz(rt)) * 8, lds0 + 1024u * i);
+    }
+  }
+}
+template <typename T>
+__device__ inline typename Vec<T>::x8 read_tr2(lds_u8 lo_p, lds_u8 hi_p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo_p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi_p);
+  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename Vec<T>::x8, both);
+}
+
 template <typename T>
 __device__ inline typename Vec<T>::x8 read16(lds_u8 p) {
   typedef __attribute__((address_space(3))) const typename Vec<T>::x8 lds_x8;
   return *reinterpret_cast<const lds_x8*>(p);
-}
-template <typename T>
-__device__ inline typename Vec<T>::x8 read_tr(lds_u8 p) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
-  const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(typename Vec<T>::x8, both);
 }
 
 // Liveness of pair (query i, key j) in a partial block: the forward's rule,
@@ -276,16 +315,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int total = keys_dead ? 0 : G * span;              // (query head, query block) pairs
   auto qblock = [&](int n) { const int m = m_begin + n % span; return m < nfull ? flist[m] : plist[m - nfull]; };
 
-  const uint32_t lane_off = (uint32_t)((lane >> 3) * f.q_sl * (int64_t)sizeof(T)) +
-                            (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+  const uint32_t off_e = u_off(f.q_sl * (int64_t)sizeof(T), lane, 0);
+  const uint32_t off_o = u_off(f.q_sl * (int64_t)sizeof(T), lane, 1);
   auto issue = [&](int n, BwdQStage& s) __attribute__((always_inline)) {
     const int g = n / span, qb = qblock(n);
     const int h = hk * G + g;
     const int q0 = qb * kBlock;
     const T* qg = static_cast<const T*>(f.q) + b * f.q_sb + h * f.q_sh;
     const T* dg = static_cast<const T*>(a.dout) + b * f.q_sb + h * f.q_sh;
-    issue_rows<T, true>(qg, f.q_sl, lane_off, q0, f.L, s.q, wave, lane);
-    issue_rows<T, true>(dg, f.q_sl, lane_off, q0, f.L, s.dout, wave, lane);
+    issue_rows_u<T>(qg, f.q_sl, off_e, off_o, q0, f.L, s.q, wave, lane);
+    issue_rows_u<T>(dg, f.q_sl, off_e, off_o, q0, f.L, s.dout, wave, lane);
     const int64_t rb = ((int64_t)b * f.H + h) * f.L;
     const int r = min(q0 + wave * 32 + lq, f.L - 1);
     if (lane < 32) {
@@ -328,8 +367,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
       f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        sacc = V::mma(read16<T>(plain_v(qt_base, lane, c) + qt * 4096), kreg[c], sacc);
-        dpacc = V::mma(read16<T>(plain_v(dt_base, lane, c) + qt * 4096), vreg[c], dpacc);
+        sacc = V::mma(read16<T>(plain_u(qt_base, lane, c) + qt * 4096), kreg[c], sacc);
+        dpacc = V::mma(read16<T>(plain_u(dt_base, lane, c) + qt * 4096), vreg[c], dpacc);
       }
       x8 pk[2], dsk[2];
 #pragma unroll
@@ -358,8 +397,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int te = 0; te < 2; ++te) {
           const int g16 = qt * 2 + gi;
-          dvacc[te] = V::mma(read_tr<T>(tr_v(dt_base, lane, te) + g16 * 2048), pk[gi], dvacc[te]);
-          dkacc[te] = V::mma(read_tr<T>(tr_v(qt_base, lane, te) + g16 * 2048), dsk[gi], dkacc[te]);
+          dvacc[te] = V::mma(read_tr2<T>(tr_u(dt_base, lane, te, 0) + g16 * 2048, tr_u(dt_base, lane, te, 1) + g16 * 2048),
+                             pk[gi], dvacc[te]);
+          dkacc[te] = V::mma(read_tr2<T>(tr_u(qt_base, lane, te, 0) + g16 * 2048, tr_u(qt_base, lane, te, 1) + g16 * 2048),
+                             dsk[gi], dkacc[te]);
         }
     }
   }
@@ -454,14 +495,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int split_len = f.m.schedule[1];
   const int m_begin = (wi.split && wi.chunk == 1) ? split_len : 0;
   const int m_end = (wi.split && wi.chunk == 0) ? split_len : nblk;
-  // K uses the V swizzle (it is also read transposed), V the K swizzle.
-  const uint32_t k_off = (uint32_t)((lane >> 3) * f.k_sl * (int64_t)sizeof(T)) +
-                         (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+  // K is u-swizzled (read plain and transposed), V K-swizzled (plain).
+  const uint32_t k_off_e = u_off(f.k_sl * (int64_t)sizeof(T), lane, 0);
+  const uint32_t k_off_o = u_off(f.k_sl * (int64_t)sizeof(T), lane, 1);
   const uint32_t v_off =
       (uint32_t)((lane >> 3) * f.v_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
   auto issue = [&](int m, BwdKStage& s) __attribute__((always_inline)) {
     const int kb = kvblock(m), kv0 = kb * kBlock;
-    issue_rows<T, true>(kg, f.k_sl, k_off, kv0, f.S, s.k, wave, lane);
+    issue_rows_u<T>(kg, f.k_sl, k_off_e, k_off_o, kv0, f.S, s.k, wave, lane);
     issue_rows<T, false>(vg, f.v_sl, v_off, kv0, f.S, s.v, wave, lane);
     if (KIND == ATTN_MASK_DOCUMENT && lane < 32)
       lds_copy4(f.m.doc + min(kv0 + wave * 32 + lane, f.S - 1), lds_offset(s.doc) + (uint32_t)wave * 128u);
@@ -498,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        sacc = V::mma(read16<T>(plain_v(kt_base, lane, c) + t * 4096), qop[c], sacc);
+        sacc = V::mma(read16<T>(plain_u(kt_base, lane, c) + t * 4096), qop[c], sacc);
         dpacc = V::mma(read16<T>(plain_k(vt_base, lane, c) + t * 4096), doop[c], dpacc);
       }
       x8 dsk[2];
@@ -517,7 +558,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
         for (int te = 0; te < 2; ++te)
-          dqacc[te] = V::mma(read_tr<T>(tr_v(kt_base, lane, te) + (t * 2 + gi) * 2048), dsk[gi], dqacc[te]);
+          dqacc[te] = V::mma(read_tr2<T>(tr_u(kt_base, lane, te, 0) + (t * 2 + gi) * 2048,
+                                         tr_u(kt_base, lane, te, 1) + (t * 2 + gi) * 2048),
+                             dsk[gi], dqacc[te]);
     }
   }
 
