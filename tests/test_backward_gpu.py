@@ -96,6 +96,11 @@ CASES = [
     (_odd("custom_blocks_700_bf16", "bf16", 2, 700, 900, wl.MASK_CUSTOM),
      wl.block_structured_mask(700, 900, 21, 0.3, 0.3, 0.4), None),
     (_odd("padded_causal_600_bf16", "bf16", 2, 600, 600, wl.MASK_CAUSAL, B=3), None, ([0, 100, 300], [600, 450, 300])),
+    (_odd("custom_gqa_softcap_f16", "f16", 4, 500, 800, wl.MASK_CUSTOM, 0, (), 15.0, H_kv=1),
+     wl.block_structured_mask(500, 800, 22, 0.25, 0.35, 0.3), None),
+    (_odd("document_L600_S900_bf16", "bf16", 2, 600, 900, wl.MASK_DOCUMENT, 0, (130, 500)), None, None),
+    (_odd("padded_empty_range_bidir_f16", "f16", 2, 384, 384, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (100,), B=2),
+     None, ([50, 200], [384, 200])),
     # more than 16 live blocks per row: dQ and dK/dV items split in two and merge
     (_odd("split_causal_4352_bf16", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL), None, None),
     (_odd("split_gqa_causal_2304_f16", "f16", 4, 2304, 2304, wl.MASK_CAUSAL, H_kv=2), None, None),
@@ -114,6 +119,15 @@ def test_backward_against_oracle(dev, w, m, ranges):
     _compare(w, dq, want[0], w.name + " dq")
     _compare(w, dk, _reduce_kv(w, want[1]), w.name + " dk")
     _compare(w, dv, _reduce_kv(w, want[2]), w.name + " dv")
+
+
+@pytest.mark.parametrize("L,S", [(0, 300), (300, 0)])
+def test_backward_empty_sequences(dev, L, S):
+    """No queries: dk = dv = 0; no keys: dq = 0 (and nothing else to write)."""
+    w = _odd(f"empty_{L}x{S}_bf16", "bf16", 2, L, S, wl.MASK_NONE)
+    _, _, (dq, dk, dv) = _run(w, dev)
+    assert dq.shape == (1, 2, L, 64) and dk.shape == (1, 2, S, 64)
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
 
 
 def test_backward_is_deterministic(dev):
