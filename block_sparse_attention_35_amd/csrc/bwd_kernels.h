@@ -526,8 +526,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     if (m + 1 < m_end) issue(m + 1, st[(m + 1 - m_begin) & 1]);
     if (kv0 >= khi || kv0 + kBlock <= klo) continue;  // no kept key
     const bool partial = m >= nfull || kv0 < klo || kv0 + kBlock > khi;
+    // Full and partial blocks get a body of their own (the pair test a
+    // compile-time choice), so each is straight-line code the scheduler can
+    // interleave.
+    auto body = [&](auto partial_c) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_c)::value;
     uint32_t mw[4] = {0u, 0u, 0u, 0u};
-    if (KIND == ATTN_MASK_CUSTOM && partial) {
+    if (KIND == ATTN_MASK_CUSTOM && PARTIAL) {
       typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
       const u32x4_t w4 = *reinterpret_cast<lds_u32x4*>((lds_u8)s.bits + (wave * 32 + lq) * 16);
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         const int jl = t * 32 + acc_row(r, hf);
         float dmod;
         float p = bwd_prob<SOFTCAP>(sacc[r], lse2, f, dmod);
-        if (partial) {
+        if (PARTIAL) {
           const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[jl] : 0;
           if (!bwd_live<KIND>(f, qi, kv0 + jl, klo, khi, di, dj, mw[t], acc_row(r, hf))) p = 0.0f;
         }
@@ -562,6 +567,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
                                          tr_u(kt_base, lane, te, 1) + (t * 2 + gi) * 2048),
                              dsk[gi], dqacc[te]);
     }
+    };
+    if (partial)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
   }
 
   if (wi.split) {
