@@ -50,10 +50,12 @@ __device__ inline uint8_t classify_interval(int64_t q0, int64_t q1, int64_t k0, 
 __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc,
     const uint32_t* __restrict__ bits, int32_t q_len, int32_t kv_len,
-    int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
+    int32_t nk, int32_t summarize, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
     int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
-  extern __shared__ uint8_t cls[];  // [nk]
+  extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk], then kv_id [nk] (documents)
   __shared__ int32_t doc_q[kBlock];
+  __shared__ int32_t qd_id[kBlock], qd_last[kBlock];  // distinct query ids, last row of each
+  __shared__ int32_t qd_n;
   __shared__ int32_t wave_counts[2][kWaves];
 
   const int tid = threadIdx.x;
@@ -68,39 +70,94 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     // causal condition holds and the two ids are equal, so the class follows
     // from the causal interval rule (or is skip for different ids). A block
     // that mixes ids can never be full; for those, every in-range pair is
-    // evaluated (ids may be in any order). One wave classifies one kv block
-    // at a time, each lane holding two of its keys, with no workgroup
-    // barrier per block.
+    // evaluated (ids may be in any order). First every kv block's keys are
+    // summarised (one id, or mixed) with all loads in flight at once, four
+    // threads per block; then one wave classifies one kv block at a time,
+    // and only blocks that mix ids read their keys again, each lane holding
+    // two, with no workgroup barrier per block.
+    int32_t* kv_id = reinterpret_cast<int32_t*>(cls + ((nk + 15) & ~15));  // [nk]
     if (tid < kBlock) doc_q[tid] = (q0 + tid <= q1) ? doc[q0 + tid] : 0;
+    for (int base = 0; summarize && base < nk; base += kThreads / 4) {
+      const int kb = base + tid / 4, part = tid % 4;
+      int32_t first = 0;
+      int uni = 1;
+      if (kb < nk) {
+        const int64_t k0 = (int64_t)kb * kBlock;
+        const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
+        first = doc[k0];
+        int32_t ids[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) ids[u] = doc[min<int64_t>(k0 + part * 32 + u, k1)];  // all in flight
+#pragma unroll
+        for (int u = 0; u < 32; ++u) uni &= ids[u] == first;
+      }
+      uni &= __shfl_xor(uni, 1);
+      uni &= __shfl_xor(uni, 2);
+      if (kb < nk && part == 0) {
+        kv_id[kb] = first;
+        cls[kb] = (uint8_t)uni;  // read below before the class overwrites it
+      }
+    }
     __syncthreads();
     const int32_t q_id = doc_q[0];
     const bool q_uniform = __syncthreads_and(tid >= kBlock || q0 + tid > q1 || doc_q[tid] == q_id);
     const int n_rows = (int)(q1 - q0 + 1);
+    // The distinct ids of the block's queries, each with its last row: a key
+    // with id d at position j has a live pair in the block iff some query
+    // row i with id d has j <= i + q_off, i.e. iff j <= (last row of d) +
+    // q0 + q_off.
+    if (tid == 0) {
+      qd_n = q_uniform ? 1 : 0;
+      qd_id[0] = q_id;
+      qd_last[0] = n_rows - 1;
+    }
+    __syncthreads();
+    if (!q_uniform && tid < n_rows) {
+      const int32_t id = doc_q[tid];
+      bool last = true;
+      for (int r = tid + 1; r < n_rows; ++r) last &= doc_q[r] != id;
+      if (last) {
+        const int at = atomicAdd(&qd_n, 1);
+        qd_id[at] = id;
+        qd_last[at] = tid;
+      }
+    }
+    __syncthreads();
+    const int nd = qd_n;
     const int wave = tid >> 6, lane = tid & 63;
     for (int kb = wave; kb < nk; kb += kWaves) {
       const int64_t k0 = (int64_t)kb * kBlock;
       const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
       uint8_t c = kSkip;
       if (q1 + q_off >= k0) {  // else every key comes after every query position
-        const int64_t j0 = k0 + lane, j1 = k0 + lane + 64;
-        const bool v0 = j0 <= k1, v1 = j1 <= k1;
-        const int32_t d0 = v0 ? doc[j0] : 0, d1 = v1 ? doc[j1] : 0;
-        const int32_t first = __shfl(d0, 0);  // key k0 is always in range
-        const bool uni = __all((!v0 || d0 == first) && (!v1 || d1 == first));
+        bool uni;
+        int32_t first;
+        if (summarize) {
+          uni = cls[kb] != 0;
+          first = kv_id[kb];
+        } else {  // (too many kv blocks to summarise in LDS: read the keys)
+          const int64_t j0 = k0 + lane, j1 = k0 + lane + 64;
+          const bool v0 = j0 <= k1, v1 = j1 <= k1;
+          const int32_t d0 = v0 ? doc[j0] : 0, d1 = v1 ? doc[j1] : 0;
+          first = __shfl(d0, 0);  // key k0 is always in range
+          uni = __all((!v0 || d0 == first) && (!v1 || d1 == first));
+        }
         if (q_uniform && uni) {
           c = (first == q_id) ? classify_interval(q0 + q_off, q1 + q_off, k0, k1, INT64_MAX / 4,
                                                   q_whole && (k1 - k0 + 1) == kBlock)
                               : kSkip;
         } else {
-          // any in-range pair (i, j) with j <= i and equal ids
+          // any in-range pair (i, j) with j <= i and equal ids, through the
+          // distinct query ids (positions stay below 2^31: p < 2^22 + 2^30)
+          const int32_t j0 = (int32_t)k0 + lane, j1 = (int32_t)k0 + lane + 64;
+          const bool v0 = j0 <= k1, v1 = j1 <= k1;
+          // (keys of one id: the summary has it; else read them)
+          const int32_t d0 = uni ? first : (v0 ? doc[j0] : 0), d1 = uni ? first : (v1 ? doc[j1] : 0);
+          const int32_t base = (int32_t)q0 + q_off;
           bool any = false;
-          for (int il0 = 0; il0 < n_rows && !__any(any); il0 += 32) {
-            const int lim = min(n_rows, il0 + 32);
-            for (int il = il0; il < lim; ++il) {
-              const int64_t i = q0 + il + q_off;  // the rule's query position
-              const int32_t di = doc_q[il];
-              any |= (v0 & (j0 <= i) & (d0 == di)) | (v1 & (j1 <= i) & (d1 == di));
-            }
+          for (int x = 0; x < nd; ++x) {
+            const int32_t id = qd_id[x], last = base + qd_last[x];
+            any |= (v0 & (d0 == id) & (j0 <= last)) | (v1 & (d1 == id) & (j1 <= last));
           }
           c = __any(any) ? kPartial : kSkip;
         }
@@ -285,6 +342,96 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
   }
 }
 
+// The same plan, ranked in parallel: every workgroup loads all rows' block
+// counts into LDS (up to kPlanLdsRows rows) and computes every item's cost
+// there; it then ranks 64 items, lane l taking item 64 b + l and each of the
+// 4 waves comparing it against a quarter of all costs (broadcast LDS reads,
+// four costs per read), and the quarters' counts are summed. Same output as
+// plan_kernel.
+constexpr int kPlanLdsRows = 4096;
+
+__device__ inline int32_t lds_item_cost(int32_t t, const int32_t* nf, const int32_t* np, int32_t split_len) {
+  const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
+  const int32_t n = nf[qb] + np[qb];
+  const int32_t k = split_count(n, split_len);
+  if (chunk >= k) return -1;
+  return chunk_end(chunk, k, n, split_len) - chunk_first(chunk, split_len);
+}
+
+__global__ __launch_bounds__(kThreads) void plan_tile_kernel(int32_t nq, int32_t nk,
+                                                             const int32_t* __restrict__ kv_num,
+                                                             const int32_t* __restrict__ kv_idx,
+                                                             const int32_t* __restrict__ full_num,
+                                                             const int32_t* __restrict__ full_idx,
+                                                             int32_t* __restrict__ plan) {
+  __shared__ int32_t nf_s[kPlanLdsRows], np_s[kPlanLdsRows];
+  __shared__ __attribute__((aligned(16))) int32_t cost_s[kMaxChunks * kPlanLdsRows];
+  __shared__ int32_t red[2][kWaves];
+  __shared__ int32_t part[kWaves][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t mx = 0;
+  for (int q = tid; q < nq; q += kThreads) {
+    const int32_t f = full_num[q], p = kv_num[q];
+    nf_s[q] = f;
+    np_s[q] = p;
+    mx = max(mx, f + p);
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  mx = 0;
+  for (int w = 0; w < kWaves; ++w) mx = max(mx, red[0][w]);
+  const int32_t split_len = max(kMinSplit, (mx + 1) / 2);
+  const int32_t n_items = kMaxChunks * nq;
+  const int32_t n_pad = (n_items + 4 * kWaves - 1) / (4 * kWaves) * (4 * kWaves);
+  int32_t cnt = 0;
+  for (int t = tid; t < n_pad; t += kThreads) {
+    const int32_t c = t < n_items ? lds_item_cost(t, nf_s, np_s, split_len) : -1;
+    cost_s[t] = c;
+    cnt += c >= 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  if (lane == 0) red[1][wave] = cnt;
+  __syncthreads();
+  int32_t count = 0;
+  for (int w = 0; w < kWaves; ++w) count += red[1][w];
+
+  const int32_t t = blockIdx.x * 64 + lane;  // this lane's item
+  const int32_t mine = t < n_items ? cost_s[t] : -1;
+  const int32_t span = n_pad / kWaves, u0 = wave * span;
+  int32_t rank = 0;
+  for (int u = u0; u < u0 + span; u += 4) {
+    const int4 c4 = *reinterpret_cast<const int4*>(&cost_s[u]);
+    rank += (c4.x > mine) | ((c4.x == mine) & (u < t));
+    rank += (c4.y > mine) | ((c4.y == mine) & (u + 1 < t));
+    rank += (c4.z > mine) | ((c4.z == mine) & (u + 2 < t));
+    rank += (c4.w > mine) | ((c4.w == mine) & (u + 3 < t));
+  }
+  part[wave][lane] = rank;
+  __syncthreads();
+  if (wave == 0 && t < n_items) {
+    rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (mine >= 0) {
+      const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
+      const int32_t nf = nf_s[qb], np = np_s[qb];
+      const int32_t first = chunk_first(chunk, split_len);
+      int4 d;
+      d.x = qb | (chunk << 20) | ((split_count(nf + np, split_len) - 1) << 22);
+      d.y = nf;
+      d.z = np;
+      d.w = (first < nf) ? full_idx[(int64_t)qb * nk + first]
+                         : (first - nf < np ? kv_idx[(int64_t)qb * nk + first - nf] : 0);
+      reinterpret_cast<int4*>(plan + 4)[rank] = d;
+    }
+    if (t >= count) reinterpret_cast<int4*>(plan + 4)[t] = make_int4(-1, -1, -1, -1);
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    plan[0] = count;
+    plan[1] = split_len;
+    plan[2] = plan[3] = 0;
+  }
+}
+
 // Dense byte mask -> CUSTOM bits. One wave per (row, 512-key chunk): lane l
 // reads byte 64 u + l of the chunk for u = 0..7 (64 consecutive bytes per
 // load instruction), and ballot u is words 16 c + 2 u and 16 c + 2 u + 1 of
@@ -334,8 +481,12 @@ hipError_t launch_pack_mask(const uint8_t* dense, int64_t row_stride, int32_t q_
 hipError_t launch_plan(int32_t nrows, int32_t ncols, const int32_t* part_num, const int32_t* part_idx,
                        const int32_t* full_num, const int32_t* full_idx, int32_t* plan, hipStream_t stream) {
   if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nrows + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, nrows, ncols, part_num, part_idx, full_num, full_idx, plan);
+  if (nrows <= kPlanLdsRows)
+    hipLaunchKernelGGL(plan_tile_kernel, dim3((kMaxChunks * nrows + 63) / 64), dim3(kThreads), 0, stream, nrows,
+                       ncols, part_num, part_idx, full_num, full_idx, plan);
+  else
+    hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nrows + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       stream, nrows, ncols, part_num, part_idx, full_num, full_idx, plan);
   return hipGetLastError();
 }
 
@@ -344,14 +495,17 @@ hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const 
                              int32_t nk, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
                              int32_t* full_idx, int32_t* schedule, hipStream_t stream) {
   if (nq == 0) return hipSuccess;
-  const size_t lds = (size_t)((nk + 15) & ~15);
+  // classes [nk] (bytes), and for document masks each kv block's id [nk]
+  // while both fit in 48 KiB
+  const size_t cls_bytes = (size_t)((nk + 15) & ~15);
+  const bool summarize = kind == ATTN_MASK_DOCUMENT && cls_bytes + (size_t)nk * sizeof(int32_t) <= 48 * 1024;
+  const size_t lds = cls_bytes + (summarize ? (size_t)nk * sizeof(int32_t) : 0);
   hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off,
-                     window, doc, bits, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
+                     window, doc, bits, q_len, kv_len, nk, summarize ? 1 : 0, kv_num, kv_idx, full_num,
+                     full_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_kernel, dim3((kMaxChunks * nq + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, nq, nk, kv_num, kv_idx, full_num, full_idx, schedule);
-  return hipGetLastError();
+  return launch_plan(nq, nk, kv_num, kv_idx, full_num, full_idx, schedule, stream);
 }
 
 }  // namespace bsattn
