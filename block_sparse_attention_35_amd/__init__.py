@@ -407,15 +407,15 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
                        score_mod: Optional[str] = None, softcap: float = 30.0,
                        scale: Optional[float] = None, key_start: Optional[torch.Tensor] = None,
                        key_end: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv) of sum(dout * out) through ``attention`` (bf16
-    or fp16), with the attention matrix recomputed from ``lse`` (the forward's
+    """Gradients (dq, dk, dv) of sum(dout * out) through ``attention`` (fp32,
+    bf16 or fp16), with the attention matrix recomputed from ``lse`` (the forward's
     logsumexp) by attn_backward. ``out`` and ``lse`` are the forward's outputs
     for the same arguments; k and v may have fewer heads (grouped-query
     attention), and dk, dv then sum over the query heads that share a K/V head.
     Tensors are made contiguous; the call is asynchronous on the current
     stream."""
-    if q.dtype not in (torch.bfloat16, torch.float16):
-        raise ValueError("the backward takes bfloat16 or float16")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
     for t in (k, v, out, dout):
         if t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v, out and dout must share dtype and device")

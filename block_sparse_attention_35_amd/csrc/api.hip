@@ -344,8 +344,8 @@ attn_status attn_backward(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t workspace_size, void* stream) {
   g_last_error[0] = '\0';
   if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
-  if (dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "the backward takes bf16 or fp16");
-  if (dtype != ATTN_BF16 && dtype != ATTN_F16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (B < 1 || H < 1 || L < 0 || S < 0)
     return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d L=%d S=%d", B, H, L, S);
   if (H_kv < 1 || H % H_kv != 0)

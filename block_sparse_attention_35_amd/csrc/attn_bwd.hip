@@ -19,8 +19,10 @@ hipError_t launch_backward(int32_t dtype, const BwdArgs& a, hipStream_t stream) 
     const dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)));
     if (dtype == ATTN_BF16)
       hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, grid, block, 0, stream, a);
-    else
+    else if (dtype == ATTN_F16)
       hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, block, 0, stream, a);
   }
   if (a.f.m.nk > 0) hipLaunchKernelGGL(bwd_transpose_kernel, dim3(a.f.m.nk), block, 0, stream, a);
   hipError_t e = hipGetLastError();

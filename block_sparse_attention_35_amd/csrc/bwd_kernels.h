@@ -146,11 +146,24 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
   const int part = threadIdx.x % 8;
   float acc = 0.0f;
   if (row < rows) {
-    const auto* o = static_cast<const typename Vec<T>::x8*>(a.f.o) + row * 8 + part;
-    const auto* d = static_cast<const typename Vec<T>::x8*>(a.dout) + row * 8 + part;
-    const typename Vec<T>::x8 ov = *o, dv = *d;
+    if constexpr (std::is_same_v<T, float>) {
+      const float4* o = static_cast<const float4*>(a.f.o) + row * 16 + part * 2;
+      const float4* d = static_cast<const float4*>(a.dout) + row * 16 + part * 2;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = fmaf((float)ov[u], (float)dv[u], acc);
+      for (int u = 0; u < 2; ++u) {
+        const float4 ov = o[u], dv = d[u];
+        acc = fmaf(ov.x, dv.x, acc);
+        acc = fmaf(ov.y, dv.y, acc);
+        acc = fmaf(ov.z, dv.z, acc);
+        acc = fmaf(ov.w, dv.w, acc);
+      }
+    } else {
+      const auto* o = static_cast<const typename Vec<T>::x8*>(a.f.o) + row * 8 + part;
+      const auto* d = static_cast<const typename Vec<T>::x8*>(a.dout) + row * 8 + part;
+      const typename Vec<T>::x8 ov = *o, dv = *d;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf((float)ov[u], (float)dv[u], acc);
+    }
   }
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
@@ -595,6 +608,307 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32: the same items, plans and split merges as the 16-bit kernels, with
+// v_mfma_f32_32x32x2_f32 (one contraction element per lane and step; lane
+// half hf takes head dim 32 hf + j at step j) on padded row-major LDS tiles
+// filled through registers, one stage per workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kB32Stride = 68;  // floats per LDS row (64 + 4 padding)
+
+// Rows row0 .. row0 + 127 of a [rows][64] fp32 matrix (row stride sl; rows
+// at or past n read as zero) into a padded LDS tile; 8 float4 per thread.
+__device__ inline void load_tile32(const float* g, int64_t sl, int row0, int n, float* tile) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = threadIdx.x + u * kThreads, row = c >> 4, ch = c & 15;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row0 + row < n) x = *reinterpret_cast<const float4*>(g + (int64_t)(row0 + row) * sl + ch * 4);
+    *reinterpret_cast<float4*>(tile + row * kB32Stride + ch * 4) = x;
+  }
+}
+
+// One row of 64 floats into the 32 per-lane contraction elements.
+__device__ inline void load_row32(const float* row, bool valid, int hf, float (&x)[32]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid) v = *reinterpret_cast<const float4*>(row + hf * 32 + c * 4);
+    x[4 * c + 0] = v.x, x[4 * c + 1] = v.y, x[4 * c + 2] = v.z, x[4 * c + 3] = v.w;
+  }
+}
+
+__device__ inline f32x16_t mma32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+struct alignas(16) Bwd32QStage {
+  float q[kBlock * kB32Stride];
+  float dout[kBlock * kB32Stride];
+  float lse2[kBlock];
+  float D[kBlock];
+  int32_t doc[kBlock];
+  uint32_t bits[4][kBlock];
+};
+
+// dK, dV of one kv block (one plan item) in fp32. Lanes are keys: S = Q K^T
+// and dP = dO V^T put query rows acc_row(r, hf) of tile qt beside this
+// lane's key, which is the B-operand layout of dV^T += dO^T P and
+// dK^T += Q^T dS (contraction over the queries in register order).
+// One workgroup per CU: the K and V rows (64 registers), four accumulator
+// tiles and a tile's scores, probabilities and dS stay in registers, more
+// than the 256 of two waves per SIMD.
+template <int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 1) void bwd32_dkdv_kernel(BwdArgs a) {
+  __shared__ Bwd32QStage s;
+  const FwdArgs& f = a.f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int G = f.kv_group, Hk = f.H / G, BHk = f.B * Hk;
+  const i32x4_t desc = ((const_i32x4_ptr)(a.tplan + 4))[blockIdx.x / BHk];
+  if (desc[0] < 0) return;
+  const int kb = desc[0] & 0xFFFFF, chunk = (desc[0] >> 20) & 3;
+  const bool split = a.split_kv && ((desc[0] >> 22) & 3) > 0;
+  if (chunk > 0 && !split) return;
+  const int bk = blockIdx.x % BHk;
+  const int b = bk / Hk, hk = bk % Hk;
+  const int kv0 = kb * kBlock;
+  const int key = kv0 + wave * 32 + lq;  // this lane's key
+  int klo = 0, khi = f.S;
+  if (f.key_start != nullptr) klo = min(max(((const_i32_ptr)f.key_start)[b], 0), f.S);
+  if (f.key_end != nullptr) khi = max(min(((const_i32_ptr)f.key_end)[b], f.S), klo);
+
+  const float* kg = static_cast<const float*>(f.k) + b * f.k_sb + hk * f.k_sh;
+  const float* vg = static_cast<const float*>(f.v) + b * f.v_sb + hk * f.v_sh;
+  float kr[32], vr[32];
+  load_row32(kg + (int64_t)key * f.k_sl, key < f.S, hf, kr);
+  load_row32(vg + (int64_t)key * f.v_sl, key < f.S, hf, vr);
+  const int32_t dj = (KIND == ATTN_MASK_DOCUMENT && key < f.S) ? f.m.doc[key] : -1;
+
+  const int nfull = desc[1], npart = desc[2];
+  const int nblk = nfull + npart;
+  const int split_len = ((const_i32_ptr)a.tplan)[1];
+  const int m_begin = (split && chunk == 1) ? split_len : 0;
+  const int m_end = (split && chunk == 0) ? split_len : nblk;
+  const int span = m_end - m_begin;
+  const const_i32_ptr flist = (const_i32_ptr)(a.tf_idx + (int64_t)kb * f.m.nq);
+  const const_i32_ptr plist = (const_i32_ptr)(a.tq_idx + (int64_t)kb * f.m.nq);
+  const bool keys_dead = kv0 >= khi || kv0 + kBlock <= klo;
+  const bool keys_cut = kv0 < klo || kv0 + kBlock > khi;
+  const int total = keys_dead ? 0 : G * span;  // (query head, query block) pairs
+
+  f32x16_t dkacc[2], dvacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkacc[te][r] = dvacc[te][r] = 0.0f;
+
+  for (int n = 0; n < total; ++n) {
+    const int g = n / span, m = m_begin + n % span;
+    const int qb = m < nfull ? flist[m] : plist[m - nfull];
+    const int h = hk * G + g, q0 = qb * kBlock;
+    const float* qg = static_cast<const float*>(f.q) + b * f.q_sb + h * f.q_sh;
+    const float* dg = static_cast<const float*>(a.dout) + b * f.q_sb + h * f.q_sh;
+    __syncthreads();
+    load_tile32(qg, f.q_sl, q0, f.L, s.q);
+    load_tile32(dg, f.q_sl, q0, f.L, s.dout);
+    if (tid < kBlock) {
+      const int64_t rb = ((int64_t)b * f.H + h) * f.L;
+      const int r = min(q0 + tid, f.L - 1);
+      s.lse2[tid] = a.lse2[rb + r];
+      s.D[tid] = a.D[rb + r];
+      if (KIND == ATTN_MASK_DOCUMENT) s.doc[tid] = f.m.doc[r];
+    }
+    if (KIND == ATTN_MASK_CUSTOM) {
+      // word 4 kb + w (wave w's keys) of rows q0 .. q0 + 127
+      for (int u = tid; u < 4 * kBlock; u += kThreads) {
+        const int w = u >> 7, row = u & (kBlock - 1);
+        s.bits[w][row] = f.m.bits[(int64_t)min(q0 + row, f.L - 1) * f.m.bits_w + 4 * kb + w];
+      }
+    }
+    __syncthreads();
+    const bool partial = m >= nfull || keys_cut;
+#pragma unroll 1
+    for (int qt = 0; qt < 4; ++qt) {
+      f32x16_t sacc = {}, dpacc = {};
+      const float* qrow = s.q + (qt * 32 + lq) * kB32Stride + hf * 32;
+      const float* drow = s.dout + (qt * 32 + lq) * kB32Stride + hf * 32;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        sacc = mma32(qrow[j], kr[j], sacc);
+        dpacc = mma32(drow[j], vr[j], dpacc);
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = qt * 32 + acc_row(r, hf);
+        float dmod;
+        float pr = bwd_prob<SOFTCAP>(sacc[r], s.lse2[rl], f, dmod);
+        if (partial) {
+          const int32_t di = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[rl] : 0;
+          const uint32_t word = (KIND == ATTN_MASK_CUSTOM) ? s.bits[wave][rl] : 0u;
+          if (!bwd_live<KIND>(f, q0 + rl, key, klo, khi, di, dj, word, lq)) pr = 0.0f;
+        }
+        p[r] = pr;
+        ds[r] = pr * (dpacc[r] - s.D[rl]) * dmod;
+      }
+#pragma unroll
+      for (int te = 0; te < 2; ++te)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = qt * 32 + acc_row(r, hf);
+          dvacc[te] = mma32(s.dout[rl * kB32Stride + te * 32 + lq], p[r], dvacc[te]);
+          dkacc[te] = mma32(s.q[rl * kB32Stride + te * 32 + lq], ds[r], dkacc[te]);
+        }
+    }
+  }
+
+  if (split) {
+    f32x16_t acc[4] = {dkacc[0], dkacc[1], dvacc[0], dvacc[1]};
+    float* base = a.part_kv + ((int64_t)kb * 2 * BHk + bk) * kBwdKvSlot;
+    if (!merge_two<4>(acc, base + (int64_t)chunk * BHk * kBwdKvSlot, base + (int64_t)(1 - chunk) * BHk * kBwdKvSlot,
+                      a.counters_kv + (int64_t)kb * BHk + bk, wave, lane))
+      return;
+    dkacc[0] = acc[0], dkacc[1] = acc[1], dvacc[0] = acc[2], dvacc[1] = acc[3];
+  }
+
+  // lane = key; registers 4 q4 .. +3 of tile te = head dims te 32 + 8 q4 + 4 hf .. +3
+  if (key < f.S) {
+    float* dkg = static_cast<float*>(a.dk) + b * f.k_sb + hk * f.k_sh + (int64_t)key * f.k_sl;
+    float* dvg = static_cast<float*>(a.dv) + b * f.v_sb + hk * f.v_sh + (int64_t)key * f.v_sl;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int e0 = te * 32 + q4 * 8 + hf * 4;
+        const f32x16_t& dk4 = dkacc[te];
+        const f32x16_t& dv4 = dvacc[te];
+        *reinterpret_cast<float4*>(dkg + e0) = make_float4(dk4[q4 * 4] * f.scale, dk4[q4 * 4 + 1] * f.scale,
+                                                           dk4[q4 * 4 + 2] * f.scale, dk4[q4 * 4 + 3] * f.scale);
+        *reinterpret_cast<float4*>(dvg + e0) = make_float4(dv4[q4 * 4], dv4[q4 * 4 + 1], dv4[q4 * 4 + 2], dv4[q4 * 4 + 3]);
+      }
+  }
+}
+
+struct alignas(16) Bwd32KStage {
+  float k[kBlock * kB32Stride];
+  float v[kBlock * kB32Stride];
+  int32_t doc[kBlock];
+};
+
+// dQ of one query block (one item of the forward's plan) in fp32. Lanes are
+// queries, as in the forward: S^T = K Q^T and dP^T = V dO^T, then
+// dQ^T += K^T dS^T with the keys of the accumulator rows as contraction.
+template <int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void bwd32_dq_kernel(BwdArgs a) {
+  __shared__ Bwd32KStage s;
+  const FwdArgs& f = a.f;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = f.B * f.H;
+  const WorkItem wi = work_item(f, blockIdx.x / BH);
+  if (wi.skip) return;
+  const int qb = wi.qb;
+  const int bh = blockIdx.x % BH;
+  const int b = bh / f.H, h = bh % f.H, hk = h / f.kv_group;
+  const int q0 = qb * kBlock;
+  const int qi = q0 + wave * 32 + lq;  // this lane's query
+  int klo = 0, khi = f.S;
+  if (f.key_start != nullptr) klo = min(max(((const_i32_ptr)f.key_start)[b], 0), f.S);
+  if (f.key_end != nullptr) khi = max(min(((const_i32_ptr)f.key_end)[b], f.S), klo);
+
+  const float* qg = static_cast<const float*>(f.q) + b * f.q_sb + h * f.q_sh;
+  const float* dg = static_cast<const float*>(a.dout) + b * f.q_sb + h * f.q_sh;
+  const float* kg = static_cast<const float*>(f.k) + b * f.k_sb + hk * f.k_sh;
+  const float* vg = static_cast<const float*>(f.v) + b * f.v_sb + hk * f.v_sh;
+  float qv[32], dov[32];
+  load_row32(qg + (int64_t)qi * f.q_sl, qi < f.L, hf, qv);
+  load_row32(dg + (int64_t)qi * f.q_sl, qi < f.L, hf, dov);
+  const int64_t row = (int64_t)bh * f.L + min(qi, f.L - 1);
+  const float lse2 = a.lse2[row], Dq = a.D[row];
+  const int32_t di = (KIND == ATTN_MASK_DOCUMENT && qi < f.L) ? f.m.doc[qi] : -1;
+
+  const int nfull = f.m.full_num[qb], npart = f.m.kv_num[qb];
+  const int nblk = nfull + npart;
+  const int32_t* flist = f.m.full_idx + (int64_t)qb * f.m.nk;
+  const int32_t* plist = f.m.kv_idx + (int64_t)qb * f.m.nk;
+  const int split_len = f.m.schedule[1];
+  const int m_begin = (wi.split && wi.chunk == 1) ? split_len : 0;
+  const int m_end = (wi.split && wi.chunk == 0) ? split_len : nblk;
+
+  f32x16_t dqacc[2];
+#pragma unroll
+  for (int te = 0; te < 2; ++te)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqacc[te][r] = 0.0f;
+
+  for (int m = m_begin; m < m_end; ++m) {
+    const int kb = m < nfull ? flist[m] : plist[m - nfull];
+    const int kv0 = kb * kBlock;
+    if (kv0 >= khi || kv0 + kBlock <= klo) continue;  // no kept key (uniform over the workgroup)
+    const bool partial = m >= nfull || kv0 < klo || kv0 + kBlock > khi;
+    __syncthreads();
+    load_tile32(kg, f.k_sl, kv0, f.S, s.k);
+    load_tile32(vg, f.v_sl, kv0, f.S, s.v);
+    if (KIND == ATTN_MASK_DOCUMENT && tid < kBlock) s.doc[tid] = f.m.doc[min(kv0 + tid, f.S - 1)];
+    uint4 mw = make_uint4(0u, 0u, 0u, 0u);
+    if (KIND == ATTN_MASK_CUSTOM && partial)
+      mw = *reinterpret_cast<const uint4*>(f.m.bits + (int64_t)min(qi, f.L - 1) * f.m.bits_w + 4 * kb);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x16_t sacc = {}, dpacc = {};
+      const float* krow = s.k + (t * 32 + lq) * kB32Stride + hf * 32;
+      const float* vrow = s.v + (t * 32 + lq) * kB32Stride + hf * 32;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        sacc = mma32(krow[j], qv[j], sacc);
+        dpacc = mma32(vrow[j], dov[j], dpacc);
+      }
+      const uint32_t word = t == 0 ? mw.x : t == 1 ? mw.y : t == 2 ? mw.z : mw.w;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jl = t * 32 + acc_row(r, hf);
+        float dmod;
+        float p = bwd_prob<SOFTCAP>(sacc[r], lse2, f, dmod);
+        if (partial) {
+          const int32_t dj = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[jl] : 0;
+          if (!bwd_live<KIND>(f, qi, kv0 + jl, klo, khi, di, dj, word, acc_row(r, hf))) p = 0.0f;
+        }
+        ds[r] = p * (dpacc[r] - Dq) * dmod;
+      }
+#pragma unroll
+      for (int te = 0; te < 2; ++te)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = t * 32 + acc_row(r, hf);
+          dqacc[te] = mma32(s.k[jl * kB32Stride + te * 32 + lq], ds[r], dqacc[te]);
+        }
+    }
+  }
+
+  if (wi.split) {
+    float* base = a.part_q + ((int64_t)qb * 2 * BH + bh) * kBwdQSlot;
+    if (!merge_two<2>(dqacc, base + (int64_t)wi.chunk * BH * kBwdQSlot, base + (int64_t)(1 - wi.chunk) * BH * kBwdQSlot,
+                      a.counters_q + (int64_t)qb * BH + bh, wave, lane))
+      return;
+  }
+
+  if (qi < f.L) {
+    float* dqg = static_cast<float*>(a.dq) + b * f.q_sb + h * f.q_sh + (int64_t)qi * f.q_sl;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16_t& d4 = dqacc[te];
+        *reinterpret_cast<float4*>(dqg + te * 32 + q4 * 8 + hf * 4) =
+            make_float4(d4[q4 * 4] * f.scale, d4[q4 * 4 + 1] * f.scale, d4[q4 * 4 + 2] * f.scale,
+                        d4[q4 * 4 + 3] * f.scale);
+      }
+  }
+}
+
 template <int KIND, bool SOFTCAP>
 hipError_t launch_bwd_kernels(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
   const int64_t Hk = a.f.H / a.f.kv_group;
@@ -610,6 +924,10 @@ hipError_t launch_bwd_kernels(int32_t dtype, const BwdArgs& a, hipStream_t strea
     case ATTN_F16:
       if (a.f.m.nk > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<_Float16, KIND, SOFTCAP>), g_dkdv, block, 0, stream, a);
       if (a.f.m.nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<_Float16, KIND, SOFTCAP>), g_dq, block, 0, stream, a);
+      break;
+    case ATTN_F32:
+      if (a.f.m.nk > 0) hipLaunchKernelGGL((bwd32_dkdv_kernel<KIND, SOFTCAP>), g_dkdv, block, 0, stream, a);
+      if (a.f.m.nq > 0) hipLaunchKernelGGL((bwd32_dq_kernel<KIND, SOFTCAP>), g_dq, block, 0, stream, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -340,7 +340,7 @@ attn_status attn_backward_workspace_size(int32_t B, int32_t H, int32_t H_kv, con
                                          size_t* bytes);
 
 /*
- * Backward of attn_forward_padded (bf16 / fp16): the gradients dq, dk, dv of
+ * Backward of attn_forward_padded (fp32 / bf16 / fp16): the gradients dq, dk, dv of
  * sum(dout * o) with respect to q, k and v, the attention matrix recomputed
  * from the forward's logsumexp instead of stored ("Flash Attention 2 and the
  * IO bottleneck" (tcdigital), section on recomputation in backpropagation).
@@ -351,8 +351,8 @@ attn_status attn_backward_workspace_size(int32_t B, int32_t H, int32_t H_kv, con
  * shared by several query heads gets the sum over them. Masked pairs, padded
  * keys and rows without a live key contribute nothing.
  *   q, o, dout, dq  device [B, H, L, E];  k, v, dk, dv  device [B, H_kv, S, E];
- *        all contiguous, 16-byte aligned, element type dtype (ATTN_BF16 or
- *        ATTN_F16); dq, dk, dv are written in full.
+ *        all contiguous, 16-byte aligned, element type dtype (ATTN_F32,
+ *        ATTN_BF16 or ATTN_F16); dq, dk, dv are written in full.
  *   lse  device fp32 [B, H, L]: the forward's logsumexp for these arguments
  *        (o too must be the forward's output).
  *   bm, score_mod, softcap, scale, key_start, key_end: as for the forward.
@@ -362,11 +362,12 @@ attn_status attn_backward_workspace_size(int32_t B, int32_t H, int32_t H_kv, con
  *        reused by later calls of any shape. Calls sharing a workspace must
  *        not run concurrently.
  * Arithmetic: products on MFMA from the input type, P and dS rounded to the
- * input type for their products, fp32 accumulation; deterministic (no
+ * input type for their products (kept in fp32 for ATTN_F32), fp32
+ * accumulation; deterministic (no
  * atomics on the gradients: the same inputs give the same bits).
  * Errors: INVALID_ARGUMENT as for the forward (null pointers, sizes, a mask
  * built for other lengths, score_mod/softcap/scale, workspace); UNSUPPORTED
- * for ATTN_F32 or another dtype, E != 64, or too many work items; HIP for a
+ * for an unknown dtype, E != 64, or too many work items; HIP for a
  * failed launch.
  */
 attn_status attn_backward(const void* q, const void* k, const void* v, const void* o,

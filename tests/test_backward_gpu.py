@@ -8,7 +8,10 @@ dK and dQ, and O in D = dO . O), relative error u = 2^-9 (bf16) or 2^-12
 of each output is a few u times the magnitude of its terms: the test bounds
 the max-abs error by 8 u and the mean-abs error by 2 u, relative to the
 reference's max-abs (resp. mean-abs) value (measured: at most 2.7 u and
-1.3 u over the cases below). At full size (the benchmark's
+1.3 u over the cases below). In fp32 nothing is rounded to a narrower type;
+the error comes from fp32 sums over up to S terms (about sqrt(S) 2^-24
+relative for sums of mixed sign, at most 2^-18 for S <= 4096) and the
+1-ulp exp2, so u = 2^-18 there. At full size (the benchmark's
 shapes) dq is compared on sampled rows, and dk, dv through identities that
 hold exactly: sum_j dV_j = sum_i dO_i over the rows with a live key, and
 sum_j dK_j = 0 without the soft-cap (each row of dS sums to zero).
@@ -24,7 +27,7 @@ from test_parity_gpu import _expand_kv
 
 pytestmark = pytest.mark.gpu
 
-U = {"bf16": 2.0 ** -9, "f16": 2.0 ** -12}
+U = {"bf16": 2.0 ** -9, "f16": 2.0 ** -12, "f32": 2.0 ** -18}
 
 
 @pytest.fixture(scope="module")
@@ -105,6 +108,16 @@ CASES = [
     (_odd("split_causal_4352_bf16", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL), None, None),
     (_odd("split_gqa_causal_2304_f16", "f16", 4, 2304, 2304, wl.MASK_CAUSAL, H_kv=2), None, None),
     (_odd("split_padded_none_2560_bf16", "bf16", 1, 2560, 2560, wl.MASK_NONE, B=2), None, ([100, 0], [2560, 2200])),
+    # fp32 (fp32 MFMA, probabilities and dS unrounded)
+    (wl.WORKLOADS["causal_256_f32"], None, None),
+    (_odd("sliding_softcap_700_f32", "f32", 2, 700, 700, wl.MASK_SLIDING_WINDOW, 150, (), 30.0), None, None),
+    (_odd("document_gqa_600_f32", "f32", 4, 600, 600, wl.MASK_DOCUMENT, 0, (100, 350), H_kv=2), None, None),
+    (_odd("custom_400x520_f32", "f32", 2, 400, 520, wl.MASK_CUSTOM),
+     wl.block_structured_mask(400, 520, 23, 0.3, 0.3, 0.4), None),
+    (_odd("padded_bidir_f32", "f32", 2, 384, 384, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (100,), B=2),
+     None, ([50, 0], [384, 300])),
+    (_odd("decode_lr_L1_S3000_f32", "f32", 8, 1, 3000, wl.MASK_CAUSAL_LOWER_RIGHT, H_kv=2), None, None),
+    (_odd("split_gqa_causal_2304_f32", "f32", 4, 2304, 2304, wl.MASK_CAUSAL, H_kv=2), None, None),
 ]
 
 
@@ -130,8 +143,9 @@ def test_backward_empty_sequences(dev, L, S):
     assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
 
 
-def test_backward_is_deterministic(dev):
-    w = _odd("det_causal_gqa_bf16", "bf16", 4, 777, 777, wl.MASK_CAUSAL, H_kv=2)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_is_deterministic(dev, dtype):
+    w = _odd(f"det_causal_gqa_{dtype}", dtype, 4, 2304, 2304, wl.MASK_CAUSAL, H_kv=2)
     _, _, g1 = _run(w, dev)
     _, _, g2 = _run(w, dev)
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))

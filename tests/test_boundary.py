@@ -328,7 +328,7 @@ def _bwd(dtype=1, B=1, H=2, H_kv=2, L=256, S=256, E=64, bm=None, score_mod=0, so
 
 
 BWD_CASES = [
-    ("fp32_unsupported", dict(dtype=0), UNSUPPORTED, "bf16 or fp16"),
+    ("fp32_misaligned_dk", dict(dtype=0, ptrs=dict(dk=FAKE + 4)), INVALID, "aligned"),
     ("unknown_dtype", dict(dtype=9), UNSUPPORTED, "dtype"),
     ("head_dim_128", dict(E=128), UNSUPPORTED, "head dim"),
     ("kv_heads_not_dividing", dict(H=3, H_kv=2), INVALID, "share"),
