@@ -412,6 +412,29 @@ def test_workspace_shared_by_calls_of_different_shapes(dev):
         assert int(shared[:2048 * 4].count_nonzero()) == 0
 
 
+def test_packed_merge_deterministic_and_clean(dev):
+    """Packed decode items cut into chunks (4 and 32 chunks here) and merged:
+    the same bits on every call, the workspace's ticket counters left at
+    zero, and one workspace shared by shapes with other chunk counts gives
+    each call's own results."""
+    dec = wl.WORKLOADS["decode_gqa_b8_h32_kv8_s8192_bf16"]
+    long = _odd("decode_b1_h32_kv8_s65536_bf16", "bf16", 32, 1, 65536, wl.MASK_CAUSAL_LOWER_RIGHT).with_(H_kv=8)
+    runs = []
+    for w, seed in ((dec, 8), (long, 9)):
+        q, k, v = (x.to(dev) for x in wl.make_qkv(w, seed))
+        bm = bsa.create_block_mask(w.kind, w.L, w.S, device=dev)
+        runs.append((q, k, v, bm, bsa.workspace_size(q, bm)))
+    refs = [bsa.attention(q, k, v, bm, workspace=torch.zeros(n, dtype=torch.uint8, device=dev), return_lse=True)
+            for q, k, v, bm, n in runs]
+    shared = torch.zeros(max(r[4] for r in runs), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        for (q, k, v, bm, _), (o_ref, l_ref) in zip(runs, refs):
+            o, lse = bsa.attention(q, k, v, bm, workspace=shared, return_lse=True)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+            assert int(shared[:2048 * 4].count_nonzero()) == 0
+
+
 def test_many_heads_without_split_sampled_rows(dev):
     """B*H*nq above 2048: long query blocks are not split."""
     w = _odd("causal_8192_h33_bf16", "bf16", 33, 8192, 8192, wl.MASK_CAUSAL)
