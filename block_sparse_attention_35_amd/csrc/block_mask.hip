@@ -50,10 +50,10 @@ __device__ inline uint8_t classify_interval(int64_t q0, int64_t q1, int64_t k0, 
 __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc,
     const uint32_t* __restrict__ bits, int32_t q_len, int32_t kv_len,
-    int32_t nk, int32_t summarize, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
+    int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
     int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk], then kv_id [nk] (documents)
-  __shared__ int32_t doc_q[kBlock];
+  extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk]
+  __shared__ __attribute__((aligned(16))) int32_t doc_q[kBlock];
   __shared__ int32_t qd_id[kBlock], qd_last[kBlock];  // distinct query ids, last row of each
   __shared__ int32_t qd_n;
   __shared__ int32_t wave_counts[2][kWaves];
@@ -70,34 +70,30 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     // causal condition holds and the two ids are equal, so the class follows
     // from the causal interval rule (or is skip for different ids). A block
     // that mixes ids can never be full; for those, every in-range pair is
-    // evaluated (ids may be in any order). First every kv block's keys are
-    // summarised (one id, or mixed) with all loads in flight at once, four
-    // threads per block; then one wave classifies one kv block at a time,
-    // and only blocks that mix ids read their keys again, each lane holding
-    // two, with no workgroup barrier per block.
-    int32_t* kv_id = reinterpret_cast<int32_t*>(cls + ((nk + 15) & ~15));  // [nk]
+    // evaluated (ids may be in any order). Wave w takes kv blocks w, w + 4,
+    // ..., sixteen at a time, each lane two keys of each (coalesced loads,
+    // all in flight); the first batch is issued before the query side is
+    // prepared, and each block is classified from the keys in registers,
+    // with no workgroup barrier per block.
+    const int wave = tid >> 6, lane = tid & 63;
+    constexpr int kBatch = 16;
+    int32_t d0[kBatch], d1[kBatch];  // keys k0 + lane and k0 + 64 + lane of block base + 4u
+    auto load_batch = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int kb = base + u * kWaves;
+        d0[u] = d1[u] = 0;
+        if (kb < nk) {
+          // keys past kv_len repeat the block's last key (an in-range id)
+          const int64_t k0 = (int64_t)kb * kBlock;
+          const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
+          d0[u] = doc[min<int64_t>(k0 + lane, k1)];
+          d1[u] = doc[min<int64_t>(k0 + 64 + lane, k1)];
+        }
+      }
+    };
+    load_batch(wave);
     if (tid < kBlock) doc_q[tid] = (q0 + tid <= q1) ? doc[q0 + tid] : 0;
-    for (int base = 0; summarize && base < nk; base += kThreads / 4) {
-      const int kb = base + tid / 4, part = tid % 4;
-      int32_t first = 0;
-      int uni = 1;
-      if (kb < nk) {
-        const int64_t k0 = (int64_t)kb * kBlock;
-        const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
-        first = doc[k0];
-        int32_t ids[32];
-#pragma unroll
-        for (int u = 0; u < 32; ++u) ids[u] = doc[min<int64_t>(k0 + part * 32 + u, k1)];  // all in flight
-#pragma unroll
-        for (int u = 0; u < 32; ++u) uni &= ids[u] == first;
-      }
-      uni &= __shfl_xor(uni, 1);
-      uni &= __shfl_xor(uni, 2);
-      if (kb < nk && part == 0) {
-        kv_id[kb] = first;
-        cls[kb] = (uint8_t)uni;  // read below before the class overwrites it
-      }
-    }
     __syncthreads();
     const int32_t q_id = doc_q[0];
     const bool q_uniform = __syncthreads_and(tid >= kBlock || q0 + tid > q1 || doc_q[tid] == q_id);
@@ -115,7 +111,16 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     if (!q_uniform && tid < n_rows) {
       const int32_t id = doc_q[tid];
       bool last = true;
-      for (int r = tid + 1; r < n_rows; ++r) last &= doc_q[r] != id;
+      // every row, four per LDS read (all threads read the same words)
+#pragma unroll 8
+      for (int r4 = 0; r4 < kBlock / 4; ++r4) {
+        const int4 x = reinterpret_cast<const int4*>(doc_q)[r4];
+        const int r = 4 * r4;
+        last &= !((r > tid) & (r < n_rows) & (x.x == id));
+        last &= !((r + 1 > tid) & (r + 1 < n_rows) & (x.y == id));
+        last &= !((r + 2 > tid) & (r + 2 < n_rows) & (x.z == id));
+        last &= !((r + 3 > tid) & (r + 3 < n_rows) & (x.w == id));
+      }
       if (last) {
         const int at = atomicAdd(&qd_n, 1);
         qd_id[at] = id;
@@ -124,45 +129,38 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
     }
     __syncthreads();
     const int nd = qd_n;
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int kb = wave; kb < nk; kb += kWaves) {
-      const int64_t k0 = (int64_t)kb * kBlock;
-      const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
-      uint8_t c = kSkip;
-      if (q1 + q_off >= k0) {  // else every key comes after every query position
-        bool uni;
-        int32_t first;
-        if (summarize) {
-          uni = cls[kb] != 0;
-          first = kv_id[kb];
-        } else {  // (too many kv blocks to summarise in LDS: read the keys)
-          const int64_t j0 = k0 + lane, j1 = k0 + lane + 64;
-          const bool v0 = j0 <= k1, v1 = j1 <= k1;
-          const int32_t d0 = v0 ? doc[j0] : 0, d1 = v1 ? doc[j1] : 0;
-          first = __shfl(d0, 0);  // key k0 is always in range
-          uni = __all((!v0 || d0 == first) && (!v1 || d1 == first));
-        }
-        if (q_uniform && uni) {
-          c = (first == q_id) ? classify_interval(q0 + q_off, q1 + q_off, k0, k1, INT64_MAX / 4,
-                                                  q_whole && (k1 - k0 + 1) == kBlock)
-                              : kSkip;
-        } else {
-          // any in-range pair (i, j) with j <= i and equal ids, through the
-          // distinct query ids (positions stay below 2^31: p < 2^22 + 2^30)
-          const int32_t j0 = (int32_t)k0 + lane, j1 = (int32_t)k0 + lane + 64;
-          const bool v0 = j0 <= k1, v1 = j1 <= k1;
-          // (keys of one id: the summary has it; else read them)
-          const int32_t d0 = uni ? first : (v0 ? doc[j0] : 0), d1 = uni ? first : (v1 ? doc[j1] : 0);
-          const int32_t base = (int32_t)q0 + q_off;
-          bool any = false;
-          for (int x = 0; x < nd; ++x) {
-            const int32_t id = qd_id[x], last = base + qd_last[x];
-            any |= (v0 & (d0 == id) & (j0 <= last)) | (v1 & (d1 == id) & (j1 <= last));
+    for (int base = wave; base < nk; base += kWaves * kBatch) {
+      if (base != wave) load_batch(base);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int kb = base + u * kWaves;
+        if (kb >= nk) break;  // (wave-uniform)
+        const int64_t k0 = (int64_t)kb * kBlock;
+        const int64_t k1 = min<int64_t>(kv_len, k0 + kBlock) - 1;
+        uint8_t c = kSkip;
+        if (q1 + q_off >= k0) {  // else every key comes after every query position
+          const int32_t first = __shfl(d0[u], 0);  // key k0
+          const bool uni = __all(d0[u] == first && d1[u] == first);
+          if (q_uniform && uni) {
+            c = (first == q_id) ? classify_interval(q0 + q_off, q1 + q_off, k0, k1, INT64_MAX / 4,
+                                                    q_whole && (k1 - k0 + 1) == kBlock)
+                                : kSkip;
+          } else {
+            // any in-range pair (i, j) with j <= i and equal ids, through the
+            // distinct query ids (positions stay below 2^31: p < 2^22 + 2^30)
+            const int32_t j0 = (int32_t)k0 + lane, j1 = (int32_t)k0 + lane + 64;
+            const bool v0 = j0 <= k1, v1 = j1 <= k1;
+            const int32_t base_p = (int32_t)q0 + q_off;
+            bool any = false;
+            for (int x = 0; x < nd; ++x) {
+              const int32_t id = qd_id[x], last = base_p + qd_last[x];
+              any |= (v0 & (d0[u] == id) & (j0 <= last)) | (v1 & (d1[u] == id) & (j1 <= last));
+            }
+            c = __any(any) ? kPartial : kSkip;
           }
-          c = __any(any) ? kPartial : kSkip;
         }
+        if (lane == 0) cls[kb] = c;
       }
-      if (lane == 0) cls[kb] = c;
     }
   } else if (kind == ATTN_MASK_CUSTOM) {
     // One wave per kv block: lane l holds rows q0 + l and q0 + l + 64 (when
@@ -495,14 +493,10 @@ hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const 
                              int32_t nk, int32_t* kv_num, int32_t* kv_idx, int32_t* full_num,
                              int32_t* full_idx, int32_t* schedule, hipStream_t stream) {
   if (nq == 0) return hipSuccess;
-  // classes [nk] (bytes), and for document masks each kv block's id [nk]
-  // while both fit in 48 KiB
-  const size_t cls_bytes = (size_t)((nk + 15) & ~15);
-  const bool summarize = kind == ATTN_MASK_DOCUMENT && cls_bytes + (size_t)nk * sizeof(int32_t) <= 48 * 1024;
-  const size_t lds = cls_bytes + (summarize ? (size_t)nk * sizeof(int32_t) : 0);
+  // classes [nk] (bytes)
+  const size_t lds = (size_t)((nk + 15) & ~15);
   hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off,
-                     window, doc, bits, q_len, kv_len, nk, summarize ? 1 : 0, kv_num, kv_idx, full_num,
-                     full_idx);
+                     window, doc, bits, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_plan(nq, nk, kv_num, kv_idx, full_num, full_idx, schedule, stream);
