@@ -59,9 +59,10 @@ def _mask_on_gpu(w: wl.Workload, dev, doc=None):
     return bm, doc
 
 
-def _check_mask(bm, w: wl.Workload, doc):
+def _check_mask(bm, w: wl.Workload, doc, want=None):
     torch.cuda.synchronize()
-    want = oracle.block_mask(w.kind, w.L, w.S, w.window, doc)
+    if want is None:
+        want = oracle.block_mask(w.kind, w.L, w.S, w.window, doc)
     got = (bm.kv_num_blocks, bm.kv_indices, bm.full_kv_num_blocks, bm.full_kv_indices)
     for name, g, e in zip(("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
                            "full_kv_indices"), got, want):
@@ -433,6 +434,38 @@ def test_packed_merge_deterministic_and_clean(dev):
             torch.cuda.synchronize()
             assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
             assert int(shared[:2048 * 4].count_nonzero()) == 0
+
+
+def test_more_query_blocks_than_the_lds_plan_holds(dev):
+    """4100 query blocks (L = S = 524800, window 256): past the 4096 rows the
+    parallel plan keeps in LDS, the plan is ranked by the fallback kernel.
+    A causal window's block lists are the same in every row past the first
+    few, shifted by the row index, so each row is checked against the
+    oracle's lists of a 16-block case (rows up to 15 as they are, later rows
+    as row 15 shifted); then the plan, and sampled rows of O."""
+    nq = 4100
+    w = _odd("sliding_w256_524800_bf16", "bf16", 1, nq * 128, nq * 128, wl.MASK_SLIDING_WINDOW, 256)
+    small = oracle.block_mask(w.kind, 16 * 128, 16 * 128, w.window, None)
+    want = [np.zeros((nq,), np.int32), np.zeros((nq, nq), np.int32),
+            np.zeros((nq,), np.int32), np.zeros((nq, nq), np.int32)]
+    for qb in range(nq):
+        r = min(qb, 15)
+        for cnt, lst in ((0, 1), (2, 3)):
+            n = int(small[cnt][r])
+            want[cnt][qb] = n
+            want[lst][qb, :n] = small[lst][r, :n] + (qb - r)
+    bm, _ = _mask_on_gpu(w, dev)
+    _check_mask(bm, w, None, want=want)
+    (q, k, v), _, o, lse = _run(w, dev, qkv=wl.make_qkv(w, 3))
+    # the first and last rows, the rows around the 4096th query block, and
+    # rows drawn uniformly (a few seconds of the oracle)
+    rows = np.unique(np.concatenate([[0, 127, 128, w.L - 1], 4096 * 128 + np.arange(-2, 2),
+                                     np.random.default_rng(5).integers(0, w.L, 40)])).astype(np.int64)
+    want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                        w.kind, w.scale, w.window, None, 0.0, rows=rows)
+    got = o.float().reshape(-1, w.E)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    got_lse = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy().astype(np.float64)
+    _compare(w, got, got_lse, want_o, want_lse, w.name)
 
 
 def test_many_heads_without_split_sampled_rows(dev):
