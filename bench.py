@@ -41,6 +41,7 @@ import block_sparse_attention_35_amd as bsa  # noqa: E402
 import workloads as wl  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "ms/forward and live-pair TFLOPS (% bf16 MFMA peak), S=8192 causal & S=32768 W=256"
 HEADLINE = "causal_8192_bf16"
@@ -49,6 +50,10 @@ SECOND = "sliding_32768_w256_bf16"
 VARIANTS = ("causal_lower_right_2048x8192_bf16", "gqa_causal_8192_h32_kv8_bf16",
             "document_bidirectional_8192_f16_softcap", "causal_8192_keypad_b2_bf16",
             "decode_gqa_b8_h32_kv8_s8192_bf16", "custom_blocks_8192_bf16")
+# The other configurations of the method's workloads (the fp32 accuracy case,
+# the window sweep at S=8192, documents with the soft-cap), timed the same way.
+CONFIGS = ("causal_256_f32", "sliding_8192_w64_bf16", "sliding_8192_w256_bf16", "sliding_8192_w1024_bf16",
+           "sliding_8192_w4096_bf16", "document_8192_f16_softcap")
 
 
 def padded_causal_pairs(L: int, start: int, end: int) -> int:
@@ -229,6 +234,9 @@ def summarize(w: wl.Workload, r):
                        "min": float(r["fwd_ms"].min()), "max": float(r["fwd_ms"].max())},
         "forward_tflops": flops / (fwd_avg * 1e-3) / 1e12,
         "forward_frac_bf16_peak": flops / (fwd_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        # fp32 runs on the fp32 MFMA, whose peak is its own
+        **({"forward_frac_fp32_peak": flops / (fwd_avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS}
+           if w.dtype == "f32" else {}),
         "forward_gbs": nbytes / (fwd_avg * 1e-3) / 1e9,
         "forward_frac_hbm_peak": nbytes / (fwd_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "dominant_kernel_traffic": measured_traffic(w.name),
@@ -308,7 +316,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workloads", default=",".join((HEADLINE, SECOND) + VARIANTS))
+    ap.add_argument("--workloads", default=",".join((HEADLINE, SECOND) + VARIANTS + CONFIGS))
     ap.add_argument("--backward", default=HEADLINE,
                     help="workloads whose backward is timed too (comma list; empty for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
