@@ -23,8 +23,8 @@
 //
 // Kernel 1 (one workgroup per query block) writes the classes to LDS, then
 // compacts them in ascending kb order with wave ballots and writes the counts,
-// the index lists and the zero padding. Kernel 2 ranks query blocks by their
-// number of live kv blocks, descending, ties by index, and writes the order.
+// the index lists and the zero padding. Kernel 2 writes the work plan (items
+// ranked by cost). For the interval rules one kernel does both.
 #include <algorithm>
 
 #include "internal.h"
@@ -47,19 +47,19 @@ __device__ inline uint8_t classify_interval(int64_t q0, int64_t q1, int64_t k0, 
   return kPartial;
 }
 
-__global__ __launch_bounds__(kThreads) void classify_compact_kernel(
-    int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc,
+// Classes of query block qb's kv blocks into cls (LDS, [nk] bytes), then the
+// compacted lists and counts of the block.
+__device__ __forceinline__ void classify_block(
+    int qb, int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc,
     const uint32_t* __restrict__ bits, int32_t q_len, int32_t kv_len,
-    int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
+    int32_t nk, uint8_t* cls, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
     int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk]
   __shared__ __attribute__((aligned(16))) int32_t doc_q[kBlock];
   __shared__ int32_t qd_id[kBlock], qd_last[kBlock];  // distinct query ids, last row of each
   __shared__ int32_t qd_n;
   __shared__ int32_t wave_counts[2][kWaves];
 
   const int tid = threadIdx.x;
-  const int qb = blockIdx.x;
   const int64_t q0 = (int64_t)qb * kBlock;
   const int64_t q1 = min<int64_t>(q_len, q0 + kBlock) - 1;
   const bool q_whole = (q1 - q0 + 1) == kBlock;
@@ -249,6 +249,17 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
   }
 }
 
+// Kernel 1 of every rule: one workgroup per query block.
+__global__ __launch_bounds__(kThreads) void classify_compact_kernel(
+    int32_t kind, int32_t q_off, int32_t window, const int32_t* __restrict__ doc,
+    const uint32_t* __restrict__ bits, int32_t q_len, int32_t kv_len,
+    int32_t nk, int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx,
+    int32_t* __restrict__ full_num, int32_t* __restrict__ full_idx) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk]
+  classify_block(blockIdx.x, kind, q_off, window, doc, bits, q_len, kv_len, nk, cls, kv_num, kv_idx, full_num,
+                 full_idx);
+}
+
 // Work plan. With max_n the largest number of live kv blocks of any query
 // block, the split length is C = max(kMinSplit, ceil(max_n / 2)); a query
 // block with n > C blocks becomes two work items, its first C visited blocks
@@ -347,6 +358,10 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(int32_t nq, int32_t nk,
 // four costs per read), and the quarters' counts are summed. Same output as
 // plan_kernel.
 constexpr int kPlanLdsRows = 4096;
+// The one-launch path for the interval rules: up to this many query blocks
+// and kv blocks (its plan arrays and classes stay within 64 KiB of LDS).
+constexpr int kIntervalMaxRows = 1024;
+constexpr int kIntervalMaxKvBlocks = 32768;
 
 __device__ inline int32_t lds_item_cost(int32_t t, const int32_t* nf, const int32_t* np, int32_t split_len) {
   const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
@@ -356,29 +371,18 @@ __device__ inline int32_t lds_item_cost(int32_t t, const int32_t* nf, const int3
   return chunk_end(chunk, k, n, split_len) - chunk_first(chunk, split_len);
 }
 
-__global__ __launch_bounds__(kThreads) void plan_tile_kernel(int32_t nq, int32_t nk,
-                                                             const int32_t* __restrict__ kv_num,
-                                                             const int32_t* __restrict__ kv_idx,
-                                                             const int32_t* __restrict__ full_num,
-                                                             const int32_t* __restrict__ full_idx,
-                                                             int32_t* __restrict__ plan) {
-  __shared__ int32_t nf_s[kPlanLdsRows], np_s[kPlanLdsRows];
-  __shared__ __attribute__((aligned(16))) int32_t cost_s[kMaxChunks * kPlanLdsRows];
-  __shared__ int32_t red[2][kWaves];
+// Ranks items 64 tile .. 64 tile + 63 of the plan from the block counts of
+// all nq query blocks in LDS (nf_s, np_s; mx their largest sum) and writes
+// their descriptors; first_block(qb, pos) is the kv block at position pos of
+// qb's visit order (full blocks, then partial), 0 past its end. Workgroup 0
+// also writes the header.
+template <class FirstBlock>
+__device__ __forceinline__ void rank_tile(int tile, int32_t nq, const int32_t* nf_s, const int32_t* np_s,
+                                          int32_t* cost_s, int32_t mx, FirstBlock first_block,
+                                          int32_t* __restrict__ plan) {
+  __shared__ int32_t red[kWaves];
   __shared__ int32_t part[kWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t mx = 0;
-  for (int q = tid; q < nq; q += kThreads) {
-    const int32_t f = full_num[q], p = kv_num[q];
-    nf_s[q] = f;
-    np_s[q] = p;
-    mx = max(mx, f + p);
-  }
-  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[0][wave] = mx;
-  __syncthreads();
-  mx = 0;
-  for (int w = 0; w < kWaves; ++w) mx = max(mx, red[0][w]);
   const int32_t split_len = max(kMinSplit, (mx + 1) / 2);
   const int32_t n_items = kMaxChunks * nq;
   const int32_t n_pad = (n_items + 4 * kWaves - 1) / (4 * kWaves) * (4 * kWaves);
@@ -389,12 +393,12 @@ __global__ __launch_bounds__(kThreads) void plan_tile_kernel(int32_t nq, int32_t
     cnt += c >= 0;
   }
   for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-  if (lane == 0) red[1][wave] = cnt;
+  if (lane == 0) red[wave] = cnt;
   __syncthreads();
   int32_t count = 0;
-  for (int w = 0; w < kWaves; ++w) count += red[1][w];
+  for (int w = 0; w < kWaves; ++w) count += red[w];
 
-  const int32_t t = blockIdx.x * 64 + lane;  // this lane's item
+  const int32_t t = tile * 64 + lane;  // this lane's item
   const int32_t mine = t < n_items ? cost_s[t] : -1;
   const int32_t span = n_pad / kWaves, u0 = wave * span;
   int32_t rank = 0;
@@ -412,22 +416,140 @@ __global__ __launch_bounds__(kThreads) void plan_tile_kernel(int32_t nq, int32_t
     if (mine >= 0) {
       const int32_t qb = t / kMaxChunks, chunk = t % kMaxChunks;
       const int32_t nf = nf_s[qb], np = np_s[qb];
-      const int32_t first = chunk_first(chunk, split_len);
       int4 d;
       d.x = qb | (chunk << 20) | ((split_count(nf + np, split_len) - 1) << 22);
       d.y = nf;
       d.z = np;
-      d.w = (first < nf) ? full_idx[(int64_t)qb * nk + first]
-                         : (first - nf < np ? kv_idx[(int64_t)qb * nk + first - nf] : 0);
+      d.w = first_block(qb, chunk_first(chunk, split_len));
       reinterpret_cast<int4*>(plan + 4)[rank] = d;
     }
     if (t >= count) reinterpret_cast<int4*>(plan + 4)[t] = make_int4(-1, -1, -1, -1);
   }
-  if (blockIdx.x == 0 && tid == 0) {
+  if (tile == 0 && tid == 0) {
     plan[0] = count;
     plan[1] = split_len;
     plan[2] = plan[3] = 0;
   }
+}
+
+// The largest of every workgroup thread's value.
+__device__ inline int32_t block_max(int32_t v) {
+  __shared__ int32_t red[kWaves];
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = red[0];
+  for (int w = 1; w < kWaves; ++w) v = max(v, red[w]);
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void plan_tile_kernel(int32_t nq, int32_t nk,
+                                                             const int32_t* __restrict__ kv_num,
+                                                             const int32_t* __restrict__ kv_idx,
+                                                             const int32_t* __restrict__ full_num,
+                                                             const int32_t* __restrict__ full_idx,
+                                                             int32_t* __restrict__ plan) {
+  __shared__ int32_t nf_s[kPlanLdsRows], np_s[kPlanLdsRows];
+  __shared__ __attribute__((aligned(16))) int32_t cost_s[kMaxChunks * kPlanLdsRows];
+  int32_t mx = 0;
+  for (int q = threadIdx.x; q < nq; q += kThreads) {
+    const int32_t f = full_num[q], p = kv_num[q];
+    nf_s[q] = f;
+    np_s[q] = p;
+    mx = max(mx, f + p);
+  }
+  mx = block_max(mx);  // (its barrier also publishes nf_s, np_s)
+  rank_tile(blockIdx.x, nq, nf_s, np_s, cost_s, mx,
+            [&](int32_t qb, int32_t pos) {
+              const int32_t nf = nf_s[qb], np = np_s[qb];
+              return (pos < nf) ? full_idx[(int64_t)qb * nk + pos]
+                                : (pos - nf < np ? kv_idx[(int64_t)qb * nk + pos - nf] : 0);
+            },
+            plan);
+}
+
+// Interval rules (none, causal, sliding window, with the query offset of the
+// bottom-right kinds): a query block's live kv blocks are one run [lo, lo +
+// n), and its full blocks one run [f, f + nf) inside it, because each class
+// condition of classify_interval is monotone in kb (k0 and k1 grow with kb,
+// so both pair offsets q - k1 and q - k0 shrink). Each bound is the first kb
+// where a condition turns true, found by bisection with the same arithmetic
+// as the classifier; the visit order is the full run, then the partial
+// blocks before it, then after it.
+struct Runs {
+  int32_t lo, n, f, nf;
+};
+__device__ inline Runs interval_runs(int32_t kind, int32_t q_off, int32_t window, int32_t q_len, int32_t kv_len,
+                                     int32_t nk, int32_t qb) {
+  const int64_t q0 = (int64_t)qb * kBlock;
+  const int64_t q1 = min<int64_t>(q_len, q0 + kBlock) - 1;
+  const bool q_whole = (q1 - q0 + 1) == kBlock;
+  const int32_t n_whole = q_whole ? kv_len / kBlock : 0;  // kv blocks with all 128 keys in range
+  Runs r;
+  if (kind == ATTN_MASK_NONE) {
+    r.lo = 0, r.n = nk, r.f = 0, r.nf = n_whole;
+    return r;
+  }
+  const int64_t p0 = q0 + q_off, p1 = q1 + q_off;
+  const int64_t w = (kind == ATTN_MASK_SLIDING_WINDOW) ? (int64_t)window : INT64_MAX / 4;
+  auto k0 = [](int32_t kb) { return (int64_t)kb * kBlock; };
+  auto k1 = [&](int32_t kb) { return min<int64_t>(kv_len, k0(kb) + kBlock) - 1; };
+  // first kb in [0, nk] where a condition false for small kb becomes true
+  auto first_true = [&](auto cond) {
+    int32_t a = 0, b = nk;
+    while (a < b) {
+      const int32_t m = (a + b) >> 1;
+      if (cond(m))
+        b = m;
+      else
+        a = m + 1;
+    }
+    return a;
+  };
+  r.lo = first_true([&](int32_t kb) { return p0 - k1(kb) <= w - 1; });   // not skipped for dmin
+  const int32_t end = first_true([&](int32_t kb) { return p1 - k0(kb) < 0; });  // skipped for dmax
+  r.n = max(0, end - r.lo);
+  r.f = first_true([&](int32_t kb) { return p1 - k0(kb) <= w - 1; });
+  const int32_t f_end = min(n_whole, first_true([&](int32_t kb) { return p0 - k1(kb) < 0; }));
+  r.nf = (r.n > 0) ? max(0, f_end - r.f) : 0;
+  return r;
+}
+__device__ inline int32_t interval_block_at(const Runs& r, int32_t pos) {
+  if (pos < r.nf) return r.f + pos;
+  const int32_t i = pos - r.nf;  // partial index
+  if (i >= r.n - r.nf) return 0;
+  if (r.nf == 0) return r.lo + i;
+  const int32_t before = r.f - r.lo;  // partial blocks before the full run
+  return i < before ? r.lo + i : r.f + r.nf + (i - before);
+}
+
+// Kernel 1 and the plan in one launch for the interval rules: workgroup qb
+// classifies query block qb, and the first (2 nq + 63) / 64 workgroups also
+// rank 64 plan items each from the counts of every query block in closed
+// form, so no workgroup waits for another. Same output as the two kernels.
+__global__ __launch_bounds__(kThreads) void interval_mask_kernel(
+    int32_t kind, int32_t q_off, int32_t window, int32_t q_len, int32_t kv_len, int32_t nq, int32_t nk,
+    int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx, int32_t* __restrict__ full_num,
+    int32_t* __restrict__ full_idx, int32_t* __restrict__ plan) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk]
+  __shared__ int32_t nf_s[kIntervalMaxRows], np_s[kIntervalMaxRows];
+  __shared__ __attribute__((aligned(16))) int32_t cost_s[kMaxChunks * kIntervalMaxRows];
+  classify_block(blockIdx.x, kind, q_off, window, nullptr, nullptr, q_len, kv_len, nk, cls, kv_num, kv_idx,
+                 full_num, full_idx);
+  if ((int)blockIdx.x >= (kMaxChunks * nq + 63) / 64) return;  // (uniform per workgroup)
+  int32_t mx = 0;
+  for (int q = threadIdx.x; q < nq; q += kThreads) {
+    const Runs r = interval_runs(kind, q_off, window, q_len, kv_len, nk, q);
+    nf_s[q] = r.nf;
+    np_s[q] = r.n - r.nf;
+    mx = max(mx, r.n);
+  }
+  mx = block_max(mx);
+  rank_tile(blockIdx.x, nq, nf_s, np_s, cost_s, mx,
+            [&](int32_t qb, int32_t pos) {
+              return interval_block_at(interval_runs(kind, q_off, window, q_len, kv_len, nk, qb), pos);
+            },
+            plan);
 }
 
 // Dense byte mask -> CUSTOM bits. One wave per (row, 512-key chunk): lane l
@@ -495,6 +617,12 @@ hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const 
   if (nq == 0) return hipSuccess;
   // classes [nk] (bytes)
   const size_t lds = (size_t)((nk + 15) & ~15);
+  if ((kind == ATTN_MASK_NONE || kind == ATTN_MASK_CAUSAL || kind == ATTN_MASK_SLIDING_WINDOW) &&
+      nq <= kIntervalMaxRows && nk <= kIntervalMaxKvBlocks) {
+    hipLaunchKernelGGL(interval_mask_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off, window, q_len,
+                       kv_len, nq, nk, kv_num, kv_idx, full_num, full_idx, schedule);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off,
                      window, doc, bits, q_len, kv_len, nk, kv_num, kv_idx, full_num, full_idx);
   hipError_t e = hipGetLastError();
