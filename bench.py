@@ -102,7 +102,7 @@ def algorithmic_bytes(w: wl.Workload) -> int:
     return (n * w.L * w.E * 2 + nkv * w.S * w.E * 2) * esize + n * w.L * 4
 
 
-def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
+def run_workload(w: wl.Workload, steps: int, warmup: int, dev, use_graph: bool = False):
     q, k, v = (x.to(dev) for x in wl.make_qkv(w, 0))
     doc = wl.make_doc(w)
     doc_t = torch.from_numpy(doc).to(dev) if doc is not None else None
@@ -120,19 +120,42 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
         ks = torch.tensor([a for a, _ in w.key_ranges], dtype=torch.int32, device=dev)
         ke = torch.tensor([b for _, b in w.key_ranges], dtype=torch.int32, device=dev)
 
+    # an explicit zero-filled workspace, so nothing is allocated inside a graph
+    nws = bsa.workspace_size(q, bm)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev) if nws > 0 else None
+
     def step():
         bm.rebuild()
         bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
-                      scale=w.scale, out=o, lse=lse, key_start=ks, key_end=ke)
+                      scale=w.scale, out=o, lse=lse, key_start=ks, key_end=ke, workspace=ws)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
+    # The step's two launches (mask build, forward) captured once in a HIP
+    # graph and replayed; a replay must give the eager step's bits.
+    replay, timing = step, "eager"
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        o_graph, lse_graph = o.clone(), lse.clone()
+        step()
+        torch.cuda.synchronize()
+        if not (torch.equal(o, o_graph) and torch.equal(lse, lse_graph)):
+            raise RuntimeError(f"{w.name}: graph replay differs from the eager step")
+        replay, timing = g.replay, "graph"
+        for _ in range(warmup // 4):
+            replay()
+        torch.cuda.synchronize()
+
     # Timed region: exactly `steps` whole steps between two synchronisations.
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        replay()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
 
@@ -149,7 +172,7 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     mask_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     def fwd():
         bsa.attention(q, k, v, bm, score_mod=score_mod, softcap=w.softcap or 30.0,
-                      scale=w.scale, out=o, lse=lse, key_start=ks, key_end=ke)
+                      scale=w.scale, out=o, lse=lse, key_start=ks, key_end=ke, workspace=ws)
 
     # Each timed batch is queued behind two untimed launches, so the host
     # stays ahead of the GPU and no host-side pause lands between the events;
@@ -171,7 +194,7 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev):
     finally:
         gc.enable()
     fwd_ms = np.array([a.elapsed_time(b) / batch for a, b in events])
-    return dict(wall_ms=wall_ms, mask_ms=mask_ms, fwd_ms=fwd_ms)
+    return dict(wall_ms=wall_ms, mask_ms=mask_ms, fwd_ms=fwd_ms, timing=timing)
 
 
 def run_backward(w: wl.Workload, steps: int, warmup: int, dev):
@@ -229,6 +252,7 @@ def summarize(w: wl.Workload, r):
     return {
         "workload": w.name,
         "ms_per_step": r["wall_ms"],
+        "step_timing": r["timing"],
         "step_tflops": flops / (r["wall_ms"] * 1e-3) / 1e12,
         "forward_ms": {"mean": fwd_avg, "median": float(np.median(r["fwd_ms"])),
                        "min": float(r["fwd_ms"].min()), "max": float(r["fwd_ms"].max())},
@@ -315,6 +339,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as a replayed HIP graph (slower here than separate launches)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workloads", default=",".join((HEADLINE, SECOND) + VARIANTS + CONFIGS))
     ap.add_argument("--backward", default=HEADLINE,
@@ -345,7 +371,7 @@ def main():
     for n in names:
         w = wl.WORKLOADS[n]
         print(f"bench: {n} ...", file=sys.stderr, flush=True)
-        results[n] = summarize(w, run_workload(w, args.steps, args.warmup, dev))
+        results[n] = summarize(w, run_workload(w, args.steps, args.warmup, dev, use_graph=args.graph))
         print(f"bench: {n} forward {results[n]['forward_ms']['mean']:.4f} ms "
               f"{results[n]['forward_tflops']:.1f} TFLOPS", file=sys.stderr, flush=True)
 
