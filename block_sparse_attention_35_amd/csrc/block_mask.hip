@@ -523,10 +523,11 @@ __device__ inline int32_t interval_block_at(const Runs& r, int32_t pos) {
   return i < before ? r.lo + i : r.f + r.nf + (i - before);
 }
 
-// Kernel 1 and the plan in one launch for the interval rules: workgroup qb
-// classifies query block qb, and the first (2 nq + 63) / 64 workgroups also
-// rank 64 plan items each from the counts of every query block in closed
-// form, so no workgroup waits for another. Same output as the two kernels.
+// Kernel 1 and the plan in one launch for the interval rules: workgroup qb <
+// nq classifies query block qb, and the (2 nq + 63) / 64 workgroups after
+// them rank 64 plan items each from the counts of every query block in
+// closed form, so no workgroup waits for another. Same output as the two
+// kernels.
 __global__ __launch_bounds__(kThreads) void interval_mask_kernel(
     int32_t kind, int32_t q_off, int32_t window, int32_t q_len, int32_t kv_len, int32_t nq, int32_t nk,
     int32_t* __restrict__ kv_num, int32_t* __restrict__ kv_idx, int32_t* __restrict__ full_num,
@@ -534,9 +535,12 @@ __global__ __launch_bounds__(kThreads) void interval_mask_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk]
   __shared__ int32_t nf_s[kIntervalMaxRows], np_s[kIntervalMaxRows];
   __shared__ __attribute__((aligned(16))) int32_t cost_s[kMaxChunks * kIntervalMaxRows];
-  classify_block(blockIdx.x, kind, q_off, window, nullptr, nullptr, q_len, kv_len, nk, cls, kv_num, kv_idx,
-                 full_num, full_idx);
-  if ((int)blockIdx.x >= (kMaxChunks * nq + 63) / 64) return;  // (uniform per workgroup)
+  if ((int)blockIdx.x < nq) {
+    classify_block(blockIdx.x, kind, q_off, window, nullptr, nullptr, q_len, kv_len, nk, cls, kv_num, kv_idx,
+                   full_num, full_idx);
+    return;
+  }
+  const int tile = blockIdx.x - nq;
   int32_t mx = 0;
   for (int q = threadIdx.x; q < nq; q += kThreads) {
     const Runs r = interval_runs(kind, q_off, window, q_len, kv_len, nk, q);
@@ -545,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void interval_mask_kernel(
     mx = max(mx, r.n);
   }
   mx = block_max(mx);
-  rank_tile(blockIdx.x, nq, nf_s, np_s, cost_s, mx,
+  rank_tile(tile, nq, nf_s, np_s, cost_s, mx,
             [&](int32_t qb, int32_t pos) {
               return interval_block_at(interval_runs(kind, q_off, window, q_len, kv_len, nk, qb), pos);
             },
@@ -619,8 +623,8 @@ hipError_t launch_block_mask(int32_t kind, int32_t q_off, int32_t window, const 
   const size_t lds = (size_t)((nk + 15) & ~15);
   if ((kind == ATTN_MASK_NONE || kind == ATTN_MASK_CAUSAL || kind == ATTN_MASK_SLIDING_WINDOW) &&
       nq <= kIntervalMaxRows && nk <= kIntervalMaxKvBlocks) {
-    hipLaunchKernelGGL(interval_mask_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off, window, q_len,
-                       kv_len, nq, nk, kv_num, kv_idx, full_num, full_idx, schedule);
+    hipLaunchKernelGGL(interval_mask_kernel, dim3(nq + (kMaxChunks * nq + 63) / 64), dim3(kThreads), lds, stream,
+                       kind, q_off, window, q_len, kv_len, nq, nk, kv_num, kv_idx, full_num, full_idx, schedule);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(classify_compact_kernel, dim3(nq), dim3(kThreads), lds, stream, kind, q_off,
