@@ -473,9 +473,8 @@ __global__ __launch_bounds__(kThreads) void plan_tile_kernel(int32_t nq, int32_t
 // n), and its full blocks one run [f, f + nf) inside it, because each class
 // condition of classify_interval is monotone in kb (k0 and k1 grow with kb,
 // so both pair offsets q - k1 and q - k0 shrink). Each bound is the first kb
-// where a condition turns true, found by bisection with the same arithmetic
-// as the classifier; the visit order is the full run, then the partial
-// blocks before it, then after it.
+// where a condition turns true: k0 = 128 kb is linear, and k1 = 128 kb + 127
+// except for a last block cut by kv_len, which is checked on its own.
 struct Runs {
   int32_t lo, n, f, nf;
 };
@@ -492,25 +491,19 @@ __device__ inline Runs interval_runs(int32_t kind, int32_t q_off, int32_t window
   }
   const int64_t p0 = q0 + q_off, p1 = q1 + q_off;
   const int64_t w = (kind == ATTN_MASK_SLIDING_WINDOW) ? (int64_t)window : INT64_MAX / 4;
-  auto k0 = [](int32_t kb) { return (int64_t)kb * kBlock; };
-  auto k1 = [&](int32_t kb) { return min<int64_t>(kv_len, k0(kb) + kBlock) - 1; };
-  // first kb in [0, nk] where a condition false for small kb becomes true
-  auto first_true = [&](auto cond) {
-    int32_t a = 0, b = nk;
-    while (a < b) {
-      const int32_t m = (a + b) >> 1;
-      if (cond(m))
-        b = m;
-      else
-        a = m + 1;
-    }
-    return a;
+  // first kb with k0 > x, with k0 >= x, and with k1 >= x
+  auto k0_gt = [&](int64_t x) { return x < 0 ? 0 : (int32_t)min<int64_t>(nk, x / kBlock + 1); };
+  auto k0_ge = [&](int64_t x) { return x <= 0 ? 0 : (int32_t)min<int64_t>(nk, (x + kBlock - 1) / kBlock); };
+  auto k1_ge = [&](int64_t x) {
+    const int64_t a = x - (kBlock - 1);
+    int32_t c = a <= 0 ? 0 : (int32_t)min<int64_t>(nk, (a + kBlock - 1) / kBlock);
+    if (c == nk - 1 && (int64_t)kv_len - 1 < x) c = nk;  // the last block, cut by kv_len
+    return c;
   };
-  r.lo = first_true([&](int32_t kb) { return p0 - k1(kb) <= w - 1; });   // not skipped for dmin
-  const int32_t end = first_true([&](int32_t kb) { return p1 - k0(kb) < 0; });  // skipped for dmax
-  r.n = max(0, end - r.lo);
-  r.f = first_true([&](int32_t kb) { return p1 - k0(kb) <= w - 1; });
-  const int32_t f_end = min(n_whole, first_true([&](int32_t kb) { return p0 - k1(kb) < 0; }));
+  r.lo = k1_ge(p0 - w + 1);                 // not skipped: p0 - k1 <= W - 1
+  r.n = max(0, k0_gt(p1) - r.lo);           // skipped from the first kb with p1 - k0 < 0
+  r.f = k0_ge(p1 - w + 1);                  // full needs p1 - k0 <= W - 1 ...
+  const int32_t f_end = min(n_whole, k1_ge(p0 + 1));  // ... and p0 - k1 >= 0, whole blocks
   r.nf = (r.n > 0) ? max(0, f_end - r.f) : 0;
   return r;
 }
@@ -534,6 +527,7 @@ __global__ __launch_bounds__(kThreads) void interval_mask_kernel(
     int32_t* __restrict__ full_idx, int32_t* __restrict__ plan) {
   extern __shared__ __attribute__((aligned(16))) uint8_t cls[];  // [nk]
   __shared__ int32_t nf_s[kIntervalMaxRows], np_s[kIntervalMaxRows];
+  __shared__ int32_t lo_s[kIntervalMaxRows], f_s[kIntervalMaxRows];
   __shared__ __attribute__((aligned(16))) int32_t cost_s[kMaxChunks * kIntervalMaxRows];
   if ((int)blockIdx.x < nq) {
     classify_block(blockIdx.x, kind, q_off, window, nullptr, nullptr, q_len, kv_len, nk, cls, kv_num, kv_idx,
@@ -546,12 +540,15 @@ __global__ __launch_bounds__(kThreads) void interval_mask_kernel(
     const Runs r = interval_runs(kind, q_off, window, q_len, kv_len, nk, q);
     nf_s[q] = r.nf;
     np_s[q] = r.n - r.nf;
+    lo_s[q] = r.lo;
+    f_s[q] = r.f;
     mx = max(mx, r.n);
   }
   mx = block_max(mx);
   rank_tile(tile, nq, nf_s, np_s, cost_s, mx,
             [&](int32_t qb, int32_t pos) {
-              return interval_block_at(interval_runs(kind, q_off, window, q_len, kv_len, nk, qb), pos);
+              const Runs r{lo_s[qb], nf_s[qb] + np_s[qb], f_s[qb], nf_s[qb]};
+              return interval_block_at(r, pos);
             },
             plan);
 }
