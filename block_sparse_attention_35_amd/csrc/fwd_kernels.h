@@ -428,6 +428,11 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   // only live tiles skip the test; for document masks the interval decides
   // only "none live".
   int tile_cls[4] = {kTileLive, kTileLive, kTileLive, kTileLive};
+  // Sliding windows: a dead tile's QK and PV MFMAs and its exponentials are
+  // skipped too (wave-uniform branches; its probabilities would be 0). Each of
+  // a window's two partial blocks holds 0..3 dead tiles per wave. For the
+  // other rules the branches cost more than they save.
+  constexpr bool SKIP_DEAD = PARTIAL && KIND == ATTN_MASK_SLIDING_WINDOW;
   // CUSTOM: this lane's row's mask words of the block (word t = tile t).
   uint32_t mw[4] = {0u, 0u, 0u, 0u};
   if (PARTIAL && KIND == ATTN_MASK_CUSTOM) {
@@ -535,7 +540,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   auto q_chunk = [&](int j) __attribute__((always_inline)) {
     if (j + 4 < 16) kf[j + 4] = k_frag(j + 4);
     const int t = j >> 2, c = j & 3;
-    s[t] = V::mma(kf[j], qop[c], c == 0 ? f32x16_t{} : s[t]);
+    if (!SKIP_DEAD || tile_cls[t] != kTileDead) s[t] = V::mma(kf[j], qop[c], c == 0 ? f32x16_t{} : s[t]);
   };
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -584,6 +589,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
   float psum[2] = {0.0f, 0.0f};
   auto prob_chunk = [&](int k) {
     const int g = k >> 1;
+    if (SKIP_DEAD && tile_cls[g >> 1] == kTileDead) return;
 #pragma unroll
     for (int u = (k & 1) * 4; u < (k & 1) * 4 + 4; u += 2) {
       const float x0 = s[g >> 1][(g & 1) * 8 + u], x1 = s[g >> 1][(g & 1) * 8 + u + 1];
@@ -608,7 +614,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     if (i + 4 < 16) vf[i + 4] = v_frag(i + 4);
-    oacc[i & 1] = V::mma(vf[i], pk[i >> 1], oacc[i & 1]);
+    if (!SKIP_DEAD || tile_cls[i >> 2] != kTileDead) oacc[i & 1] = V::mma(vf[i], pk[i >> 1], oacc[i & 1]);
     if (i + 2 < 16) prob_chunk(i + 2);
     sched_fence();
   }
