@@ -32,7 +32,7 @@ import torch
 __all__ = [
     "BlockMask", "BsattnError", "create_block_mask", "create_block_mask_from_dense",
     "create_block_mask_from_bits", "pack_mask", "mask_words", "attention", "attention_backward",
-    "num_blocks", "library_path",
+    "num_blocks", "schedule_len", "library_path",
     "workspace_size",
     "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
     "MASK_CAUSAL_LOWER_RIGHT", "MASK_SLIDING_WINDOW_LOWER_RIGHT", "MASK_DOCUMENT_BIDIRECTIONAL",
@@ -105,6 +105,8 @@ def _load():
     i64p = ctypes.POINTER(ctypes.c_int64)
     lib.attn_num_blocks.restype = i32
     lib.attn_num_blocks.argtypes = [i32, i32]
+    lib.attn_block_mask_schedule_len.restype = i32
+    lib.attn_block_mask_schedule_len.argtypes = [i32, i32, i32]
     lib.attn_build_block_mask.restype = i32
     lib.attn_build_block_mask.argtypes = [i32, i32, vp, i32, i32, i32,
                                           ctypes.POINTER(_BlockMaskStruct), vp]
@@ -159,6 +161,14 @@ def num_blocks(length: int, block_size: int = BLOCK_SIZE) -> int:
     return n
 
 
+def schedule_len(q_len: int, kv_len: int, block_size: int = BLOCK_SIZE) -> int:
+    """int32 entries of a BlockMask's work-plan array (from the library)."""
+    n = _load().attn_block_mask_schedule_len(q_len, kv_len, block_size)
+    if n < 0:
+        raise BsattnError(-1, f"bad lengths {q_len}, {kv_len} or block size {block_size}")
+    return n
+
+
 def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -187,7 +197,7 @@ class BlockMask:
         self.kv_indices = torch.empty(nq, nk, **opt)
         self.full_kv_num_blocks = torch.empty(nq, **opt)
         self.full_kv_indices = torch.empty(nq, nk, **opt)
-        self.schedule = torch.zeros(4 + 8 * nq, **opt)
+        self.schedule = torch.zeros(schedule_len(q_len, kv_len), **opt)
         self._struct = _BlockMaskStruct()
         s = self._struct
         s.kv_num_blocks = self.kv_num_blocks.data_ptr()
@@ -324,6 +334,38 @@ def _strides(t: torch.Tensor):
     return arr
 
 
+def _check_forward_args(q, k, v, out, lse, workspace, key_start, key_end):
+    """Host-side checks of attention()'s tensors (every tensor on q's device;
+    the library writes B*H*L*E elements through out's strides and B*H*L floats
+    of lse, so both must have exactly those shapes). Returns (B, H, H_kv, L,
+    S, E); raises ValueError."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, seq, E]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float16")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, L, E = q.shape
+    H_kv, S = k.shape[1], k.shape[2]
+    if k.shape != (B, H_kv, S, E) or v.shape != (B, H_kv, S, E) or H_kv < 1 or H % H_kv:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is not None and (tuple(out.shape) != (B, H, L, E) or out.dtype != q.dtype
+                            or out.device != q.device or (out.numel() and out.stride(-1) != 1)):
+        raise ValueError(f"out must be a {q.dtype} tensor of shape {(B, H, L, E)} on {q.device} "
+                         "with a contiguous head dim")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, L) or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, L] tensor on q's device")
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != q.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    for t in (key_start, key_end):
+        if t is not None and (t.dtype != torch.int32 or t.device != q.device
+                              or tuple(t.shape) != (B,) or not t.is_contiguous()):
+            raise ValueError("key_start / key_end must be contiguous int32 tensors [B] on q's device")
+    return B, H, H_kv, L, S, E
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
               score_mod: Optional[str] = None, softcap: float = 30.0,
               scale: Optional[float] = None, return_lse: bool = False,
@@ -344,16 +386,9 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
     zero-filled uint8 GPU tensor of at least ``workspace_size(q, block_mask)``
     bytes; by default one cached per device and stream is used.
     """
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, H, seq, E]")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
-        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float16")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
-    B, H, L, E = q.shape
-    H_kv, S = k.shape[1], k.shape[2]
-    if k.shape != (B, H_kv, S, E) or v.shape != (B, H_kv, S, E) or H_kv < 1 or H % H_kv:
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    B, H, H_kv, L, S, E = _check_forward_args(q, k, v, out, lse, workspace, key_start, key_end)
     if scale is None:
         scale = 1.0 / math.sqrt(E)
     sm = {None: SCORE_NONE, "none": SCORE_NONE, "softcap": SCORE_SOFTCAP}[score_mod]
@@ -361,9 +396,6 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
         out = torch.empty(B, H, L, E, dtype=q.dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or lse.shape != (B, H, L)):
-        raise ValueError("lse must be a contiguous float32 [B, H, L] tensor")
     with torch.cuda.device(q.device):
         stream = _stream_handle(q.device)
         need = workspace_size(q, block_mask)
@@ -372,12 +404,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         lse_ptr = lse.data_ptr() if lse is not None else None
-        pads = []
-        for t in (key_start, key_end):
-            if t is not None:
-                if t.dtype != torch.int32 or not t.is_cuda or t.shape != (B,) or not t.is_contiguous():
-                    raise ValueError("key_start / key_end must be contiguous int32 GPU tensors [B]")
-            pads.append(t.data_ptr() if t is not None else None)
+        pads = [t.data_ptr() if t is not None else None for t in (key_start, key_end)]
         if key_start is not None or key_end is not None:
             _check(_load().attn_forward_padded(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
@@ -402,6 +429,33 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: Blo
     return (out, lse) if return_lse else out
 
 
+def _check_backward_args(q, k, v, out, lse, dout, key_start, key_end):
+    """Host-side checks of attention_backward()'s tensors (one dtype and device;
+    k and v [B, H_kv, S, E] with H_kv dividing H; the library reads and writes
+    contiguous tensors of exactly these shapes). Returns (B, H, H_kv, L, S, E);
+    raises ValueError."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (k, v, out, dout):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, out and dout must share dtype and device")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, seq, E]")
+    B, H, L, E = q.shape
+    Hk, S = k.shape[1], k.shape[2]
+    if (out.shape != q.shape or dout.shape != q.shape or tuple(k.shape) != (B, Hk, S, E)
+            or v.shape != k.shape or Hk < 1 or H % Hk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} "
+                         f"out{tuple(out.shape)} dout{tuple(dout.shape)}")
+    if tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32 or lse.device != q.device:
+        raise ValueError("lse must be float32 [B, H, L] on q's device")
+    for t in (key_start, key_end):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (B,) or t.device != q.device
+                              or not t.is_contiguous()):
+            raise ValueError("key_start / key_end must be contiguous int32 [B] on the tensors' device")
+    return B, H, Hk, L, S, E
+
+
 def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                        lse: torch.Tensor, dout: torch.Tensor, block_mask: BlockMask,
                        score_mod: Optional[str] = None, softcap: float = 30.0,
@@ -414,19 +468,9 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     attention), and dk, dv then sum over the query heads that share a K/V head.
     Tensors are made contiguous; the call is asynchronous on the current
     stream."""
-    if q.dtype not in _DTYPES:
-        raise ValueError(f"unsupported dtype {q.dtype}")
-    for t in (k, v, out, dout):
-        if t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v, out and dout must share dtype and device")
     if q.device.type != "cuda":
         raise ValueError("tensors must be on a cuda device")
-    B, H, L, E = q.shape
-    Hk, S = k.shape[1], k.shape[2]
-    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or k.shape[0] != B:
-        raise ValueError("shape mismatch")
-    if lse.shape != (B, H, L) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [B, H, L]")
+    B, H, Hk, L, S, E = _check_backward_args(q, k, v, out, lse, dout, key_start, key_end)
     q, k, v, out, dout, lse = (t.contiguous() for t in (q, k, v, out, dout, lse))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     lib = _load()
@@ -439,9 +483,6 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
         raise ValueError(f"unknown score_mod {score_mod!r}")
     sc = 1.0 / math.sqrt(E) if scale is None else float(scale)
     ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
-    for t in (key_start, key_end):
-        if t is not None and (t.dtype != torch.int32 or t.shape != (B,) or t.device != q.device):
-            raise ValueError("key_start / key_end must be int32 [B] on the tensors' device")
     with torch.cuda.device(q.device):
         _check(lib.attn_backward(ptr(q), ptr(k), ptr(v), ptr(out), ptr(lse), ptr(dout), ptr(dq), ptr(dk),
                                  ptr(dv), _DTYPES[q.dtype], B, H, Hk, L, S, E,

@@ -75,6 +75,12 @@ int32_t attn_num_blocks(int32_t len, int32_t block_size) {
   return (int32_t)(((int64_t)len + block_size - 1) / block_size);
 }
 
+int32_t attn_block_mask_schedule_len(int32_t q_len, int32_t kv_len, int32_t block_size) {
+  const int32_t nq = attn_num_blocks(q_len, block_size);
+  if (nq < 0 || attn_num_blocks(kv_len, block_size) < 0) return -1;
+  return 4 + 8 * nq;
+}
+
 }  // extern "C"
 
 namespace {

@@ -166,6 +166,20 @@ typedef struct attn_block_mask {
 int32_t attn_num_blocks(int32_t len, int32_t block_size);
 
 /*
+ * Length in int32 entries of the `schedule` array a BlockMask over q_len
+ * queries and kv_len keys needs: 4 + 8 * ceil(q_len / 128) (a 4-entry header
+ * and at most two 4-entry item descriptors per query block, as laid out
+ * above). The work plan is this library's own: the pages fix only that the
+ * kernel's cost should follow the live blocks ("FlexAttention on Apple
+ * Silicon: block masks", closing section on block skipping) and that work is
+ * spread over parallel units ("Flash Attention 2 and the IO bottleneck",
+ * differences between FlashAttention 1 and 2). -1 for a negative length or
+ * block_size != 128. kv_len does not change the length; it is taken so the
+ * call names the mask's whole shape.
+ */
+int32_t attn_block_mask_schedule_len(int32_t q_len, int32_t kv_len, int32_t block_size);
+
+/*
  * Build a BlockMask for `kind` over q_len queries and kv_len keys.
  *   window        the two SLIDING_WINDOW kinds: >= 1; ignored (and stored as
  *                 0) otherwise

@@ -363,3 +363,128 @@ def test_backward_workspace_size():
     assert n.value == fixed + al(6 * 2 * 4 * 16384 * 4) + al(3 * 2 * 8 * 8192 * 4)
     assert lib.attn_backward_workspace_size(0, 4, 2, ctypes.byref(bm), ctypes.byref(n)) == INVALID
     assert lib.attn_backward_workspace_size(2, 4, 3, ctypes.byref(bm), ctypes.byref(n)) == INVALID
+
+
+# The binding's own argument checks (host logic, no GPU): every tensor the
+# library writes through must have exactly the shape, dtype and device it
+# assumes, or the call is refused before any pointer crosses the boundary.
+
+def _fwd_tensors(dt=torch.bfloat16, B=2, H=4, Hk=2, L=256, S=384, E=64):
+    q = torch.zeros(B, H, L, E, dtype=dt)
+    k = torch.zeros(B, Hk, S, E, dtype=dt)
+    v = torch.zeros(B, Hk, S, E, dtype=dt)
+    return q, k, v
+
+
+def test_forward_arg_checks_accept_a_valid_call():
+    q, k, v = _fwd_tensors()
+    out = torch.empty_like(q)
+    lse = torch.empty(2, 4, 256)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    ks = torch.zeros(2, dtype=torch.int32)
+    assert bsa._check_forward_args(q, k, v, out, lse, ws, ks, ks) == (2, 4, 2, 256, 384, 64)
+    assert bsa._check_forward_args(q, k, v, None, None, None, None, None) == (2, 4, 2, 256, 384, 64)
+
+
+@pytest.mark.parametrize("case", [
+    "out_small", "out_dtype", "out_stride", "out_device", "lse_shape", "lse_dtype",
+    "lse_noncontig", "lse_device", "ws_dtype", "ws_device", "key_dtype", "key_shape",
+    "key_noncontig", "key_device", "k_dim", "k_head_dim", "heads_not_dividing"])
+def test_forward_arg_checks_reject(case):
+    q, k, v = _fwd_tensors()
+    out, lse, ws, ks = torch.empty_like(q), torch.empty(2, 4, 256), None, None
+    meta = torch.device("meta")
+    if case == "out_small":
+        out = torch.empty(2, 4, 128, 64, dtype=q.dtype)
+    elif case == "out_dtype":
+        out = torch.empty(2, 4, 256, 64, dtype=torch.float16)
+    elif case == "out_stride":
+        out = torch.empty(2, 4, 64, 256, dtype=q.dtype).transpose(2, 3)
+    elif case == "out_device":
+        out = torch.empty(2, 4, 256, 64, dtype=q.dtype, device=meta)
+    elif case == "lse_shape":
+        lse = torch.empty(2, 4, 255)
+    elif case == "lse_dtype":
+        lse = torch.empty(2, 4, 256, dtype=torch.float64)
+    elif case == "lse_noncontig":
+        lse = torch.empty(2, 256, 4).transpose(1, 2)
+    elif case == "lse_device":
+        lse = torch.empty(2, 4, 256, device=meta)
+    elif case == "ws_dtype":
+        ws = torch.zeros(16, dtype=torch.int32)
+    elif case == "ws_device":
+        ws = torch.zeros(64, dtype=torch.uint8, device=meta)
+    elif case == "key_dtype":
+        ks = torch.zeros(2, dtype=torch.int64)
+    elif case == "key_shape":
+        ks = torch.zeros(3, dtype=torch.int32)
+    elif case == "key_noncontig":
+        ks = torch.zeros(4, dtype=torch.int32)[::2]
+    elif case == "key_device":
+        ks = torch.zeros(2, dtype=torch.int32, device=meta)
+    elif case == "k_dim":
+        k = k[0]
+    elif case == "k_head_dim":
+        k = torch.zeros(2, 2, 384, 32, dtype=q.dtype)
+        v = k.clone()
+    elif case == "heads_not_dividing":
+        k = torch.zeros(2, 3, 384, 64, dtype=q.dtype)
+        v = k.clone()
+    with pytest.raises(ValueError):
+        bsa._check_forward_args(q, k, v, out, lse, ws, ks, None)
+
+
+@pytest.mark.parametrize("case", [
+    "k_dim", "k_head_dim", "k_batch", "v_shape", "heads_not_dividing", "lse_device", "lse_shape",
+    "out_shape", "dout_dtype", "key_noncontig", "key_device"])
+def test_backward_arg_checks_reject(case):
+    q, k, v = _fwd_tensors()
+    out, dout, lse, ks = torch.empty_like(q), torch.empty_like(q), torch.empty(2, 4, 256), None
+    meta = torch.device("meta")
+    if case == "k_dim":
+        k = k[0]
+    elif case == "k_head_dim":
+        k = torch.zeros(2, 2, 384, 32, dtype=q.dtype)
+        v = k.clone()
+    elif case == "k_batch":
+        k = torch.zeros(1, 2, 384, 64, dtype=q.dtype)
+        v = k.clone()
+    elif case == "v_shape":
+        v = torch.zeros(2, 2, 383, 64, dtype=q.dtype)
+    elif case == "heads_not_dividing":
+        k = torch.zeros(2, 3, 384, 64, dtype=q.dtype)
+        v = k.clone()
+    elif case == "lse_device":
+        lse = torch.empty(2, 4, 256, device=meta)
+    elif case == "lse_shape":
+        lse = torch.empty(2, 4, 128)
+    elif case == "out_shape":
+        out = torch.empty(2, 4, 128, 64, dtype=q.dtype)
+    elif case == "dout_dtype":
+        dout = torch.empty_like(q, dtype=torch.float16)
+    elif case == "key_noncontig":
+        ks = torch.zeros(4, dtype=torch.int32)[::2]
+    elif case == "key_device":
+        ks = torch.zeros(2, dtype=torch.int32, device=meta)
+    with pytest.raises(ValueError):
+        bsa._check_backward_args(q, k, v, out, lse, dout, ks, None)
+
+
+def test_backward_arg_checks_accept_a_valid_call():
+    q, k, v = _fwd_tensors()
+    got = bsa._check_backward_args(q, k, v, torch.empty_like(q), torch.empty(2, 4, 256),
+                                   torch.empty_like(q), torch.zeros(2, dtype=torch.int32), None)
+    assert got == (2, 4, 2, 256, 384, 64)
+
+
+def test_schedule_len():
+    lib = bsa._load()
+    # a 4-entry header and two 4-entry descriptors per query block
+    for L, S in ((0, 0), (1, 8192), (256, 256), (300, 200), (8192, 8192), (32768, 32768)):
+        assert lib.attn_block_mask_schedule_len(L, S, 128) == 4 + 8 * ((L + 127) // 128)
+        assert bsa.schedule_len(L, S) == 4 + 8 * ((L + 127) // 128)
+    assert lib.attn_block_mask_schedule_len(-1, 128, 128) == -1
+    assert lib.attn_block_mask_schedule_len(128, -1, 128) == -1
+    assert lib.attn_block_mask_schedule_len(128, 128, 64) == -1
+    with pytest.raises(bsa.BsattnError):
+        bsa.schedule_len(-5, 10)
