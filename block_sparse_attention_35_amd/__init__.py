@@ -32,7 +32,7 @@ import torch
 __all__ = [
     "BlockMask", "BsattnError", "create_block_mask", "create_block_mask_from_dense",
     "create_block_mask_from_bits", "pack_mask", "mask_words", "attention", "attention_backward",
-    "num_blocks", "schedule_len", "library_path",
+    "num_blocks", "schedule_len", "library_path", "attention_noalloc",
     "workspace_size",
     "MASK_NONE", "MASK_CAUSAL", "MASK_SLIDING_WINDOW", "MASK_DOCUMENT",
     "MASK_CAUSAL_LOWER_RIGHT", "MASK_SLIDING_WINDOW_LOWER_RIGHT", "MASK_DOCUMENT_BIDIRECTIONAL",
@@ -136,6 +136,10 @@ def _load():
                                         i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
                                         i32, ctypes.c_float, ctypes.c_float, vp, vp, vp,
                                         ctypes.c_size_t, vp]
+    lib.attn_forward_noalloc.restype = i32
+    lib.attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                         i64p, i64p, i64p, i64p, ctypes.POINTER(_BlockMaskStruct),
+                                         i32, ctypes.c_float, ctypes.c_float, vp, vp, vp]
     lib.attn_forward_workspace_size.restype = i32
     lib.attn_forward_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(_BlockMaskStruct),
                                                 ctypes.POINTER(ctypes.c_size_t)]
@@ -489,3 +493,30 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
                                  ctypes.byref(block_mask._struct), sm, float(softcap), sc,
                                  ptr(key_start), ptr(key_end), ws.data_ptr(), ws.numel(), stream))
     return dq, dk, dv
+
+
+def attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
+                      out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                      score_mod: Optional[str] = None, softcap: float = 30.0,
+                      scale: Optional[float] = None, key_start: Optional[torch.Tensor] = None,
+                      key_end: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``attention`` through attn_forward_noalloc: the library allocates no
+    device memory (its split items use a fixed per-GPU scratch array) and the
+    caller passes ``out`` (and ``lse``). Calls that overlap in time on one GPU
+    race on that scratch."""
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if out is None:
+        raise ValueError("attention_noalloc needs out")
+    B, H, H_kv, L, S, E = _check_forward_args(q, k, v, out, lse, None, key_start, key_end)
+    sc = 1.0 / math.sqrt(E) if scale is None else float(scale)
+    sm = {None: SCORE_NONE, "none": SCORE_NONE, "softcap": SCORE_SOFTCAP}[score_mod]
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(q.device):
+        _check(_load().attn_forward_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ptr(lse),
+            _DTYPES[q.dtype], B, H, H_kv, L, S, E,
+            _strides(q), _strides(k), _strides(v), _strides(out),
+            ctypes.byref(block_mask._struct), sm, float(softcap), sc,
+            ptr(key_start), ptr(key_end), _stream_handle(q.device)))
+    return out

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "bsattn.h"
 #include "internal.h"
@@ -178,6 +179,12 @@ attn_status attn_build_block_mask_custom(const uint32_t* bits, int32_t q_len, in
 
 namespace {
 
+// Zeroes n 32-bit words (a kernel rather than a memset node, so a captured
+// call clears the counters on every replay too).
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 // attn_forward with H_kv K/V heads (H_kv == H: no sharing).
 attn_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                          int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L, int32_t S,
@@ -185,7 +192,7 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
                          const int64_t* v_strides, const int64_t* o_strides,
                          const attn_block_mask* bm, int32_t score_mod, float softcap, float scale,
                          const int32_t* key_start, const int32_t* key_end, void* workspace,
-                         size_t workspace_size, void* stream) {
+                         size_t workspace_size, void* stream, bool clear_counters = false) {
   g_last_error[0] = '\0';
   if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
   // A tensor with no elements may have a null pointer.
@@ -287,6 +294,13 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
   a.m.window = bm->window;
   a.scale = scale;
   a.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
+  if (clear_counters && need > 0) {
+    const int n = (int)(bsattn::kCountersBytes / sizeof(int32_t));
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<int32_t*>(workspace), n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "scratch counter clear launch");
+  }
   return hip_status(bsattn::launch_forward(dtype, a, static_cast<hipStream_t>(stream)),
                     "forward launch");
 }
@@ -328,6 +342,75 @@ attn_status attn_forward_padded(const void* q, const void* k, const void* v, voi
   return forward_impl(q, k, v, o, lse, dtype, B, H, H_kv, L, S, E, q_strides, k_strides, v_strides,
                       o_strides, bm, score_mod, softcap, scale, key_start, key_end, workspace,
                       workspace_size, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch memory of attn_forward_noalloc: one copy per GPU, allocated with
+// the library's code object when it is loaded on that GPU and held until the
+// process ends. In host code `scratch` names a host-side stand-in, not the
+// GPU's copy, so it is never passed to a kernel or a copy: each device's
+// address comes from hipGetSymbolAddress with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up once per device).
+attn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "device %d: the no-alloc scratch tracks %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(ATTN_ERR_HIP, "scratch symbol has no usable device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_forward_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L,
+                                 int32_t S, int32_t E, const int64_t* q_strides,
+                                 const int64_t* k_strides, const int64_t* v_strides,
+                                 const int64_t* o_strides, const attn_block_mask* bm,
+                                 int32_t score_mod, float softcap, float scale,
+                                 const int32_t* key_start, const int32_t* key_end, void* stream) {
+  g_last_error[0] = '\0';
+  if (bm == nullptr) return fail(ATTN_ERR_INVALID_ARGUMENT, "block mask is null");
+  if (B < 1 || H < 1) return fail(ATTN_ERR_INVALID_ARGUMENT, "bad sizes B=%d H=%d", B, H);
+  const size_t need =
+      bsattn::workspace_bytes(dtype, (int64_t)B * H, bm->num_q_blocks, bm->num_kv_blocks);
+  if (need > kNoAllocScratchBytes)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of scratch; attn_forward_noalloc holds %zu "
+                "(use attn_forward_padded with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    attn_status st = scratch_of_current_device(&ws);
+    if (st != ATTN_OK) return st;
+  }
+  // The shared body validates everything attn_forward_padded does before it
+  // enqueues anything; split work items then start from zeroed counters.
+  return forward_impl(q, k, v, o, lse, dtype, B, H, H_kv, L, S, E, q_strides, k_strides, v_strides,
+                      o_strides, bm, score_mod, softcap, scale, key_start, key_end, ws,
+                      need > 0 ? kNoAllocScratchBytes : 0, stream, /*clear_counters=*/true);
 }
 
 attn_status attn_backward_workspace_size(int32_t B, int32_t H, int32_t H_kv, const attn_block_mask* bm,

@@ -340,6 +340,30 @@ attn_status attn_forward_padded(const void* q, const void* k, const void* v, voi
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * attn_forward_padded without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code recorded under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The split
+ * work items' partial results and ticket counters live in a fixed scratch
+ * array of 128 MiB that the library holds on each GPU it runs on until the
+ * process ends; every call clears the counters first (with a kernel on
+ * `stream`, so a captured call clears them on every replay). All other
+ * arguments, the results (bit-identical to attn_forward_padded's) and the
+ * errors are as for attn_forward_padded, plus UNSUPPORTED when the shape
+ * needs more scratch than 128 MiB (attn_forward_workspace_size tells; at most
+ * about 138 MB for bf16/fp16 work with B*H*nq <= 2048, 0 otherwise).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race
+ * and must be serialised by the caller.
+ */
+attn_status attn_forward_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t L,
+                                 int32_t S, int32_t E, const int64_t* q_strides,
+                                 const int64_t* k_strides, const int64_t* v_strides,
+                                 const int64_t* o_strides, const attn_block_mask* bm,
+                                 int32_t score_mod, float softcap, float scale,
+                                 const int32_t* key_start, const int32_t* key_end, void* stream);
+
+/*
  * Bytes of device workspace attn_backward needs (always > 0): two fixed 8 KiB
  * regions of ticket counters, D and lse2 (B*H*q_len floats each), the
  * BlockMask transposed ([nk] counts and [nk * nq] indices, twice), the dK/dV

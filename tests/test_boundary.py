@@ -488,3 +488,18 @@ def test_schedule_len():
     assert lib.attn_block_mask_schedule_len(128, 128, 64) == -1
     with pytest.raises(bsa.BsattnError):
         bsa.schedule_len(-5, 10)
+
+
+@no_gpu
+def test_forward_noalloc_refuses_shapes_beyond_its_scratch():
+    # 2048 split items (B*H*nq) of two 33 KiB partial slots: above 128 MiB.
+    # Refused on the host before the scratch is looked up or anything enqueued.
+    lib = bsa._load()
+    bm = _built_mask(8192, 8192)
+    assert lib.attn_forward_noalloc(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 32, 32, 8192, 8192, 64,
+                                    None, None, None, None, ctypes.byref(bm), 0, 0.0, 0.125,
+                                    None, None, None) == UNSUPPORTED
+    assert "scratch" in lib.attn_last_error().decode()
+    assert lib.attn_forward_noalloc(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 2, 2, 256, 256, 64,
+                                    None, None, None, None, None, 0, 0.0, 0.125,
+                                    None, None, None) == INVALID
