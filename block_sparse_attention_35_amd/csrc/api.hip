@@ -294,6 +294,11 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
   a.m.window = bm->window;
   a.scale = scale;
   a.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
+  if (a.pack_split == 0 && a.kv_split == 0) {
+    a.chain = bsattn::chain_grid(dtype, form.kind, bm->window, key_start != nullptr || key_end != nullptr,
+                                 (int64_t)B * H, bm->num_q_blocks, S);
+    if (a.chain > 0) a.split = 0;  // no plan entry of such a window is split
+  }
   if (clear_counters && need > 0) {
     const int n = (int)(bsattn::kCountersBytes / sizeof(int32_t));
     hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0,

@@ -941,6 +941,201 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chained work items (sliding windows): the items of a window are short (a
+// few kv blocks each) and many, so a workgroup that owned one item would pay
+// the item's start-up latency (descriptor, Q rows, first K/V tiles) and its
+// output stores with nothing to overlap them. Here each resident workgroup
+// owns one batch*head and walks the plan entries r0, r0 + R, r0 + 2R, ... of
+// it (R = grid size / (B*H), so the R workgroups of a head run R consecutive
+// query blocks at a time and share their K/V tiles in L2; with B*H a multiple
+// of 8 all of a head's workgroups sit on one XCD). The two-stage block
+// pipeline runs across item boundaries: during an item's last block the next
+// item's first K/V tiles are copied and its Q rows loaded, and an item's
+// output is stored only after the next item's first barrier, so neither the
+// loads nor the stores of one item wait behind the other.
+// ---------------------------------------------------------------------------
+template <typename T, int KIND, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
+  using V = Vec<T>;
+  using x8 = typename V::x8;
+  using x4 = typename V::x4;
+  __shared__ Lds lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.H, h = bh % a.H;
+  const int rstep = gridDim.x / BH;
+  const int nitems = ((const_i32_ptr)a.m.schedule)[0];
+
+  const T* qg = static_cast<const T*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const int hk = h / a.kv_group;
+  const T* kg = static_cast<const T*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const T* vg = static_cast<const T*>(a.v) + b * a.v_sb + hk * a.v_sh;
+  T* og = static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh;
+  const uint32_t k_off =
+      (uint32_t)((lane >> 3) * a.k_sl * (int64_t)sizeof(T)) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  const uint32_t v_off = (uint32_t)((lane >> 3) * a.v_sl * (int64_t)sizeof(T)) +
+                         (uint32_t)(((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 16);
+  const LanePtrs lp = make_lane_ptrs(lds, lane);
+
+  // The next plan entry with work (a later chunk of a split query block has
+  // none: splitting is off here, so a first chunk visits every block).
+  auto next_item = [&](int& r, WorkItem& w) {
+    for (; r < nitems; r += rstep) {
+      w = work_item(a, r);
+      if (!w.skip) break;
+    }
+  };
+  int r = blockIdx.x / BH;
+  WorkItem wi;
+  next_item(r, wi);
+  if (r >= nitems) return;
+
+  // Q operands of query block qb for this lane's row (zero past L).
+  auto load_q = [&](int qb, x8 (&dst)[4]) {
+    const int qi = qb * kBlock + wave * 32 + lq;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      dst[c] = (qi < a.L) ? *reinterpret_cast<const x8*>(qg + (int64_t)qi * a.q_sl + c * 16 + hf * 8) : x8{};
+  };
+  auto issue_block = [&](int kv0, int stage) {
+    issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv0, a.S, lds.k[stage], wave, lane);
+    issue_rows<T, true>(vg, a.v_sl, v_off, kv0, a.S, lds.v[stage].v, wave, lane);
+  };
+  // First key of visited block n of item w (full blocks first, then partial).
+  auto kv_start = [&](const WorkItem& w, int n) {
+    const const_i32_ptr fl = (const_i32_ptr)(a.m.full_idx + (int64_t)w.qb * a.m.nk);
+    const const_i32_ptr pl = (const_i32_ptr)(a.m.kv_idx + (int64_t)w.qb * a.m.nk);
+    return (n < w.nfull ? fl[n] : pl[n - w.nfull]) * kBlock;
+  };
+
+  x8 qop[4];
+  load_q(wi.qb, qop);
+  int kv_next = wi.first_kb * kBlock;
+  issue_block(kv_next, 0);
+  wait_vm_zero();
+
+  // The previous item's output, held until the next item's first barrier.
+  x4 ohold[2][4];
+  float lse_hold = 0.0f;
+  int prev_qi = -1;  // this lane's row of the held output (-1: none)
+  auto flush_held = [&]() {
+    if (prev_qi >= 0 && prev_qi < a.L) {
+#pragma unroll
+      for (int te = 0; te < 2; ++te)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<x4*>(og + (int64_t)prev_qi * a.o_sl + te * 32 + r4 * 8 + hf * 4) = ohold[te][r4];
+      if (a.lse != nullptr && hf == 0) a.lse[(int64_t)bh * a.L + prev_qi] = lse_hold;
+    }
+    prev_qi = -1;
+  };
+
+  int par = 0;  // stage of the current block
+  while (true) {
+    const int qb = wi.qb;
+    const int nfull = wi.nfull, nblk = wi.nfull + wi.npart;
+    const int row0 = qb * kBlock + wave * 32;
+    const int qi = row0 + lq;
+    // The entry after this one, looked up now so its descriptor has landed
+    // by this item's last block.
+    int r_n = r + rstep;
+    WorkItem wn = wi;
+    next_item(r_n, wn);
+    const bool has_next = r_n < nitems;
+    // First key of the block after the next one (a block ahead, as in the
+    // one-item kernel, so no copy waits on a scalar load).
+    int kv_after = nblk > 1 ? kv_start(wi, 1) : (has_next ? wn.first_kb * kBlock : 0);
+    const int32_t dq = (KIND == ATTN_MASK_DOCUMENT && qi < a.L) ? a.m.doc[qi] : -1;
+
+    f32x16_t oacc[2];
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) oacc[te][rr] = 0.0f;
+    float m_ref = -INFINITY, l = 0.0f;
+    x8 qnext[4];
+
+    auto block = [&](auto partial_c, int m) __attribute__((always_inline)) {
+      constexpr bool PARTIAL = decltype(partial_c)::value;
+      lds_u8 kp[4], vp[2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kp[c] = lp.k[c] + par * (int)sizeof(KStage);
+        asm volatile("" : "+v"(kp[c]));
+      }
+#pragma unroll
+      for (int te = 0; te < 2; ++te) {
+        vp[te] = lp.v[te] + par * (int)sizeof(VStage);
+        asm volatile("" : "+v"(vp[te]));
+      }
+      const int kv0 = kv_next;
+      wait_vm_zero();    // this wave's copies of block m (and older stores)
+      wait_lgkm_zero();  // this wave's reads of the previous block
+      barrier_only();
+      // The previous item's output: its stores are issued now and finish
+      // during this block.
+      if (m == 0) flush_held();
+      if (m + 1 < nblk) {
+        kv_next = kv_after;
+        issue_block(kv_next, 1 - par);
+        if (m + 2 < nblk)
+          kv_after = kv_start(wi, m + 2);
+        else if (has_next)
+          kv_after = wn.first_kb * kBlock;
+      } else if (has_next) {
+        // Last block: the next item's first tiles and Q rows.
+        kv_next = kv_after;
+        issue_block(kv_next, 1 - par);
+        load_q(wn.qb, qnext);
+      }
+      fwd_block<T, KIND, SOFTCAP, PARTIAL, false>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0, lane,
+                                                  a, dq, 0, a.S, nullptr);
+      par ^= 1;
+    };
+    int m = 0;
+    for (; m < nfull; ++m) block(std::false_type{}, m);
+    for (; m < nblk; ++m) block(std::true_type{}, m);
+    if (nblk == 0) {
+      // No live block (rows without keys): the tiles copied for this item
+      // go unused; the next item's first tiles replace them in the same
+      // stage once this wave's own copies have landed (each wave writes only
+      // its quarter of a stage).
+      flush_held();
+      wait_vm_zero();
+      if (has_next) {
+        kv_next = wn.first_kb * kBlock;
+        issue_block(kv_next, par);
+        load_q(wn.qb, qnext);
+      }
+    }
+
+    // Epilogue: O = O^T / l (0 for a row without live keys), held in
+    // registers until the next item's first barrier (or stored now).
+    const float lt = half_sum(l);
+    const float inv = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+#pragma unroll
+    for (int te = 0; te < 2; ++te)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ohold[te][r4][u] = (T)(oacc[te][r4 * 4 + u] * inv);
+    lse_hold = (lt > 0.0f) ? (m_ref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    prev_qi = qi;
+    if (!has_next) break;
+    r = r_n;
+    wi = wn;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qop[c] = qnext[c];
+  }
+  flush_held();
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: same structure with v_mfma_f32_32x32x2_f32 (one element of the
 // contraction per lane and step), probabilities kept in fp32.
 // ---------------------------------------------------------------------------
@@ -1497,9 +1692,27 @@ hipError_t launch_split(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int KIND, bool SOFTCAP>
+hipError_t launch_chain(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.chain), block(kThreads);
+  switch (dtype) {
+    case ATTN_BF16:
+      hipLaunchKernelGGL((fwd16_chain_kernel<__bf16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      break;
+    case ATTN_F16:
+      hipLaunchKernelGGL((fwd16_chain_kernel<_Float16, KIND, SOFTCAP>), grid, block, 0, stream, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Split-KV items have kernels of their own, so the others keep their code.
 template <int KIND, bool SOFTCAP, bool PADDED>
 hipError_t launch_kind(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
+  if constexpr (KIND == ATTN_MASK_SLIDING_WINDOW && !PADDED)
+    if (a.chain > 0) return launch_chain<KIND, SOFTCAP>(dtype, a, stream);
   if (a.pack_split > 0) return launch_packed<KIND, SOFTCAP>(dtype, a, stream);
   return (a.kv_split > 0 && dtype != ATTN_F32) ? launch_split<KIND, SOFTCAP, PADDED, true>(dtype, a, stream)
                                                : launch_split<KIND, SOFTCAP, PADDED, false>(dtype, a, stream);

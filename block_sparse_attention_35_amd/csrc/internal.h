@@ -82,7 +82,27 @@ struct FwdArgs {
   // one 32-row tile; the visit list is cut into pack_split chunks, merged
   // from partial results when there is more than one.
   int32_t pack_split;
+  // Chained items (chain > 0): a grid of that many resident workgroups,
+  // each walking the plan entries of one batch*head (sliding windows).
+  int32_t chain;
 };
+
+// Sliding windows with at most this many kv blocks per query block (W <=
+// 1920: never split by the plan) run as chained items when there are at
+// least kChainMinItems work items; the grid holds kChainSlots workgroups
+// (two per compute unit), rounded down to a multiple of B*H.
+constexpr int32_t kChainMaxWindow = 15 * kBlock;
+constexpr int64_t kChainMinItems = 1024;
+constexpr int64_t kChainSlots = 512;
+// (The chained kernel copies a first block for every item, block 0 for an
+// item without live blocks, so it needs at least one key.)
+inline int32_t chain_grid(int32_t dtype, int32_t form_kind, int32_t window, bool padded, int64_t bh, int32_t nq,
+                          int32_t kv_len) {
+  if (dtype == 0 /* ATTN_F32 */ || form_kind != 2 /* ATTN_MASK_SLIDING_WINDOW */ || padded || kv_len < 1) return 0;
+  if (window > kChainMaxWindow || bh * nq < kChainMinItems) return 0;
+  const int64_t per_head = bh >= kChainSlots ? 1 : kChainSlots / bh;
+  return (int32_t)(bh * (per_head < nq ? per_head : nq));
+}
 
 // Partial result of one split item: the 4 waves' O^T accumulators in
 // register order ([wave][32 registers][64 lanes]) -- for split-KV items the

@@ -210,6 +210,14 @@ SMALL = [
     _odd("packed_doc_L8_S2000_f16", "f16", 4, 8, 2000, wl.MASK_DOCUMENT, 0, (5, 700, 1500)).with_(H_kv=1),
     _odd("packed_doc_bidir_L2_S3000_softcap_bf16", "bf16", 8, 2, 3000, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0,
          (1, 1200), 30.0).with_(H_kv=4),
+    # chained items (sliding windows with >= 1024 work items): query blocks
+    # with no key at all, B*H not dividing the 512-workgroup grid, B*H above
+    # it, fp16 with the soft-cap and a ragged last block
+    _odd("chain_sliding_lr_empty_blocks_bf16", "bf16", 64, 2176, 1000, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 100),
+    _odd("chain_sliding_h12_ragged_softcap_f16", "f16", 12, 11000, 11000, wl.MASK_SLIDING_WINDOW, 300, (),
+         20.0),
+    _odd("chain_sliding_bh520_bf16", "bf16", 130, 256, 256, wl.MASK_SLIDING_WINDOW, 64, B=4),
+    _odd("chain_sliding_w1920_bf16", "bf16", 8, 16384, 16384, wl.MASK_SLIDING_WINDOW, 1920),
     # mask variants and grouped-query attention
     _odd("causal_lr_L200_S700_bf16", "bf16", 2, 200, 700, wl.MASK_CAUSAL_LOWER_RIGHT),
     _odd("causal_lr_L700_S200_f16", "f16", 1, 700, 200, wl.MASK_CAUSAL_LOWER_RIGHT),
