@@ -326,16 +326,23 @@ def _workspace(nbytes: int, device: torch.device, stream: int, role: str = "forw
 
 
 def workspace_size(q: torch.Tensor, block_mask: BlockMask) -> int:
-    """Bytes of workspace attention() needs for q's batch, heads and dtype."""
-    n = ctypes.c_size_t(0)
-    _check(_load().attn_forward_workspace_size(_DTYPES[q.dtype], q.shape[0], q.shape[1],
-                                               ctypes.byref(block_mask._struct), ctypes.byref(n)))
-    return n.value
+    """Bytes of workspace attention() needs for q's batch, heads and dtype
+    (a function of those and the mask's lengths, cached on the mask)."""
+    key = (_DTYPES[q.dtype], q.shape[0], q.shape[1])
+    cache = block_mask.__dict__.setdefault("_ws_sizes", {})
+    if key not in cache:
+        n = ctypes.c_size_t(0)
+        _check(_load().attn_forward_workspace_size(key[0], key[1], key[2],
+                                                   ctypes.byref(block_mask._struct), ctypes.byref(n)))
+        cache[key] = n.value
+    return cache[key]
 
 
 def _strides(t: torch.Tensor):
-    arr = (ctypes.c_int64 * 4)(*t.stride())
-    return arr
+    """Element strides for the library, or None (the contiguous layout)."""
+    if t.is_contiguous():
+        return None
+    return (ctypes.c_int64 * 4)(*t.stride())
 
 
 def _check_forward_args(q, k, v, out, lse, workspace, key_start, key_end):

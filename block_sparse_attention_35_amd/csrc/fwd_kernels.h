@@ -960,6 +960,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
   using x8 = typename V::x8;
   using x4 = typename V::x4;
   __shared__ Lds lds;
+  // Landing area of the L2 prefetches (their bytes are never read).
+  __shared__ uint32_t pf_sink[4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1006,6 +1008,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
     issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv0, a.S, lds.k[stage], wave, lane);
     issue_rows<T, true>(vg, a.v_sl, v_off, kv0, a.S, lds.v[stage].v, wave, lane);
   };
+  // L2 prefetch of the block after the next one: one 4-byte read per K row
+  // (lanes 0..31) and V row (lanes 32..63) of this wave's 32 rows, so the
+  // tile copies issued a block later find them in L2 (a window's K/V block
+  // is first read, from HBM, by the query block whose diagonal it is). It is
+  // the last vector memory operation of its block step, so the next block's
+  // wait leaves it in flight; the operations of a wave complete in issue
+  // order, so a prefetch issued earlier would hold up later copies.
+  const uint32_t pf_lds = lds_offset(pf_sink) + (uint32_t)wave * 256u;
+  auto prefetch_block = [&](int kv0) {
+    const int64_t row = min(kv0 + wave * 32 + lq, a.S - 1);
+    const void* p = hf ? (const void*)(vg + row * a.v_sl) : (const void*)(kg + row * a.k_sl);
+    lds_copy4(p, pf_lds);
+  };
   // First key of visited block n of item w (full blocks first, then partial).
   auto kv_start = [&](const WorkItem& w, int n) {
     const const_i32_ptr fl = (const_i32_ptr)(a.m.full_idx + (int64_t)w.qb * a.m.nk);
@@ -1035,7 +1050,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
     prev_qi = -1;
   };
 
-  int par = 0;  // stage of the current block
+  int par = 0;               // stage of the current block
+  bool pf_pending = false;  // a prefetch is the last vector memory operation issued
   while (true) {
     const int qb = wi.qb;
     const int nfull = wi.nfull, nblk = wi.nfull + wi.npart;
@@ -1074,19 +1090,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
         asm volatile("" : "+v"(vp[te]));
       }
       const int kv0 = kv_next;
-      wait_vm_zero();    // this wave's copies of block m (and older stores)
+      // This wave's copies of block m (and older stores); a prefetch issued
+      // after them may stay in flight.
+      if (pf_pending)
+        wait_vm<1>();
+      else
+        wait_vm_zero();
       wait_lgkm_zero();  // this wave's reads of the previous block
       barrier_only();
+      pf_pending = false;
       // The previous item's output: its stores are issued now and finish
       // during this block.
       if (m == 0) flush_held();
       if (m + 1 < nblk) {
         kv_next = kv_after;
         issue_block(kv_next, 1 - par);
+        const bool more = m + 2 < nblk || has_next;
         if (m + 2 < nblk)
           kv_after = kv_start(wi, m + 2);
         else if (has_next)
           kv_after = wn.first_kb * kBlock;
+        if (more) {
+          prefetch_block(kv_after);
+          pf_pending = true;
+        }
       } else if (has_next) {
         // Last block: the next item's first tiles and Q rows.
         kv_next = kv_after;
@@ -1107,6 +1134,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
       // its quarter of a stage).
       flush_held();
       wait_vm_zero();
+      pf_pending = false;
       if (has_next) {
         kv_next = wn.first_kb * kBlock;
         issue_block(kv_next, par);
