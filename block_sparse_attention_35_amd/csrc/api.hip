@@ -294,6 +294,7 @@ attn_status forward_impl(const void* q, const void* k, const void* v, void* o, f
   a.m.window = bm->window;
   a.scale = scale;
   a.softcap = (score_mod == ATTN_SCORE_SOFTCAP) ? softcap : 0.0f;
+  a.items_per_qb = bsattn::plan_never_splits(form.kind, bm->window, bm->num_kv_blocks) ? 1 : bsattn::kMaxChunks;
   if (a.pack_split == 0 && a.kv_split == 0) {
     a.chain = bsattn::chain_grid(dtype, form.kind, bm->window, key_start != nullptr || key_end != nullptr,
                                  (int64_t)B * H, bm->num_q_blocks, S);

@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void classify_compact_kernel(
 //   {qb | chunk << 20 | (k - 1) << 22, full blocks of qb, partial blocks of
 //   qb, index of the item's first visited kv block}; unused entries hold -1.
 // Every workgroup recomputes max_n, so the kernel needs no second pass.
-constexpr int kMinSplit = 16;
+constexpr int kMinSplit = kPlanMinSplit;
 
 __device__ inline int32_t split_count(int32_t n, int32_t split_len) { return n <= split_len ? 1 : 2; }
 

@@ -103,6 +103,10 @@ __device__ inline float half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ inline float half_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ inline float half_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -118,6 +122,16 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float softcap_log2(float s, float two_log2e_scale_over_cap, float cap_log2e) {
   const float e = fast_exp2(s * two_log2e_scale_over_cap);
   return fmaf(-2.0f * cap_log2e, __builtin_amdgcn_rcpf(1.0f + e), cap_log2e);
+}
+
+// The soft-cap's reciprocal term r = 1 / (e^(2y) + 1) of a raw score s (y =
+// s * scale / c): the capped score in base-2 units is cL - 2 cL r with cL =
+// c log2(e), so a block keeps r (the largest capped score is that of the
+// smallest r) and a probability is exp2(fma(r, -2 cL, cL - m)): one FMA
+// fewer per score than forming the capped score first. A masked pair has
+// r = +inf, hence probability 0.
+__device__ inline float softcap_recip(float s, float two_log2e_scale_over_cap) {
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(s * two_log2e_scale_over_cap));
 }
 
 // A query at rule position p (its row i plus the mask's query offset) may see
@@ -488,7 +502,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
 
   // Score_mod, mask and running max of scores 4k .. 4k+3 (tile k / 4), in
   // the tile's mode.
-  float mx = -INFINITY;
+  float mx = SOFTCAP ? INFINITY : -INFINITY;
   f32x16_t s[4];
   auto mask_chunk = [&](auto mode_c, int k) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
@@ -498,14 +512,18 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
       const int r = e & 15;
       if (MODE == kTileDead) {
         // Written here, in the dead tile's own path (a constant would be
-        // materialised before the branch, on every path).
-        float ninf;
-        asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(ninf));
-        s[t][r] = ninf;
+        // materialised before the branch, on every path): -inf, or with the
+        // soft-cap +inf in the reciprocal form.
+        float dead;
+        if (SOFTCAP)
+          asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(dead));
+        else
+          asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(dead));
+        s[t][r] = dead;
         continue;
       }
       float x = s[t][r];
-      if (SOFTCAP) x = softcap_log2(x, 2.0f * kLog2e * a.scale / a.softcap, a.softcap * kLog2e);
+      if (SOFTCAP) x = softcap_recip(x, 2.0f * kLog2e * a.scale / a.softcap);
       if (MODE == kTileMixed) {
         const int c = ((r >> 2) << 3) + (r & 3);
         bool live = c <= hi - 32 * t;
@@ -514,10 +532,10 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
         // 16-byte LDS read.)
         if (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
         if (KIND == ATTN_MASK_CUSTOM) live &= (mw[t] >> (c + 4 * hf)) & 1u;
-        x = live ? x : -INFINITY;
+        x = live ? x : (SOFTCAP ? INFINITY : -INFINITY);
       }
       s[t][r] = x;
-      mx = fmaxf(mx, x);
+      mx = SOFTCAP ? fminf(mx, x) : fmaxf(mx, x);
     }
   };
   // Runs f with the mode of tile t as a compile-time constant (one scalar
@@ -565,9 +583,10 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
 #pragma unroll
     for (int k = 12; k < 16; ++k) mask_chunk(mode_c, k);
   });
-  mx = half_max(mx);
-  // Without the soft-cap the max is over raw scores; scale > 0 keeps order.
-  const float m_blk = SOFTCAP ? mx : mx * c1;
+  // Without the soft-cap the max is over raw scores (scale > 0 keeps order);
+  // with it, the smallest reciprocal term gives the largest capped score.
+  const float cap2 = a.softcap * kLog2e;
+  const float m_blk = SOFTCAP ? fmaf(-2.0f * cap2, half_min(mx), cap2) : half_max(mx) * c1;
 
   // Lazy rescale (wave-uniform branch).
   const bool grow = m_blk > m_ref + kRescaleLog2;
@@ -593,8 +612,8 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
 #pragma unroll
     for (int u = (k & 1) * 4; u < (k & 1) * 4 + 4; u += 2) {
       const float x0 = s[g >> 1][(g & 1) * 8 + u], x1 = s[g >> 1][(g & 1) * 8 + u + 1];
-      const float p0 = SOFTCAP ? fast_exp2(x0 - m_use) : fast_exp2(fmaf(x0, c1, -m_use));
-      const float p1 = SOFTCAP ? fast_exp2(x1 - m_use) : fast_exp2(fmaf(x1, c1, -m_use));
+      const float p0 = SOFTCAP ? fast_exp2(fmaf(x0, -2.0f * cap2, cap2 - m_use)) : fast_exp2(fmaf(x0, c1, -m_use));
+      const float p1 = SOFTCAP ? fast_exp2(fmaf(x1, -2.0f * cap2, cap2 - m_use)) : fast_exp2(fmaf(x1, c1, -m_use));
       const typename V::x2 pr = {(T)p0, (T)p1};
       psum[(u >> 1) & 1] = V::add_pair(pr, psum[(u >> 1) & 1]);
       pk[g][u] = pr[0];
@@ -1698,7 +1717,7 @@ template <int KIND, bool SOFTCAP, bool PADDED, bool KVSPLIT>
 hipError_t launch_split(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   // Up to kMaxChunks work items per query block (items past the plan's end
   // return at once), or kv_split split-KV chunks followed by their merge.
-  const int64_t chunks = a.kv_split > 0 ? a.kv_split : kMaxChunks;
+  const int64_t chunks = a.kv_split > 0 ? a.kv_split : a.items_per_qb;
   const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * chunks));
   const dim3 block(kThreads);
   const dim3 merge_grid((unsigned)((int64_t)a.B * a.H * a.L));  // one workgroup per output row

@@ -85,7 +85,22 @@ struct FwdArgs {
   // Chained items (chain > 0): a grid of that many resident workgroups,
   // each walking the plan entries of one batch*head (sliding windows).
   int32_t chain;
+  // Plan entries per query block a launch provides workgroups for:
+  // kMaxChunks, or 1 when the plan cannot split (plan_never_splits).
+  int32_t items_per_qb;
 };
+
+// The work plan splits a query block only when it visits more than
+// max(kPlanMinSplit, ceil(max_n / 2)) kv blocks, so a plan never splits when
+// no query block can visit more than kPlanMinSplit blocks: at most that many
+// kv blocks in all, or a sliding window of at most kPlanMinSplit - 1 blocks
+// (W <= 1920: its query blocks touch at most 16 kv blocks). Such launches
+// need one workgroup per query block instead of kMaxChunks.
+constexpr int32_t kPlanMinSplit = 16;
+inline bool plan_never_splits(int32_t form_kind, int32_t window, int32_t nk) {
+  return nk <= kPlanMinSplit ||
+         (form_kind == 2 /* ATTN_MASK_SLIDING_WINDOW */ && window <= (kPlanMinSplit - 1) * kBlock);
+}
 
 // Sliding windows with at most this many kv blocks per query block (W <=
 // 1920: never split by the plan) run as chained items when there are at
