@@ -359,7 +359,7 @@ namespace {
 // process ends. In host code `scratch` names a host-side stand-in, not the
 // GPU's copy, so it is never passed to a kernel or a copy: each device's
 // address comes from hipGetSymbolAddress with that device current.
-constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 constexpr int kMaxDevices = 64;

@@ -876,67 +876,69 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
   }
 
   if (wi.split) {
-    // Leave this chunk's partial result, then take a ticket; the last of the
-    // k chunks to finish merges them all. The partials are written and read
-    // with device-scope (sc1) accesses, and every write has completed before
-    // the ticket is taken, so the chunks may run on different XCDs; this
-    // avoids device-scope fences, which would write back and invalidate the
-    // whole L2 of the XCD (and with it the K/V tiles other workgroups reuse).
+    // The two chunks of a split query block each take a ticket when they
+    // finish. The first to finish leaves its partial result (O^T, m, l) in
+    // the query block's slot and then marks it written; the second waits for
+    // that mark and merges both, in chunk order, so the result does not
+    // depend on which finished first and only one partial is ever written.
+    // Counter: first ticket 0 -> 1, second ticket -> 2 (or 3 -> 4), the
+    // first's mark adds 2: both finished and the partial written = 4. The
+    // partial is written and read with device-scope (sc1) accesses, and its
+    // writes have completed before the mark is added, so the chunks may run
+    // on different XCDs without device-scope fences (which would write back
+    // and invalidate the XCD's whole L2, K/V tiles of other workgroups
+    // included). The second chunk waits only on a chunk that has already
+    // taken its ticket, that is, one that is running and writes without
+    // waiting on anything.
     const int64_t bhn = (int64_t)a.B * a.H;
-    auto slot = [&](int c) { return a.partials + (((int64_t)qb * kMaxChunks + c) * bhn + bh) * kSlotFloats; };
+    float* slot = a.partials + ((int64_t)qb * bhn + bh) * kSlotFloats;
     auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     auto get = [](float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-    float* mine = slot(wi.chunk);
-#pragma unroll
-    for (int te = 0; te < 2; ++te)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) put(mine + (wave * 32 + te * 16 + r) * 64 + lane, oacc[te][r]);
-    if (hf == 0) {
-      put(mine + 4 * 32 * 64 + wave * 32 + lq, m_ref);
-      put(mine + 4 * 32 * 64 + kBlock + wave * 32 + lq, lt);
-    }
-    wait_vm_zero();  // this wave's partial writes have completed
-    __syncthreads();
     __shared__ int ticket;
     int32_t* counter = a.counters + (int64_t)qb * bhn + bh;
     if (tid == 0) ticket = atomicAdd(counter, 1);
     __syncthreads();
-    if (ticket != wi.k - 1) return;  // a later chunk merges
-    if (tid == 0) atomicExch(counter, 0);  // ready for the next call
-    // Merge in chunk order (the same operations whichever chunk merges):
-    // weights w_c = 2^(m_c - max m), O = sum_c w_c O_c, l = sum_c w_c l_c.
-    float mc[kMaxChunks], lc[kMaxChunks], wc[kMaxChunks];
-    float m_new = -INFINITY;
+    if (ticket == 0) {
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      if (c < wi.k) {
-        mc[c] = (c == wi.chunk) ? m_ref : get(slot(c) + 4 * 32 * 64 + wave * 32 + lq);
-        lc[c] = (c == wi.chunk) ? lt : get(slot(c) + 4 * 32 * 64 + kBlock + wave * 32 + lq);
-        m_new = fmaxf(m_new, mc[c]);
+      for (int te = 0; te < 2; ++te)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) put(slot + (wave * 32 + te * 16 + r) * 64 + lane, oacc[te][r]);
+      if (hf == 0) {
+        put(slot + 4 * 32 * 64 + wave * 32 + lq, m_ref);
+        put(slot + 4 * 32 * 64 + kBlock + wave * 32 + lq, lt);
       }
+      wait_vm_zero();  // this wave's partial writes have completed
+      __syncthreads();
+      if (tid == 0) atomicAdd(counter, 2);
+      return;
     }
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < wi.k) wc[c] = (mc[c] == -INFINITY) ? 0.0f : fast_exp2(mc[c] - m_new);
+    if (tid == 0) {
+      // (Bounded: the first chunk marks its partial within microseconds.)
+      for (int spin = 0; spin < (1 << 24); ++spin) {
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    }
+    __syncthreads();
+    // Merge in chunk order: weights w_c = 2^(m_c - max m), O = w_0 O_0 +
+    // w_1 O_1, l = w_0 l_0 + w_1 l_1.
+    const float m_o = get(slot + 4 * 32 * 64 + wave * 32 + lq);
+    const float l_o = get(slot + 4 * 32 * 64 + kBlock + wave * 32 + lq);
+    const float m0 = wi.chunk == 0 ? m_ref : m_o, m1 = wi.chunk == 0 ? m_o : m_ref;
+    const float l0 = wi.chunk == 0 ? lt : l_o, l1 = wi.chunk == 0 ? l_o : lt;
+    const float m_new = fmaxf(m0, m1);
+    const float w0 = (m0 == -INFINITY) ? 0.0f : fast_exp2(m0 - m_new);
+    const float w1 = (m1 == -INFINITY) ? 0.0f : fast_exp2(m1 - m_new);
 #pragma unroll
     for (int te = 0; te < 2; ++te)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) {
-          if (c < wi.k) {
-            const float ov = (c == wi.chunk) ? oacc[te][r] : get(slot(c) + (wave * 32 + te * 16 + r) * 64 + lane);
-            acc = (c == 0) ? wc[0] * ov : fmaf(wc[c], ov, acc);
-          }
-        }
-        oacc[te][r] = acc;
+        const float ov = get(slot + (wave * 32 + te * 16 + r) * 64 + lane);
+        const float o0 = wi.chunk == 0 ? oacc[te][r] : ov, o1 = wi.chunk == 0 ? ov : oacc[te][r];
+        oacc[te][r] = fmaf(w1, o1, w0 * o0);
       }
-    float lsum = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < wi.k) lsum = (c == 0) ? wc[0] * lc[0] : fmaf(wc[c], lc[c], lsum);
-    lt = lsum;
+    lt = fmaf(w1, l1, w0 * l0);
     m_ref = m_new;
   }
 

@@ -122,7 +122,9 @@ inline int32_t chain_grid(int32_t dtype, int32_t form_kind, int32_t window, bool
 // Partial result of one split item: the 4 waves' O^T accumulators in
 // register order ([wave][32 registers][64 lanes]) -- for split-KV items the
 // rows' O row-major ([128 rows][64]) -- then the running max and the sum of
-// each of the 128 rows. Slots are [query block][chunk][B*H].
+// each of the 128 rows. Two-way split items keep one slot per (query block,
+// B*H), the partial of whichever chunk finishes first: [query block][B*H];
+// split-KV items one per chunk: [query block][chunk][B*H].
 constexpr int64_t kSlotFloats = 4 * 32 * 64 + 2 * kBlock;
 // Long query blocks are split only when there are few work items.
 constexpr int64_t kSplitMaxItems = 2048;
@@ -154,7 +156,7 @@ inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq, int32_t nk)
   const int32_t ks = kv_split_count(dtype, bh, nq, nk);
   if (ks > 0) return kCountersBytes + (size_t)nq * ks * (size_t)bh * kSlotFloats * sizeof(float);
   if (!use_split(dtype, bh, nq)) return 0;
-  return kCountersBytes + (size_t)nq * kMaxChunks * (size_t)bh * kSlotFloats * sizeof(float);
+  return kCountersBytes + (size_t)nq * (size_t)bh * kSlotFloats * sizeof(float);
 }
 
 // Packed rows: when the L queries of the G = H / H_kv query heads sharing a

@@ -241,8 +241,8 @@ attn_status attn_build_block_mask_custom(const uint32_t* bits, int32_t q_len, in
  *     query block's visit list cut into k chunks whose partial results a
  *     second kernel merges: 8192 + nq * k * B * H * 8448 * 4 bytes;
  *   else, with B * H * nq <= 2048: long query blocks split into two work
- *     items, the later of which merges (ticket counters):
- *     8192 + nq * 2 * B * H * 8448 * 4 bytes;
+ *     items; the first to finish leaves its partial result, the other merges
+ *     (ticket counters): 8192 + nq * B * H * 8448 * 4 bytes;
  *   else 0.
  * Layout: 8192 bytes of int32 ticket counters, then fp32 partial slots.
  * When the L queries of the H / H_kv query heads sharing a K/V head number
@@ -344,13 +344,13 @@ attn_status attn_forward_padded(const void* q, const void* k, const void* v, voi
  * allocation, for callers that cannot allocate: code recorded under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. The split
  * work items' partial results and ticket counters live in a fixed scratch
- * array of 128 MiB that the library holds on each GPU it runs on until the
+ * array of 64 MiB that the library holds on each GPU it runs on until the
  * process ends; every call clears the counters first (with a kernel on
  * `stream`, so a captured call clears them on every replay). All other
  * arguments, the results (bit-identical to attn_forward_padded's) and the
  * errors are as for attn_forward_padded, plus UNSUPPORTED when the shape
- * needs more scratch than 128 MiB (attn_forward_workspace_size tells; at most
- * about 138 MB for bf16/fp16 work with B*H*nq <= 2048, 0 otherwise).
+ * needs more scratch than 64 MiB (attn_forward_workspace_size tells; at most
+ * about 69 MB, for bf16/fp16 work with B*H*nq near 2048).
  * Every call on one GPU shares that GPU's scratch: calls that overlap in
  * time on one GPU (on different streams, or from different threads) race
  * and must be serialised by the caller.

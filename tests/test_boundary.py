@@ -222,23 +222,24 @@ def _ws_size(dtype, B, H, L, S=None):
 
 def test_workspace_size():
     # split items need ticket counters (a fixed region of 2048 int32, the
-    # most a splitting call has) and two fp32 partial slots per query block
-    # and head of 4 waves x 32 registers x 64 lanes plus a max and a sum per row
+    # most a splitting call has) and one fp32 partial slot per query block
+    # and head (the first of the two chunks to finish leaves its partial) of
+    # 4 waves x 32 registers x 64 lanes plus a max and a sum per row
     slot = (4 * 32 * 64 + 2 * 128) * 4
     nq, bh = 64, 8
     counters = 2048 * 4
-    assert _ws_size(1, 1, 8, 8192) == counters + nq * 2 * bh * slot
-    assert _ws_size(2, 2, 4, 8192) == counters + nq * 2 * bh * slot
-    assert _ws_size(1, 1, 1, 300) == counters + 3 * 2 * 1 * slot
+    assert _ws_size(1, 1, 8, 8192) == counters + nq * bh * slot
+    assert _ws_size(2, 2, 4, 8192) == counters + nq * bh * slot
+    assert _ws_size(1, 1, 1, 300) == counters + 3 * 1 * slot
     assert _ws_size(0, 1, 8, 8192) == 0            # fp32 never splits
-    assert _ws_size(1, 1, 32, 8192) == counters + 64 * 2 * 32 * slot  # 2048 items
+    assert _ws_size(1, 1, 32, 8192) == counters + 64 * 32 * slot  # 2048 items
     assert _ws_size(1, 1, 33, 8192) == 0           # many items: no split
     assert _ws_size(1, 1, 8, 0) == 0               # no query blocks
     # decode (one query block, many kv blocks): split-KV, k = min(64,
     # ceil(1024 / (B*H*nq)), nk / 2) chunks of one slot each
     assert _ws_size(1, 1, 8, 1, 8192) == counters + 1 * 32 * 8 * slot      # k = 32
     assert _ws_size(2, 4, 32, 16, 8192) == counters + 1 * 8 * 128 * slot   # k = 8
-    assert _ws_size(1, 1, 8, 1, 640) == counters + 1 * 2 * 8 * slot        # nk = 5: two-way split
+    assert _ws_size(1, 1, 8, 1, 640) == counters + 1 * 8 * slot            # nk = 5: two-way split
 
 
 @no_gpu
@@ -492,7 +493,7 @@ def test_schedule_len():
 
 @no_gpu
 def test_forward_noalloc_refuses_shapes_beyond_its_scratch():
-    # 2048 split items (B*H*nq) of two 33 KiB partial slots: above 128 MiB.
+    # 2048 split items (B*H*nq) with a 33 KiB partial slot each: above 64 MiB.
     # Refused on the host before the scratch is looked up or anything enqueued.
     lib = bsa._load()
     bm = _built_mask(8192, 8192)
