@@ -9,7 +9,8 @@
 // mod' = 1 - (s'/c)^2 with the soft-cap (1 without). D uses the forward's
 // output O (sum_j P_ij dP_ij = dO_i . O_i).
 //
-// Two kernels, no atomics (deterministic): dK/dV per (batch, K/V head, kv
+// Two kernels, no floating-point atomics (deterministic; one integer ticket
+// per split item): dK/dV per (batch, K/V head, kv
 // block), looping over the query heads that share the K/V head and over the
 // query blocks that see the kv block (the BlockMask transposed); dQ per
 // (batch, query head, query block), over the kv blocks the forward visits.
@@ -232,28 +233,43 @@ __global__ __launch_bounds__(kThreads) void bwd_transpose_kernel(BwdArgs a) {
   }
 }
 
-// Two-way split items: each chunk leaves its fp32 accumulators (N tiles of
-// 16 registers, register order [wave][tile*16 + r][lane]) in its slot with
-// device-scope stores, all writes complete before the ticket; the later of
-// the two adds the other chunk's partial (two terms: the sum does not depend
-// on which finishes last) and resets the counter for the next call. Returns
-// false in the chunk that exits.
+// Two-way split items: each chunk takes a ticket when it finishes; the first
+// leaves its fp32 accumulators (N tiles of 16 registers, register order
+// [wave][tile*16 + r][lane]) in its slot with device-scope stores and, once
+// they have completed, marks the slot written; the second waits for the mark,
+// adds the other chunk's partial (two terms: the sum does not depend on which
+// finished first) and resets the counter for the next call. Counter: tickets
+// 0 -> 1 -> 2 (or 3 -> 4), the mark adds 2: 4 = both finished and the partial
+// written. The second chunk waits only on a chunk that has taken its ticket
+// and writes without waiting on anything. Returns false in the chunk that
+// exits.
 template <int N>
 __device__ inline bool merge_two(f32x16_t (&acc)[N], float* mine, float* other, int32_t* counter, int wave,
                                  int lane) {
   auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto get = [](float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-#pragma unroll
-  for (int t = 0; t < N; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) put(mine + ((wave * N + t) * 16 + r) * 64 + lane, acc[t][r]);
-  wait_vm_zero();
-  __syncthreads();
   __shared__ int ticket;
   if (threadIdx.x == 0) ticket = atomicAdd(counter, 1);
   __syncthreads();
-  if (ticket != 1) return false;
-  if (threadIdx.x == 0) atomicExch(counter, 0);
+  if (ticket == 0) {
+#pragma unroll
+    for (int t = 0; t < N; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) put(mine + ((wave * N + t) * 16 + r) * 64 + lane, acc[t][r]);
+    wait_vm_zero();
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(counter, 2);
+    return false;
+  }
+  if (threadIdx.x == 0) {
+    // (Bounded: the first chunk marks its partial within microseconds.)
+    for (int spin = 0; spin < (1 << 24); ++spin) {
+      if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
 #pragma unroll
   for (int t = 0; t < N; ++t)
 #pragma unroll
