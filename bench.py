@@ -271,7 +271,7 @@ def summarize(w: wl.Workload, r):
 
 
 TRAFFIC_PROFILES = [os.path.join(ROOT, "profiles", f) for f in (
-    "fwd16_causal_8192_sliding_32768_w256_hbm_traffic.md",
+    "fwd16_hbm_traffic_causal_sliding_documents.md",
     "packed_decode_gqa_b8_h32_kv8_s8192_hbm_traffic.md")]
 FWD_SOURCE = os.path.join(ROOT, "block_sparse_attention_35_amd", "csrc", "fwd_kernels.h")
 
