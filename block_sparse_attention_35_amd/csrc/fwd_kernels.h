@@ -96,6 +96,15 @@ struct Vec<_Float16> {
   }
 };
 
+// A v_dot2c result may be read by another VALU instruction only three wait
+// states after it is written. The compiler keeps that distance for the
+// instructions it knows, not for the asm dot above, so the two row sums pass
+// through this (tied to both, so it sits after the last dot and before the
+// first other reader) before anything else reads them.
+__device__ inline void dot_results_settle(float& a, float& b) {
+  asm volatile("s_nop 2" : "+v"(a), "+v"(b));
+}
+
 // Other half's value combined with ours: v_permlane32_swap exchanges lanes
 // l and l^32 between its two operands; with both operands equal, the two
 // results of each lane are {x_l, x_(l^32)} in some order.
@@ -257,14 +266,17 @@ typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 // these LDS writes from the tiles being read, adds no wait for the copies in
 // flight before every LDS read; every wait on them is explicit (wait_vm_zero,
 // then a barrier). The instructions have no result registers and their
-// address registers are read at issue. The first form takes a 64-bit
-// address per lane; the second a wave-uniform base in SGPRs plus a 32-bit
-// byte offset per lane, which keeps the per-tile address arithmetic scalar.
+// address registers are read at issue. An LDS DMA reads M0 one wait state
+// after the write at the earliest (the compiler spaces its own such pairs,
+// but not inside asm), hence the s_nop between the two. The first form takes
+// a 64-bit address per lane; the second a wave-uniform base in SGPRs plus a
+// 32-bit byte offset per lane, which keeps the per-tile address arithmetic
+// scalar.
 __device__ inline uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 __device__ inline void lds_copy16(const void* src, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
                : "memory", "m0");
@@ -275,14 +287,14 @@ __device__ inline void lds_copy16_base(const void* sbase, uint32_t lane_off, uin
   const uint64_t p = (uint64_t)(uintptr_t)sbase;
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(lane_off), "s"((const void*)(uintptr_t)(lo | (hi << 32))),
                  "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
                : "memory", "m0");
 }
 __device__ inline void lds_copy4(const void* src, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
                : "memory", "m0");
@@ -637,6 +649,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
     if (i + 2 < 16) prob_chunk(i + 2);
     sched_fence();
   }
+  dot_results_settle(psum[0], psum[1]);
   l += psum[0] + psum[1];
   __builtin_amdgcn_s_setprio(0);
 }
@@ -1599,6 +1612,7 @@ __global__ __launch_bounds__(kThreads, 2) void packed_kernel(FwdArgs a) {
         pk[gi][u] = pr[0];
         pk[gi][u + 1] = pr[1];
       }
+    dot_results_settle(psum[0], psum[1]);
     l += psum[0] + psum[1];
     // O^T += V^T P^T over the wave's two 16-key groups (2 wave, 2 wave + 1).
 #pragma unroll
