@@ -262,11 +262,13 @@ __device__ inline bool merge_two(f32x16_t (&acc)[N], float* mine, float* other, 
     return false;
   }
   if (threadIdx.x == 0) {
-    // (Bounded: the first chunk marks its partial within microseconds.)
-    for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
+    // A ticket of 3 already includes the mark. Otherwise wait for it
+    // (bounded: the first chunk marks its partial within microseconds).
+    if (ticket != 3)
+      for (int spin = 0; spin < (1 << 24); ++spin) {
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
     __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();

@@ -926,11 +926,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
       return;
     }
     if (tid == 0) {
-      // (Bounded: the first chunk marks its partial within microseconds.)
-      for (int spin = 0; spin < (1 << 24); ++spin) {
-        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
+      // A ticket of 3 is the first chunk's ticket plus its mark: the partial
+      // is already there. Otherwise wait for the mark (bounded: the first
+      // chunk marks its partial within microseconds).
+      if (ticket != 3)
+        for (int spin = 0; spin < (1 << 24); ++spin) {
+          if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 4) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
       __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     }
     __syncthreads();
