@@ -402,27 +402,41 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
         dpacc = V::mma(read16<T>(plain_u(dt_base, lane, c) + qt * 4096), vreg[c], dpacc);
       }
       x8 pk[2], dsk[2];
+      // P and dS of the tile, with the pair test a compile-time choice (one
+      // uniform branch per tile: a runtime test per element cut the code
+      // into many small branched blocks), at raised wave priority: the
+      // vector phase between the tile's MFMAs, issued first when the other
+      // wave on the SIMD is in its MFMAs.
+      auto elem = [&](auto partial_c) __attribute__((always_inline)) {
+        constexpr bool PARTIAL = decltype(partial_c)::value;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int rl = qt * 32 + 8 * q4 + 4 * hf;  // block row of registers 4 q4 .. 4 q4 + 3
-        typedef __attribute__((address_space(3))) const f32x4_t lds_f4;
-        const f32x4_t l4 = *reinterpret_cast<lds_f4*>((lds_u8)s.lse2 + rl * 4);
-        const f32x4_t d4 = *reinterpret_cast<lds_f4*>((lds_u8)s.D + rl * 4);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int rl = qt * 32 + 8 * q4 + 4 * hf;  // block row of registers 4 q4 .. 4 q4 + 3
+          typedef __attribute__((address_space(3))) const f32x4_t lds_f4;
+          const f32x4_t l4 = *reinterpret_cast<lds_f4*>((lds_u8)s.lse2 + rl * 4);
+          const f32x4_t d4 = *reinterpret_cast<lds_f4*>((lds_u8)s.D + rl * 4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * q4 + u;
-          float dmod;
-          float p = bwd_prob<SOFTCAP>(sacc[r], l4[u], f, dmod);
-          if (partial) {
-            const int32_t di = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[rl + u] : 0;
-            const uint32_t word = (KIND == ATTN_MASK_CUSTOM) ? s.bits[wave][rl + u] : 0u;
-            if (!bwd_live<KIND>(f, q0 + rl + u, key, klo, khi, di, dj, word, lq)) p = 0.0f;
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * q4 + u;
+            float dmod;
+            float p = bwd_prob<SOFTCAP>(sacc[r], l4[u], f, dmod);
+            if (PARTIAL) {
+              const int32_t di = (KIND == ATTN_MASK_DOCUMENT) ? s.doc[rl + u] : 0;
+              const uint32_t word = (KIND == ATTN_MASK_CUSTOM) ? s.bits[wave][rl + u] : 0u;
+              if (!bwd_live<KIND>(f, q0 + rl + u, key, klo, khi, di, dj, word, lq)) p = 0.0f;
+            }
+            const float ds = p * (dpacc[r] - d4[u]) * dmod;
+            pk[r >> 3][r & 7] = (T)p;
+            dsk[r >> 3][r & 7] = (T)ds;
           }
-          const float ds = p * (dpacc[r] - d4[u]) * dmod;
-          pk[r >> 3][r & 7] = (T)p;
-          dsk[r >> 3][r & 7] = (T)ds;
         }
-      }
+      };
+      __builtin_amdgcn_s_setprio(1);
+      if (partial)
+        elem(std::true_type{});
+      else
+        elem(std::false_type{});
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
@@ -579,6 +593,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         dpacc = V::mma(read16<T>(plain_k(vt_base, lane, c) + t * 4096), doop[c], dpacc);
       }
       x8 dsk[2];
+      __builtin_amdgcn_s_setprio(1);  // the vector phase (as in dK/dV)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int jl = t * 32 + acc_row(r, hf);
@@ -590,6 +605,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         }
         dsk[r >> 3][r & 7] = (T)(p * (dpacc[r] - Dq) * dmod);
       }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
