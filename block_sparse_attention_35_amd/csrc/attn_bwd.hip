@@ -15,16 +15,18 @@ hipError_t launch_backward_custom(int32_t dtype, const BwdArgs& a, hipStream_t s
 hipError_t launch_backward(int32_t dtype, const BwdArgs& a, hipStream_t stream) {
   const dim3 block(kThreads);
   const int64_t rows = (int64_t)a.f.B * a.f.H * a.f.L;
-  if (rows > 0) {
-    const dim3 grid((unsigned)((rows + kThreads / 8 - 1) / (kThreads / 8)));
+  // D and lse2 (one workgroup per 32 rows) and the transposed BlockMask (one
+  // per kv block) in one launch.
+  const int64_t blocks = (int64_t)a.f.m.nk + (rows + kThreads / 8 - 1) / (kThreads / 8);
+  if (blocks > 0) {
+    const dim3 grid((unsigned)blocks);
     if (dtype == ATTN_BF16)
-      hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(bwd_prep_transpose_kernel<__bf16>, grid, block, 0, stream, a);
     else if (dtype == ATTN_F16)
-      hipLaunchKernelGGL(bwd_prep_kernel<_Float16>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(bwd_prep_transpose_kernel<_Float16>, grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(bwd_prep_transpose_kernel<float>, grid, block, 0, stream, a);
   }
-  if (a.f.m.nk > 0) hipLaunchKernelGGL(bwd_transpose_kernel, dim3(a.f.m.nk), block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the dK/dV work plan over kv blocks and their query-block lists

@@ -141,9 +141,9 @@ __device__ inline float bwd_prob(float x, float lse2, const FwdArgs& a, float& d
 // D = dO . O and the logsumexp in log2 units, one row per 8 threads.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_prep(const BwdArgs& a, int block) {
   const int64_t rows = (int64_t)a.f.B * a.f.H * a.f.L;
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / 8) + threadIdx.x / 8;
+  const int64_t row = (int64_t)block * (kThreads / 8) + threadIdx.x / 8;
   const int part = threadIdx.x % 8;
   float acc = 0.0f;
   if (row < rows) {
@@ -193,9 +193,9 @@ __device__ inline bool sorted_has(const int32_t* row, int n, int x) {
   return lo < n && row[lo] == x;
 }
 
-__global__ __launch_bounds__(kThreads) void bwd_transpose_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_transpose(const BwdArgs& a, int kb) {
   __shared__ int32_t wave_counts[2][kThreads / 64];
-  const int kb = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nq = a.f.m.nq, nk = a.f.m.nk;
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t base_p = 0, base_f = 0;
@@ -231,6 +231,16 @@ __global__ __launch_bounds__(kThreads) void bwd_transpose_kernel(BwdArgs a) {
     a.tq_num[kb] = base_p;
     a.tf_num[kb] = base_f;
   }
+}
+
+// Both in one launch (they are independent): workgroups 0 .. nk - 1
+// transpose, the rest compute D and lse2.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_prep_transpose_kernel(BwdArgs a) {
+  if ((int)blockIdx.x < a.f.m.nk)
+    bwd_transpose(a, blockIdx.x);
+  else
+    bwd_prep<T>(a, blockIdx.x - a.f.m.nk);
 }
 
 // Two-way split items: each chunk takes a ticket when it finishes; the first
