@@ -266,12 +266,15 @@ typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
 // these LDS writes from the tiles being read, adds no wait for the copies in
 // flight before every LDS read; every wait on them is explicit (wait_vm_zero,
 // then a barrier). The instructions have no result registers and their
-// address registers are read at issue. An LDS DMA reads M0 one wait state
-// after the write at the earliest (the compiler spaces its own such pairs,
-// but not inside asm), hence the s_nop between the two. The first form takes
-// a 64-bit address per lane; the second a wave-uniform base in SGPRs plus a
-// 32-bit byte offset per lane, which keeps the per-tile address arithmetic
-// scalar.
+// address registers are read at issue. The compiler spaces its own memory
+// instructions from the writes they depend on, but not inside asm: an LDS
+// DMA reads M0 one wait state after the write at the earliest (the s_nop 0
+// between the two), and a vector memory instruction reads an SGPR that a VALU
+// instruction wrote (a v_readfirstlane of the base) five wait states after
+// the write at the earliest (the s_nop 4 of the second form). The first form
+// takes a 64-bit address per lane; the second a wave-uniform base in SGPRs
+// plus a 32-bit byte offset per lane, which keeps the per-tile address
+// arithmetic scalar.
 __device__ inline uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
@@ -287,7 +290,7 @@ __device__ inline void lds_copy16_base(const void* sbase, uint32_t lane_off, uin
   const uint64_t p = (uint64_t)(uintptr_t)sbase;
   const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(lane_off), "s"((const void*)(uintptr_t)(lo | (hi << 32))),
                  "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
