@@ -354,6 +354,17 @@ struct alignas(16) Lds {
   KStage k[2];
   VStage v[2];
 };
+// The chained sliding-window kernel: K stages without document ids (the
+// rule needs none), two V stages, and the next item's Q rows, copied by LDS
+// DMA during an item's last block: 80 KiB, two workgroups per CU.
+struct alignas(16) KStageRows {
+  uint8_t k[kBlock * 128];
+};
+struct alignas(16) LdsChain {
+  KStageRows k[2];
+  VStage v[2];
+  uint8_t q[kBlock * 128];
+};
 // For CUSTOM masks, also each stage's mask words: [query row][4].
 struct alignas(16) LdsBits {
   KStage k[2];
@@ -424,8 +435,8 @@ __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 //  P. O^T += V^T P^T (MFMA i: 16-key group i / 2, head-dim tile i % 2; V
 //     fragments read four MFMAs ahead), with the probabilities of the next
 //     group.
-template <typename T, int KIND, bool SOFTCAP, bool PARTIAL, bool PADDED>
-__device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
+template <typename T, int KIND, bool SOFTCAP, bool PARTIAL, bool PADDED, class KSt>
+__device__ __forceinline__ void fwd_block(const KSt& kst, const lds_u8 (&kp)[4], const lds_u8 (&vp)[2],
                                           const typename Vec<T>::x8 (&qop)[4], f32x16_t (&oacc)[2],
                                           float& m_ref, float& l, int qi, int row0, int kv0, int lane, const FwdArgs& a,
                                           int32_t dq, int klo, int khi, const uint32_t* mbits) {
@@ -545,7 +556,7 @@ __device__ __forceinline__ void fwd_block(const KStage& kst, const lds_u8 (&kp)[
         if (KIND == ATTN_MASK_SLIDING_WINDOW || PADDED) live &= c >= lo - 32 * t;
         // (Read unconditionally: the four ids of a register group are one
         // 16-byte LDS read.)
-        if (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
+        if constexpr (KIND == ATTN_MASK_DOCUMENT) live &= kst.doc[t * 32 + acc_row(r, hf)] == dq;
         if (KIND == ATTN_MASK_CUSTOM) live &= (mw[t] >> (c + 4 * hf)) & 1u;
         x = live ? x : (SOFTCAP ? INFINITY : -INFINITY);
       }
@@ -990,7 +1001,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdArgs a) {
 // query blocks at a time and share their K/V tiles in L2; with B*H a multiple
 // of 8 all of a head's workgroups sit on one XCD). The two-stage block
 // pipeline runs across item boundaries: during an item's last block the next
-// item's first K/V tiles are copied and its Q rows loaded, and an item's
+// item's first K/V tiles and its Q rows are copied into LDS, and an item's
 // output is stored only after the next item's first barrier, so neither the
 // loads nor the stores of one item wait behind the other.
 // ---------------------------------------------------------------------------
@@ -999,9 +1010,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
   using V = Vec<T>;
   using x8 = typename V::x8;
   using x4 = typename V::x4;
-  __shared__ Lds lds;
-  // Landing area of the L2 prefetches (their bytes are never read).
-  __shared__ uint32_t pf_sink[4 * 64];
+  __shared__ LdsChain lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1037,29 +1046,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
   next_item(r, wi);
   if (r >= nitems) return;
 
-  // Q operands of query block qb for this lane's row (zero past L).
-  auto load_q = [&](int qb, x8 (&dst)[4]) {
-    const int qi = qb * kBlock + wave * 32 + lq;
+  // Q rows of query block qb: each wave copies its 32 rows (4 KiB, rows past
+  // L clamped to the last row) into the Q stage by LDS DMA, like the K/V
+  // tiles, and reads its operands from there once the copies have landed
+  // (zero past L). Loads into registers here would be tracked by the
+  // compiler's wait insertion, which does not see the asm copies: a wait it
+  // adds for such a load also waits for every copy issued after it.
+  auto issue_q = [&](int qb) {
+    const uint32_t lds0 = lds_offset(lds.q) + (uint32_t)wave * 4096u;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      dst[c] = (qi < a.L) ? *reinterpret_cast<const x8*>(qg + (int64_t)qi * a.q_sl + c * 16 + hf * 8) : x8{};
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(qb * kBlock + wave * 32 + 8 * i + (lane >> 3), a.L - 1);
+      lds_copy16(qg + (int64_t)row * a.q_sl + (lane & 7) * 8, lds0 + 1024u * i);
+    }
+  };
+  auto read_q = [&](int qb, x8 (&dst)[4]) {
+    typedef __attribute__((address_space(3))) const x8 lds_x8;
+    const int qi = qb * kBlock + wave * 32 + lq;
+    const lds_u8 rowp = (lds_u8)lds.q + (wave * 32 + lq) * 128;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[c] = (qi < a.L) ? *reinterpret_cast<const lds_x8*>(rowp + c * 32 + hf * 16) : x8{};
   };
   auto issue_block = [&](int kv0, int stage) {
-    issue_k<T, KIND>(kg, a.k_sl, k_off, a.m.doc, kv0, a.S, lds.k[stage], wave, lane);
+    issue_rows<T, false>(kg, a.k_sl, k_off, kv0, a.S, lds.k[stage].k, wave, lane);
     issue_rows<T, true>(vg, a.v_sl, v_off, kv0, a.S, lds.v[stage].v, wave, lane);
-  };
-  // L2 prefetch of the block after the next one: one 4-byte read per K row
-  // (lanes 0..31) and V row (lanes 32..63) of this wave's 32 rows, so the
-  // tile copies issued a block later find them in L2 (a window's K/V block
-  // is first read, from HBM, by the query block whose diagonal it is). It is
-  // the last vector memory operation of its block step, so the next block's
-  // wait leaves it in flight; the operations of a wave complete in issue
-  // order, so a prefetch issued earlier would hold up later copies.
-  const uint32_t pf_lds = lds_offset(pf_sink) + (uint32_t)wave * 256u;
-  auto prefetch_block = [&](int kv0) {
-    const int64_t row = min(kv0 + wave * 32 + lq, a.S - 1);
-    const void* p = hf ? (const void*)(vg + row * a.v_sl) : (const void*)(kg + row * a.k_sl);
-    lds_copy4(p, pf_lds);
   };
   // First key of visited block n of item w (full blocks first, then partial).
   auto kv_start = [&](const WorkItem& w, int n) {
@@ -1069,7 +1079,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
   };
 
   x8 qop[4];
-  load_q(wi.qb, qop);
+  issue_q(wi.qb);
   int kv_next = wi.first_kb * kBlock;
   issue_block(kv_next, 0);
   wait_vm_zero();
@@ -1090,8 +1100,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
     prev_qi = -1;
   };
 
-  int par = 0;               // stage of the current block
-  bool pf_pending = false;  // a prefetch is the last vector memory operation issued
+  int par = 0;  // stage of the current block
   while (true) {
     const int qb = wi.qb;
     const int nfull = wi.nfull, nblk = wi.nfull + wi.npart;
@@ -1114,51 +1123,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) oacc[te][rr] = 0.0f;
     float m_ref = -INFINITY, l = 0.0f;
-    x8 qnext[4];
 
     auto block = [&](auto partial_c, int m) __attribute__((always_inline)) {
       constexpr bool PARTIAL = decltype(partial_c)::value;
       lds_u8 kp[4], vp[2];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        kp[c] = lp.k[c] + par * (int)sizeof(KStage);
+        kp[c] = lp.k[c] + par * (int)sizeof(lds.k[0]);
         asm volatile("" : "+v"(kp[c]));
       }
 #pragma unroll
       for (int te = 0; te < 2; ++te) {
-        vp[te] = lp.v[te] + par * (int)sizeof(VStage);
+        vp[te] = lp.v[te] + par * (int)sizeof(lds.v[0]);
         asm volatile("" : "+v"(vp[te]));
       }
       const int kv0 = kv_next;
-      // This wave's copies of block m (and older stores); a prefetch issued
-      // after them may stay in flight.
-      if (pf_pending)
-        wait_vm<1>();
-      else
-        wait_vm_zero();
+      wait_vm_zero();    // this wave's copies of block m (and Q rows, older stores)
       wait_lgkm_zero();  // this wave's reads of the previous block
       barrier_only();
-      pf_pending = false;
-      // The previous item's output: its stores are issued now and finish
-      // during this block.
-      if (m == 0) flush_held();
+      if (m == 0) {
+        // The previous item's output: its stores are issued now and finish
+        // during this block. This item's Q rows (this wave's own copies).
+        flush_held();
+        read_q(qb, qop);
+      }
       if (m + 1 < nblk) {
         kv_next = kv_after;
         issue_block(kv_next, 1 - par);
-        const bool more = m + 2 < nblk || has_next;
         if (m + 2 < nblk)
           kv_after = kv_start(wi, m + 2);
         else if (has_next)
           kv_after = wn.first_kb * kBlock;
-        if (more) {
-          prefetch_block(kv_after);
-          pf_pending = true;
-        }
       } else if (has_next) {
-        // Last block: the next item's first tiles and Q rows.
+        // Last block: the next item's first tiles and Q rows (the Q stage is
+        // rewritten once this wave's reads of it have completed).
         kv_next = kv_after;
         issue_block(kv_next, 1 - par);
-        load_q(wn.qb, qnext);
+        if (m == 0) wait_lgkm_zero();
+        issue_q(wn.qb);
       }
       fwd_block<T, KIND, SOFTCAP, PARTIAL, false>(lds.k[par], kp, vp, qop, oacc, m_ref, l, qi, row0, kv0, lane,
                                                   a, dq, 0, a.S, nullptr);
@@ -1174,11 +1176,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
       // its quarter of a stage).
       flush_held();
       wait_vm_zero();
-      pf_pending = false;
       if (has_next) {
         kv_next = wn.first_kb * kBlock;
         issue_block(kv_next, par);
-        load_q(wn.qb, qnext);
+        issue_q(wn.qb);
       }
     }
 
@@ -1197,8 +1198,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_chain_kernel(FwdArgs a) {
     if (!has_next) break;
     r = r_n;
     wi = wn;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qop[c] = qnext[c];
   }
   flush_held();
 }
