@@ -162,15 +162,17 @@ inline size_t workspace_bytes(int32_t dtype, int64_t bh, int32_t nq, int32_t nk)
 // Packed rows: when the L queries of the G = H / H_kv query heads sharing a
 // K/V head number at most kPackRows, one work item per (batch, K/V head,
 // chunk) computes them all from one read of the K/V head. The chunk count
-// aims at kPackTarget work items (one per CU: longer chunks beat more of
-// them, and one chunk needs no merge) with at least two kv blocks each, and
+// aims at kPackTarget work items (two per CU, the most the kernel's LDS
+// allows: each keeps one block of copies in flight per wave, so two
+// workgroups per CU double the bytes in flight) with at least two kv blocks
+// each, and
 // is capped by the partial slots that fit in the workspace the shape asks
 // for (the formula above, which does not depend on H_kv or L); with one chunk
 // the items write the output directly. Slot: O [32][64] row-major, then the
 // rows' maxima [32] and sums [32].
 constexpr int kPackRows = 32;
 constexpr int64_t kPackSlotFloats = kPackRows * kHeadDim + 2 * kPackRows;
-constexpr int64_t kPackTarget = 256;
+constexpr int64_t kPackTarget = 512;
 inline bool use_packed(int32_t dtype, int32_t L, int32_t G) {
   return dtype != 0 /* ATTN_F32 */ && L >= 1 && G >= 1 && (int64_t)L * G <= kPackRows;
 }
