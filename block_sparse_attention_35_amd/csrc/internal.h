@@ -143,7 +143,7 @@ constexpr size_t kCountersBytes = kSplitMaxItems * sizeof(int32_t);
 // block's kv blocks are cut into k chunks, k chosen from the shape alone
 // (about kKvSplitTarget items, at least two kv blocks per chunk, at most
 // kKvSplitMax), when that gives more than the two-way split of the plan.
-constexpr int64_t kKvSplitTarget = 1024;
+constexpr int64_t kKvSplitTarget = 512;
 constexpr int32_t kKvSplitMax = 64;
 inline int32_t kv_split_count(int32_t dtype, int64_t bh, int32_t nq, int32_t nk) {
   if (dtype == 0 /* ATTN_F32 */ || nq <= 0 || bh <= 0) return 0;
