@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const WorkItem wi = work_item(f, blockIdx.x / BH);
   if (wi.skip) return;
   const int qb = wi.qb;
-  const int bh = blockIdx.x % BH;
+  const int bh = xcd_head_order(blockIdx.x % BH, BH, f.kv_group);
   const int b = bh / f.H, h = bh % f.H, hk = h / f.kv_group;
   const int q0 = qb * kBlock;
   const int qi = q0 + wave * 32 + lq;  // this lane's query
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd32_dq_kernel(BwdArgs a) {
   const WorkItem wi = work_item(f, blockIdx.x / BH);
   if (wi.skip) return;
   const int qb = wi.qb;
-  const int bh = blockIdx.x % BH;
+  const int bh = xcd_head_order(blockIdx.x % BH, BH, f.kv_group);
   const int b = bh / f.H, h = bh % f.H, hk = h / f.kv_group;
   const int q0 = qb * kBlock;
   const int qi = q0 + wave * 32 + lq;  // this lane's query
