@@ -107,6 +107,10 @@ CASES = [
     # more than 16 live blocks per row: dQ and dK/dV items split in two and merge
     (_odd("split_causal_4352_bf16", "bf16", 1, 4352, 4352, wl.MASK_CAUSAL), None, None),
     (_odd("split_gqa_causal_2304_f16", "f16", 4, 2304, 2304, wl.MASK_CAUSAL, H_kv=2), None, None),
+    # B*H a multiple of 8 with grouped heads: the dQ items take the XCD head
+    # order, with split items merging by their (batch, head) slot
+    (_odd("split_gqa_xcd_order_B2_h8_kv2_2304_bf16", "bf16", 8, 2304, 2304, wl.MASK_CAUSAL, B=2, H_kv=2),
+     None, None),
     (_odd("split_padded_none_2560_bf16", "bf16", 1, 2560, 2560, wl.MASK_NONE, B=2), None, ([100, 0], [2560, 2200])),
     # fp32 (fp32 MFMA, probabilities and dS unrounded)
     (wl.WORKLOADS["causal_256_f32"], None, None),

@@ -241,6 +241,9 @@ SMALL = [
     _odd("gqa_none_h4_kv2_f32", "f32", 4, 300, 200, wl.MASK_NONE).with_(H_kv=2),
     _odd("gqa_causal_lr_B2_h8_kv2_bf16", "bf16", 8, 256, 768, wl.MASK_CAUSAL_LOWER_RIGHT,
          B=2).with_(H_kv=2),
+    # B*H a multiple of 8 with grouped heads (the XCD head order) and split
+    # query blocks merging by their (batch, head) slot
+    _odd("gqa_causal_split_B2_h8_kv2_2304_bf16", "bf16", 8, 2304, 2304, wl.MASK_CAUSAL, B=2).with_(H_kv=2),
 ]
 
 
