@@ -1362,16 +1362,62 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
   }
 }
 
-// Merge of one output row over the k <= 64 chunks of a split visit list.
-// Chunk c's partial result sits at slot0 + c * cstride: the row's
+// Merges of one output row over the k <= kKvSplitMax chunks of a split visit
+// list. Chunk c's partial result sits at slot0 + c * cstride: the row's
 // unnormalised O (64 floats) at o_off, its max (log2 units) at m_off and its
-// sum at l_off. Thread t takes chunk t / 4 and head dims 16 (t % 4) .. +15,
-// so every load is in flight at once; with w_c = 2^(m_c - max m) (0 for a
-// chunk without live keys), O = sum w_c O_c / sum w_c l_c (0 when the sum is
-// 0) and lse = (max m + log2 sum w_c l_c) ln 2, the sums taken in chunk
-// order through LDS.
+// sum at l_off. With w_c = 2^(m_c - max m) (0 for a chunk without live keys),
+// O = sum w_c O_c / sum w_c l_c (0 when the sum is 0) and lse = (max m + log2
+// sum w_c l_c) ln 2, the sums taken in chunk order, each product rounded
+// before it is added. Both forms below give the same bits.
+static_assert(kKvSplitMax <= 64, "one lane per chunk in merge_row");
+constexpr int kMergeRows = kThreads / 64;  // output rows per merge_row workgroup (one per wave)
+
+// One wave per row, lane e holding head dim e (the split-KV merge: many rows,
+// a few chunks each). Lane c reads chunk c's m and l, and the row's O values
+// of the first 16 chunks are read in the same round (later ones 16 at a
+// time); no fused multiply-adds are formed.
 template <typename T>
 __device__ inline void merge_row(const float* slot0, int64_t cstride, int o_off, int m_off, int l_off, int k,
+                                 int lane, T* out, float* lse) {
+#pragma clang fp contract(off)
+  float o[16];
+  auto load_o = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[j] = (c0 + j < k) ? slot0[(int64_t)(c0 + j) * cstride + o_off + lane] : 0.0f;
+  };
+  // the first 16 chunks' values are read in the same round as m and l
+  load_o(0);
+  const float* mine = slot0 + (int64_t)min(lane, k - 1) * cstride;
+  const float mc = lane < k ? mine[m_off] : -INFINITY;
+  const float lc = lane < k ? mine[l_off] : 0.0f;
+  float mmax = mc;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+  const float wc = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - mmax);
+  const float wlc = wc * lc;
+  float acc = 0.0f, lsum = 0.0f;
+  for (int c0 = 0; c0 < k; c0 += 16) {
+    if (c0 > 0) load_o(c0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (c0 + j < k) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), c0 + j));
+        const float wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlc), c0 + j));
+        acc = acc + w * o[j];
+        lsum = lsum + wl;
+      }
+    }
+  }
+  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+  out[lane] = (T)(acc * inv);
+  if (lse != nullptr && lane == 0) *lse = (lsum > 0.0f) ? (mmax + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+}
+
+// One workgroup per row (the packed decode merge: few rows, more chunks):
+// thread t takes chunk t / 4 and head dims 16 (t % 4) .. +15, so every load
+// is in flight at once, and the products and sums go through LDS.
+template <typename T>
+__device__ inline void merge_row_block(const float* slot0, int64_t cstride, int o_off, int m_off, int l_off, int k,
                                  T* out, float* lse) {
   static_assert(kThreads == 4 * kKvSplitMax, "one thread per (chunk, quarter row)");
   __shared__ float s_m[kKvSplitMax], s_wl[kKvSplitMax];
@@ -1415,19 +1461,22 @@ __device__ inline void merge_row(const float* slot0, int64_t cstride, int o_off,
   }
 }
 
-// Merge of split-KV chunks: one workgroup per output row (query block qb,
-// row r of it, batch*head bh); slots are [qb][chunk][B*H].
+// Merge of split-KV chunks: one wave per output row, rows ordered query row
+// first, then batch*head, so the waves of a workgroup read neighbouring rows
+// of the same slots; slots are [qb][chunk][B*H].
 template <typename T>
 __global__ __launch_bounds__(kThreads) void kv_merge_kernel(FwdArgs a) {
+  const int64_t gr = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH, rq = blockIdx.x / BH;
-  const int qi = rq, qb = rq / kBlock, row = rq % kBlock;
-  if (qi >= a.L) return;
+  if (gr >= (int64_t)BH * a.L) return;
+  const int bh = (int)(gr / a.L), qi = (int)(gr % a.L);
+  const int qb = qi / kBlock, row = qi % kBlock;
   const int b = bh / a.H, h = bh % a.H;
   const int k = a.kv_split;
   const float* slot0 = a.partials + ((int64_t)qb * k * BH + bh) * kSlotFloats;
   merge_row<T>(slot0, (int64_t)BH * kSlotFloats, row * kHeadDim, 4 * 32 * 64 + row, 4 * 32 * 64 + kBlock + row, k,
-               static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl,
+               lane, static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl,
                a.lse == nullptr ? nullptr : a.lse + (int64_t)bh * a.L + qi);
 }
 
@@ -1719,10 +1768,10 @@ __global__ __launch_bounds__(kThreads) void packed_merge_kernel(FwdArgs a) {
   const int b = bk / Hk, hk = bk % Hk;
   const int h = hk * G + row / a.L, qi = row % a.L;
   const float* slot0 = a.partials + (int64_t)bk * a.pack_split * kPackSlotFloats;
-  merge_row<T>(slot0, kPackSlotFloats, row * kHeadDim, kPackRows * kHeadDim + row,
-               kPackRows * kHeadDim + kPackRows + row, a.pack_split,
-               static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl,
-               a.lse == nullptr ? nullptr : a.lse + ((int64_t)b * a.H + h) * a.L + qi);
+  merge_row_block<T>(slot0, kPackSlotFloats, row * kHeadDim, kPackRows * kHeadDim + row,
+                     kPackRows * kHeadDim + kPackRows + row, a.pack_split,
+                     static_cast<T*>(a.o) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sl,
+                     a.lse == nullptr ? nullptr : a.lse + ((int64_t)b * a.H + h) * a.L + qi);
 }
 
 template <int KIND, bool SOFTCAP>
@@ -1753,7 +1802,7 @@ hipError_t launch_split(int32_t dtype, const FwdArgs& a, hipStream_t stream) {
   const int64_t chunks = a.kv_split > 0 ? a.kv_split : a.items_per_qb;
   const dim3 grid((unsigned)((int64_t)a.B * a.H * a.m.nq * chunks));
   const dim3 block(kThreads);
-  const dim3 merge_grid((unsigned)((int64_t)a.B * a.H * a.L));  // one workgroup per output row
+  const dim3 merge_grid((unsigned)(((int64_t)a.B * a.H * a.L + kMergeRows - 1) / kMergeRows));
   switch (dtype) {
     case ATTN_BF16:
       hipLaunchKernelGGL((fwd16_kernel<__bf16, KIND, SOFTCAP, PADDED, KVSPLIT>), grid, block, 0, stream, a);
