@@ -349,6 +349,53 @@ def test_key_padding_full_size_every_row(dev):
              w.name)
 
 
+def _half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of the output type at |x| (normal range)."""
+    bits = {"bf16": 8, "f16": 11, "f32": 24}[dtype]
+    ax = np.maximum(np.abs(x), np.finfo(np.float64).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(int) - bits)
+
+
+FEW_KEYS = [
+    # rows that keep one to three keys: O is a mix of one or two V rows and
+    # can exceed 4 in magnitude, where half an ulp of bf16 (2^-6) is above
+    # the 1e-2 bound that holds for rows averaging many keys
+    (_odd("few_keys_S4_pad_bf16", "bf16", 4, 485, 4, wl.MASK_NONE, B=3), ([3, 2, 0], [4, 4, 1])),
+    (_odd("few_keys_window2_bf16", "bf16", 8, 900, 900, wl.MASK_SLIDING_WINDOW, 2), None),
+    (_odd("few_keys_window3_f16", "f16", 8, 900, 900, wl.MASK_SLIDING_WINDOW, 3), None),
+]
+
+
+@pytest.mark.parametrize("w,ranges", FEW_KEYS, ids=[c[0].name for c in FEW_KEYS])
+def test_few_key_rows_within_output_rounding(dev, w, ranges):
+    """Rows with one to three live keys: every element of O within 1e-2 plus
+    half an ulp of the output type at the reference value (the rounding of O
+    itself), the mean error within 1e-3 plus the mean of that half ulp, the
+    logsumexp within the usual bound."""
+    if ranges is None:
+        (q, k, v), doc, o, lse = _run(w, dev, seed=5)
+        starts = ends = None
+    else:
+        (q, k, v), doc, o, lse = _run_padded(w, ranges, dev)
+        starts, ends = ranges
+    want_o, want_lse = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                        w.kind, w.scale, w.window, doc, w.softcap,
+                                        key_start=starts, key_end=ends)
+    got_o = o.float().cpu().numpy().astype(np.float64)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    err = np.abs(got_o - want_o)
+    bound = TOL[w.dtype][0] + _half_ulp(want_o, w.dtype)
+    print(f"{w.name}: max |O| {np.abs(want_o).max():.3g} max-abs {err.max():.3g} "
+          f"worst err - bound {(err - bound).max():.3g}", flush=True)
+    assert np.all(err <= bound), f"{w.name}: error above 1e-2 + half an ulp"
+    assert err.mean() <= TOL[w.dtype][1] + _half_ulp(want_o, w.dtype).mean()
+    empty = np.isneginf(want_lse)
+    assert np.array_equal(np.isneginf(got_lse), empty)
+    assert np.all(got_o[empty] == 0.0)
+    if (~empty).any():
+        assert np.abs(got_lse[~empty] - want_lse[~empty]).max() <= TOL[w.dtype][2]
+
+
 def test_key_padding_whole_range_matches_unpadded(dev):
     """Ranges covering every key run the padded kernel with nothing to drop:
     bit-identical to the unpadded kernel."""
