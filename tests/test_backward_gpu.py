@@ -186,3 +186,69 @@ def test_backward_full_size_causal_8192(dev):
     # sum over keys of dK = 0
     sk = dk.double().sum(2).cpu().numpy()
     assert np.abs(sk).max() <= 16 * U["bf16"] * dk.double().abs().sum(2).max().item()
+
+
+def _term_scales(w, q, k, v, dout, o, lse, live):
+    """Magnitude of the terms each gradient element sums (no cancellation):
+    scale sum_j |dS_ij| |k_j| for dq, scale sum_i |dS_ij| |q_i| for dk and
+    sum_i P_ij |dO_i| for dv, with P = exp(s' - lse) from the oracle's
+    logsumexp and dS = P (dP - D) (1 - t^2), D = dO . O from the oracle's O.
+    A scale for the error bound, not a reference value."""
+    G = w.H // w.kv_heads
+    q, k, v, dout = (x.double().numpy() for x in (q, k, v, dout))
+    k, v = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    s = np.einsum("bhie,bhje->bhij", q, k) * w.scale
+    t = np.tanh(s / w.softcap) if w.softcap else np.zeros_like(s)
+    sp = w.softcap * t if w.softcap else s
+    p = np.where(live, np.exp(sp - np.where(np.isneginf(lse), 0.0, lse)[..., None]), 0.0)
+    dp = np.einsum("bhie,bhje->bhij", dout, v)
+    d = (dout * o).sum(-1)[..., None]
+    ds = np.abs(p * (dp - d) * (1.0 - t * t))
+    tq = w.scale * np.einsum("bhij,bhje->bhie", ds, np.abs(k))
+    tk = w.scale * np.einsum("bhij,bhie->bhje", ds, np.abs(q))
+    tv = np.einsum("bhij,bhie->bhje", p, np.abs(dout))
+    return tq, _reduce_kv(w, torch.from_numpy(tk)).numpy(), _reduce_kv(w, torch.from_numpy(tv)).numpy()
+
+
+TWO_KEYS = [
+    # every row keeps keys 613 and 614 only (key range on a single document)
+    (_odd("two_keys_range_bidir_softcap_gqa_bf16", "bf16", 6, 228, 615, wl.MASK_DOCUMENT_BIDIRECTIONAL, 0, (),
+          5.0, H_kv=3), ([613], [615])),
+    # a window of two: each row its own key and the one before
+    (_odd("two_keys_window2_bf16", "bf16", 4, 700, 700, wl.MASK_SLIDING_WINDOW, 2), None),
+]
+
+
+@pytest.mark.parametrize("w,ranges", TWO_KEYS, ids=[c[0].name for c in TWO_KEYS])
+def test_backward_two_key_rows(dev, w, ranges):
+    """Rows with two live keys: each gradient element is a sum of two terms
+    that may cancel, so the mean error is bounded by 2u times the mean of
+    the terms' magnitude (rather than of the result, as elsewhere); the
+    max-abs bound stays 8u of the reference's largest value."""
+    (q, k, v, dout), doc, (dq, dk, dv) = _run(w, dev, None, ranges, seed=18)
+    kwargs = dict(key_start=None if ranges is None else ranges[0], key_end=None if ranges is None else ranges[1])
+    want = oracle.attention_backward(q.double().numpy(), _expand_kv(w, k).double().numpy(),
+                                     _expand_kv(w, v).double().numpy(), dout.double().numpy(), w.kind,
+                                     w.scale, w.window, doc, w.softcap, **kwargs)
+    o, lse = oracle.attention(q.double().numpy(), _expand_kv(w, k).double().numpy(),
+                              _expand_kv(w, v).double().numpy(), w.kind, w.scale, w.window, doc, w.softcap,
+                              **kwargs)
+    i = np.arange(w.L)[:, None]
+    j = np.arange(w.S)[None, :]
+    if ranges is not None:
+        live = (j >= ranges[0][0]) & (j < ranges[1][0]) & np.ones((w.L, 1), bool)
+    else:
+        live = (i >= j) & (i - j < w.window)
+    assert live.sum(1).max() == 2
+    scales = _term_scales(w, q, k, v, dout, o, lse, live[None, None])
+    u = U[w.dtype]
+    for name, g, ref, sc in zip(("dq", "dk", "dv"), (dq, dk, dv),
+                                (want[0], _reduce_kv(w, want[1]), _reduce_kv(w, want[2])), scales):
+        got = g.float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        print(f"{w.name} {name}: max-abs {err.max():.3g} (bound {8 * u * np.abs(ref).max():.3g}), "
+              f"mean-abs {err.mean():.3g} (2u mean |ref| {2 * u * np.abs(ref).mean():.3g}, "
+              f"2u mean terms {2 * u * sc.mean():.3g})", flush=True)
+        assert np.isfinite(got).all()
+        assert err.max() <= 8 * u * np.abs(ref).max(), name
+        assert err.mean() <= 2 * u * sc.mean(), name
