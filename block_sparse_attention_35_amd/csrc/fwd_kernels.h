@@ -1369,48 +1369,73 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdArgs a) {
 // O = sum w_c O_c / sum w_c l_c (0 when the sum is 0) and lse = (max m + log2
 // sum w_c l_c) ln 2, the sums taken in chunk order, each product rounded
 // before it is added. Both forms below give the same bits.
-static_assert(kKvSplitMax <= 64, "one lane per chunk in merge_row");
-constexpr int kMergeRows = kThreads / 64;  // output rows per merge_row workgroup (one per wave)
+static_assert(kKvSplitMax <= 64, "four chunks per lane in merge_row");
+constexpr int kMergeRows = kThreads / 16;  // output rows per merge_row workgroup (16 lanes each)
 
-// One wave per row, lane e holding head dim e (the split-KV merge: many rows,
-// a few chunks each). Lane c reads chunk c's m and l, and the row's O values
-// of the first 16 chunks are read in the same round (later ones 16 at a
-// time); no fused multiply-adds are formed.
+// Sixteen lanes per row, four rows per wave (the split-KV merge: many rows, a
+// few chunks each): lane e of a row's group holds head dims 4e .. 4e + 3 and
+// reads them with one 16-byte load per chunk; lane c reads the m and l of
+// chunks c, c + 16, c + 32 and c + 48 in the same round as the O values of the
+// first 16 chunks (later ones 16 at a time). The weights reach the group's
+// lanes by shuffles; no fused multiply-adds are formed.
 template <typename T>
 __device__ inline void merge_row(const float* slot0, int64_t cstride, int o_off, int m_off, int l_off, int k,
                                  int lane, T* out, float* lse) {
 #pragma clang fp contract(off)
-  float o[16];
+  const int e = lane & 15, base = lane & ~15;
+  float4 o[16];
   auto load_o = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[j] = (c0 + j < k) ? slot0[(int64_t)(c0 + j) * cstride + o_off + lane] : 0.0f;
+    for (int j = 0; j < 16; ++j)
+      o[j] = (c0 + j < k) ? *reinterpret_cast<const float4*>(slot0 + (int64_t)(c0 + j) * cstride + o_off + 4 * e)
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   };
-  // the first 16 chunks' values are read in the same round as m and l
   load_o(0);
-  const float* mine = slot0 + (int64_t)min(lane, k - 1) * cstride;
-  const float mc = lane < k ? mine[m_off] : -INFINITY;
-  const float lc = lane < k ? mine[l_off] : 0.0f;
-  float mmax = mc;
+  float mc[4], lc[4];
+  float mmax = -INFINITY;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
-  const float wc = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - mmax);
-  const float wlc = wc * lc;
-  float acc = 0.0f, lsum = 0.0f;
+  for (int t = 0; t < 4; ++t) {
+    const int c = e + 16 * t;
+    mc[t] = c < k ? slot0[(int64_t)c * cstride + m_off] : -INFINITY;
+    lc[t] = c < k ? slot0[(int64_t)c * cstride + l_off] : 0.0f;
+    mmax = fmaxf(mmax, mc[t]);
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+  float wc[4], wlc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    wc[t] = (mc[t] == -INFINITY) ? 0.0f : fast_exp2(mc[t] - mmax);
+    wlc[t] = wc[t] * lc[t];
+  }
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float lsum = 0.0f;
   for (int c0 = 0; c0 < k; c0 += 16) {
     if (c0 > 0) load_o(c0);
+    const int t = c0 >> 4;
+    const float wt = t == 0 ? wc[0] : t == 1 ? wc[1] : t == 2 ? wc[2] : wc[3];
+    const float wlt = t == 0 ? wlc[0] : t == 1 ? wlc[1] : t == 2 ? wlc[2] : wlc[3];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (c0 + j < k) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), c0 + j));
-        const float wl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlc), c0 + j));
-        acc = acc + w * o[j];
+        const float w = __shfl(wt, base + j);
+        const float wl = __shfl(wlt, base + j);
+        acc.x = acc.x + w * o[j].x;
+        acc.y = acc.y + w * o[j].y;
+        acc.z = acc.z + w * o[j].z;
+        acc.w = acc.w + w * o[j].w;
         lsum = lsum + wl;
       }
     }
   }
   const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
-  out[lane] = (T)(acc * inv);
-  if (lse != nullptr && lane == 0) *lse = (lsum > 0.0f) ? (mmax + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+  typename Vec<T>::x4 ov;
+  ov[0] = (T)(acc.x * inv);
+  ov[1] = (T)(acc.y * inv);
+  ov[2] = (T)(acc.z * inv);
+  ov[3] = (T)(acc.w * inv);
+  *reinterpret_cast<typename Vec<T>::x4*>(out + 4 * e) = ov;
+  if (lse != nullptr && e == 0) *lse = (lsum > 0.0f) ? (mmax + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
 }
 
 // One workgroup per row (the packed decode merge: few rows, more chunks):
@@ -1461,12 +1486,12 @@ __device__ inline void merge_row_block(const float* slot0, int64_t cstride, int 
   }
 }
 
-// Merge of split-KV chunks: one wave per output row, rows ordered query row
-// first, then batch*head, so the waves of a workgroup read neighbouring rows
-// of the same slots; slots are [qb][chunk][B*H].
+// Merge of split-KV chunks: sixteen lanes per output row, rows ordered query
+// row first, then batch*head, so a workgroup reads neighbouring rows of the
+// same slots; slots are [qb][chunk][B*H].
 template <typename T>
 __global__ __launch_bounds__(kThreads) void kv_merge_kernel(FwdArgs a) {
-  const int64_t gr = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);
+  const int64_t gr = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 4);
   const int lane = threadIdx.x & 63;
   const int BH = a.B * a.H;
   if (gr >= (int64_t)BH * a.L) return;
