@@ -616,7 +616,9 @@ __device__ __forceinline__ void fwd_block(const KSt& kst, const lds_u8 (&kp)[4],
 
   // Lazy rescale (wave-uniform branch).
   const bool grow = m_blk > m_ref + kRescaleLog2;
-  if (__ballot(grow) != 0) {
+  // (Before a row's first live key, m_ref = -inf and the accumulators are
+  // zero: nothing to rescale, as at every item's first block.)
+  if (__ballot(grow && m_ref != -INFINITY) != 0) {
     const float alpha = grow ? fast_exp2(m_ref - m_blk) : 1.0f;
     l *= alpha;
 #pragma unroll
@@ -1678,7 +1680,7 @@ __global__ __launch_bounds__(kThreads, 2) void packed_kernel(FwdArgs a) {
     mx = half_max(mx);
     const float m_blk = SOFTCAP ? mx : mx * c1;
     const bool grow = m_blk > m_ref + kRescaleLog2;
-    if (__ballot(grow) != 0) {
+    if (__ballot(grow && m_ref != -INFINITY) != 0) {
       const float alpha = grow ? fast_exp2(m_ref - m_blk) : 1.0f;
       l *= alpha;
 #pragma unroll
