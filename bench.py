@@ -384,7 +384,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path runs on a single MI355X; see the sharding note in the design)",
+              "(the path runs on a single MI355X; heads are independent, so several GPUs "
+              "would each take a share of the heads with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
