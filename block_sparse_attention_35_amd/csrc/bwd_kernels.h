@@ -405,6 +405,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const lds_u8 qt_base = (lds_u8)s.q, dt_base = (lds_u8)s.dout;
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
+      // Sliding windows: a query tile of a partial block whose rule
+      // positions all lie before this wave's keys, or all a window or more
+      // past them, has no live pair; its MFMAs and vector work are skipped
+      // (wave-uniform; its P and dS would be 0).
+      if (KIND == ATTN_MASK_SLIDING_WINDOW && partial) {
+        const int p0 = q0 + 32 * qt + f.m.q_off, j0 = kv0 + 32 * wave;
+        if (p0 + 31 < j0 || p0 - (j0 + 31) >= f.m.window) continue;
+      }
       f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -596,6 +604,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const lds_u8 kt_base = (lds_u8)s.k, vt_base = (lds_u8)s.v;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      // Sliding windows: a key tile that every row of this wave sees as
+      // after its position, or a window or more behind it, is skipped
+      // (wave-uniform; its dS would be 0).
+      if (KIND == ATTN_MASK_SLIDING_WINDOW && PARTIAL) {
+        const int p0 = q0 + 32 * wave + f.m.q_off, j0 = kv0 + 32 * t;
+        if (p0 + 31 < j0 || p0 - (j0 + 31) >= f.m.window) continue;
+      }
       f32x16_t sacc = {}, dpacc = {};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {

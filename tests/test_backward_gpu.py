@@ -112,6 +112,14 @@ CASES = [
     (_odd("split_gqa_xcd_order_B2_h8_kv2_2304_bf16", "bf16", 8, 2304, 2304, wl.MASK_CAUSAL, B=2, H_kv=2),
      None, None),
     (_odd("split_padded_none_2560_bf16", "bf16", 1, 2560, 2560, wl.MASK_NONE, B=2), None, ([100, 0], [2560, 2200])),
+    # sliding windows skip the query tiles (dK/dV) and key tiles (dQ) of a
+    # partial block that no pair reaches: with a query offset, with key
+    # ranges, and with windows not a multiple of the tile
+    (_odd("sliding_lr_L300_S1000_w100_bf16", "bf16", 2, 300, 1000, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT, 100),
+     None, None),
+    (_odd("sliding_padded_w150_f16", "f16", 2, 900, 900, wl.MASK_SLIDING_WINDOW, 150, B=2), None,
+     ([0, 300], [900, 517])),
+    (_odd("sliding_w256_2304_gqa_bf16", "bf16", 4, 2304, 2304, wl.MASK_SLIDING_WINDOW, 256, H_kv=2), None, None),
     # fp32 (fp32 MFMA, probabilities and dS unrounded)
     (wl.WORKLOADS["causal_256_f32"], None, None),
     (_odd("sliding_softcap_700_f32", "f32", 2, 700, 700, wl.MASK_SLIDING_WINDOW, 150, (), 30.0), None, None),
