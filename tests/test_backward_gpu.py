@@ -260,3 +260,28 @@ def test_backward_two_key_rows(dev, w, ranges):
         assert np.isfinite(got).all()
         assert err.max() <= 8 * u * np.abs(ref).max(), name
         assert err.mean() <= 2 * u * sc.mean(), name
+
+
+def test_backward_one_key(dev):
+    """One key (S = 1): P = 1 and O = V exactly, so dP - D = dO . (V - O) and
+    with it dq and dk vanish; the kernel forms dP (MFMA) and D (the prep
+    kernel) as two fp32 sums of the 64 exact products dO_e v_e, so dS is
+    their rounding difference, at most 2 * 64 * 2^-24 sum_e |dO_e v_e| <=
+    2^-16 sum_e |dO_e v_e| (with the soft-cap factor <= 1), and dq, dk are
+    bounded through it; dv = sum_i dO_i keeps the usual bounds."""
+    w = _odd("one_key_S1_softcap_bf16", "bf16", 3, 645, 1, wl.MASK_NONE, 0, (), 5.0, B=2)
+    (q, k, v, dout), doc, (dq, dk, dv) = _run(w, dev, None, None, seed=74)
+    want = oracle.attention_backward(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     dout.double().numpy(), w.kind, w.scale, w.window, doc, w.softcap)
+    qn, kn, vn, dn = (x.double().numpy() for x in (q, k, v, dout))
+    ds_bound = 2.0 ** -16 * np.abs(dn * vn).sum(-1)  # [B, H, L]: |fl(dP) - fl(D)| per row
+    dq_bound = w.scale * ds_bound[..., None] * np.abs(kn)  # the single key's row
+    dk_bound = w.scale * (ds_bound[..., None] * np.abs(qn)).sum(2, keepdims=True)
+    got_dq = dq.float().cpu().numpy().astype(np.float64)
+    got_dk = dk.float().cpu().numpy().astype(np.float64)
+    print(f"one key: dq max {np.abs(got_dq).max():.3g} (bound {dq_bound.max():.3g}), "
+          f"dk max {np.abs(got_dk).max():.3g} (bound {dk_bound.max():.3g})", flush=True)
+    assert np.abs(want[0]).max() < 1e-12 and np.abs(want[1]).max() < 1e-12
+    assert np.all(np.abs(got_dq) <= dq_bound * (1 + 2.0 ** -8) + 1e-30)
+    assert np.all(np.abs(got_dk) <= dk_bound * (1 + 2.0 ** -8) + 1e-30)
+    _compare(w, dv, want[2], "one key dv")
