@@ -244,6 +244,11 @@ SMALL = [
     # B*H a multiple of 8 with grouped heads (the XCD head order) and split
     # query blocks merging by their (batch, head) slot
     _odd("gqa_causal_split_B2_h8_kv2_2304_bf16", "bf16", 8, 2304, 2304, wl.MASK_CAUSAL, B=2).with_(H_kv=2),
+    # fp32 at the decode and many-block shapes (fp32 never splits, packs or
+    # chains: one item per query block), and with no keys
+    _odd("decode_gqa_L1_S3000_lr_f32", "f32", 8, 1, 3000, wl.MASK_CAUSAL_LOWER_RIGHT).with_(H_kv=2),
+    _odd("sliding_w100_2500_h4_ragged_f32", "f32", 4, 2500, 2500, wl.MASK_SLIDING_WINDOW, 100),
+    _odd("none_zero_kv_f32", "f32", 1, 130, 0, wl.MASK_NONE),
 ]
 
 
