@@ -197,6 +197,44 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, dev, use_graph: bool =
     return dict(wall_ms=wall_ms, mask_ms=mask_ms, fwd_ms=fwd_ms, timing=timing)
 
 
+_KIND_LABEL = {wl.MASK_NONE: "none", wl.MASK_CAUSAL: "causal", wl.MASK_SLIDING_WINDOW: "sliding_window",
+               wl.MASK_DOCUMENT: "document", wl.MASK_CAUSAL_LOWER_RIGHT: "causal_lower_right",
+               wl.MASK_SLIDING_WINDOW_LOWER_RIGHT: "sliding_window_lower_right",
+               wl.MASK_DOCUMENT_BIDIRECTIONAL: "document_bidirectional", wl.MASK_CUSTOM: "custom"}
+
+
+def forward_kernel_label(w: wl.Workload) -> str:
+    """The forward kernel a workload's launch runs, as a kernel trace names it:
+    fp32 has its own kernel; at most 32 query rows per K/V head (L times the
+    heads sharing it) run packed; sliding windows of at most 15 blocks with at
+    least 1024 work items (B*H*query blocks) run the chained form."""
+    kind = _KIND_LABEL[w.kind]
+    if w.dtype == "f32":
+        return f"fwd32_kernel<{kind}>"
+    if w.L >= 1 and w.L * (w.H // (w.H_kv or w.H)) <= 32:
+        return f"packed_kernel<{w.dtype}, {kind}>"
+    chained = (w.kind in (wl.MASK_SLIDING_WINDOW, wl.MASK_SLIDING_WINDOW_LOWER_RIGHT)
+               and w.window <= 15 * 128 and w.B * w.H * -(-w.L // 128) >= 1024)
+    return f"{'fwd16_chain_kernel' if chained else 'fwd16_kernel'}<{w.dtype}, {kind}>"
+
+
+def roofline(w: wl.Workload, r, traffic):
+    """Roofline of the workload's forward kernel: matrix-bound (against the
+    MFMA peak of its dtype) when its live flops per algorithmic byte reach the
+    peak's flops per byte of HBM bandwidth, else bandwidth-bound."""
+    peak_flops = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    out = {"kernel": forward_kernel_label(w), "launch_ms": r["forward_ms"]["mean"]}
+    if r["live_gflop"] * 1e9 / r["algorithmic_bytes"] >= peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9):
+        out.update(bound="mfma", achieved=r["forward_tflops"], peak=peak_flops, unit="TFLOP/s",
+                   frac=r["forward_tflops"] / peak_flops, per_launch_flop=r["live_gflop"] * 1e9)
+    else:
+        out.update(bound="hbm", achieved=r["forward_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                   frac=r["forward_gbs"] / PEAK_HBM_GBS, per_launch_bytes=r["algorithmic_bytes"])
+    out["traffic"] = traffic
+    return {k: out[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                "per_launch_flop", "per_launch_bytes", "launch_ms") if k in out}
+
+
 def run_backward(w: wl.Workload, steps: int, warmup: int, dev):
     """Per-call time of the backward (attn_backward: D and the transposed mask,
     then the dK/dV and dQ kernels) after one forward, in batches of back-to-back
@@ -429,21 +467,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) q/k/v rounded to the workload dtype",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "S": w.S, "E": w.E,
-                   "mask": "causal", "block": 128, "scale": w.scale},
+                   "mask": _KIND_LABEL[w.kind], "block": 128, "scale": w.scale},
         "frac_bf16_peak": head["step_tflops"] / PEAK_BF16_TFLOPS,
         "forward_only": {"ms": head["forward_ms"], "tflops": head["forward_tflops"],
                          "frac_bf16_peak": head["forward_frac_bf16_peak"]},
         "mask_build_ms": head["mask_build_ms"],
-        "roofline": {"bound": "mfma", "achieved": head["forward_tflops"],
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": head["forward_tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(names[0]),
-                     "kernel": "fwd16_kernel<bf16, causal>",
-                     "per_launch_flop": head["live_gflop"] * 1e9,
-                     "launch_ms": head["forward_ms"]["mean"]},
+        "roofline": roofline(w, head, measured_traffic(names[0])),
         "workloads": results,
         "backward": backward,
     }
@@ -453,7 +485,8 @@ def main():
             "forward_ms": s["forward_ms"], "tflops": s["forward_tflops"],
             "frac_bf16_peak": s["forward_frac_bf16_peak"], "gbs": s["forward_gbs"],
             "frac_hbm_peak": s["forward_gbs"] / PEAK_HBM_GBS, "step_ms": s["ms_per_step"],
-            "traffic": measured_traffic(SECOND)}
+            "traffic": measured_traffic(SECOND),
+            "roofline": roofline(wl.WORKLOADS[SECOND], s, measured_traffic(SECOND))}
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_budget)
