@@ -175,25 +175,34 @@ def test_backward_workspace_shared_by_shapes(dev):
         assert all(torch.equal(a, b) for a, b in zip(g1, g2)), w.name
 
 
-def test_backward_full_size_causal_8192(dev):
-    """The benchmark's backward shape: dq on sampled rows against the oracle;
-    dk and dv through the exact identities; everything finite."""
-    w = wl.WORKLOADS["causal_8192_bf16"]
-    (q, k, v, dout), _, (dq, dk, dv) = _run(w, dev)
+FULL_SIZE = ["causal_8192_bf16", "sliding_32768_w256_bf16", "document_8192_f16_softcap"]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_backward_full_size(dev, name):
+    """The benchmark's shapes: dq on sampled rows against the oracle; dk and
+    dv through exact identities (every row of these workloads has a live
+    key); everything finite."""
+    w = wl.WORKLOADS[name]
+    (q, k, v, dout), doc, (dq, dk, dv) = _run(w, dev)
     rows = wl.sample_rows(w, 48)
     want = oracle.attention_backward_dq_rows(q.double().numpy(), k.double().numpy(), v.double().numpy(),
-                                             dout.double().numpy(), w.kind, w.scale, rows)
+                                             dout.double().numpy(), w.kind, w.scale, rows, w.window, doc,
+                                             w.softcap)
     got = dq.reshape(-1, w.E)[torch.from_numpy(rows).to(dev)]
     _compare(w, got, want, "dq rows")
     for g in (dq, dk, dv):
         assert torch.isfinite(g).all()
-    # sum over keys of dV = sum over rows of dO (every causal row has a live key)
+    u = U[w.dtype]
+    # sum over keys of dV = sum over rows of dO
     sv = dv.double().sum(2).cpu().numpy()
     so = dout.double().sum(2).numpy()
-    assert np.abs(sv - so).max() <= 16 * U["bf16"] * np.abs(dout.double().numpy()).sum(2).max()
-    # sum over keys of dK = 0
-    sk = dk.double().sum(2).cpu().numpy()
-    assert np.abs(sk).max() <= 16 * U["bf16"] * dk.double().abs().sum(2).max().item()
+    assert np.abs(sv - so).max() <= 16 * u * np.abs(dout.double().numpy()).sum(2).max()
+    # sum over keys of dK = scale sum_i q_i sum_j dS_ij = 0 without the
+    # soft-cap (each row of dS sums to zero; the cap weights it by 1 - t^2)
+    if not w.softcap:
+        sk = dk.double().sum(2).cpu().numpy()
+        assert np.abs(sk).max() <= 16 * u * dk.double().abs().sum(2).max().item()
 
 
 def _term_scales(w, q, k, v, dout, o, lse, live):
